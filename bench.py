@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of the Local-Hessian NVFP4 calibration hot path on one MI355X.
+
+One step = the whole path over one layer's synthetic inputs, inputs resident
+in HBM: global amax -> local Hessians -> 126-candidate scale sweep ->
+NVFP4 fake-quant (dequantised fp32 weights + packed E2M1 nibbles + E4M3
+scale codes).  W warm-up steps, then K timed steps between device
+synchronisations; every kernel is also timed with HIP events recorded on the
+stream it is launched on (the current torch stream, which the binding
+passes to the library).
+
+Prints ONE JSON line.  value = NVFP4 blocks scale-swept per second over the
+whole step; the line also carries the Hessian pass in GB/s, the sweep in
+blocks/s and TFLOP/s, the roofline of the dominant kernel (the sweep) and
+the CPU oracle's rate on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 blocks/s scale-swept (126 cand) + Hessian-accum GB/s, % roofline"
+HBM_PEAK_GBPS = 8000.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3       # MI355X published fp32 vector peak (packed)
+FP32_NONPACKED_TFLOPS = 78.6          # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
+SWEEP_FLOP_PER_BLOCK = 126 * (16 * 16 + 16) * 2   # 68,544: dense dw^T H dw per candidate
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=2, help="named workload 1..5 (default: dense-4096)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "nvfp4_scale_calibration_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, workload: str, src_hash: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries
+    (FETCH_SIZE + WRITE_SIZE, copy-kernel calibrated); None when absent or
+    taken on other kernel sources."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get("%s/%s" % (kernel, workload))
+    if not ent or ent.get("source_hash") != src_hash:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(work, budget_s: float) -> dict:
+    """The oracle as it stands, on host cores, on a bounded sample: Hessians
+    of a few input blocks and the sweep + fake-quant of the first rows; the
+    per-unit costs are scaled to the whole step of the workload."""
+    import numpy as np
+    import lh_workloads as wl
+    import oracle
+
+    G, c_out, c_in, n = work.n_groups, work.c_out, work.c_in, work.n_tok
+    nb = c_in // 16
+    w_np, x_np = wl.np_bits(work.w), wl.np_bits(work.x)
+    threads = oracle.num_threads()
+    t0 = time.perf_counter()
+    amax = oracle.absmax(w_np, c_out, c_in, n_groups=G)
+    t_amax = time.perf_counter() - t0
+    # Hessian: grow the sample until it costs ~15% of the budget
+    hs = max(1, threads)
+    while True:
+        sel = np.arange(min(hs, G * nb), dtype=np.int64)
+        t0 = time.perf_counter()
+        _, h32s = oracle.hessian(x_np, c_in, n, n_groups=G, sel=sel)
+        th = time.perf_counter() - t0
+        if th > 0.15 * budget_s or len(sel) >= G * nb:
+            break
+        hs *= 4
+    t_hess_total = th / len(sel) * (G * nb)
+    h_full = np.zeros((G * nb, 16, 16), np.float32)
+    h_full[: len(sel)] = h32s
+    h_full[len(sel):] = np.eye(16, dtype=np.float32)  # blocks outside the sample: any valid H
+    # sweep + fake-quant on the first rows of group 0 (blocks b < len(sel) use the oracle's H)
+    nsw = max(threads * 8, 64)
+    while True:
+        ssel = np.arange(min(nsw, G * c_out * nb), dtype=np.int64)
+        t0 = time.perf_counter()
+        res = oracle.sweep(w_np, h_full, amax, c_out, c_in, n_groups=G, sel=ssel)
+        idx_full = np.zeros(G * c_out * nb, np.uint8)
+        idx_full[ssel] = res["idx"].astype(np.uint8)
+        oracle.fake_quant(w_np, idx_full, amax, c_out, c_in, n_groups=G, sel=ssel)
+        ts = time.perf_counter() - t0
+        if ts > 0.6 * budget_s or len(ssel) >= G * c_out * nb:
+            break
+        nsw *= 4
+    blocks = G * c_out * nb
+    step_s = t_amax + t_hess_total + ts / len(ssel) * blocks
+    return {
+        "value": blocks / step_s, "unit": "blocks/s", "cores": threads, "kind": "oracle",
+        "sample": "Hessians of %d of %d input blocks (all %d tokens) + sweep and fake-quant of the first %d of "
+                  "%d blocks, per-unit times scaled to the whole step; global amax over the full tensor"
+                  % (len(sel), G * nb, n, len(ssel), blocks),
+        "hessian_gbps": work.x_bytes / t_hess_total / 1e9,
+        "sweep_blocks_per_s": len(ssel) / ts,
+        "est_step_s": step_s,
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (asked for %d)." % max(args.gpus, world),
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import lh_workloads as wl
+    import nvfp4_scale_calibration_amd as lh
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    work = wl.make(args.workload)
+    G, c_out, c_in, n = work.n_groups, work.c_out, work.c_in, work.n_tok
+    nb = c_in // 16
+    blocks = work.n_blocks
+    w = work.w.to(dev)
+    x = work.x.to(dev)
+    amax = torch.empty(G, dtype=torch.float32, device=dev)
+    h = torch.empty((G, nb, 16, 16), dtype=torch.float32, device=dev)
+    ws_bytes = lh.lh_hessian_workspace_bytes(c_in, n, G)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    idx = torch.empty((G, c_out, nb), dtype=torch.uint8, device=dev)
+    err = torch.empty((G, c_out, nb), dtype=torch.float32, device=dev)
+    bam = torch.empty((G, c_out, nb), dtype=torch.float32, device=dev)
+    wq = torch.empty((G, c_out, c_in), dtype=torch.float32, device=dev)
+    packed = torch.empty((G, c_out, c_in // 2), dtype=torch.uint8, device=dev)
+    codes = torch.empty((G, c_out, nb), dtype=torch.uint8, device=dev)
+    gscale = torch.empty(G, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    names = ("absmax", "hessian", "sweep", "fake_quant")
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        lh.lh_absmax(w, out=amax)
+        mark(1)
+        lh.lh_accumulate_hessian(x, h=h, workspace=ws if ws_bytes else None)
+        mark(2)
+        lh.lh_scale_sweep(w, h, amax, best_idx=idx, best_err=err, best_amax=bam)
+        mark(3)
+        lh.lh_fake_quant_nvfp4(w, idx, amax, w_q=wq, packed=packed, scale_e4m3=codes, global_scale=gscale)
+        mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_kernel_ms = {nm: sum(e[i].elapsed_time(e[i + 1]) for e in events) / args.steps for i, nm in enumerate(names)}
+    ms_per_step = wall * 1e3 / args.steps
+    sweep_s = per_kernel_ms["sweep"] / 1e3
+    hess_s = per_kernel_ms["hessian"] / 1e3
+    achieved_tflops = SWEEP_FLOP_PER_BLOCK * blocks / sweep_s / 1e12
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profiles("sweep", wl.SHORT_NAMES[args.workload], src_hash)
+    out = {
+        "metric": METRIC,
+        "value": blocks / (ms_per_step / 1e3),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": work.description, "name": wl.SHORT_NAMES[args.workload], "n_groups": G,
+                   "c_out": c_out, "c_in": c_in, "n_tokens": n, "blocks": blocks, "storage": work.dtype},
+        "roofline": {"bound": "alu", "achieved": achieved_tflops, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": traffic},
+        "kernels_ms": per_kernel_ms,
+        "sweep": {"blocks_per_s": blocks / sweep_s, "tflops": achieved_tflops,
+                  "frac_nonpacked_fp32": achieved_tflops / FP32_NONPACKED_TFLOPS},
+        "hessian": {"gbps": work.x_bytes / hess_s / 1e9, "frac_hbm": work.x_bytes / hess_s / 1e9 / HBM_PEAK_GBPS,
+                    "x_bytes": work.x_bytes, "warm": True},
+        "source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(work, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

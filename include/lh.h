@@ -1,0 +1,197 @@
+/*
+ * lh.h - C ABI of the Local-Hessian NVFP4 weight-scale calibration library
+ *        (liblh.so, HIP kernels for AMD Instinct MI355X / gfx950).
+ *
+ * The method (pages cited by title and section):
+ *   "Local-Hessian weight-scale guide" (xxmr.cn/news/266017)
+ *     - "What is Local-Hessian": NVFP4 stores FP4 E2M1 values, 16 weights
+ *       share one FP8 E4M3 block scale, a block scale maps the block into
+ *       the E2M1 range [-6, 6]; the scale sweep tries all 126 positive
+ *       non-zero FP8 values.
+ *     - "Algorithm principle": linear layer Y = W X with W [C_out x C_in]
+ *       and calibration input X [C_in x N]; Q(W, s) = Cast(W / s) * s,
+ *       Delta = Q - W; output error E(s) = ||Delta X||_F^2 =
+ *       tr(Delta X X^T Delta^T); block-diagonal approximation per 16-weight
+ *       block b: E_b(s_b) = Delta_b (X_b X_b^T) Delta_b^T; the sweep kernel
+ *       takes weights [N_BLOCKS, 16] in (cout, cin // 16) order, the global
+ *       FP32 amax and per-block Hessians [cin // 16, 16, 16], minimises
+ *       dw^T H dw over the 126 E4M3 candidates and outputs the per-block
+ *       best amax; candidate generation is bit-consistent with fake-quant.
+ *     - "Entry API and calibration flow", phase 2: H accumulates the sum of
+ *       X^T X over calibration batches; phase 3 passes the normalised
+ *       per-block Hessian to the search.
+ *     - "Combining with GPTQ": the cast rounds to nearest (RTN).
+ *   "ModelOpt overview" (linlog.top/article/1517), "Local-Hessian": 126
+ *     candidate scales per block, each block optimised independently.
+ *
+ * Readings taken where the pages leave a step open:
+ *   - candidates: the 126 positive finite OCP E4M3FN values (codes
+ *     0x01..0x7E, max 448); candidate index k <-> E4M3 code k + 1;
+ *   - S_g = fl32(g / 2688) (2688 = 6 * 448), s_k = fl32(c_k * S_g);
+ *   - Cast: x = fl32(|w| / s_k) (IEEE division), nearest E2M1 magnitude
+ *     {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even code, saturation at 6;
+ *     Q = fl32(sign(w) * r * s_k), -0 written as +0; s_k = 0 gives Q = 0;
+ *   - "normalised" = divided by the token count N (alpha = 1 / N);
+ *   - equal errors resolve to the lowest candidate index.
+ *
+ * Conventions for every entry point:
+ *   - all data pointers are DEVICE pointers (hipMalloc'd or a framework's
+ *     device tensor); the caller owns and frees every buffer;
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream);
+ *     every call only enqueues work on it and returns; the library never
+ *     synchronises the device, never allocates, keeps no state between
+ *     calls and is safe to call from several host threads;
+ *   - arguments are validated on the host before anything is launched; a
+ *     non-zero lh_status means nothing was enqueued (LH_ERR_HIP: a launch
+ *     failed; lh_last_error_message() holds the HIP error text);
+ *   - sizes are element counts; strides / leading dimensions are in
+ *     elements of the buffer's own dtype;
+ *   - empty problems (a zero size) are valid and enqueue nothing, except the
+ *     Hessian with n_tokens = 0, which still applies h = beta * h;
+ *   - non-finite inputs give unspecified (but memory-safe) results.
+ */
+#ifndef LH_H
+#define LH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lh_status {
+    LH_OK = 0,
+    LH_ERR_NULL = 1,      /* a required pointer is NULL                      */
+    LH_ERR_SHAPE = 2,     /* negative size, c_in % 16 != 0, ld / stride too small */
+    LH_ERR_DTYPE = 3,     /* unknown dtype code                               */
+    LH_ERR_LAYOUT = 4,    /* unknown layout code                              */
+    LH_ERR_WORKSPACE = 5, /* workspace non-empty but smaller than required    */
+    LH_ERR_ARG = 6,       /* other invalid argument (e.g. no output requested) */
+    LH_ERR_HIP = 7        /* a HIP launch failed (see lh_last_error_message)  */
+} lh_status;
+
+typedef enum lh_dtype {
+    LH_DTYPE_F32 = 0,  /* IEEE binary32                                       */
+    LH_DTYPE_BF16 = 1  /* bfloat16 (upper half of binary32), RNE-rounded data */
+} lh_dtype;
+
+typedef enum lh_layout {
+    LH_LAYOUT_CHANNEL_MAJOR = 0, /* x[c * ld_x + t]: X as [C_in][N] (the pages' X) */
+    LH_LAYOUT_TOKEN_MAJOR = 1    /* x[t * ld_x + c]: X^T as [N][C_in] (hooked activations) */
+} lh_layout;
+
+/* Library ABI version (this header describes version 1). */
+int lh_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *lh_status_string(int status);
+
+/* Message of the last failing call on this host thread ("" if none). */
+const char *lh_last_error_message(void);
+
+/*
+ * Global amax per group:  amax[g] = max |w[g][r][c]| over r < rows, c < cols.
+ * The per-tensor FP32 amax the sweep derives its candidates from ("Algorithm
+ * principle": the kernel receives the global FP32 amax).
+ *   w        [n_groups] x [rows][ld_w] elements of w_dtype, group stride
+ *            group_stride_w (>= 0).
+ *   amax     [n_groups] fp32, written (device).
+ * ld_w >= cols.  rows, cols, n_groups >= 0 (rows * cols == 0 writes 0).
+ * Result is exact (a max), independent of launch shape.
+ */
+lh_status lh_absmax(const void *w, int w_dtype, int64_t rows, int64_t cols, int64_t ld_w,
+                    int64_t n_groups, int64_t group_stride_w, float *amax, void *stream);
+
+/*
+ * Scratch bytes that let lh_accumulate_hessian split the token dimension of
+ * each block over several workgroups and reduce the partial sums in a fixed
+ * order (deterministic).  0 bytes is always accepted (one workgroup per
+ * block); the value depends only on the three sizes.
+ */
+size_t lh_hessian_workspace_bytes(int64_t c_in, int64_t n_tokens, int64_t n_groups);
+
+/*
+ * Local-Hessian accumulation ("Algorithm principle": local Hessian
+ * X_b X_b^T, 16 x 16 per input block; "Entry API and calibration flow",
+ * phase 2: H is the sum of X^T X, normalised before the search):
+ *
+ *   h[g][b][i][j] = beta * h[g][b][i][j]
+ *                 + alpha * sum_{t < n_tokens} X[g][16b+i][t] * X[g][16b+j][t]
+ *
+ * for every group g < n_groups, input block b < c_in / 16, 0 <= i, j < 16.
+ * alpha = 1/n_tokens, beta = 0 gives the normalised one-shot Hessian;
+ * alpha = 1, beta = 1 streams further token chunks into h.  beta == 0 never
+ * reads h (so h may be uninitialised).  Products are exact (bf16 x bf16 or
+ * fp32 x fp32 on matrix cores), sums are fp32.
+ *   x        activations, x_dtype, `layout` (see lh_layout), leading
+ *            dimension ld_x (channel-major: >= n_tokens; token-major:
+ *            >= c_in), group stride group_stride_x (>= 0).
+ *   h        [n_groups][c_in/16][16][16] fp32, group stride group_stride_h
+ *            (>= (c_in/16)*256 when n_groups > 1), read (beta != 0) and written.
+ *   workspace, workspace_bytes: NULL/0, or a device buffer of at least
+ *            lh_hessian_workspace_bytes(c_in, n_tokens, n_groups) bytes,
+ *            256-byte aligned; contents on entry are ignored.
+ * c_in % 16 == 0.  Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_DTYPE,
+ * LH_ERR_LAYOUT, LH_ERR_WORKSPACE, LH_ERR_HIP.
+ */
+lh_status lh_accumulate_hessian(const void *x, int x_dtype, int layout, int64_t c_in,
+                                int64_t n_tokens, int64_t ld_x, int64_t n_groups,
+                                int64_t group_stride_x, float alpha, float beta, float *h,
+                                int64_t group_stride_h, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/*
+ * Local-Hessian scale sweep ("Algorithm principle": per 16-weight block,
+ * all 126 FP8 E4M3 candidate scales derived from the global FP32 amax,
+ * minimise dw^T H_b dw with dw = Q(w, s) - w; "ModelOpt overview",
+ * "Local-Hessian": blocks are independent).
+ *
+ * For every group g, output row r < c_out and input block b < c_in/16, with
+ * w_b = w[g][r][16b .. 16b+15], H_b = h[g][b] and global amax amax[g]:
+ *   k*  = the lowest k in [0, 125] minimising E_k = dw_k^T H_b dw_k
+ *   best_idx [g][r][b] = k*              (E4M3 block-scale code = k* + 1)
+ *   best_err [g][r][b] = E_k* (fp32)     (optional)
+ *   best_amax[g][r][b] = fl32(6 * s_k*)  (optional; the per-block amax)
+ *   w         weights, w_dtype, row stride ld_w >= c_in, group stride
+ *             group_stride_w (>= 0).
+ *   h         fp32 [n_groups][c_in/16][16][16] (any square matrix is used as
+ *             given; the Hessian output of lh_accumulate_hessian fits),
+ *             group stride group_stride_h (>= 0).
+ *   amax      fp32 [n_groups] (device), e.g. from lh_absmax.
+ *   best_idx  uint8 [n_groups][c_out][c_in/16], required.
+ *   best_err, best_amax  fp32, same shape, NULL to skip.
+ * Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_HIP.
+ */
+lh_status lh_scale_sweep(const void *w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
+                         int64_t n_groups, int64_t group_stride_w, const float *h,
+                         int64_t group_stride_h, const float *amax, uint8_t *best_idx,
+                         float *best_err, float *best_amax, void *stream);
+
+/*
+ * NVFP4 fake-quant with chosen block scales ("Algorithm principle":
+ * Q(W, s) = Cast(W / s) * s; the candidate scales match the sweep bit for
+ * bit; "What is Local-Hessian": two-level format = E2M1 values, E4M3 block
+ * scale, FP32 per-tensor scale).  For every weight of block (g, r, b) with
+ * s = s_{best_idx[g][r][b]}:
+ *   w_q[g][r][c]               = Q(w, s) (fp32, exactly the Q of the sweep)
+ *   packed_e2m1[g][r][c/2]     = E2M1 nibble (bit 3 = sign, bits 0-2 =
+ *                                magnitude code); low nibble = even column
+ *   scale_e4m3[g][r][b]        = best_idx + 1 (OCP E4M3FN byte)
+ *   global_scale[g]            = S_g = fl32(amax[g] / 2688)
+ * Every output is optional (NULL to skip) but at least one must be given.
+ * Output layouts are dense ([n_groups][c_out][c_in], [.][.][c_in/2],
+ * [.][.][c_in/16], [n_groups]).  best_idx entries must be < 126.
+ * Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_ARG, LH_ERR_HIP.
+ */
+lh_status lh_fake_quant_nvfp4(const void *w, int w_dtype, int64_t c_out, int64_t c_in,
+                              int64_t ld_w, int64_t n_groups, int64_t group_stride_w,
+                              const uint8_t *best_idx, const float *amax, float *w_q,
+                              uint8_t *packed_e2m1, uint8_t *scale_e4m3, float *global_scale,
+                              void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LH_H */

@@ -1,0 +1,229 @@
+"""Local-Hessian NVFP4 weight-scale calibration on AMD Instinct MI355X.
+
+Thin ctypes binding over the C ABI of ``liblh.so`` (declared in
+``include/lh.h``).  The functions carry the C names and only marshal
+arguments: tensor pointers, strides, dtypes and the current HIP stream.
+Every step of the computation runs in the library's HIP kernels; there is no
+CPU fallback.  If the library is missing the import raises.
+
+Tensors must live on a ROCm device.  Shapes:
+  weights      [c_out, c_in] or [n_groups, c_out, c_in], bf16 or fp32,
+               last dim contiguous (any row / group stride)
+  activations  channel-major [c_in, N] / [n_groups, c_in, N], or
+               token-major   [N, c_in] / [n_groups, N, c_in]
+  hessians     fp32 [n_groups, c_in/16, 16, 16]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblh.so")
+
+LH_DTYPE_F32, LH_DTYPE_BF16 = 0, 1
+LH_LAYOUT_CHANNEL_MAJOR, LH_LAYOUT_TOKEN_MAJOR = 0, 1
+N_CANDIDATES = 126
+BLOCK = 16
+
+
+class LHError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s (status %d)" % (message, status))
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("liblh.so not built: run __graft_entry__.build() or "
+                          "python nvfp4_scale_calibration_amd/_build.py (%s)" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.lh_abi_version.restype = I
+    lib.lh_status_string.argtypes = [I]
+    lib.lh_status_string.restype = ctypes.c_char_p
+    lib.lh_last_error_message.restype = ctypes.c_char_p
+    lib.lh_absmax.argtypes = [P, I, I64, I64, I64, I64, I64, P, P]
+    lib.lh_absmax.restype = I
+    lib.lh_hessian_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.lh_hessian_workspace_bytes.restype = SZ
+    lib.lh_accumulate_hessian.argtypes = [P, I, I, I64, I64, I64, I64, I64, F, F, P, I64, P, SZ, P]
+    lib.lh_accumulate_hessian.restype = I
+    lib.lh_scale_sweep.argtypes = [P, I, I64, I64, I64, I64, I64, P, I64, P, P, P, P, P]
+    lib.lh_scale_sweep.restype = I
+    lib.lh_fake_quant_nvfp4.argtypes = [P, I, I64, I64, I64, I64, I64, P, P, P, P, P, P, P]
+    lib.lh_fake_quant_nvfp4.restype = I
+    return lib
+
+
+lib = _load()
+EXPORTS = ("lh_abi_version", "lh_status_string", "lh_last_error_message", "lh_absmax",
+           "lh_hessian_workspace_bytes", "lh_accumulate_hessian", "lh_scale_sweep",
+           "lh_fake_quant_nvfp4")
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = lib.lh_last_error_message().decode() or lib.lh_status_string(status).decode()
+        raise LHError(status, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return LH_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return LH_DTYPE_BF16
+    raise TypeError("expected float32 or bfloat16, got %s" % t.dtype)
+
+
+def _as3(t: torch.Tensor) -> torch.Tensor:
+    if t.dim() == 2:
+        return t.unsqueeze(0)
+    if t.dim() != 3:
+        raise ValueError("expected a 2-D or 3-D tensor, got shape %s" % (tuple(t.shape),))
+    return t
+
+
+def _require_device(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("liblh works on device tensors only (got a %s tensor)" % t.device)
+
+
+def _group_stride(t3: torch.Tensor) -> int:
+    return t3.stride(0) if t3.shape[0] > 1 else 0
+
+
+def _ld(t3: torch.Tensor) -> int:
+    """Row stride; a dimension of size 1 has no meaningful stride (torch may
+    report 1), so the contiguous extent is passed instead."""
+    return t3.stride(1) if t3.shape[1] > 1 else t3.shape[2]
+
+
+def lh_abi_version() -> int:
+    return lib.lh_abi_version()
+
+
+def lh_absmax(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Global amax per group: out[g] = max |w[g]| (fp32)."""
+    _require_device(w)
+    w3 = _as3(w)
+    if w3.stride(-1) != 1:
+        raise ValueError("last dim of w must be contiguous")
+    g, rows, cols = w3.shape
+    if out is None:
+        out = torch.empty(g, dtype=torch.float32, device=w.device)
+    _check(lib.lh_absmax(_ptr(w3), _dtype(w3), rows, cols, _ld(w3), g, _group_stride(w3),
+                         _ptr(out), _stream(w)))
+    return out
+
+
+def lh_hessian_workspace_bytes(c_in: int, n_tokens: int, n_groups: int = 1) -> int:
+    return int(lib.lh_hessian_workspace_bytes(c_in, n_tokens, n_groups))
+
+
+def lh_accumulate_hessian(x: torch.Tensor, layout: str = "channel", alpha: float | None = None,
+                          beta: float = 0.0, h: torch.Tensor | None = None,
+                          workspace: torch.Tensor | bool | None = True) -> torch.Tensor:
+    """h = beta * h + alpha * X_b X_b^T for every 16-channel block.
+
+    x: channel-major [.., c_in, N] (layout="channel") or token-major
+    [.., N, c_in] (layout="token").  alpha defaults to 1/N (the normalised
+    Hessian).  workspace=True allocates the split-token scratch buffer the
+    library asks for, False/None runs without one, a uint8 device tensor is
+    used as given."""
+    _require_device(x, h)
+    x3 = _as3(x)
+    if x3.stride(-1) != 1:
+        raise ValueError("last dim of x must be contiguous")
+    lay = {"channel": LH_LAYOUT_CHANNEL_MAJOR, "token": LH_LAYOUT_TOKEN_MAJOR}[layout]
+    g = x3.shape[0]
+    c_in, n_tok = (x3.shape[1], x3.shape[2]) if lay == LH_LAYOUT_CHANNEL_MAJOR else (x3.shape[2], x3.shape[1])
+    nb = c_in // BLOCK
+    if alpha is None:
+        alpha = 1.0 / n_tok if n_tok > 0 else 0.0
+    if h is None:
+        h = torch.empty((g, nb, BLOCK, BLOCK), dtype=torch.float32, device=x.device)
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an existing h")
+    ws, ws_bytes = None, 0
+    if workspace is True:
+        ws_bytes = lh_hessian_workspace_bytes(c_in, n_tok, g)
+        if ws_bytes:
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    elif isinstance(workspace, torch.Tensor):
+        ws, ws_bytes = workspace, workspace.numel() * workspace.element_size()
+    h_gstride = h.stride(0) if h.dim() == 4 and h.shape[0] > 1 else 0
+    _check(lib.lh_accumulate_hessian(_ptr(x3), _dtype(x3), lay, c_in, n_tok, _ld(x3), g,
+                                     _group_stride(x3), float(alpha), float(beta), _ptr(h), h_gstride,
+                                     _ptr(ws), ws_bytes, _stream(x)))
+    return h
+
+
+def lh_scale_sweep(w: torch.Tensor, h: torch.Tensor, amax: torch.Tensor,
+                   best_idx: torch.Tensor | None = None, best_err: torch.Tensor | bool | None = True,
+                   best_amax: torch.Tensor | bool | None = True):
+    """Per-block best candidate index (E4M3 code = idx + 1), its error
+    dw^T H_b dw and the per-block amax 6 * s_idx.  Returns (idx, err, amax);
+    err / amax are None when not requested (False/None)."""
+    _require_device(w, h, amax)
+    w3 = _as3(w)
+    if w3.stride(-1) != 1:
+        raise ValueError("last dim of w must be contiguous")
+    g, c_out, c_in = w3.shape
+    nb = c_in // BLOCK
+    shape = (g, c_out, nb)
+    dev = w.device
+    if best_idx is None:
+        best_idx = torch.empty(shape, dtype=torch.uint8, device=dev)
+    if best_err is True:
+        best_err = torch.empty(shape, dtype=torch.float32, device=dev)
+    if best_amax is True:
+        best_amax = torch.empty(shape, dtype=torch.float32, device=dev)
+    best_err = best_err if isinstance(best_err, torch.Tensor) else None
+    best_amax = best_amax if isinstance(best_amax, torch.Tensor) else None
+    h_gstride = h.stride(0) if h.dim() == 4 and h.shape[0] > 1 else 0
+    _check(lib.lh_scale_sweep(_ptr(w3), _dtype(w3), c_out, c_in, _ld(w3), g, _group_stride(w3),
+                              _ptr(h), h_gstride, _ptr(amax), _ptr(best_idx), _ptr(best_err),
+                              _ptr(best_amax), _stream(w)))
+    return best_idx, best_err, best_amax
+
+
+def lh_fake_quant_nvfp4(w: torch.Tensor, best_idx: torch.Tensor, amax: torch.Tensor,
+                        w_q: bool | torch.Tensor = True, packed: bool | torch.Tensor = False,
+                        scale_e4m3: bool | torch.Tensor = False,
+                        global_scale: bool | torch.Tensor = False) -> dict:
+    """NVFP4 fake-quant / packing with the chosen block scales.  Returns a
+    dict with the requested outputs: w_q [g, c_out, c_in] fp32, packed
+    [g, c_out, c_in/2] uint8, scale_e4m3 [g, c_out, c_in/16] uint8,
+    global_scale [g] fp32."""
+    _require_device(w, best_idx, amax)
+    w3 = _as3(w)
+    if w3.stride(-1) != 1:
+        raise ValueError("last dim of w must be contiguous")
+    g, c_out, c_in = w3.shape
+    dev = w.device
+
+    def out(req, shape, dtype):
+        if isinstance(req, torch.Tensor):
+            return req
+        return torch.empty(shape, dtype=dtype, device=dev) if req else None
+
+    res = dict(w_q=out(w_q, (g, c_out, c_in), torch.float32),
+               packed=out(packed, (g, c_out, c_in // 2), torch.uint8),
+               scale_e4m3=out(scale_e4m3, (g, c_out, c_in // BLOCK), torch.uint8),
+               global_scale=out(global_scale, (g,), torch.float32))
+    _check(lib.lh_fake_quant_nvfp4(_ptr(w3), _dtype(w3), c_out, c_in, _ld(w3), g, _group_stride(w3),
+                                   _ptr(best_idx), _ptr(amax), _ptr(res["w_q"]), _ptr(res["packed"]),
+                                   _ptr(res["scale_e4m3"]), _ptr(res["global_scale"]), _stream(w)))
+    return {k: v for k, v in res.items() if v is not None}

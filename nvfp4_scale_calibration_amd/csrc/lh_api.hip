@@ -1,0 +1,160 @@
+// lh_api.hip - C ABI front end of liblh: argument validation (pure host code,
+// no HIP call before it passes), launch, and error reporting.
+// The contract of every entry point is documented in include/lh.h.
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "lh.h"
+#include "lh_internal.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+lh_status fail(lh_status st, const char* fmt, const char* what) {
+  snprintf(g_msg, sizeof g_msg, fmt, what);
+  return st;
+}
+
+lh_status hip_fail(hipError_t e, const char* where) {
+  snprintf(g_msg, sizeof g_msg, "%s: %s", where, hipGetErrorString(e));
+  return LH_ERR_HIP;
+}
+
+bool valid_dtype(int d) { return d == LH_DTYPE_F32 || d == LH_DTYPE_BF16; }
+size_t elem_size(int d) { return d == LH_DTYPE_BF16 ? 2 : 4; }
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int lh_abi_version(void) { return 1; }
+
+const char* lh_status_string(int status) {
+  switch (status) {
+    case LH_OK: return "LH_OK";
+    case LH_ERR_NULL: return "LH_ERR_NULL: a required pointer is NULL";
+    case LH_ERR_SHAPE: return "LH_ERR_SHAPE: invalid size, leading dimension or stride";
+    case LH_ERR_DTYPE: return "LH_ERR_DTYPE: unknown dtype";
+    case LH_ERR_LAYOUT: return "LH_ERR_LAYOUT: unknown layout";
+    case LH_ERR_WORKSPACE: return "LH_ERR_WORKSPACE: workspace too small";
+    case LH_ERR_ARG: return "LH_ERR_ARG: invalid argument";
+    case LH_ERR_HIP: return "LH_ERR_HIP: HIP launch failed";
+    default: return "unknown lh_status";
+  }
+}
+
+const char* lh_last_error_message(void) { return g_msg; }
+
+lh_status lh_absmax(const void* w, int w_dtype, int64_t rows, int64_t cols, int64_t ld_w,
+                    int64_t n_groups, int64_t group_stride_w, float* amax, void* stream) {
+  g_msg[0] = '\0';
+  if (!valid_dtype(w_dtype)) return fail(LH_ERR_DTYPE, "%s: w_dtype must be 0 (f32) or 1 (bf16)", "lh_absmax");
+  if (rows < 0 || cols < 0 || n_groups < 0 || group_stride_w < 0)
+    return fail(LH_ERR_SHAPE, "%s: negative size or stride", "lh_absmax");
+  if (ld_w < cols) return fail(LH_ERR_SHAPE, "%s: ld_w < cols", "lh_absmax");
+  if (n_groups > 0 && amax == nullptr) return fail(LH_ERR_NULL, "%s: amax is NULL", "lh_absmax");
+  if (n_groups > 0 && rows > 0 && cols > 0 && w == nullptr) return fail(LH_ERR_NULL, "%s: w is NULL", "lh_absmax");
+  if (!aligned(w, elem_size(w_dtype)) || !aligned(amax, 4))
+    return fail(LH_ERR_ARG, "%s: pointer not aligned to its element size", "lh_absmax");
+  if (n_groups == 0) return LH_OK;
+  lh::AbsmaxArgs a{w, w_dtype, rows, cols, ld_w, n_groups, group_stride_w, amax};
+  hipError_t e = lh::launch_absmax(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LH_OK : hip_fail(e, "lh_absmax");
+}
+
+size_t lh_hessian_workspace_bytes(int64_t c_in, int64_t n_tokens, int64_t n_groups) {
+  if (c_in <= 0 || n_tokens <= 0 || n_groups <= 0 || c_in % 16 != 0) return 0;
+  return lh::hessian_ws_bytes(c_in, n_tokens, n_groups);
+}
+
+lh_status lh_accumulate_hessian(const void* x, int x_dtype, int layout, int64_t c_in,
+                                int64_t n_tokens, int64_t ld_x, int64_t n_groups,
+                                int64_t group_stride_x, float alpha, float beta, float* h,
+                                int64_t group_stride_h, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  const char* fn = "lh_accumulate_hessian";
+  g_msg[0] = '\0';
+  if (!valid_dtype(x_dtype)) return fail(LH_ERR_DTYPE, "%s: x_dtype must be 0 (f32) or 1 (bf16)", fn);
+  if (layout != LH_LAYOUT_CHANNEL_MAJOR && layout != LH_LAYOUT_TOKEN_MAJOR)
+    return fail(LH_ERR_LAYOUT, "%s: layout must be 0 (channel-major) or 1 (token-major)", fn);
+  if (c_in < 0 || n_tokens < 0 || n_groups < 0 || group_stride_x < 0 || group_stride_h < 0)
+    return fail(LH_ERR_SHAPE, "%s: negative size or stride", fn);
+  if (c_in % 16 != 0) return fail(LH_ERR_SHAPE, "%s: c_in must be a multiple of 16", fn);
+  const int64_t min_ld = layout == LH_LAYOUT_CHANNEL_MAJOR ? n_tokens : c_in;
+  if (ld_x < min_ld || ld_x < 1) return fail(LH_ERR_SHAPE, "%s: ld_x smaller than the contiguous extent", fn);
+  const int64_t nb = c_in / 16;
+  if (n_groups > 1 && group_stride_h < nb * 256)
+    return fail(LH_ERR_SHAPE, "%s: group_stride_h < (c_in/16)*256 would overlap outputs", fn);
+  const bool work = n_groups > 0 && nb > 0;
+  if (work && h == nullptr) return fail(LH_ERR_NULL, "%s: h is NULL", fn);
+  if (work && n_tokens > 0 && x == nullptr) return fail(LH_ERR_NULL, "%s: x is NULL", fn);
+  if (workspace == nullptr && workspace_bytes > 0) return fail(LH_ERR_NULL, "%s: workspace is NULL but workspace_bytes > 0", fn);
+  if (!aligned(x, elem_size(x_dtype)) || !aligned(h, 4) || !aligned(workspace, 4))
+    return fail(LH_ERR_ARG, "%s: pointer not aligned to its element size", fn);
+  if (workspace != nullptr && workspace_bytes > 0 && work && n_tokens > 0) {
+    const size_t need = lh::hessian_ws_bytes(c_in, n_tokens, n_groups);
+    if (workspace_bytes < need) return fail(LH_ERR_WORKSPACE, "%s: workspace smaller than lh_hessian_workspace_bytes()", fn);
+  }
+  if (!work) return LH_OK;
+  lh::HessianArgs a{x, x_dtype, layout, c_in, n_tokens, ld_x, group_stride_x, n_groups, alpha, beta,
+                    h, group_stride_h, workspace, workspace_bytes};
+  hipError_t e = lh::launch_hessian(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LH_OK : hip_fail(e, fn);
+}
+
+lh_status lh_scale_sweep(const void* w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
+                         int64_t n_groups, int64_t group_stride_w, const float* h,
+                         int64_t group_stride_h, const float* amax, uint8_t* best_idx,
+                         float* best_err, float* best_amax, void* stream) {
+  const char* fn = "lh_scale_sweep";
+  g_msg[0] = '\0';
+  if (!valid_dtype(w_dtype)) return fail(LH_ERR_DTYPE, "%s: w_dtype must be 0 (f32) or 1 (bf16)", fn);
+  if (c_out < 0 || c_in < 0 || n_groups < 0 || group_stride_w < 0 || group_stride_h < 0)
+    return fail(LH_ERR_SHAPE, "%s: negative size or stride", fn);
+  if (c_in % 16 != 0) return fail(LH_ERR_SHAPE, "%s: c_in must be a multiple of 16", fn);
+  if (ld_w < c_in) return fail(LH_ERR_SHAPE, "%s: ld_w < c_in", fn);
+  const bool work = n_groups > 0 && c_out > 0 && c_in > 0;
+  if (work && (w == nullptr || h == nullptr || amax == nullptr || best_idx == nullptr))
+    return fail(LH_ERR_NULL, "%s: w, h, amax and best_idx are required", fn);
+  if (!aligned(w, elem_size(w_dtype)) || !aligned(amax, 4) || !aligned(best_err, 4) || !aligned(best_amax, 4))
+    return fail(LH_ERR_ARG, "%s: pointer not aligned to its element size", fn);
+  if (!aligned(h, 16) || group_stride_h % 4 != 0)
+    return fail(LH_ERR_ARG, "%s: h must be 16-byte aligned and group_stride_h a multiple of 4", fn);
+  if (!work) return LH_OK;
+  lh::SweepArgs a{w, w_dtype, c_out, c_in, ld_w, n_groups, group_stride_w, h, group_stride_h, amax,
+                  best_idx, best_err, best_amax};
+  hipError_t e = lh::launch_sweep(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LH_OK : hip_fail(e, fn);
+}
+
+lh_status lh_fake_quant_nvfp4(const void* w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
+                              int64_t n_groups, int64_t group_stride_w, const uint8_t* best_idx,
+                              const float* amax, float* w_q, uint8_t* packed_e2m1,
+                              uint8_t* scale_e4m3, float* global_scale, void* stream) {
+  const char* fn = "lh_fake_quant_nvfp4";
+  g_msg[0] = '\0';
+  if (!valid_dtype(w_dtype)) return fail(LH_ERR_DTYPE, "%s: w_dtype must be 0 (f32) or 1 (bf16)", fn);
+  if (c_out < 0 || c_in < 0 || n_groups < 0 || group_stride_w < 0)
+    return fail(LH_ERR_SHAPE, "%s: negative size or stride", fn);
+  if (c_in % 16 != 0) return fail(LH_ERR_SHAPE, "%s: c_in must be a multiple of 16", fn);
+  if (ld_w < c_in) return fail(LH_ERR_SHAPE, "%s: ld_w < c_in", fn);
+  if (!w_q && !packed_e2m1 && !scale_e4m3 && !global_scale)
+    return fail(LH_ERR_ARG, "%s: no output requested", fn);
+  const bool blocks = n_groups > 0 && c_out > 0 && c_in > 0;
+  if (n_groups > 0 && amax == nullptr) return fail(LH_ERR_NULL, "%s: amax is NULL", fn);
+  if (blocks && (w_q || packed_e2m1 || scale_e4m3) && (w == nullptr || best_idx == nullptr))
+    return fail(LH_ERR_NULL, "%s: w and best_idx are required for per-block outputs", fn);
+  if (!aligned(w, elem_size(w_dtype)) || !aligned(amax, 4) || !aligned(global_scale, 4) ||
+      !aligned(w_q, 16) || !aligned(packed_e2m1, 8))
+    return fail(LH_ERR_ARG, "%s: misaligned pointer (w_q needs 16 bytes, packed_e2m1 8)", fn);
+  if (n_groups == 0) return LH_OK;
+  lh::FakeQuantArgs a{w, w_dtype, c_out, c_in, ld_w, n_groups, group_stride_w, best_idx, amax,
+                      w_q, packed_e2m1, scale_e4m3, global_scale};
+  hipError_t e = lh::launch_fake_quant(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LH_OK : hip_fail(e, fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,326 @@
+// lh_hessian.hip - local Hessian accumulation on CDNA4 matrix cores.
+//
+// "Local-Hessian weight-scale guide" (xxmr.cn/news/266017), "Algorithm
+// principle": for input block b the local Hessian is X_b X_b^T (16 x 16),
+// X_b = the 16 rows of X [C_in x N] that multiply weight block b; "Entry API
+// and calibration flow", phase 2: H accumulates the sum of X^T X over the
+// calibration tokens and is normalised before the search.
+//
+//   h[g][b] = beta * h[g][b] + alpha * X_b X_b^T
+//
+// Design: one 256-thread workgroup (4 wave64s) per (group, block, token
+// slice).  The contraction over tokens runs on MFMA with fp32 accumulation:
+// v_mfma_f32_16x16x32_bf16 for bf16 X, v_mfma_f32_16x16x4_f32 for fp32 X.
+// For H = X_b X_b^T the A operand (16 channels x K tokens) and the B operand
+// (its transpose) hold the same values in each lane (lane l: channel l%16,
+// K-slot group l/16), so one register set feeds both.  The token order inside
+// a K step is free (a sum), which lets each lane read 16 contiguous tokens
+// (channel-major) or a bank-conflict-free LDS column (token-major).
+// The four waves of a workgroup reduce in LDS in a fixed order; token slices
+// of one block reduce in a second kernel in a fixed order: results do not
+// depend on timing.
+#include "lh_device.h"
+#include "lh_internal.h"
+
+namespace lh {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int kSlab = 64;                 // tokens per wave per step
+constexpr int kRound = kSlab * 4;         // tokens per workgroup per step
+
+// Sixteen token values of one channel, in the lane's register layout.
+template <typename T>
+struct Vals16;
+template <>
+struct Vals16<uint16_t> {
+  uint4 u[2];  // 16 bf16
+};
+template <>
+struct Vals16<float> {
+  float f[16];
+};
+
+__device__ __forceinline__ f32x4_t mfma_accumulate(const Vals16<uint16_t>& v, f32x4_t acc) {
+  const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, v.u[0]);
+  const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, v.u[1]);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, a0, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, a1, acc, 0, 0, 0);
+  return acc;
+}
+
+__device__ __forceinline__ f32x4_t mfma_accumulate(const Vals16<float>& v, f32x4_t acc) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v.f[i], v.f[i], acc, 0, 0, 0);
+  return acc;
+}
+
+// Channel-major: lane reads tokens [tb, tb+16) of its channel row.
+template <bool kVec>
+__device__ __forceinline__ void load_cm(const uint16_t* row, int64_t tb, int64_t t1, Vals16<uint16_t>& v) {
+  if (kVec && tb + 16 <= t1) {
+    v.u[0] = *reinterpret_cast<const uint4*>(row + tb);
+    v.u[1] = *reinterpret_cast<const uint4*>(row + tb + 8);
+  } else {
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t lo = (tb + 2 * i < t1) ? row[tb + 2 * i] : 0u;
+      const uint32_t hi = (tb + 2 * i + 1 < t1) ? row[tb + 2 * i + 1] : 0u;
+      w[i] = lo | (hi << 16);
+    }
+    v.u[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    v.u[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+template <bool kVec>
+__device__ __forceinline__ void load_cm(const float* row, int64_t tb, int64_t t1, Vals16<float>& v) {
+  if (kVec && tb + 16 <= t1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = *reinterpret_cast<const float4*>(row + tb + 4 * q);
+      v.f[4 * q + 0] = f.x;
+      v.f[4 * q + 1] = f.y;
+      v.f[4 * q + 2] = f.z;
+      v.f[4 * q + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v.f[i] = (tb + i < t1) ? row[tb + i] : 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Channel-major kernel: x[(16b + c) * ld + t].
+// ---------------------------------------------------------------------------
+template <typename T, bool kVec>
+__global__ __launch_bounds__(kThreads) void hessian_cm_kernel(const T* __restrict__ x, int64_t n_tok,
+                                                              int64_t ld, int64_t gstride, int64_t nb,
+                                                              int64_t n_groups, int64_t nsplit,
+                                                              int64_t chunk, float alpha, float beta,
+                                                              float* __restrict__ h, int64_t h_gstride,
+                                                              float* __restrict__ ws) {
+  __shared__ float red[4][256];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ch = lane & 15, kg = lane >> 4;
+  int64_t id = blockIdx.x;
+  const int64_t s = id % nsplit;
+  id /= nsplit;
+  const int64_t b = id % nb, grp = id / nb;
+  const int64_t t0 = s * chunk;
+  const int64_t t1 = min(n_tok, t0 + chunk);
+  const T* row = x + grp * gstride + (16 * b + ch) * ld;
+
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  int64_t t = t0 + wave * kSlab;
+  // Two slabs per trip keep four 16-byte loads per lane in flight.
+  for (; t + kRound < t1; t += 2 * kRound) {
+    Vals16<T> v0, v1;
+    load_cm<kVec>(row, t + 16 * kg, t1, v0);
+    load_cm<kVec>(row, t + kRound + 16 * kg, t1, v1);
+    acc = mfma_accumulate(v0, acc);
+    acc = mfma_accumulate(v1, acc);
+  }
+  for (; t < t1; t += kRound) {
+    Vals16<T> v0;
+    load_cm<kVec>(row, t + 16 * kg, t1, v0);
+    acc = mfma_accumulate(v0, acc);
+  }
+
+  // C layout: lane holds rows 4*kg .. 4*kg+3 of column ch.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[wave][(4 * kg + i) * 16 + ch] = acc[i];
+  __syncthreads();
+  const int e = threadIdx.x;
+  const float v = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+  if (nsplit == 1) {
+    float* hp = h + grp * h_gstride + b * 256 + e;
+    *hp = (beta == 0.0f) ? alpha * v : beta * (*hp) + alpha * v;
+  } else {
+    ws[((s * n_groups + grp) * nb + b) * 256 + e] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Token-major kernel: x[t * ld + 16b + c].  Each wave stages a 64-token x
+// 16-channel tile in LDS (row = one token, 16 values, no padding) and lane
+// (ch, kg) reads tokens kg, kg+4, ..., kg+60 of column ch: for bf16 the 64
+// lanes touch 32 distinct words in 32 distinct banks, for fp32 every bank
+// serves exactly two lanes (the minimum for 64 four-byte reads).
+// The trip count is uniform over the workgroup (slabs past the end load
+// zeros), so the barriers are reached by every wave.
+// ---------------------------------------------------------------------------
+template <typename T, bool kVec>
+__global__ __launch_bounds__(kThreads) void hessian_tm_kernel(const T* __restrict__ x, int64_t n_tok,
+                                                              int64_t ld, int64_t gstride, int64_t nb,
+                                                              int64_t n_groups, int64_t nsplit,
+                                                              int64_t chunk, float alpha, float beta,
+                                                              float* __restrict__ h, int64_t h_gstride,
+                                                              float* __restrict__ ws) {
+  constexpr int kElemsPer16B = 16 / sizeof(T);          // 8 bf16 or 4 fp32
+  constexpr int kLanesPerTok = 16 / kElemsPer16B;       // 2 or 4
+  constexpr int kToksPerLoad = 64 / kLanesPerTok;       // 32 or 16
+  constexpr int kLoads = kSlab / kToksPerLoad;          // 2 or 4
+  __shared__ __attribute__((aligned(16))) T tile[4][kSlab * 16];
+  __shared__ float red[4][256];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ch = lane & 15, kg = lane >> 4;
+  int64_t id = blockIdx.x;
+  const int64_t s = id % nsplit;
+  id /= nsplit;
+  const int64_t b = id % nb, grp = id / nb;
+  const int64_t t0 = s * chunk;
+  const int64_t t1 = min(n_tok, t0 + chunk);
+  const T* base = x + grp * gstride + 16 * b;
+  T* my = tile[wave];
+  const int ltok = lane / kLanesPerTok;                 // token within a load
+  const int lcol = (lane % kLanesPerTok) * kElemsPer16B;  // first channel
+
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int64_t rounds = (t1 - t0 + kRound - 1) / kRound;
+  for (int64_t r = 0; r < rounds; ++r) {
+    const int64_t t = t0 + r * kRound + wave * kSlab;
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+      const int trow = q * kToksPerLoad + ltok;
+      const int64_t tok = t + trow;
+      T* dst = my + trow * 16 + lcol;
+      if (kVec && tok < t1) {
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(base + tok * ld + lcol);
+      } else {
+#pragma unroll
+        for (int c = 0; c < kElemsPer16B; ++c) dst[c] = (tok < t1) ? base[tok * ld + lcol + c] : T(0);
+      }
+    }
+    __syncthreads();
+    Vals16<T> v;
+    if constexpr (sizeof(T) == 2) {
+      uint32_t w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = my[(kg + 4 * (2 * i)) * 16 + ch];
+        const uint32_t hi = my[(kg + 4 * (2 * i + 1)) * 16 + ch];
+        w[i] = lo | (hi << 16);
+      }
+      v.u[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      v.u[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v.f[i] = my[(kg + 4 * i) * 16 + ch];
+    }
+    __syncthreads();
+    acc = mfma_accumulate(v, acc);
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[wave][(4 * kg + i) * 16 + ch] = acc[i];
+  __syncthreads();
+  const int e = threadIdx.x;
+  const float v = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+  if (nsplit == 1) {
+    float* hp = h + grp * h_gstride + b * 256 + e;
+    *hp = (beta == 0.0f) ? alpha * v : beta * (*hp) + alpha * v;
+  } else {
+    ws[((s * n_groups + grp) * nb + b) * 256 + e] = v;
+  }
+}
+
+// Sum of the token slices in slice order, then h = beta * h + alpha * sum.
+__global__ __launch_bounds__(kThreads) void hessian_finalize_kernel(const float* __restrict__ ws,
+                                                                    int64_t nsplit, int64_t n_groups,
+                                                                    int64_t nb, float alpha, float beta,
+                                                                    float* __restrict__ h,
+                                                                    int64_t h_gstride) {
+  const int64_t blk = blockIdx.x;  // grp * nb + b
+  const int64_t grp = blk / nb, b = blk % nb;
+  const int e = threadIdx.x;
+  const int64_t per_split = n_groups * nb * 256;
+  float v = ws[blk * 256 + e];
+  for (int64_t s = 1; s < nsplit; ++s) v += ws[s * per_split + blk * 256 + e];
+  float* hp = h + grp * h_gstride + b * 256 + e;
+  *hp = (beta == 0.0f) ? alpha * v : beta * (*hp) + alpha * v;
+}
+
+// n_tok == 0: h = beta * h (the sum is empty).
+__global__ __launch_bounds__(kThreads) void hessian_scale_kernel(float beta, float* __restrict__ h,
+                                                                 int64_t h_gstride, int64_t nb) {
+  const int64_t blk = blockIdx.x;
+  const int64_t grp = blk / nb, b = blk % nb;
+  float* hp = h + grp * h_gstride + b * 256 + threadIdx.x;
+  *hp = (beta == 0.0f) ? 0.0f : beta * (*hp);
+}
+
+template <typename T, bool kVec>
+hipError_t launch_typed(const HessianArgs& a, const HessianPlan& p, hipStream_t stream) {
+  const int64_t nb = a.c_in / 16;
+  const int64_t grid = a.n_groups * nb * p.nsplit;
+  float* ws = p.nsplit > 1 ? static_cast<float*>(a.ws) : nullptr;
+  const T* x = static_cast<const T*>(a.x);
+  if (a.layout == 0)
+    hessian_cm_kernel<T, kVec><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+        x, a.n_tok, a.ld, a.gstride, nb, a.n_groups, p.nsplit, p.chunk, a.alpha, a.beta, a.h,
+        a.h_gstride, ws);
+  else
+    hessian_tm_kernel<T, kVec><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+        x, a.n_tok, a.ld, a.gstride, nb, a.n_groups, p.nsplit, p.chunk, a.alpha, a.beta, a.h,
+        a.h_gstride, ws);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || p.nsplit == 1) return err;
+  hessian_finalize_kernel<<<dim3((unsigned)(a.n_groups * nb)), dim3(kThreads), 0, stream>>>(
+      ws, p.nsplit, a.n_groups, nb, a.alpha, a.beta, a.h, a.h_gstride);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Token slices per block: aim for >= 2048 workgroups (8 per CU on 256 CUs)
+// while keeping >= 1024 tokens per slice (one 2-slab trip per wave).
+HessianPlan hessian_plan(int64_t c_in, int64_t n_tok, int64_t n_groups, bool have_ws) {
+  HessianPlan p{1, ((n_tok + kRound - 1) / kRound) * kRound};
+  const int64_t blocks = n_groups * (c_in / 16);
+  if (!have_ws || blocks <= 0 || n_tok <= 0) return p;
+  int64_t want = (2048 + blocks - 1) / blocks;
+  const int64_t by_len = n_tok / 1024;
+  int64_t ns = want < by_len ? want : by_len;
+  if (ns > 64) ns = 64;
+  if (ns <= 1) return p;
+  int64_t chunk = (n_tok + ns - 1) / ns;
+  chunk = ((chunk + kRound - 1) / kRound) * kRound;
+  p.chunk = chunk;
+  p.nsplit = (n_tok + chunk - 1) / chunk;
+  if (p.nsplit <= 1) p = HessianPlan{1, ((n_tok + kRound - 1) / kRound) * kRound};
+  return p;
+}
+
+size_t hessian_ws_bytes(int64_t c_in, int64_t n_tok, int64_t n_groups) {
+  const HessianPlan p = hessian_plan(c_in, n_tok, n_groups, true);
+  if (p.nsplit <= 1) return 0;
+  return (size_t)p.nsplit * (size_t)n_groups * (size_t)(c_in / 16) * 256u * sizeof(float);
+}
+
+hipError_t launch_hessian(const HessianArgs& a, hipStream_t stream) {
+  const int64_t nb = a.c_in / 16;
+  if (a.n_groups == 0 || nb == 0) return hipSuccess;
+  if (a.n_tok == 0) {
+    if (a.beta == 1.0f) return hipSuccess;
+    hessian_scale_kernel<<<dim3((unsigned)(a.n_groups * nb)), dim3(kThreads), 0, stream>>>(
+        a.beta, a.h, a.h_gstride, nb);
+    return hipGetLastError();
+  }
+  const size_t need = hessian_ws_bytes(a.c_in, a.n_tok, a.n_groups);
+  const bool have_ws = a.ws != nullptr && need > 0 && a.ws_bytes >= need;
+  const HessianPlan p = hessian_plan(a.c_in, a.n_tok, a.n_groups, have_ws);
+  const size_t esz = a.dtype == 1 ? 2 : 4;
+  const int64_t epv = 16 / (int64_t)esz;  // elements per 16-byte vector
+  const bool aligned = (reinterpret_cast<uintptr_t>(a.x) % 16 == 0) && (a.ld % epv == 0) &&
+                       (a.gstride % epv == 0);
+  if (a.dtype == 1)
+    return aligned ? launch_typed<uint16_t, true>(a, p, stream) : launch_typed<uint16_t, false>(a, p, stream);
+  return aligned ? launch_typed<float, true>(a, p, stream) : launch_typed<float, false>(a, p, stream);
+}
+
+}  // namespace lh

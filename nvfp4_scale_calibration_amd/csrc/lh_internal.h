@@ -1,0 +1,67 @@
+// lh_internal.h - launchers shared between the C ABI front end (lh_api.hip)
+// and the kernel translation units.  Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lh {
+
+struct HessianArgs {
+  const void* x;
+  int dtype;      // 0 fp32, 1 bf16
+  int layout;     // 0 channel-major, 1 token-major
+  int64_t c_in, n_tok, ld, gstride;
+  int64_t n_groups;
+  float alpha, beta;
+  float* h;
+  int64_t h_gstride;
+  void* ws;       // nullable
+  size_t ws_bytes;
+};
+
+// Token-split plan: `nsplit` slices of `chunk` tokens each (chunk % 256 == 0).
+struct HessianPlan {
+  int64_t nsplit;
+  int64_t chunk;
+};
+HessianPlan hessian_plan(int64_t c_in, int64_t n_tok, int64_t n_groups, bool have_ws);
+size_t hessian_ws_bytes(int64_t c_in, int64_t n_tok, int64_t n_groups);
+hipError_t launch_hessian(const HessianArgs& a, hipStream_t stream);
+
+struct SweepArgs {
+  const void* w;
+  int dtype;
+  int64_t c_out, c_in, ld_w, n_groups, gstride_w;
+  const float* h;
+  int64_t gstride_h;
+  const float* amax;
+  uint8_t* idx;
+  float* err;
+  float* best_amax;
+};
+hipError_t launch_sweep(const SweepArgs& a, hipStream_t stream);
+
+struct FakeQuantArgs {
+  const void* w;
+  int dtype;
+  int64_t c_out, c_in, ld_w, n_groups, gstride_w;
+  const uint8_t* idx;
+  const float* amax;
+  float* wq;
+  uint8_t* packed;
+  uint8_t* codes;
+  float* gscale;
+};
+hipError_t launch_fake_quant(const FakeQuantArgs& a, hipStream_t stream);
+
+struct AbsmaxArgs {
+  const void* w;
+  int dtype;
+  int64_t rows, cols, ld, n_groups, gstride;
+  float* out;
+};
+hipError_t launch_absmax(const AbsmaxArgs& a, hipStream_t stream);
+
+}  // namespace lh

@@ -1,0 +1,135 @@
+"""C-ABI boundary tests that need no GPU: the library loads, exports every
+function include/lh.h declares, and rejects invalid arguments on the host
+with the documented status code before any HIP call (so no call here
+reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lh.h")
+LIB = os.path.join(ROOT, "nvfp4_scale_calibration_amd", "liblh.so")
+
+OK, NULL, SHAPE, DTYPE, LAYOUT, WORKSPACE, ARG, HIP = range(8)
+FAKE = 0x10000  # aligned non-null address; never dereferenced (validation fails first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lh_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        import nvfp4_scale_calibration_amd._build as b
+        b.build()
+    import nvfp4_scale_calibration_amd as m
+    return m.lib
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("lh_accumulate_hessian", "lh_scale_sweep", "lh_fake_quant_nvfp4"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+    import nvfp4_scale_calibration_amd as m
+    assert set(m.EXPORTS) == set(declared_functions())
+    assert lib.lh_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for st in range(8):
+        s = lib.lh_status_string(st).decode()
+        assert s.startswith("LH_")
+    assert "unknown" in lib.lh_status_string(99).decode()
+
+
+def _msg(lib):
+    return lib.lh_last_error_message().decode()
+
+
+def test_sweep_validation(lib):
+    P = ctypes.c_void_p
+    ok = dict(w=P(FAKE), dt=1, c_out=4, c_in=32, ld=32, g=1, gs=0, h=P(FAKE), hs=0, amax=P(FAKE),
+              idx=P(FAKE), err=None, am=None, st=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.lh_scale_sweep(a["w"], a["dt"], a["c_out"], a["c_in"], a["ld"], a["g"], a["gs"], a["h"],
+                                  a["hs"], a["amax"], a["idx"], a["err"], a["am"], a["st"])
+
+    assert call(dt=7) == DTYPE
+    assert call(c_in=24) == SHAPE and "multiple of 16" in _msg(lib)
+    assert call(ld=16) == SHAPE
+    assert call(c_out=-1) == SHAPE
+    assert call(w=None) == NULL
+    assert call(idx=None) == NULL
+    assert call(amax=None) == NULL
+    assert call(h=P(FAKE + 4)) == ARG  # H must be 16-byte aligned
+    assert call(w=P(FAKE + 1)) == ARG  # bf16 needs 2-byte alignment
+    # empty problems are valid no-ops and never touch the device
+    assert call(c_out=0, w=None, idx=None) == OK
+    assert call(g=0) == OK
+
+
+def test_hessian_validation(lib):
+    P = ctypes.c_void_p
+    ok = dict(x=P(FAKE), dt=1, lay=0, c_in=32, n=64, ld=64, g=1, gs=0, a=1.0, b=0.0, h=P(FAKE), hs=0,
+              ws=None, wsb=0, st=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.lh_accumulate_hessian(a["x"], a["dt"], a["lay"], a["c_in"], a["n"], a["ld"], a["g"], a["gs"],
+                                         a["a"], a["b"], a["h"], a["hs"], a["ws"], a["wsb"], a["st"])
+
+    assert call(dt=2) == DTYPE
+    assert call(lay=2) == LAYOUT
+    assert call(c_in=40) == SHAPE
+    assert call(ld=63) == SHAPE           # channel-major needs ld >= N
+    assert call(lay=1, ld=31) == SHAPE    # token-major needs ld >= c_in
+    assert call(g=2, hs=256) == SHAPE     # output groups would overlap
+    assert call(x=None) == NULL
+    assert call(h=None) == NULL
+    assert call(ws=None, wsb=16) == NULL
+    assert call(n=-5) == SHAPE
+    big = lib.lh_hessian_workspace_bytes(4096, 1 << 16, 1)
+    assert big > 0
+    assert call(c_in=4096, n=1 << 16, ld=1 << 16, ws=P(FAKE), wsb=big - 4) == WORKSPACE
+    assert call(g=0) == OK and call(c_in=0) == OK
+
+
+def test_fake_quant_and_absmax_validation(lib):
+    P = ctypes.c_void_p
+    f = lib.lh_fake_quant_nvfp4
+    assert f(P(FAKE), 0, 4, 32, 32, 1, 0, P(FAKE), P(FAKE), None, None, None, None, None) == ARG
+    assert f(P(FAKE), 0, 4, 32, 32, 1, 0, None, P(FAKE), P(FAKE), None, None, None, None) == NULL
+    assert f(P(FAKE), 0, 4, 32, 32, 1, 0, P(FAKE), None, P(FAKE), None, None, None, None) == NULL
+    assert f(P(FAKE), 0, 4, 33, 33, 1, 0, P(FAKE), P(FAKE), P(FAKE), None, None, None, None) == SHAPE
+    assert f(P(FAKE), 0, 4, 32, 32, 1, 0, P(FAKE), P(FAKE), P(FAKE + 8), None, None, None, None) == ARG
+    assert f(P(FAKE), 3, 4, 32, 32, 1, 0, P(FAKE), P(FAKE), P(FAKE), None, None, None, None) == DTYPE
+    a = lib.lh_absmax
+    assert a(P(FAKE), 1, 4, 32, 16, 1, 0, P(FAKE), None) == SHAPE
+    assert a(P(FAKE), 1, 4, 32, 32, 1, 0, None, None) == NULL
+    assert a(None, 1, 4, 32, 32, 1, 0, P(FAKE), None) == NULL
+    assert a(P(FAKE), 9, 4, 32, 32, 1, 0, P(FAKE), None) == DTYPE
+    assert a(P(FAKE), 1, 4, 32, 32, 0, 0, P(FAKE), None) == OK
+
+
+def test_workspace_plan_is_host_logic(lib):
+    ws = lib.lh_hessian_workspace_bytes
+    assert ws(256, 128, 1) == 0               # too few tokens to split
+    assert ws(0, 100, 1) == 0 and ws(16, 0, 1) == 0 and ws(17, 4096, 1) == 0
+    b = ws(4096, 4096, 1)
+    assert b > 0 and b % (256 * 4 * 256) == 0  # whole [nsplit][256 blocks][256] fp32 slabs
+    assert ws(17408, 16384, 1) >= 0
+    # depends only on its three arguments
+    assert ws(4096, 4096, 1) == ws(4096, 4096, 1)

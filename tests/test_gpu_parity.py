@@ -1,0 +1,274 @@
+"""GPU parity: the HIP library (called through its C ABI via the thin
+binding) against the CPU oracle on identical seeded inputs.
+
+Covers: the small named workload end to end; ragged shapes (block counts
+that are not multiples of the wave width, token counts that end mid-tile,
+several groups, unaligned leading dimensions, both activation layouts, fp32
+and bf16); split-token vs one-pass Hessians and their determinism; alpha /
+beta chunking and empty token sets; degenerate amax (zero, tiny, huge,
+smaller than the weights); all-zero blocks; planted exact solutions;
+weights placed on both sides of every rounding threshold.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lh_workloads as wl
+import oracle
+import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def lh():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import nvfp4_scale_calibration_amd as m
+    return m
+
+
+def _np(t):
+    t = t.detach().cpu().contiguous()
+    return wl.np_bits(t) if t.dtype in (torch.bfloat16, torch.float32) else t.numpy()
+
+
+def run_path(lh, w, x, layout="channel", workspace=True):
+    """absmax -> Hessian -> sweep -> fake-quant on the GPU."""
+    wd, xd = w.to(DEV), x.to(DEV)
+    if layout == "token":
+        xd = xd.transpose(1, 2).contiguous()
+    amax = lh.lh_absmax(wd)
+    h = lh.lh_accumulate_hessian(xd, layout=layout, workspace=workspace)
+    idx, err, bam = lh.lh_scale_sweep(wd, h, amax)
+    fq = lh.lh_fake_quant_nvfp4(wd, idx, amax, w_q=True, packed=True, scale_e4m3=True, global_scale=True)
+    torch.cuda.synchronize()
+    return dict(amax=amax.cpu().numpy(), h=h.cpu().numpy(), idx=idx.cpu().numpy(), err=err.cpu().numpy(),
+                bam=bam.cpu().numpy(), fq={k: v.cpu().numpy() for k, v in fq.items()})
+
+
+def check_all(lh, work: wl.Workload, layout="channel", n_hess_sel=None, n_sweep_sel=None, seed=0):
+    G, c_out, c_in, n = work.n_groups, work.c_out, work.c_in, work.n_tok
+    nb = c_in // 16
+    print("case %s G=%d c_out=%d c_in=%d N=%d %s %s" % (work.name, G, c_out, c_in, n, work.dtype, layout), flush=True)
+    got = run_path(lh, work.w, work.x, layout)
+    w_np, x_np = wl.np_bits(work.w), wl.np_bits(work.x)
+    # global amax: exact
+    np.testing.assert_array_equal(got["amax"], oracle.absmax(w_np, c_out, c_in, n_groups=G))
+    rng = np.random.default_rng(seed)
+    # Hessian
+    hsel = np.arange(G * nb) if n_hess_sel is None else np.sort(rng.choice(G * nb, min(n_hess_sel, G * nb), replace=False))
+    h64, _ = oracle.hessian(x_np, c_in, n, n_groups=G, sel=hsel)
+    parity.check_hessian(got["h"].reshape(G * nb, 16, 16)[hsel], h64, work.name)
+    # sweep on the GPU's H
+    total = G * c_out * nb
+    ssel = np.arange(total) if n_sweep_sel is None else np.sort(rng.choice(total, min(n_sweep_sel, total), replace=False))
+    stats = parity.sweep_against_oracle(w_np, got["h"], got["amax"], c_out, c_in, G, ssel, got["idx"], got["err"],
+                                        got["bam"], work.name)
+    # fake-quant with the GPU's indices: bit-exact
+    parity.fake_quant_against_oracle(w_np, got["idx"], got["amax"], c_out, c_in, G, ssel, got["fq"], work.name)
+    np.testing.assert_array_equal(got["fq"]["global_scale"], got["amax"] / np.float32(2688.0))
+    print("  ok: %s" % stats, flush=True)
+    return got, stats
+
+
+def test_linear_256_end_to_end(lh):
+    work = wl.make(1)
+    got, stats = check_all(lh, work)
+    assert stats["n"] == 4096
+    # end to end, each side with its own H: report the index agreement
+    _, h32 = oracle.hessian(wl.np_bits(work.x), 256, 128)
+    res = oracle.sweep(wl.np_bits(work.w), h32, got["amax"], 256, 256)
+    agree = float((res["idx"] == got["idx"].reshape(-1)).mean())
+    print("  end-to-end index agreement with the oracle's own H: %.5f" % agree)
+    assert agree > 0.99
+
+
+@pytest.mark.parametrize("G,c_out,c_in,n,dtype,layout", [
+    (3, 37, 48, 77, "bf16", "channel"),
+    (2, 5, 16, 1, "f32", "token"),
+    (1, 129, 1040, 300, "bf16", "token"),
+    (4, 64, 64, 1000, "f32", "channel"),
+    (1, 3, 2064, 2500, "bf16", "channel"),
+    (2, 70, 112, 513, "bf16", "token"),
+])
+def test_ragged_shapes(lh, G, c_out, c_in, n, dtype, layout):
+    work = wl.make_custom(c_out, c_in, n, n_groups=G, dtype=dtype, seed=c_out + n, w_dist="t3",
+                          x_dist="lognormal")
+    check_all(lh, work, layout=layout)
+
+
+def test_hessian_split_vs_one_pass_and_determinism(lh):
+    work = wl.make_custom(8, 256, 8192 + 77, dtype="bf16", seed=5, x_dist="lognormal")
+    xd = work.x.to(DEV)
+    assert lh.lh_hessian_workspace_bytes(256, 8192 + 77, 1) > 0
+    h_split = lh.lh_accumulate_hessian(xd, workspace=True)
+    h_split2 = lh.lh_accumulate_hessian(xd, workspace=True)
+    h_one = lh.lh_accumulate_hessian(xd, workspace=False)
+    torch.cuda.synchronize()
+    assert torch.equal(h_split, h_split2)  # fixed reduction order
+    h64, _ = oracle.hessian(wl.np_bits(work.x), 256, 8192 + 77)
+    parity.check_hessian(h_split.cpu().numpy(), h64, "split")
+    parity.check_hessian(h_one.cpu().numpy(), h64, "one-pass")
+    # token-major gives the same matrix within tolerance
+    h_tm = lh.lh_accumulate_hessian(xd.transpose(1, 2).contiguous(), layout="token")
+    parity.check_hessian(h_tm.cpu().numpy(), h64, "token-major")
+
+
+def test_hessian_alpha_beta_chunks_and_empty(lh):
+    work = wl.make_custom(4, 64, 600, dtype="bf16", seed=9)
+    x = work.x.to(DEV)
+    h = lh.lh_accumulate_hessian(x[:, :, :250].contiguous(), alpha=1.0, beta=0.0)
+    h = lh.lh_accumulate_hessian(x[:, :, 250:].contiguous(), alpha=1.0, beta=1.0, h=h)
+    h64, _ = oracle.hessian(wl.np_bits(work.x), 64, 600, alpha=1.0)
+    parity.check_hessian(h.cpu().numpy(), h64, "chunks")
+    # strided view (ld > N) without a copy
+    hv = lh.lh_accumulate_hessian(x[:, :, 100:400], alpha=1.0)
+    hv64, _ = oracle.hessian(np.ascontiguousarray(wl.np_bits(work.x)[:, :, 100:400]), 64, 300, alpha=1.0)
+    parity.check_hessian(hv.cpu().numpy(), hv64, "strided")
+    # zero tokens: h = beta * h
+    h0 = h.clone()
+    lh.lh_accumulate_hessian(x[:, :, :0], alpha=1.0, beta=0.5, h=h0)
+    torch.cuda.synchronize()
+    assert torch.equal(h0, h * 0.5)
+
+
+def _sweep_case(lh, w_np32, h_np, amax_val, what, check_err=True):
+    """w_np32: [c_out, c_in] fp32; H [nb,16,16]; explicit amax."""
+    c_out, c_in = w_np32.shape
+    w = torch.from_numpy(w_np32).to(DEV)
+    hd = torch.from_numpy(np.ascontiguousarray(h_np, np.float32)).reshape(1, c_in // 16, 16, 16).to(DEV)
+    am = torch.tensor([amax_val], dtype=torch.float32, device=DEV)
+    idx, err, bam = lh.lh_scale_sweep(w, hd, am)
+    fq = lh.lh_fake_quant_nvfp4(w, idx, am, w_q=True, packed=True, scale_e4m3=True)
+    torch.cuda.synchronize()
+    am_np = np.array([amax_val], np.float32)
+    sel = np.arange(c_out * (c_in // 16))
+    stats = parity.sweep_against_oracle(w_np32.reshape(1, c_out, c_in), hd.cpu().numpy(), am_np, c_out, c_in, 1, sel,
+                                        idx.cpu().numpy(), err.cpu().numpy() if check_err else None,
+                                        bam.cpu().numpy(), what)
+    parity.fake_quant_against_oracle(w_np32.reshape(1, c_out, c_in), idx.cpu().numpy(), am_np, c_out, c_in, 1, sel,
+                                     {k: v.cpu().numpy() for k, v in fq.items()}, what)
+    return idx.cpu().numpy().reshape(-1), err.cpu().numpy().reshape(-1), stats
+
+
+def _spd(rng, nb, n=64, scale=1.0):
+    x = rng.standard_normal((nb * 16, n)).astype(np.float32) * np.float32(scale)
+    _, h32 = oracle.hessian(x, nb * 16, n)
+    return h32
+
+
+def test_degenerate_amax_and_zero_blocks(lh):
+    rng = np.random.default_rng(21)
+    h = _spd(rng, 4)
+    w = (rng.standard_normal((8, 64)) * 0.02).astype(np.float32)
+    w[0, :16] = 0.0           # all-zero block
+    w[1, 16:32] = -0.0
+    g = float(np.abs(w).max())
+    idx, err, _ = _sweep_case(lh, w, h, g, "zero-blocks")
+    assert idx[0] == 0 and err[0] == 0.0 and idx[4 + 1] == 0
+    _sweep_case(lh, w, h, 0.0, "amax=0")                     # every scale 0: Q = 0, index 0
+    _sweep_case(lh, w, h, g * 0.3, "amax<max|w|")           # saturation region
+    for scale in (2.0 ** -70, 2.0 ** -100, 1e-33, 2.0 ** 90, 1e30):
+        ws = (w.astype(np.float64) * scale).astype(np.float32)
+        gs = float(np.abs(ws).max())
+        hs = h * np.float32(1.0 / scale) if scale > 1 else h  # keep E inside fp32 range
+        _sweep_case(lh, ws, hs, gs, "scaled %g" % scale, check_err=(2.0 ** -40 <= scale <= 2.0 ** 100))  # tiny weights: E underflows fp32
+
+
+def test_planted_solutions(lh):
+    rng = np.random.default_rng(22)
+    c_out, c_in = 64, 128
+    h = _spd(rng, c_in // 16)
+    g = np.float32(0.37)
+    s = oracle.candidate_scales(g)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    w = np.empty((c_out, c_in), np.float32)
+    want = rng.integers(0, 126, (c_out, c_in // 16))
+    for r in range(c_out):
+        for b in range(c_in // 16):
+            codes = rng.integers(0, 8, 16)
+            codes[0], codes[1] = 1, 7
+            rng.shuffle(codes)
+            sign = np.where(rng.random(16) < 0.5, -1, 1).astype(np.float32)
+            w[r, 16 * b:16 * b + 16] = (sign * grid[codes]) * s[want[r, b]]
+    g_act = float(np.abs(w).max())
+    assert g_act <= g * (1 + 1e-6)  # 6 * s_125 is within one ulp of g
+    idx, err, _ = _sweep_case(lh, w, h, float(g), "planted")
+    np.testing.assert_array_equal(idx, want.reshape(-1))
+    assert np.all(err == 0.0)
+
+
+def test_weights_on_every_rounding_threshold(lh):
+    """Weights within a few ulps of x = 0.25, 0.75, ..., 5 times a candidate
+    scale, so that fl32(|w| / s) falls below, on and above each threshold."""
+    rng = np.random.default_rng(23)
+    g = np.float32(1.7)
+    s = oracle.candidate_scales(g)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+    rows = []
+    for t in range(512):
+        k = int(rng.integers(0, 126))
+        m = mids[rng.integers(0, 7, 16)]
+        base = (m * s[k]).astype(np.float32)
+        off = rng.integers(-3, 4, 16).astype(np.int32)
+        v = base.view(np.int32) + off
+        vals = v.view(np.float32) * np.where(rng.random(16) < 0.5, -1, 1).astype(np.float32)
+        rows.append(vals)
+    w = np.stack(rows).reshape(64, 128).astype(np.float32)
+    w[0, 0] = g  # keep the global amax
+    h = _spd(rng, 8)
+    _sweep_case(lh, w, h, float(g), "thresholds")
+    # fake-quant with random indices: every cast bit-exact
+    c_out, c_in = w.shape
+    idx = torch.from_numpy(rng.integers(0, 126, (1, c_out, c_in // 16)).astype(np.uint8)).to(DEV)
+    wd = torch.from_numpy(w).to(DEV)
+    am = torch.tensor([g], device=DEV)
+    fq = lh.lh_fake_quant_nvfp4(wd, idx, am, w_q=True, packed=True, scale_e4m3=True)
+    torch.cuda.synchronize()
+    parity.fake_quant_against_oracle(w.reshape(1, c_out, c_in), idx.cpu().numpy(), np.array([g], np.float32),
+                                     c_out, c_in, 1, np.arange(c_out * c_in // 16),
+                                     {k: v.cpu().numpy() for k, v in fq.items()}, "thresholds-fq")
+
+
+def test_unaligned_leading_dimensions(lh):
+    rng = np.random.default_rng(24)
+    c_out, c_in, n = 33, 64, 203
+    wbig = torch.from_numpy((rng.standard_normal((c_out, c_in + 3)) * 0.02).astype(np.float32)).to(torch.bfloat16)
+    xbig = torch.from_numpy(rng.standard_normal((c_in, n + 5)).astype(np.float32)).to(torch.bfloat16)
+    wd = wbig.to(DEV)[:, 1:1 + c_in]   # ld = c_in + 3, base offset by one element
+    xd = xbig.to(DEV)[:, 2:2 + n]
+    amax = lh.lh_absmax(wd)
+    h = lh.lh_accumulate_hessian(xd)
+    idx, err, bam = lh.lh_scale_sweep(wd, h, amax)
+    fq = lh.lh_fake_quant_nvfp4(wd, idx, amax, w_q=True, packed=True)
+    torch.cuda.synchronize()
+    w_np = wl.np_bits(wd.cpu().contiguous()).reshape(1, c_out, c_in)
+    x_np = wl.np_bits(xd.cpu().contiguous())
+    np.testing.assert_array_equal(amax.cpu().numpy(), oracle.absmax(w_np, c_out, c_in))
+    h64, _ = oracle.hessian(x_np, c_in, n)
+    parity.check_hessian(h.cpu().numpy(), h64, "unaligned")
+    sel = np.arange(c_out * c_in // 16)
+    parity.sweep_against_oracle(w_np, h.cpu().numpy(), amax.cpu().numpy(), c_out, c_in, 1, sel,
+                                idx.cpu().numpy(), err.cpu().numpy(), bam.cpu().numpy(), "unaligned")
+    parity.fake_quant_against_oracle(w_np, idx.cpu().numpy(), amax.cpu().numpy(), c_out, c_in, 1, sel,
+                                     {k: v.cpu().numpy() for k, v in fq.items()}, "unaligned")
+
+
+def test_empty_problems(lh):
+    w = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    amax = lh.lh_absmax(w)
+    torch.cuda.synchronize()
+    assert amax.item() == 0.0
+    h = torch.zeros((1, 4, 16, 16), device=DEV)
+    idx, err, bam = lh.lh_scale_sweep(w, h, amax)
+    assert idx.numel() == 0
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
+def test_full_size_workloads_sampled(lh, n):
+    """The named workloads at full size, in the launch configuration the
+    benchmark times; outputs sampled for the oracle."""
+    work = wl.make(n)
+    check_all(lh, work, n_hess_sel=24, n_sweep_sel=3000, seed=n)
