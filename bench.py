@@ -42,7 +42,24 @@ def parse():
     p.add_argument("--workload", type=int, default=2, help="named workload 1..5 (default: dense-4096)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run a plain 256 MiB device copy 5 times (HBM counter calibration)")
     return p.parse_args()
+
+
+def copy_probe() -> None:
+    """A plain copy kernel of known size: reads and writes 256 MiB per launch.
+    Its FETCH_SIZE / WRITE_SIZE counter readings scale the counters taken on
+    the library's kernels to bytes."""
+    import torch
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_per_launch": n}), flush=True)
 
 
 def kernel_source_hash() -> str:
@@ -126,6 +143,9 @@ def cpu_baseline(work, budget_s: float) -> dict:
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (asked for %d)." % max(args.gpus, world),

@@ -4,11 +4,18 @@ tests, the smoke check and the benchmark's self-check).
 Rules (the repository's design notes derive them):
   * Hessian: |H_gpu - H_oracle|_ij <= 1e-3 * sqrt(H_ii H_jj) (+1e-30): relative
     on the diagonal, Cauchy-Schwarz-scaled off it; the oracle sums in fp64.
-  * Sweep (judged on the same fp32 H fed to both sides): the chosen index is
-    bit-exact unless the oracle's best and second-best errors differ by less
-    than 1e-5 relative (or the second best is 0); the error is within
-    1e-4 * max(e1, tau) with tau = 1e-7 * sum_ij |H_ij| |dw_i| |dw_j| for the
-    oracle's best dw (guards exact-zero errors); the per-block amax is
+  * Sweep (judged on the same fp32 H fed to both sides): the GPU evaluates
+    E = dw^T H dw in fp32, so its forward error is bounded by
+    gamma * S with S = sum_ij |H_ij| |dw_i| |dw_j| and gamma = 4e-6 (about
+    twice the 35 unit roundoffs of the evaluation: dw = fl(Q - w), 16-term
+    fused dot products, the 16-term outer sum).  Where the quadratic form
+    cancels (e.g. a rank-1 H from one token) S >> E and no fp32 evaluation
+    can reach a relative tolerance, so:
+      - the chosen index is bit-exact unless the oracle's best and
+        second-best errors differ by less than max(1e-5 * e2, 2 gamma S)
+        (or e2 == 0);
+      - the error is within max(1e-4 * e1, gamma * S);
+    S is taken at the oracle's best candidate.  The per-block amax is
     bit-exact where the index agrees.
   * Fake-quant: Q, packed nibbles and E4M3 codes bit-exact for the same indices.
   * Global amax: bit-exact.
@@ -22,6 +29,7 @@ import oracle
 H_RTOL = 1e-3
 TIE_RTOL = 1e-5
 ERR_RTOL = 1e-4
+FP32_GAMMA = 4e-6
 
 
 def check_hessian(h_gpu: np.ndarray, h_or64: np.ndarray, what: str = "") -> float:
@@ -41,18 +49,20 @@ def check_hessian(h_gpu: np.ndarray, h_or64: np.ndarray, what: str = "") -> floa
     return float(rel.max()) if rel.size else 0.0
 
 
-def tau_for(w_sel: np.ndarray, q_sel: np.ndarray, h_sel: np.ndarray) -> np.ndarray:
-    """1e-7 * sum |H||dw||dw| for each selected block (fp64)."""
+def abs_form(w_sel: np.ndarray, q_sel: np.ndarray, h_sel: np.ndarray) -> np.ndarray:
+    """S = sum_ij |H_ij| |dw_i| |dw_j| for each selected block (fp64)."""
     dw = np.abs(q_sel.astype(np.float64) - w_sel.astype(np.float64))
-    return 1e-7 * np.einsum("ni,nij,nj->n", dw, np.abs(h_sel.astype(np.float64)), dw)
+    return np.einsum("ni,nij,nj->n", dw, np.abs(h_sel.astype(np.float64)), dw)
 
 
-def check_sweep(gpu_idx, gpu_err, gpu_amax, orc: dict, tau: np.ndarray, what: str = "") -> dict:
-    """gpu_* are compact arrays for the same selected blocks as the oracle dict."""
+def check_sweep(gpu_idx, gpu_err, gpu_amax, orc: dict, S: np.ndarray, what: str = "") -> dict:
+    """gpu_* are compact arrays for the same selected blocks as the oracle
+    dict; S = sum |H||dw||dw| at the oracle's best candidate."""
     gi = np.asarray(gpu_idx).astype(np.int64)
     oi = orc["idx"].astype(np.int64)
     e1, e2 = orc["e1"], orc["e2"]
-    near_tie = (e2 == 0) | ((e2 - e1) < TIE_RTOL * e2)
+    bound = FP32_GAMMA * S
+    near_tie = (e2 == 0) | ((e2 - e1) < np.maximum(TIE_RTOL * e2, 2 * bound))
     mism = (gi != oi) & ~near_tie
     if mism.any():
         n = int(np.flatnonzero(mism)[0])
@@ -61,7 +71,7 @@ def check_sweep(gpu_idx, gpu_err, gpu_amax, orc: dict, tau: np.ndarray, what: st
     stats = dict(n=len(gi), near_tie=int(near_tie.sum()), idx_diff_in_ties=int(((gi != oi) & near_tie).sum()))
     if gpu_err is not None:
         ge = np.asarray(gpu_err, np.float64)
-        tol = ERR_RTOL * np.maximum(e1, tau)
+        tol = np.maximum(ERR_RTOL * e1, bound)
         bad = np.abs(ge - e1) > tol
         if bad.any():
             n = int(np.flatnonzero(bad)[0])
@@ -97,16 +107,16 @@ def sweep_against_oracle(w_np, h_np, amax_np, c_out, c_in, n_groups, sel, gpu_id
     """Run the oracle sweep on `sel` with the GPU's H and compare."""
     nb = c_in // 16
     res = oracle.sweep(w_np, h_np, amax_np, c_out, c_in, n_groups=n_groups, sel=sel)
-    # tau from the oracle's chosen candidate
+    # S from the oracle's chosen candidate
     idx_full = np.zeros(n_groups * c_out * nb, np.uint8)
     idx_full[sel] = res["idx"].astype(np.uint8)
     fq = oracle.fake_quant(w_np, idx_full, amax_np, c_out, c_in, n_groups=n_groups, sel=sel)
     grp = sel // (c_out * nb)
     hb = h_np.reshape(n_groups, nb, 16, 16)[grp, sel % nb]
-    tau = tau_for(block_rows(w_np, sel, c_out, c_in), fq["q"], hb)
+    S = abs_form(block_rows(w_np, sel, c_out, c_in), fq["q"], hb)
     ge = None if gpu_err_full is None else gpu_err_full.reshape(-1)[sel]
     ga = None if gpu_amax_full is None else gpu_amax_full.reshape(-1)[sel]
-    return check_sweep(gpu_idx_full.reshape(-1)[sel], ge, ga, res, tau, what)
+    return check_sweep(gpu_idx_full.reshape(-1)[sel], ge, ga, res, S, what)
 
 
 def fake_quant_against_oracle(w_np, idx_full, amax_np, c_out, c_in, n_groups, sel, gpu: dict, what=""):
