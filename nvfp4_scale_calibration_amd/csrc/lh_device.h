@@ -61,11 +61,4 @@ __device__ __forceinline__ float e2m1_round_mag(float x) {
   return (xc + magic) - magic;
 }
 
-// E2M1 magnitude code (0..7) of a grid value produced by e2m1_round_mag.
-__device__ __forceinline__ uint32_t e2m1_code_of(float r) {
-  // 0 -> 0, 0.5 -> 1, 1 -> 2, 1.5 -> 3, 2 -> 4, 3 -> 5, 4 -> 6, 6 -> 7
-  if (r < 2.0f) return (uint32_t)(r * 2.0f);
-  return r == 2.0f ? 4u : (r == 3.0f ? 5u : (r == 4.0f ? 6u : 7u));
-}
-
 }  // namespace lh

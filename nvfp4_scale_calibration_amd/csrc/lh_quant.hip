@@ -49,7 +49,14 @@ __device__ __forceinline__ void load16(const T* p, float (&w)[16]) {
   }
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
 // One thread per 16-weight block.  Outputs are dense and each optional.
+// x = fl32(w / s) by IEEE division; v_cvt_scalef32_pk_fp4_f32 (scale 1)
+// rounds pairs of x to signed E2M1 nibbles (nearest, ties to even,
+// saturating), which is the packed output once a sign on a zero magnitude is
+// cleared (-0 is written as +0); v_cvt_scalef32_pk_f32_fp4 decodes them and
+// Q = fl32(r * s).  s == 0 (amax 0) gives x = 0 for every weight.
 template <typename T, bool kVec>
 __global__ __launch_bounds__(kThreads) void fake_quant_kernel(const T* __restrict__ wt, int64_t c_out,
                                                               int64_t ld_w, int64_t gstride_w, int64_t nb,
@@ -68,31 +75,40 @@ __global__ __launch_bounds__(kThreads) void fake_quant_kernel(const T* __restric
   const float s = e4m3_candidate(k) * Sg;
   float w[16];
   load16<T, kVec>(wt + grp * gstride_w + row * ld_w + 16 * b, w);
-  float q[16];
-  uint32_t nib[16];
+  float x[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float x = (s == 0.0f) ? 0.0f : fabsf(w[i]) / s;  // IEEE division
-    const float r = e2m1_round_mag(x);
-    const float mag = r * s;
-    const bool neg = (w[i] < 0.0f) && (mag != 0.0f);
-    q[i] = neg ? -mag : mag;  // -0 never produced
-    nib[i] = e2m1_code_of(r) | (neg ? 8u : 0u);
+  for (int i = 0; i < 16; ++i) x[i] = (s == 0.0f) ? 0.0f : w[i] / s;  // IEEE division
+  uint32_t pk[2] = {0u, 0u};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], x[8 * h + 0], x[8 * h + 1], 1.0f, 0);
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], x[8 * h + 2], x[8 * h + 3], 1.0f, 1);
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], x[8 * h + 4], x[8 * h + 5], 1.0f, 2);
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], x[8 * h + 6], x[8 * h + 7], 1.0f, 3);
+    // keep the sign bit (bit 3 of a nibble) only where the magnitude is non-zero
+    const uint32_t nz = (pk[h] | (pk[h] >> 1) | (pk[h] >> 2)) & 0x11111111u;
+    pk[h] &= 0x77777777u | (nz << 3);
   }
-  const int64_t c_in = nb * 16;
   if (wq) {
-    float4* o = reinterpret_cast<float4*>(wq + rg * c_in + 16 * b);
+    float q[16];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int byte = 0; byte < 4; ++byte) {
+        f32x2_t r;
+        if (byte == 0) r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 0);
+        else if (byte == 1) r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 1);
+        else if (byte == 2) r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 2);
+        else r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 3);
+        q[8 * h + 2 * byte] = r.x * s;       // Q = fl32(r * s)
+        q[8 * h + 2 * byte + 1] = r.y * s;
+      }
+    }
+    float4* o = reinterpret_cast<float4*>(wq + rg * (nb * 16) + 16 * b);
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd) o[qd] = make_float4(q[4 * qd], q[4 * qd + 1], q[4 * qd + 2], q[4 * qd + 3]);
   }
-  if (packed) {
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) lo |= nib[i] << (4 * i);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) hi |= nib[8 + i] << (4 * i);
-    *reinterpret_cast<uint2*>(packed + rg * (c_in / 2) + 8 * b) = make_uint2(lo, hi);
-  }
+  if (packed) *reinterpret_cast<uint2*>(packed + rg * (nb * 8) + 8 * b) = make_uint2(pk[0], pk[1]);
   if (codes) codes[f] = (uint8_t)(k + 1);
 }
 
@@ -131,7 +147,23 @@ __global__ void absmax_init_kernel(float* __restrict__ out, int64_t n) {
   if (i < n) out[i] = 0.0f;
 }
 
-template <typename T, bool kVec>
+__device__ __forceinline__ uint32_t absbits_max(uint32_t m, const uint4 u, bool bf16) {
+  const uint32_t v[4] = {u.x, u.y, u.z, u.w};
+  if (bf16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, max((v[i] << 16) & 0x7FFF0000u, v[i] & 0x7FFF0000u));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, v[i] & 0x7FFFFFFFu);
+  }
+  return m;
+}
+
+// Contiguous groups (ld == cols): the group is one flat array of n16 16-byte
+// vectors; grid-stride loop with four loads in flight per thread.
+// Otherwise rows are walked one by one (kFlat == false), vectorised when the
+// row length and strides allow (kVec).
+template <typename T, bool kVec, bool kFlat>
 __global__ __launch_bounds__(kThreads) void absmax_kernel(const T* __restrict__ w, int64_t rows, int64_t cols,
                                                           int64_t ld, int64_t gstride, int64_t per_group,
                                                           float* __restrict__ out) {
@@ -139,31 +171,35 @@ __global__ __launch_bounds__(kThreads) void absmax_kernel(const T* __restrict__ 
   const int64_t grp = (int64_t)blockIdx.x / per_group;
   const int64_t chunk = (int64_t)blockIdx.x - grp * per_group;
   const T* base = w + grp * gstride;
+  constexpr bool kBf16 = sizeof(T) == 2;
   uint32_t m = 0;
-  constexpr int kV = 16 / sizeof(T);
-  for (int64_t r = chunk; r < rows; r += per_group) {
-    const T* rp = base + r * ld;
-    if (kVec) {
-      for (int64_t c = (int64_t)threadIdx.x * kV; c < cols; c += (int64_t)kThreads * kV) {
-        const uint4 u = *reinterpret_cast<const uint4*>(rp + c);
-        const uint32_t v[4] = {u.x, u.y, u.z, u.w};
-        if constexpr (sizeof(T) == 2) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = (v[i] << 16) & 0x7FFF0000u, hi = v[i] & 0x7FFF0000u;
-            m = max(m, max(lo, hi));
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) m = max(m, v[i] & 0x7FFFFFFFu);
+  if (kFlat) {
+    const uint4* v = reinterpret_cast<const uint4*>(base);
+    const int64_t n16 = rows * cols * (int64_t)sizeof(T) / 16;
+    const int64_t stride = per_group * kThreads;
+    int64_t i = chunk * kThreads + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+      const uint4 a = v[i], b = v[i + stride], c = v[i + 2 * stride], d = v[i + 3 * stride];
+      m = absbits_max(m, a, kBf16);
+      m = absbits_max(m, b, kBf16);
+      m = absbits_max(m, c, kBf16);
+      m = absbits_max(m, d, kBf16);
+    }
+    for (; i < n16; i += stride) m = absbits_max(m, v[i], kBf16);
+  } else {
+    constexpr int kV = 16 / sizeof(T);
+    for (int64_t r = chunk; r < rows; r += per_group) {
+      const T* rp = base + r * ld;
+      if (kVec) {
+        for (int64_t c = (int64_t)threadIdx.x * kV; c < cols; c += (int64_t)kThreads * kV)
+          m = absbits_max(m, *reinterpret_cast<const uint4*>(rp + c), kBf16);
+      } else {
+        for (int64_t c = threadIdx.x; c < cols; c += kThreads) {
+          uint32_t bits;
+          if constexpr (kBf16) bits = (uint32_t)rp[c] << 16;
+          else bits = __float_as_uint(rp[c]);
+          m = max(m, bits & 0x7FFFFFFFu);
         }
-      }
-    } else {
-      for (int64_t c = threadIdx.x; c < cols; c += kThreads) {
-        uint32_t bits;
-        if constexpr (sizeof(T) == 2) bits = (uint32_t)rp[c] << 16;
-        else bits = __float_as_uint(rp[c]);
-        m = max(m, bits & 0x7FFFFFFFu);
       }
     }
   }
@@ -179,12 +215,20 @@ __global__ __launch_bounds__(kThreads) void absmax_kernel(const T* __restrict__ 
   }
 }
 
-template <typename T, bool kVec>
+template <typename T, bool kVec, bool kFlat>
 hipError_t launch_absmax_typed(const AbsmaxArgs& a, hipStream_t stream) {
-  int64_t per_group = (2048 + a.n_groups - 1) / a.n_groups;
-  if (per_group > a.rows) per_group = a.rows;
+  int64_t per_group;
+  if (kFlat) {
+    const int64_t n16 = a.rows * a.cols * (int64_t)sizeof(T) / 16;
+    per_group = (1024 + a.n_groups - 1) / a.n_groups;              // ~4 workgroups per CU in total
+    const int64_t need = (n16 + 4 * kThreads - 1) / (4 * kThreads);  // >= 4 vectors per thread
+    if (per_group > need) per_group = need;
+  } else {
+    per_group = (2048 + a.n_groups - 1) / a.n_groups;
+    if (per_group > a.rows) per_group = a.rows;
+  }
   if (per_group < 1) per_group = 1;
-  absmax_kernel<T, kVec><<<dim3((unsigned)(per_group * a.n_groups)), dim3(kThreads), 0, stream>>>(
+  absmax_kernel<T, kVec, kFlat><<<dim3((unsigned)(per_group * a.n_groups)), dim3(kThreads), 0, stream>>>(
       static_cast<const T*>(a.w), a.rows, a.cols, a.ld, a.gstride, per_group, a.out);
   return hipGetLastError();
 }
@@ -211,9 +255,14 @@ hipError_t launch_absmax(const AbsmaxArgs& a, hipStream_t stream) {
   const int64_t epv = 16 / esz;
   const bool aligned = (reinterpret_cast<uintptr_t>(a.w) % 16 == 0) && (a.ld % epv == 0) &&
                        (a.gstride % epv == 0) && (a.cols % epv == 0);
-  if (a.dtype == 1)
-    return aligned ? launch_absmax_typed<uint16_t, true>(a, stream) : launch_absmax_typed<uint16_t, false>(a, stream);
-  return aligned ? launch_absmax_typed<float, true>(a, stream) : launch_absmax_typed<float, false>(a, stream);
+  const bool flat = aligned && (a.ld == a.cols || a.rows == 1);
+  if (a.dtype == 1) {
+    if (flat) return launch_absmax_typed<uint16_t, true, true>(a, stream);
+    return aligned ? launch_absmax_typed<uint16_t, true, false>(a, stream)
+                   : launch_absmax_typed<uint16_t, false, false>(a, stream);
+  }
+  if (flat) return launch_absmax_typed<float, true, true>(a, stream);
+  return aligned ? launch_absmax_typed<float, true, false>(a, stream) : launch_absmax_typed<float, false, false>(a, stream);
 }
 
 }  // namespace lh

@@ -59,8 +59,8 @@ struct Best {
 };
 
 __device__ __forceinline__ void keep_best(Best& b, float e, int k) {
-  // lowest index on equal errors
-  const bool take = (e < b.err) || (e == b.err && k < b.k);
+  // lowest index on equal errors (bitwise ops: no branches)
+  const bool take = (e < b.err) | ((e == b.err) & (k < b.k));
   b.err = take ? e : b.err;
   b.k = take ? k : b.k;
 }
@@ -82,20 +82,34 @@ __device__ __forceinline__ float quad_form(const float (&diag)[16], const float 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // Candidate k with scale s = 2^j * sigma, from the per-mantissa quotients
-// p_i = fl32(w_i / sigma) (signed).
+// p_i = fl32(w_i / sigma) (signed).  The eight FP4 pairs are packed into the
+// four bytes of two dwords (byte select 0..3); `pk` carries them from one
+// candidate to the next so no register has to be cleared first.
 __device__ __forceinline__ void eval_scaled(Best& best, int k, int j, float sigma, const float (&p)[16],
                                             const float (&w)[16], const float (&diag)[16],
-                                            const float (&sym)[120]) {
+                                            const float (&sym)[120], uint32_t (&pk)[2]) {
   const float s = ldexpf(sigma, j);
   const float pow2j = __uint_as_float((uint32_t)(127 + j) << 23);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 0], p[8 * h + 1], pow2j, 0);
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 2], p[8 * h + 3], pow2j, 1);
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 4], p[8 * h + 5], pow2j, 2);
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 6], p[8 * h + 7], pow2j, 3);
+  }
+  float r[16];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const f32x2_t r0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 0);
+    const f32x2_t r1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 1);
+    const f32x2_t r2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 2);
+    const f32x2_t r3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 3);
+    r[8 * h + 0] = r0.x; r[8 * h + 1] = r0.y; r[8 * h + 2] = r1.x; r[8 * h + 3] = r1.y;
+    r[8 * h + 4] = r2.x; r[8 * h + 5] = r2.y; r[8 * h + 6] = r3.x; r[8 * h + 7] = r3.y;
+  }
   float dw[16];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, p[2 * i], p[2 * i + 1], pow2j, 0);
-    const f32x2_t r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
-    dw[2 * i] = r.x * s - w[2 * i];          // Q = fl32(r * s), then Q - w
-    dw[2 * i + 1] = r.y * s - w[2 * i + 1];
-  }
+  for (int i = 0; i < 16; ++i) dw[i] = r[i] * s - w[i];  // Q = fl32(r * s), then Q - w
   keep_best(best, quad_form(diag, sym, dw), k);
 }
 
@@ -117,27 +131,28 @@ __device__ __forceinline__ void eval_direct(Best& best, int k, float Sg, int e, 
 // All candidates of mantissa class m (mu = 1 + m/8), in increasing index.
 template <int m>
 __device__ __forceinline__ void sweep_mantissa(Best& best, float Sg, const float (&w)[16],
-                                               const float (&diag)[16], const float (&sym)[120]) {
+                                               const float (&diag)[16], const float (&sym)[120],
+                                               uint32_t (&pk)[2]) {
   const float sigma = (1.0f + 0.125f * (float)m) * Sg;  // fl32(mu * S_g)
   float p[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) p[i] = w[i] / sigma;  // IEEE division
   // subnormal E4M3 codes that share this mantissa: code = 1..7 -> k = code-1
   if constexpr (m == 0) {
-    eval_scaled(best, 0, -9, sigma, p, w, diag, sym);   // 1 * 2^-9
-    eval_scaled(best, 1, -8, sigma, p, w, diag, sym);   // 2 * 2^-9
-    eval_scaled(best, 3, -7, sigma, p, w, diag, sym);   // 4 * 2^-9
+    eval_scaled(best, 0, -9, sigma, p, w, diag, sym, pk);   // 1 * 2^-9
+    eval_scaled(best, 1, -8, sigma, p, w, diag, sym, pk);   // 2 * 2^-9
+    eval_scaled(best, 3, -7, sigma, p, w, diag, sym, pk);   // 4 * 2^-9
   } else if constexpr (m == 2) {
-    eval_scaled(best, 4, -7, sigma, p, w, diag, sym);   // 5 * 2^-9
+    eval_scaled(best, 4, -7, sigma, p, w, diag, sym, pk);   // 5 * 2^-9
   } else if constexpr (m == 4) {
-    eval_scaled(best, 2, -8, sigma, p, w, diag, sym);   // 3 * 2^-9
-    eval_scaled(best, 5, -7, sigma, p, w, diag, sym);   // 6 * 2^-9
+    eval_scaled(best, 2, -8, sigma, p, w, diag, sym, pk);   // 3 * 2^-9
+    eval_scaled(best, 5, -7, sigma, p, w, diag, sym, pk);   // 6 * 2^-9
   } else if constexpr (m == 6) {
-    eval_scaled(best, 6, -7, sigma, p, w, diag, sym);   // 7 * 2^-9
+    eval_scaled(best, 6, -7, sigma, p, w, diag, sym, pk);   // 7 * 2^-9
   }
   // normal codes 8E + m (E = 1..15; code 0x7F is NaN): value mu * 2^(E-7)
   constexpr int emax = (m == 7) ? 14 : 15;
-  for (int E = 1; E <= emax; ++E) eval_scaled(best, 8 * E + m - 1, E - 7, sigma, p, w, diag, sym);
+  for (int E = 1; E <= emax; ++E) eval_scaled(best, 8 * E + m - 1, E - 7, sigma, p, w, diag, sym, pk);
 }
 
 template <typename T, bool kVec>
@@ -223,17 +238,18 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const T* __restrict__ w
     float w[16];
     load_block<T, kVec>(wt + grp * gstride_w + row * ld_w + 16 * b, w);
     Best best{INFINITY, kCandidates};
+    uint32_t pk[2] = {0u, 0u};
     if (fast) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) w[i] = ldexpf(w[i], -e);
-      sweep_mantissa<0>(best, Su, w, diag, sym);
-      sweep_mantissa<1>(best, Su, w, diag, sym);
-      sweep_mantissa<2>(best, Su, w, diag, sym);
-      sweep_mantissa<3>(best, Su, w, diag, sym);
-      sweep_mantissa<4>(best, Su, w, diag, sym);
-      sweep_mantissa<5>(best, Su, w, diag, sym);
-      sweep_mantissa<6>(best, Su, w, diag, sym);
-      sweep_mantissa<7>(best, Su, w, diag, sym);
+      sweep_mantissa<0>(best, Su, w, diag, sym, pk);
+      sweep_mantissa<1>(best, Su, w, diag, sym, pk);
+      sweep_mantissa<2>(best, Su, w, diag, sym, pk);
+      sweep_mantissa<3>(best, Su, w, diag, sym, pk);
+      sweep_mantissa<4>(best, Su, w, diag, sym, pk);
+      sweep_mantissa<5>(best, Su, w, diag, sym, pk);
+      sweep_mantissa<6>(best, Su, w, diag, sym, pk);
+      sweep_mantissa<7>(best, Su, w, diag, sym, pk);
     } else {
       for (int k = 0; k < kCandidates; ++k) eval_direct(best, k, Sg, e, w, diag, sym);
     }
