@@ -168,6 +168,7 @@ def main():
     h = torch.empty((G, nb, 16, 16), dtype=torch.float32, device=dev)
     ws_bytes = lh.lh_hessian_workspace_bytes(c_in, n, G)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    sws = torch.empty(max(lh.lh_sweep_workspace_bytes(c_in, G), 4), dtype=torch.uint8, device=dev)
     idx = torch.empty((G, c_out, nb), dtype=torch.uint8, device=dev)
     err = torch.empty((G, c_out, nb), dtype=torch.float32, device=dev)
     bam = torch.empty((G, c_out, nb), dtype=torch.float32, device=dev)
@@ -187,7 +188,7 @@ def main():
         mark(1)
         lh.lh_accumulate_hessian(x, h=h, workspace=ws if ws_bytes else None)
         mark(2)
-        lh.lh_scale_sweep(w, h, amax, best_idx=idx, best_err=err, best_amax=bam)
+        lh.lh_scale_sweep(w, h, amax, best_idx=idx, best_err=err, best_amax=bam, workspace=sws)
         mark(3)
         lh.lh_fake_quant_nvfp4(w, idx, amax, w_q=wq, packed=packed, scale_e4m3=codes, global_scale=gscale)
         mark(4)

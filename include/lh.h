@@ -131,7 +131,7 @@ size_t lh_hessian_workspace_bytes(int64_t c_in, int64_t n_tokens, int64_t n_grou
  *            (>= (c_in/16)*256 when n_groups > 1), read (beta != 0) and written.
  *   workspace, workspace_bytes: NULL/0, or a device buffer of at least
  *            lh_hessian_workspace_bytes(c_in, n_tokens, n_groups) bytes,
- *            256-byte aligned; contents on entry are ignored.
+ *            4-byte aligned; contents on entry are ignored.
  * c_in % 16 == 0.  Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_DTYPE,
  * LH_ERR_LAYOUT, LH_ERR_WORKSPACE, LH_ERR_HIP.
  */
@@ -140,6 +140,15 @@ lh_status lh_accumulate_hessian(const void *x, int x_dtype, int layout, int64_t 
                                 int64_t group_stride_x, float alpha, float beta, float *h,
                                 int64_t group_stride_h, void *workspace, size_t workspace_bytes,
                                 void *stream);
+
+/*
+ * Scratch bytes that let lh_scale_sweep skip provably worse candidates with a
+ * tight per-block certificate (a lower bound on the smallest eigenvalue of
+ * the block's correlation matrix, one fp32 per block).  0 bytes is always
+ * accepted: the sweep then uses a weaker certificate computed on the fly.
+ * Results are identical either way; only the speed differs.
+ */
+size_t lh_sweep_workspace_bytes(int64_t c_in, int64_t n_groups);
 
 /*
  * Local-Hessian scale sweep ("Algorithm principle": per 16-weight block,
@@ -153,20 +162,27 @@ lh_status lh_accumulate_hessian(const void *x, int x_dtype, int layout, int64_t 
  *   best_idx [g][r][b] = k*              (E4M3 block-scale code = k* + 1)
  *   best_err [g][r][b] = E_k* (fp32)     (optional)
  *   best_amax[g][r][b] = fl32(6 * s_k*)  (optional; the per-block amax)
+ * The minimum is exact over all 126 candidates: a candidate is only skipped
+ * when a certified lower bound proves it worse than one already evaluated.
  *   w         weights, w_dtype, row stride ld_w >= c_in, group stride
  *             group_stride_w (>= 0).
- *   h         fp32 [n_groups][c_in/16][16][16] (any square matrix is used as
- *             given; the Hessian output of lh_accumulate_hessian fits),
- *             group stride group_stride_h (>= 0).
+ *   h         fp32 [n_groups][c_in/16][16][16], 16-byte aligned (any square
+ *             matrix is used as given; the output of lh_accumulate_hessian
+ *             fits), group stride group_stride_h (>= 0, multiple of 4).
  *   amax      fp32 [n_groups] (device), e.g. from lh_absmax.
  *   best_idx  uint8 [n_groups][c_out][c_in/16], required.
  *   best_err, best_amax  fp32, same shape, NULL to skip.
- * Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_HIP.
+ *   workspace, workspace_bytes: NULL/0, or a device buffer of at least
+ *             lh_sweep_workspace_bytes(c_in, n_groups) bytes, 4-byte
+ *             aligned; contents on entry are ignored.
+ * Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_WORKSPACE,
+ * LH_ERR_ARG, LH_ERR_HIP.
  */
 lh_status lh_scale_sweep(const void *w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
                          int64_t n_groups, int64_t group_stride_w, const float *h,
                          int64_t group_stride_h, const float *amax, uint8_t *best_idx,
-                         float *best_err, float *best_amax, void *stream);
+                         float *best_err, float *best_amax, void *workspace,
+                         size_t workspace_bytes, void *stream);
 
 /*
  * NVFP4 fake-quant with chosen block scales ("Algorithm principle":

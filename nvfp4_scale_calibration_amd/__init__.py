@@ -51,7 +51,9 @@ def _load() -> ctypes.CDLL:
     lib.lh_hessian_workspace_bytes.restype = SZ
     lib.lh_accumulate_hessian.argtypes = [P, I, I, I64, I64, I64, I64, I64, F, F, P, I64, P, SZ, P]
     lib.lh_accumulate_hessian.restype = I
-    lib.lh_scale_sweep.argtypes = [P, I, I64, I64, I64, I64, I64, P, I64, P, P, P, P, P]
+    lib.lh_sweep_workspace_bytes.argtypes = [I64, I64]
+    lib.lh_sweep_workspace_bytes.restype = SZ
+    lib.lh_scale_sweep.argtypes = [P, I, I64, I64, I64, I64, I64, P, I64, P, P, P, P, P, SZ, P]
     lib.lh_scale_sweep.restype = I
     lib.lh_fake_quant_nvfp4.argtypes = [P, I, I64, I64, I64, I64, I64, P, P, P, P, P, P, P]
     lib.lh_fake_quant_nvfp4.restype = I
@@ -60,7 +62,7 @@ def _load() -> ctypes.CDLL:
 
 lib = _load()
 EXPORTS = ("lh_abi_version", "lh_status_string", "lh_last_error_message", "lh_absmax",
-           "lh_hessian_workspace_bytes", "lh_accumulate_hessian", "lh_scale_sweep",
+           "lh_hessian_workspace_bytes", "lh_accumulate_hessian", "lh_sweep_workspace_bytes", "lh_scale_sweep",
            "lh_fake_quant_nvfp4")
 
 
@@ -170,12 +172,19 @@ def lh_accumulate_hessian(x: torch.Tensor, layout: str = "channel", alpha: float
     return h
 
 
+def lh_sweep_workspace_bytes(c_in: int, n_groups: int = 1) -> int:
+    return int(lib.lh_sweep_workspace_bytes(c_in, n_groups))
+
+
 def lh_scale_sweep(w: torch.Tensor, h: torch.Tensor, amax: torch.Tensor,
                    best_idx: torch.Tensor | None = None, best_err: torch.Tensor | bool | None = True,
-                   best_amax: torch.Tensor | bool | None = True):
+                   best_amax: torch.Tensor | bool | None = True,
+                   workspace: torch.Tensor | bool | None = True):
     """Per-block best candidate index (E4M3 code = idx + 1), its error
     dw^T H_b dw and the per-block amax 6 * s_idx.  Returns (idx, err, amax);
-    err / amax are None when not requested (False/None)."""
+    err / amax are None when not requested (False/None).  workspace=True
+    allocates the certificate scratch the library asks for (faster skipping),
+    False/None runs without it, a device tensor is used as given."""
     _require_device(w, h, amax)
     w3 = _as3(w)
     if w3.stride(-1) != 1:
@@ -193,9 +202,16 @@ def lh_scale_sweep(w: torch.Tensor, h: torch.Tensor, amax: torch.Tensor,
     best_err = best_err if isinstance(best_err, torch.Tensor) else None
     best_amax = best_amax if isinstance(best_amax, torch.Tensor) else None
     h_gstride = h.stride(0) if h.dim() == 4 and h.shape[0] > 1 else 0
+    ws, ws_bytes = None, 0
+    if workspace is True:
+        ws_bytes = lh_sweep_workspace_bytes(c_in, g)
+        if ws_bytes:
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    elif isinstance(workspace, torch.Tensor):
+        ws, ws_bytes = workspace, workspace.numel() * workspace.element_size()
     _check(lib.lh_scale_sweep(_ptr(w3), _dtype(w3), c_out, c_in, _ld(w3), g, _group_stride(w3),
                               _ptr(h), h_gstride, _ptr(amax), _ptr(best_idx), _ptr(best_err),
-                              _ptr(best_amax), _stream(w)))
+                              _ptr(best_amax), _ptr(ws), ws_bytes, _stream(w)))
     return best_idx, best_err, best_amax
 
 

@@ -105,10 +105,16 @@ lh_status lh_accumulate_hessian(const void* x, int x_dtype, int layout, int64_t 
   return e == hipSuccess ? LH_OK : hip_fail(e, fn);
 }
 
+size_t lh_sweep_workspace_bytes(int64_t c_in, int64_t n_groups) {
+  if (c_in <= 0 || n_groups <= 0 || c_in % 16 != 0) return 0;
+  return lh::sweep_ws_bytes(c_in, n_groups);
+}
+
 lh_status lh_scale_sweep(const void* w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
                          int64_t n_groups, int64_t group_stride_w, const float* h,
                          int64_t group_stride_h, const float* amax, uint8_t* best_idx,
-                         float* best_err, float* best_amax, void* stream) {
+                         float* best_err, float* best_amax, void* workspace, size_t workspace_bytes,
+                         void* stream) {
   const char* fn = "lh_scale_sweep";
   g_msg[0] = '\0';
   if (!valid_dtype(w_dtype)) return fail(LH_ERR_DTYPE, "%s: w_dtype must be 0 (f32) or 1 (bf16)", fn);
@@ -123,9 +129,13 @@ lh_status lh_scale_sweep(const void* w, int w_dtype, int64_t c_out, int64_t c_in
     return fail(LH_ERR_ARG, "%s: pointer not aligned to its element size", fn);
   if (!aligned(h, 16) || group_stride_h % 4 != 0)
     return fail(LH_ERR_ARG, "%s: h must be 16-byte aligned and group_stride_h a multiple of 4", fn);
+  if (workspace == nullptr && workspace_bytes > 0) return fail(LH_ERR_NULL, "%s: workspace is NULL but workspace_bytes > 0", fn);
+  if (!aligned(workspace, 4)) return fail(LH_ERR_ARG, "%s: workspace not 4-byte aligned", fn);
+  if (workspace != nullptr && workspace_bytes > 0 && work && workspace_bytes < lh::sweep_ws_bytes(c_in, n_groups))
+    return fail(LH_ERR_WORKSPACE, "%s: workspace smaller than lh_sweep_workspace_bytes()", fn);
   if (!work) return LH_OK;
   lh::SweepArgs a{w, w_dtype, c_out, c_in, ld_w, n_groups, group_stride_w, h, group_stride_h, amax,
-                  best_idx, best_err, best_amax};
+                  best_idx, best_err, best_amax, workspace, workspace_bytes};
   hipError_t e = lh::launch_sweep(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LH_OK : hip_fail(e, fn);
 }

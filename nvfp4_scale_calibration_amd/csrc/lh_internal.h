@@ -40,7 +40,10 @@ struct SweepArgs {
   uint8_t* idx;
   float* err;
   float* best_amax;
+  void* ws;       // nullable: per-block skip certificates
+  size_t ws_bytes;
 };
+size_t sweep_ws_bytes(int64_t c_in, int64_t n_groups);
 hipError_t launch_sweep(const SweepArgs& a, hipStream_t stream);
 
 struct FakeQuantArgs {

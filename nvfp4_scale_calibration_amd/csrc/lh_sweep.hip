@@ -33,6 +33,21 @@
 // signed grid values.  Then Q = fl32(r * s) and dw = Q - w.  Three VALU
 // instructions per weight and candidate.
 //
+// Skipping (exact): for a symmetric H with positive diagonal and
+// C = D^-1/2 H D^-1/2 (D = diag H), Gershgorin gives lambda_min(C) >= gamma =
+// 1 - max_i sum_{j != i} |C_ij|, so every candidate satisfies
+// E_k >= gamma * sum_i H_ii dw_i^2 >= gamma * sum_{e in T} H_ee dw_e^2 for any
+// subset T.  Each lane keeps T = its four elements with the largest
+// H_ii w_i^2; the bound costs ~20 VALU operations against ~207 for a full
+// evaluation.  A candidate is skipped only when every lane of the wave proves
+// lb > best * (1 + 2^-10); the skipped candidate then cannot be the minimum
+// or tie with it, so indices and errors are bit-identical to the exhaustive
+// loop.  The margin covers fp32 rounding of the bound and of E, which for
+// gamma >= 0.1 (cond(C) <= 19) is below 1e-4 relative; lanes with smaller
+// gamma (or a non-positive diagonal) never vote to skip.  Each row first
+// evaluates the lane's max-scaling candidate with the same arithmetic as the
+// loop, so the bound has a good incumbent from the start.
+//
 // Units: the lane works in units of 2^e with e = ilogb(S_g): w' = w 2^-e and
 // sigma' = sigma 2^-e are exact, so every Q', dw' = dw 2^-e and the error
 // E' = E 2^-2e are the same fp32 numbers scaled by a power of two (identical
@@ -128,31 +143,109 @@ __device__ __forceinline__ void eval_direct(Best& best, int k, float Sg, int e, 
   keep_best(best, quad_form(diag, sym, dw), k);
 }
 
+constexpr float kSkipMargin = 1.0f + 0x1p-10f;
+
+// Per-row state of the skip test: the four bound elements (prescaled weights,
+// gamma * H_ee) and their packed FP4 codes.
+struct SkipSet {
+  float w[4];
+  float dg[4];
+  float p[4];      // w[e] / sigma of the current mantissa class (same bits as p[idx])
+  uint32_t pk;
+  bool on;         // this lane's gamma allows skipping
+};
+
+// True when this lane cannot prove the candidate worse than its incumbent.
+__device__ __forceinline__ bool needs_eval(SkipSet& t, const Best& best, int j, float s) {
+  const float pow2j = __uint_as_float((uint32_t)(127 + j) << 23);
+  t.pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t.pk, t.p[0], t.p[1], pow2j, 0);
+  t.pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t.pk, t.p[2], t.p[3], pow2j, 1);
+  const f32x2_t r01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.pk, 1.0f, 0);
+  const f32x2_t r23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.pk, 1.0f, 1);
+  const float d0 = r01.x * s - t.w[0], d1 = r01.y * s - t.w[1];
+  const float d2 = r23.x * s - t.w[2], d3 = r23.y * s - t.w[3];
+  float lb = (t.dg[0] * d0) * d0;
+  lb = __builtin_fmaf(t.dg[1] * d1, d1, lb);
+  lb = __builtin_fmaf(t.dg[2] * d2, d2, lb);
+  lb = __builtin_fmaf(t.dg[3] * d3, d3, lb);
+  return !(t.on && lb > best.err * kSkipMargin);
+}
+
+// All candidates of mantissa class m (mu = 1 + m/8), in increasing index.
+// Evaluates candidate (k, j) unless every lane of the wave can skip it.
+__device__ __forceinline__ void try_scaled(Best& best, SkipSet& t, int k, int j, float sigma, const float (&p)[16],
+                                           const float (&w)[16], const float (&diag)[16],
+                                           const float (&sym)[120], uint32_t (&pk)[2]) {
+  const bool need = needs_eval(t, best, j, ldexpf(sigma, j));
+  if (__ballot(need) != 0) eval_scaled(best, k, j, sigma, p, w, diag, sym, pk);
+}
+
 // All candidates of mantissa class m (mu = 1 + m/8), in increasing index.
 template <int m>
-__device__ __forceinline__ void sweep_mantissa(Best& best, float Sg, const float (&w)[16],
+__device__ __forceinline__ void sweep_mantissa(Best& best, SkipSet& t, float Sg, const float (&w)[16],
                                                const float (&diag)[16], const float (&sym)[120],
                                                uint32_t (&pk)[2]) {
   const float sigma = (1.0f + 0.125f * (float)m) * Sg;  // fl32(mu * S_g)
   float p[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) p[i] = w[i] / sigma;  // IEEE division
+#pragma unroll
+  for (int e = 0; e < 4; ++e) t.p[e] = t.w[e] / sigma;  // same operation on the same bits as p[idx]
   // subnormal E4M3 codes that share this mantissa: code = 1..7 -> k = code-1
   if constexpr (m == 0) {
-    eval_scaled(best, 0, -9, sigma, p, w, diag, sym, pk);   // 1 * 2^-9
-    eval_scaled(best, 1, -8, sigma, p, w, diag, sym, pk);   // 2 * 2^-9
-    eval_scaled(best, 3, -7, sigma, p, w, diag, sym, pk);   // 4 * 2^-9
+    try_scaled(best, t, 0, -9, sigma, p, w, diag, sym, pk);   // 1 * 2^-9
+    try_scaled(best, t, 1, -8, sigma, p, w, diag, sym, pk);   // 2 * 2^-9
+    try_scaled(best, t, 3, -7, sigma, p, w, diag, sym, pk);   // 4 * 2^-9
   } else if constexpr (m == 2) {
-    eval_scaled(best, 4, -7, sigma, p, w, diag, sym, pk);   // 5 * 2^-9
+    try_scaled(best, t, 4, -7, sigma, p, w, diag, sym, pk);   // 5 * 2^-9
   } else if constexpr (m == 4) {
-    eval_scaled(best, 2, -8, sigma, p, w, diag, sym, pk);   // 3 * 2^-9
-    eval_scaled(best, 5, -7, sigma, p, w, diag, sym, pk);   // 6 * 2^-9
+    try_scaled(best, t, 2, -8, sigma, p, w, diag, sym, pk);   // 3 * 2^-9
+    try_scaled(best, t, 5, -7, sigma, p, w, diag, sym, pk);   // 6 * 2^-9
   } else if constexpr (m == 6) {
-    eval_scaled(best, 6, -7, sigma, p, w, diag, sym, pk);   // 7 * 2^-9
+    try_scaled(best, t, 6, -7, sigma, p, w, diag, sym, pk);   // 7 * 2^-9
   }
   // normal codes 8E + m (E = 1..15; code 0x7F is NaN): value mu * 2^(E-7)
   constexpr int emax = (m == 7) ? 14 : 15;
-  for (int E = 1; E <= emax; ++E) eval_scaled(best, 8 * E + m - 1, E - 7, sigma, p, w, diag, sym, pk);
+  for (int E = 1; E <= emax; ++E) try_scaled(best, t, 8 * E + m - 1, E - 7, sigma, p, w, diag, sym, pk);
+}
+
+// Mantissa class and power of two of candidate k: c_k = (1 + m/8) 2^j.
+__device__ __forceinline__ void candidate_class(int k, int& m, int& j) {
+  const int code = k + 1;
+  if (code >= 8) {
+    m = code & 7;
+    j = (code >> 3) - 7;
+    return;
+  }
+  // subnormal codes c * 2^-9, c = 1..7
+  const int cm[8] = {0, 0, 0, 4, 0, 2, 4, 6};
+  const int cj[8] = {0, -9, -8, -8, -7, -7, -7, -7};
+  m = cm[code];
+  j = cj[code];
+}
+
+// The lane's max-scaling candidate: smallest c_k >= max|w| / (6 S_g), i.e. the
+// block scale that keeps every weight on the grid without saturating.
+__device__ __forceinline__ int max_scaling_candidate(const float (&w)[16], float Su) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(w[i]));
+  float t = a / (6.0f * Su);
+  t = fminf(fmaxf(t, 0x1p-9f), 448.0f);
+  int code;
+  if (t <= 0x1p-6f) {
+    code = (int)ceilf(t * 512.0f);  // subnormal codes 1..8 (8 is 2^-6)
+  } else {
+    int e2 = ilogbf(t);
+    int mm = (int)ceilf((ldexpf(t, -e2) - 1.0f) * 8.0f);
+    if (mm == 8) {
+      mm = 0;
+      ++e2;
+    }
+    code = (e2 + 7) * 8 + mm;
+  }
+  code = code < 1 ? 1 : (code > kCandidates ? kCandidates : code);
+  return code - 1;
 }
 
 template <typename T, bool kVec>
@@ -188,6 +281,90 @@ __device__ __forceinline__ void load_block(const T* p, float (&w)[16]) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Skip certificate pre-pass.  With S = (H + H^T)/2, D = diag S and
+// C = D^-1/2 S D^-1/2 (unit diagonal), it finds a large tau with C - tau I
+// positive definite, testing each tau with an fp32 Cholesky factorisation: if every pivot is positive, the
+// computed factor is the exact factor of C - tau I + dA with
+// |dA| <= 17u |L||L^T| (Cholesky backward error), and |L||L^T| <= 1
+// entrywise, so lambda_min(C) >= tau - 16*17u.  The certificate stored is
+// tau - 2e-3.  It is zeroed (no skipping) when the diagonal is not positive
+// and finite, when it falls below 0.02, or when the fp32 error bound of the
+// quadratic form, 35u (1 + rho) / tau with rho the largest off-diagonal row
+// sum of |C| (so lambda_max(|C|) <= 1 + rho), would exceed 2^-11.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float sym_entry(const float* hb, const float (&rs)[16], int i, int j) {
+  return (i == j) ? hb[i * 17] * rs[i] * rs[i] : 0.5f * (hb[i * 16 + j] + hb[j * 16 + i]) * rs[i] * rs[j];
+}
+
+__device__ bool shifted_pd(const float* hb, const float (&rs)[16], float tau) {
+  float L[136];  // packed lower triangle: L[i (i + 1) / 2 + j], j <= i
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+#pragma unroll
+    for (int j = 0; j <= i; ++j) {
+      float a = sym_entry(hb, rs, i, j) - (i == j ? tau : 0.0f);
+#pragma unroll
+      for (int m = 0; m < j; ++m) a = __builtin_fmaf(-L[i * (i + 1) / 2 + m], L[j * (j + 1) / 2 + m], a);
+      if (i == j) {
+        if (!(a > 0.0f)) return false;
+        L[i * (i + 1) / 2 + i] = sqrtf(a);
+      } else {
+        L[i * (i + 1) / 2 + j] = a / L[j * (j + 1) / 2 + j];
+      }
+    }
+  }
+  return true;
+}
+
+// Sixteen lanes per block: lane q tests tau = q/16 (lane 0 tests the
+// Gershgorin bound, which needs no factorisation); the block keeps the
+// largest tau that passes.  One factorisation per lane keeps the latency low.
+__global__ __launch_bounds__(kThreads) void sweep_certificate_kernel(const float* __restrict__ h, int64_t gstride_h,
+                                                                     int64_t nb, int64_t total,
+                                                                     float* __restrict__ cert) {
+  const int64_t t = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 4;
+  const int q = threadIdx.x & 15;
+  const bool live = t < total;  // all 16 lanes of a block share t
+  const int64_t tc = live ? t : 0;
+  const int64_t grp = tc / nb, b = tc - grp * nb;
+  const float* hb = h + grp * gstride_h + b * 256;
+  float rs[16];
+  bool pos = true;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float d = hb[i * 17];
+    pos = pos && (d > 0.0f) && (d < INFINITY);
+    rs[i] = d > 0.0f ? 1.0f / sqrtf(d) : 0.0f;
+  }
+  float rho = 0.0f;
+  if (pos) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float r = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j != i) r += fabsf(sym_entry(hb, rs, i, j));
+      rho = fmaxf(rho, r);
+    }
+  }
+  float tau = 0.0f;
+  if (pos && live) {
+    if (q == 0) {
+      tau = fmaxf(1.0f - rho - 1e-3f, 0.0f);
+    } else {
+      const float tq = (float)q * 0.0625f;
+      tau = shifted_pd(hb, rs, tq) ? tq - 2e-3f : 0.0f;
+    }
+  }
+  // max over the 16 lanes of this block
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) tau = fmaxf(tau, __shfl_xor(tau, off, 16));
+  const float err = 35.0f * 0x1p-24f * (1.0f + rho) / tau;
+  if (!(tau >= 0.02f) || !(err <= 0x1p-11f)) tau = 0.0f;
+  if (live && q == 0) cert[t] = tau;
+}
+
 template <typename T, bool kVec>
 __global__ __launch_bounds__(kThreads) void sweep_kernel(const T* __restrict__ wt, int64_t c_out,
                                                          int64_t ld_w, int64_t gstride_w, int64_t nb,
@@ -196,7 +373,8 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const T* __restrict__ w
                                                          const float* __restrict__ amax,
                                                          uint8_t* __restrict__ idx_out,
                                                          float* __restrict__ err_out,
-                                                         float* __restrict__ amax_out) {
+                                                         float* __restrict__ amax_out,
+                                                         const float* __restrict__ cert) {
   const int64_t L = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (L >= lanes) return;
   const int64_t per_group = nb * rows_step;
@@ -228,6 +406,44 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const T* __restrict__ w
     }
   }
 
+  // Skip certificate: from the pre-pass when given, else scaled Gershgorin
+  // gamma = 1 - max_i sum_{j != i} |S_ij| / (2 sqrt(H_ii H_jj)), less 1e-3 for
+  // the rounding of this estimate, used only when >= 0.1 (then the fp32 error
+  // of E is below 35u * 19).
+  float gamma;
+  if (cert) {
+    gamma = cert[grp * nb + b];
+  } else {
+    bool pos = true;
+    float rs[16], rho[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      pos = pos && (diag[i] > 0.0f) && (diag[i] < INFINITY);
+      rs[i] = diag[i] > 0.0f ? 1.0f / sqrtf(diag[i]) : 0.0f;
+      rho[i] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int j = i + 1; j < 16; ++j) {
+        const float c = fabsf(sym[tri(i, j)]) * 0.5f * rs[i] * rs[j];
+        rho[i] += c;
+        rho[j] += c;
+      }
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, rho[i]);
+    gamma = 1.0f - mx - 1e-3f;
+    if (!pos || !(gamma >= 0.1f)) gamma = 0.0f;
+  }
+  // Per-lane scratch in LDS, element-major so that 64 lanes hit 64 consecutive
+  // words: the diagonal (fixed) and the current row's prescaled weights.
+  __shared__ float lds_diag[16][kThreads];
+  __shared__ float lds_w[16][kThreads];
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) lds_diag[i][tid] = diag[i];
+
   const float g = amax[grp];
   const float Sg = g / kAmaxDivisor;
   const bool fast = (Sg >= 0x1p-117f) && (Sg <= 0x1p127f);
@@ -242,14 +458,52 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const T* __restrict__ w
     if (fast) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) w[i] = ldexpf(w[i], -e);
-      sweep_mantissa<0>(best, Su, w, diag, sym, pk);
-      sweep_mantissa<1>(best, Su, w, diag, sym, pk);
-      sweep_mantissa<2>(best, Su, w, diag, sym, pk);
-      sweep_mantissa<3>(best, Su, w, diag, sym, pk);
-      sweep_mantissa<4>(best, Su, w, diag, sym, pk);
-      sweep_mantissa<5>(best, Su, w, diag, sym, pk);
-      sweep_mantissa<6>(best, Su, w, diag, sym, pk);
-      sweep_mantissa<7>(best, Su, w, diag, sym, pk);
+      // bound set: the four largest H_ii w_i^2 (insertion network on indices)
+      SkipSet t;
+      {
+        float kv[4] = {-1.0f, -1.0f, -1.0f, -1.0f};
+        int ki[4] = {0, 1, 2, 3};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          lds_w[i][tid] = w[i];
+          const float key = diag[i] * w[i] * w[i];
+          const bool c0 = key > kv[0], c1 = key > kv[1], c2 = key > kv[2], c3 = key > kv[3];
+          kv[3] = c2 ? kv[2] : (c3 ? key : kv[3]);
+          ki[3] = c2 ? ki[2] : (c3 ? i : ki[3]);
+          kv[2] = c1 ? kv[1] : (c2 ? key : kv[2]);
+          ki[2] = c1 ? ki[1] : (c2 ? i : ki[2]);
+          kv[1] = c0 ? kv[0] : (c1 ? key : kv[1]);
+          ki[1] = c0 ? ki[0] : (c1 ? i : ki[1]);
+          kv[0] = c0 ? key : kv[0];
+          ki[0] = c0 ? i : ki[0];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          t.w[q] = lds_w[ki[q]][tid];
+          t.dg[q] = gamma * lds_diag[ki[q]][tid];
+        }
+        t.pk = 0u;
+        t.on = gamma > 0.0f;
+      }
+      // incumbent: the max-scaling candidate, evaluated exactly as in the loop
+      {
+        const int k0 = max_scaling_candidate(w, Su);
+        int m0, j0;
+        candidate_class(k0, m0, j0);
+        const float sigma0 = (1.0f + 0.125f * (float)m0) * Su;
+        float p0[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p0[i] = w[i] / sigma0;
+        eval_scaled(best, k0, j0, sigma0, p0, w, diag, sym, pk);
+      }
+      sweep_mantissa<0>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<1>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<2>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<3>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<4>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<5>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<6>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<7>(best, t, Su, w, diag, sym, pk);
     } else {
       for (int k = 0; k < kCandidates; ++k) eval_direct(best, k, Sg, e, w, diag, sym);
     }
@@ -265,8 +519,9 @@ template <typename T, bool kVec>
 hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
   const int64_t nb = a.c_in / 16;
   const int64_t per_k = a.n_groups * nb;
-  // Enough lanes to fill 256 CUs x 4 SIMDs x 2 waves; rows split evenly.
-  const int64_t target = 256LL * 4 * 2 * 64;
+  // Two rounds of lanes at one wave per SIMD (the kernel's register use) on
+  // 256 CUs; rows split evenly.
+  const int64_t target = 256LL * 4 * 1 * 64 * 2;
   int64_t k = (target + per_k - 1) / per_k;
   if (k > a.c_out) k = a.c_out;
   if (k < 1) k = 1;
@@ -274,13 +529,25 @@ hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
   k = (a.c_out + rows_per_lane - 1) / rows_per_lane;
   const int64_t lanes = per_k * k;
   const int64_t grid = (lanes + kThreads - 1) / kThreads;
+  float* cert = nullptr;
+  if (a.ws != nullptr && a.ws_bytes >= sweep_ws_bytes(a.c_in, a.n_groups)) {
+    cert = static_cast<float*>(a.ws);
+    sweep_certificate_kernel<<<dim3((unsigned)((16 * per_k + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream>>>(
+        a.h, a.gstride_h, nb, per_k, cert);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   sweep_kernel<T, kVec><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
       static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, k, lanes, a.h, a.gstride_h, a.amax,
-      a.idx, a.err, a.best_amax);
+      a.idx, a.err, a.best_amax, cert);
   return hipGetLastError();
 }
 
 }  // namespace
+
+size_t sweep_ws_bytes(int64_t c_in, int64_t n_groups) {
+  return (size_t)n_groups * (size_t)(c_in / 16) * sizeof(float);
+}
 
 hipError_t launch_sweep(const SweepArgs& a, hipStream_t stream) {
   if (a.n_groups == 0 || a.c_out == 0 || a.c_in == 0) return hipSuccess;

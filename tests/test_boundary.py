@@ -60,12 +60,12 @@ def _msg(lib):
 def test_sweep_validation(lib):
     P = ctypes.c_void_p
     ok = dict(w=P(FAKE), dt=1, c_out=4, c_in=32, ld=32, g=1, gs=0, h=P(FAKE), hs=0, amax=P(FAKE),
-              idx=P(FAKE), err=None, am=None, st=None)
+              idx=P(FAKE), err=None, am=None, ws=None, wsb=0, st=None)
 
     def call(**kw):
         a = dict(ok, **kw)
         return lib.lh_scale_sweep(a["w"], a["dt"], a["c_out"], a["c_in"], a["ld"], a["g"], a["gs"], a["h"],
-                                  a["hs"], a["amax"], a["idx"], a["err"], a["am"], a["st"])
+                                  a["hs"], a["amax"], a["idx"], a["err"], a["am"], a["ws"], a["wsb"], a["st"])
 
     assert call(dt=7) == DTYPE
     assert call(c_in=24) == SHAPE and "multiple of 16" in _msg(lib)
@@ -76,6 +76,11 @@ def test_sweep_validation(lib):
     assert call(amax=None) == NULL
     assert call(h=P(FAKE + 4)) == ARG  # H must be 16-byte aligned
     assert call(w=P(FAKE + 1)) == ARG  # bf16 needs 2-byte alignment
+    assert call(ws=None, wsb=8) == NULL
+    assert call(ws=P(FAKE), wsb=4) == WORKSPACE   # 2 blocks need 8 bytes
+    assert call(ws=P(FAKE + 2), wsb=8) == ARG
+    assert lib.lh_sweep_workspace_bytes(32, 3) == 3 * 2 * 4
+    assert lib.lh_sweep_workspace_bytes(33, 1) == 0
     # empty problems are valid no-ops and never touch the device
     assert call(c_out=0, w=None, idx=None) == OK
     assert call(g=0) == OK

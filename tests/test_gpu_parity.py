@@ -272,3 +272,32 @@ def test_full_size_workloads_sampled(lh, n):
     benchmark times; outputs sampled for the oracle."""
     work = wl.make(n)
     check_all(lh, work, n_hess_sel=24, n_sweep_sel=3000, seed=n)
+
+
+def test_skipping_never_changes_results(lh):
+    """The sweep with the certificate pre-pass, with the on-the-fly
+    certificate, and on Hessians that admit no certificate (rank-deficient,
+    indefinite) returns bit-identical indices, errors and amax, and matches
+    the oracle."""
+    rng = np.random.default_rng(25)
+    c_out, c_in = 96, 256
+    nb = c_in // 16
+    w = torch.from_numpy((rng.standard_t(4, size=(c_out, c_in)) * 0.02).astype(np.float32)).to(DEV)
+    amax = lh.lh_absmax(w)
+    cases = []
+    for n_tok in (512, 3):  # well-conditioned; rank 3 < 16 (singular)
+        x = torch.from_numpy(rng.standard_normal((c_in, n_tok)).astype(np.float32)).to(DEV)
+        cases.append(("N=%d" % n_tok, lh.lh_accumulate_hessian(x)))
+    h_ind = cases[0][1].clone()
+    h_ind[:, :, 3, 3] = -h_ind[:, :, 3, 3]  # indefinite: no certificate
+    cases.append(("indefinite", h_ind))
+    for name, h in cases:
+        outs = [lh.lh_scale_sweep(w, h, amax, workspace=ws) for ws in (True, False)]
+        torch.cuda.synchronize()
+        for a, b in zip(outs[0], outs[1]):
+            assert torch.equal(a, b), name
+        sel = np.arange(c_out * nb)
+        w_np = w.cpu().numpy().reshape(1, c_out, c_in)
+        parity.sweep_against_oracle(w_np, h.cpu().numpy(), amax.cpu().numpy(), c_out, c_in, 1, sel,
+                                    outs[0][0].cpu().numpy(), outs[0][1].cpu().numpy(), outs[0][2].cpu().numpy(),
+                                    name)
