@@ -365,8 +365,11 @@ __global__ __launch_bounds__(kThreads) void sweep_certificate_kernel(const float
   if (live && q == 0) cert[t] = tau;
 }
 
+// Two waves per SIMD: the allocator then spills ~14 row-setup values to
+// scratch (none inside the candidate loop), which costs far less than the
+// latency a single wave per SIMD leaves exposed.
 template <typename T, bool kVec>
-__global__ __launch_bounds__(kThreads) void sweep_kernel(const T* __restrict__ wt, int64_t c_out,
+__global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const T* __restrict__ wt, int64_t c_out,
                                                          int64_t ld_w, int64_t gstride_w, int64_t nb,
                                                          int64_t rows_step, int64_t lanes,
                                                          const float* __restrict__ h, int64_t gstride_h,
@@ -519,9 +522,8 @@ template <typename T, bool kVec>
 hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
   const int64_t nb = a.c_in / 16;
   const int64_t per_k = a.n_groups * nb;
-  // Two rounds of lanes at one wave per SIMD (the kernel's register use) on
-  // 256 CUs; rows split evenly.
-  const int64_t target = 256LL * 4 * 1 * 64 * 2;
+  // Two rounds of lanes at two waves per SIMD on 256 CUs; rows split evenly.
+  const int64_t target = 256LL * 4 * 2 * 64 * 2;
   int64_t k = (target + per_k - 1) / per_k;
   if (k > a.c_out) k = a.c_out;
   if (k < 1) k = 1;
