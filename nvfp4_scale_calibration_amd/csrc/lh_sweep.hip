@@ -80,6 +80,19 @@ __device__ __forceinline__ void keep_best(Best& b, float e, int k) {
   b.k = take ? k : b.k;
 }
 
+constexpr float kSkipMargin = 1.0f + 0x1p-10f;
+
+// Per-row state of the skip test: the four bound elements (prescaled weights,
+// gamma * H_ee) and their packed FP4 codes.
+struct SkipSet {
+  float w[4];
+  float dg[4];
+  float p[4];      // w[e] / sigma of the current mantissa class (same bits as p[idx])
+  uint32_t pk;
+  float gamma;     // certificate (0 when off)
+  bool on;         // this lane's gamma allows skipping
+};
+
 // E = dw^T H dw = sum_i dw_i (H_ii dw_i + sum_{j>i} (H_ij + H_ji) dw_j)
 __device__ __forceinline__ float quad_form(const float (&diag)[16], const float (&sym)[120],
                                            const float (&dw)[16]) {
@@ -87,6 +100,20 @@ __device__ __forceinline__ float quad_form(const float (&diag)[16], const float 
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     float y = diag[i] * dw[i];
+#pragma unroll
+    for (int j = i + 1; j < 16; ++j) y = __builtin_fmaf(sym[tri(i, j)], dw[j], y);
+    e = __builtin_fmaf(dw[i], y, e);
+  }
+  return e;
+}
+
+// Same sum with the row starts y_i = H_ii dw_i already formed.
+__device__ __forceinline__ float quad_form_from(const float (&yd)[16], const float (&sym)[120],
+                                                const float (&dw)[16]) {
+  float e = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float y = yd[i];
 #pragma unroll
     for (int j = i + 1; j < 16; ++j) y = __builtin_fmaf(sym[tri(i, j)], dw[j], y);
     e = __builtin_fmaf(dw[i], y, e);
@@ -128,6 +155,47 @@ __device__ __forceinline__ void eval_scaled(Best& best, int k, int j, float sigm
   keep_best(best, quad_form(diag, sym, dw), k);
 }
 
+// eval_scaled with a second skip test after the cast: E >= gamma *
+// sum_i H_ii dw_i^2 over all 16 weights, which reuses the products H_ii dw_i
+// that start the rows of the quadratic form; the rest of the form runs only
+// if some lane of the wave still needs it.  Bit-identical E when it runs.
+__device__ __forceinline__ void eval_scaled_skip(Best& best, const SkipSet& t, int k, int j, float sigma,
+                                                 const float (&p)[16], const float (&w)[16],
+                                                 const float (&diag)[16], const float (&sym)[120],
+                                                 uint32_t (&pk)[2]) {
+  const float s = ldexpf(sigma, j);
+  const float pow2j = __uint_as_float((uint32_t)(127 + j) << 23);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 0], p[8 * h + 1], pow2j, 0);
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 2], p[8 * h + 3], pow2j, 1);
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 4], p[8 * h + 5], pow2j, 2);
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 6], p[8 * h + 7], pow2j, 3);
+  }
+  float r[16];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const f32x2_t r0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 0);
+    const f32x2_t r1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 1);
+    const f32x2_t r2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 2);
+    const f32x2_t r3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 3);
+    r[8 * h + 0] = r0.x; r[8 * h + 1] = r0.y; r[8 * h + 2] = r1.x; r[8 * h + 3] = r1.y;
+    r[8 * h + 4] = r2.x; r[8 * h + 5] = r2.y; r[8 * h + 6] = r3.x; r[8 * h + 7] = r3.y;
+  }
+  float dw[16], yd[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    dw[i] = r[i] * s - w[i];  // Q = fl32(r * s), then Q - w
+    yd[i] = diag[i] * dw[i];
+  }
+  float d2 = yd[0] * dw[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) d2 = __builtin_fmaf(yd[i], dw[i], d2);
+  const bool need = !(t.on && t.gamma * d2 > best.err * kSkipMargin);
+  if (__ballot(need) == 0) return;
+  keep_best(best, quad_form_from(yd, sym, dw), k);
+}
+
 // Candidate k straight from the definition: x = fl32(|w| / s), software
 // rounding to the grid, Q = fl32(sign(w) r s), dw = Q - w, then dw 2^-e.
 __device__ __forceinline__ void eval_direct(Best& best, int k, float Sg, int e, const float (&w)[16],
@@ -142,18 +210,6 @@ __device__ __forceinline__ void eval_direct(Best& best, int k, float Sg, int e, 
   }
   keep_best(best, quad_form(diag, sym, dw), k);
 }
-
-constexpr float kSkipMargin = 1.0f + 0x1p-10f;
-
-// Per-row state of the skip test: the four bound elements (prescaled weights,
-// gamma * H_ee) and their packed FP4 codes.
-struct SkipSet {
-  float w[4];
-  float dg[4];
-  float p[4];      // w[e] / sigma of the current mantissa class (same bits as p[idx])
-  uint32_t pk;
-  bool on;         // this lane's gamma allows skipping
-};
 
 // True when this lane cannot prove the candidate worse than its incumbent.
 __device__ __forceinline__ bool needs_eval(SkipSet& t, const Best& best, int j, float s) {
@@ -177,7 +233,7 @@ __device__ __forceinline__ void try_scaled(Best& best, SkipSet& t, int k, int j,
                                            const float (&w)[16], const float (&diag)[16],
                                            const float (&sym)[120], uint32_t (&pk)[2]) {
   const bool need = needs_eval(t, best, j, ldexpf(sigma, j));
-  if (__ballot(need) != 0) eval_scaled(best, k, j, sigma, p, w, diag, sym, pk);
+  if (__ballot(need) != 0) eval_scaled_skip(best, t, k, j, sigma, p, w, diag, sym, pk);
 }
 
 // All candidates of mantissa class m (mu = 1 + m/8), in increasing index.
@@ -486,6 +542,7 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const T* __restrict_
           t.dg[q] = gamma * lds_diag[ki[q]][tid];
         }
         t.pk = 0u;
+        t.gamma = gamma;
         t.on = gamma > 0.0f;
       }
       // incumbent: the max-scaling candidate, evaluated exactly as in the loop
