@@ -58,10 +58,11 @@ __device__ __forceinline__ f32x4_t mfma_accumulate(const Vals16<float>& v, f32x4
   return acc;
 }
 
-// Channel-major: lane reads tokens [tb, tb+16) of its channel row.
-template <bool kVec>
+// Channel-major: lane reads tokens [tb, tb+16) of its channel row.  With
+// kInRange the caller guarantees tb + 16 <= t1.
+template <bool kVec, bool kInRange = false>
 __device__ __forceinline__ void load_cm(const uint16_t* row, int64_t tb, int64_t t1, Vals16<uint16_t>& v) {
-  if (kVec && tb + 16 <= t1) {
+  if (kVec && (kInRange || tb + 16 <= t1)) {
     v.u[0] = *reinterpret_cast<const uint4*>(row + tb);
     v.u[1] = *reinterpret_cast<const uint4*>(row + tb + 8);
   } else {
@@ -77,9 +78,9 @@ __device__ __forceinline__ void load_cm(const uint16_t* row, int64_t tb, int64_t
   }
 }
 
-template <bool kVec>
+template <bool kVec, bool kInRange = false>
 __device__ __forceinline__ void load_cm(const float* row, int64_t tb, int64_t t1, Vals16<float>& v) {
-  if (kVec && tb + 16 <= t1) {
+  if (kVec && (kInRange || tb + 16 <= t1)) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 f = *reinterpret_cast<const float4*>(row + tb + 4 * q);
@@ -117,13 +118,16 @@ __global__ __launch_bounds__(kThreads) void hessian_cm_kernel(const T* __restric
 
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
   int64_t t = t0 + wave * kSlab;
-  // Two slabs per trip keep four 16-byte loads per lane in flight.
-  for (; t + kRound < t1; t += 2 * kRound) {
-    Vals16<T> v0, v1;
-    load_cm<kVec>(row, t + 16 * kg, t1, v0);
-    load_cm<kVec>(row, t + kRound + 16 * kg, t1, v1);
-    acc = mfma_accumulate(v0, acc);
-    acc = mfma_accumulate(v1, acc);
+  // Two slabs per trip keep four 16-byte loads per lane in flight; while both
+  // slabs lie inside the slice no load needs a bounds check.
+  if (kVec) {
+    for (; t + kRound + kSlab <= t1; t += 2 * kRound) {
+      Vals16<T> v0, v1;
+      load_cm<true, true>(row, t + 16 * kg, t1, v0);
+      load_cm<true, true>(row, t + kRound + 16 * kg, t1, v1);
+      acc = mfma_accumulate(v0, acc);
+      acc = mfma_accumulate(v1, acc);
+    }
   }
   for (; t < t1; t += kRound) {
     Vals16<T> v0;

@@ -353,21 +353,24 @@ __device__ __forceinline__ float sym_entry(const float* hb, const float (&rs)[16
   return (i == j) ? hb[i * 17] * rs[i] * rs[i] : 0.5f * (hb[i * 16 + j] + hb[j * 16 + i]) * rs[i] * rs[j];
 }
 
-__device__ bool shifted_pd(const float* hb, const float (&rs)[16], float tau) {
-  float L[136];  // packed lower triangle: L[i (i + 1) / 2 + j], j <= i
+// In-place Cholesky of the packed lower triangle a (a[i (i + 1) / 2 + j],
+// j <= i); true when every pivot is positive.
+__device__ bool cholesky_ok(float (&a)[136]) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int j = 0; j < 16; ++j) {
+    float d = a[j * (j + 1) / 2 + j];
 #pragma unroll
-    for (int j = 0; j <= i; ++j) {
-      float a = sym_entry(hb, rs, i, j) - (i == j ? tau : 0.0f);
+    for (int m = 0; m < j; ++m) d = __builtin_fmaf(-a[j * (j + 1) / 2 + m], a[j * (j + 1) / 2 + m], d);
+    if (!(d > 0.0f)) return false;
+    const float ljj = sqrtf(d);
+    a[j * (j + 1) / 2 + j] = ljj;
+    const float inv = 1.0f / ljj;
 #pragma unroll
-      for (int m = 0; m < j; ++m) a = __builtin_fmaf(-L[i * (i + 1) / 2 + m], L[j * (j + 1) / 2 + m], a);
-      if (i == j) {
-        if (!(a > 0.0f)) return false;
-        L[i * (i + 1) / 2 + i] = sqrtf(a);
-      } else {
-        L[i * (i + 1) / 2 + j] = a / L[j * (j + 1) / 2 + j];
-      }
+    for (int i = j + 1; i < 16; ++i) {
+      float v = a[i * (i + 1) / 2 + j];
+#pragma unroll
+      for (int m = 0; m < j; ++m) v = __builtin_fmaf(-a[i * (i + 1) / 2 + m], a[j * (j + 1) / 2 + m], v);
+      a[i * (i + 1) / 2 + j] = v * inv;
     }
   }
   return true;
@@ -375,16 +378,31 @@ __device__ bool shifted_pd(const float* hb, const float (&rs)[16], float tau) {
 
 // Sixteen lanes per block: lane q tests tau = q/16 (lane 0 tests the
 // Gershgorin bound, which needs no factorisation); the block keeps the
-// largest tau that passes.  One factorisation per lane keeps the latency low.
+// largest tau that passes.  The 16 lanes first stage the block's H in LDS
+// (one row each), so each factorisation reads LDS, not global memory.
 __global__ __launch_bounds__(kThreads) void sweep_certificate_kernel(const float* __restrict__ h, int64_t gstride_h,
                                                                      int64_t nb, int64_t total,
                                                                      float* __restrict__ cert) {
-  const int64_t t = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 4;
+  __shared__ float hs[kThreads / 16][257];  // +1 pad: rows of different blocks on different banks
+  const int slot = threadIdx.x >> 4;
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / 16) + slot;
   const int q = threadIdx.x & 15;
   const bool live = t < total;  // all 16 lanes of a block share t
   const int64_t tc = live ? t : 0;
   const int64_t grp = tc / nb, b = tc - grp * nb;
-  const float* hb = h + grp * gstride_h + b * 256;
+  {
+    const float4* src = reinterpret_cast<const float4*>(h + grp * gstride_h + b * 256 + q * 16);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float4 v = src[c];
+      hs[slot][q * 16 + 4 * c + 0] = v.x;
+      hs[slot][q * 16 + 4 * c + 1] = v.y;
+      hs[slot][q * 16 + 4 * c + 2] = v.z;
+      hs[slot][q * 16 + 4 * c + 3] = v.w;
+    }
+  }
+  __syncthreads();
+  const float* hb = hs[slot];
   float rs[16];
   bool pos = true;
 #pragma unroll
@@ -410,7 +428,12 @@ __global__ __launch_bounds__(kThreads) void sweep_certificate_kernel(const float
       tau = fmaxf(1.0f - rho - 1e-3f, 0.0f);
     } else {
       const float tq = (float)q * 0.0625f;
-      tau = shifted_pd(hb, rs, tq) ? tq - 2e-3f : 0.0f;
+      float a[136];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int j = 0; j <= i; ++j) a[i * (i + 1) / 2 + j] = sym_entry(hb, rs, i, j) - (i == j ? tq : 0.0f);
+      tau = cholesky_ok(a) ? tq - 2e-3f : 0.0f;
     }
   }
   // max over the 16 lanes of this block
@@ -591,7 +614,7 @@ hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
   float* cert = nullptr;
   if (a.ws != nullptr && a.ws_bytes >= sweep_ws_bytes(a.c_in, a.n_groups)) {
     cert = static_cast<float*>(a.ws);
-    sweep_certificate_kernel<<<dim3((unsigned)((16 * per_k + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream>>>(
+    sweep_certificate_kernel<<<dim3((unsigned)((per_k + kThreads / 16 - 1) / (kThreads / 16))), dim3(kThreads), 0, stream>>>(
         a.h, a.gstride_h, nb, per_k, cert);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
