@@ -34,19 +34,23 @@
 // instructions per weight and candidate.
 //
 // Skipping (exact): for a symmetric H with positive diagonal and
-// C = D^-1/2 H D^-1/2 (D = diag H), Gershgorin gives lambda_min(C) >= gamma =
-// 1 - max_i sum_{j != i} |C_ij|, so every candidate satisfies
-// E_k >= gamma * sum_i H_ii dw_i^2 >= gamma * sum_{e in T} H_ee dw_e^2 for any
-// subset T.  Each lane keeps T = its four elements with the largest
-// H_ii w_i^2; the bound costs ~20 VALU operations against ~207 for a full
-// evaluation.  A candidate is skipped only when every lane of the wave proves
-// lb > best * (1 + 2^-10); the skipped candidate then cannot be the minimum
-// or tie with it, so indices and errors are bit-identical to the exhaustive
-// loop.  The margin covers fp32 rounding of the bound and of E, which for
-// gamma >= 0.1 (cond(C) <= 19) is below 1e-4 relative; lanes with smaller
-// gamma (or a non-positive diagonal) never vote to skip.  Each row first
-// evaluates the lane's max-scaling candidate with the same arithmetic as the
-// loop, so the bound has a good incumbent from the start.
+// C = D^-1/2 H D^-1/2 (D = diag H), any tau <= lambda_min(C) gives
+// E_k >= tau * sum_i H_ii dw_i^2 >= tau * sum_{e in T} H_ee dw_e^2 for every
+// candidate and any subset T.  tau comes from a pre-pass that certifies
+// C - tau I positive definite with an fp32 Cholesky factorisation (when the
+// caller passes a workspace), else from Gershgorin in-kernel.  Level 1: each
+// lane keeps T = its four elements with the largest H_ii w_i^2 and bounds
+// every candidate with ~20 VALU operations before casting all 16 weights
+// (~207 for a full evaluation).  Level 2: after the cast, the full diagonal
+// bound reuses the products H_ii dw_i that start the rows of the quadratic
+// form.  A candidate (or the rest of its form) is skipped only when every
+// lane of the wave proves lb > best * (1 + 2^-10); the skipped candidate then
+// cannot be the minimum or tie with it, so indices and errors are
+// bit-identical to the exhaustive loop.  The margin covers the fp32 rounding
+// of the bound and of E, which the certificate keeps below 2^-11 relative;
+// lanes without a certificate never vote to skip.  Each row first evaluates
+// the lane's max-scaling candidate with the same arithmetic as the loop, so
+// the bound has a good incumbent from the start.
 //
 // Units: the lane works in units of 2^e with e = ilogb(S_g): w' = w 2^-e and
 // sigma' = sigma 2^-e are exact, so every Q', dw' = dw 2^-e and the error
