@@ -27,6 +27,7 @@ _SRC = os.path.join(_HERE, "lh_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liblh_oracle.so")
 
 F32, BF16 = 0, 1
+RULE_SWEEP, RULE_MAX, RULE_FOUR_OVER_SIX, RULE_AMAX_SEARCH = 0, 1, 2, 3
 CHANNEL_MAJOR, TOKEN_MAJOR = 0, 1
 
 _lib = None
@@ -63,6 +64,13 @@ def _load():
     lib.oracle_hessian.argtypes = [P, I32, I32, I64, I64, I64, I64, D, D, P, I64, P, P]
     lib.oracle_sweep.argtypes = [P, I32, I64, I64, I64, I64, P, I64, P, P, I64, P, P, P, P, P]
     lib.oracle_fake_quant.argtypes = [P, I32, I64, I64, I64, I64, P, P, P, I64, P, P, P]
+    lib.oracle_e4m3_round_code.argtypes = [F]
+    lib.oracle_e4m3_round_code.restype = I32
+    lib.oracle_amax_multiplier.argtypes = [I32]
+    lib.oracle_amax_multiplier.restype = F
+    lib.oracle_rule_candidates.argtypes = [I32, P, F, P]
+    lib.oracle_rule_candidates.restype = I32
+    lib.oracle_select.argtypes = [I32, P, I32, I64, I64, I64, I64, P, I64, P, P, I64, P, P, P, P, P]
     lib.oracle_num_threads.restype = I32
     lib.oracle_set_num_threads.argtypes = [I32]
     _lib = lib
@@ -196,4 +204,48 @@ def fake_quant(w: np.ndarray, idx: np.ndarray, amax: np.ndarray, c_out: int, c_i
     _load().oracle_fake_quant(_ptr(w), _dtype_code(w), c_out, c_in, ld_w, gsw, _ptr(idx),
                               _ptr(amax), _ptr(sel), n, _ptr(out["q"]), _ptr(out["packed"]),
                               _ptr(out["code"]))
+    return out
+
+
+def e4m3_round_code(t: float) -> int:
+    """E4M3 byte (1..126) stored for a wanted block-scale value t (nearest,
+    ties to the even code, saturating at 448, never zero)."""
+    return int(_load().oracle_e4m3_round_code(float(t)))
+
+
+def amax_multiplier(i: int) -> float:
+    """The i-th multiplier of the amax search (0.25 + 0.1 i)."""
+    return float(_load().oracle_amax_multiplier(int(i)))
+
+
+def rule_candidates(rule: int, w16, g: float) -> np.ndarray:
+    """Distinct candidate indices (ascending) that a scale rule considers."""
+    w16 = np.ascontiguousarray(w16, np.float32)
+    out = np.empty(126, np.int32)
+    n = _load().oracle_rule_candidates(int(rule), _ptr(w16), float(g), _ptr(out))
+    return out[:n].copy()
+
+
+def select(rule: int, w: np.ndarray, H, amax: np.ndarray, c_out: int, c_in: int,
+           ld_w: int | None = None, n_groups: int = 1, group_stride_w: int | None = None,
+           group_stride_h: int | None = None, sel: np.ndarray | None = None) -> dict:
+    """Scale selection by rule (RULE_SWEEP: all 126 candidates, RULE_MAX,
+    RULE_FOUR_OVER_SIX, RULE_AMAX_SEARCH) for the selected flat block
+    indices.  H is the fp32 Hessian tensor, or None for the plain weight
+    error (H = I).  Returns idx, e1, e2, err, amax like ``sweep``."""
+    w = np.ascontiguousarray(w)
+    Hc = None if H is None else np.ascontiguousarray(H, np.float32)
+    amax = np.ascontiguousarray(amax, np.float32).reshape(-1)
+    nb = c_in // 16
+    ld_w = c_in if ld_w is None else ld_w
+    gsw = c_out * ld_w if group_stride_w is None else group_stride_w
+    gsh = nb * 256 if group_stride_h is None else group_stride_h
+    sel = np.arange(n_groups * c_out * nb, dtype=np.int64) if sel is None else np.ascontiguousarray(sel, np.int64)
+    n = len(sel)
+    out = dict(idx=np.empty(n, np.int32), e1=np.empty(n, np.float64), e2=np.empty(n, np.float64),
+               err=np.empty(n, np.float32), amax=np.empty(n, np.float32))
+    _load().oracle_select(int(rule), _ptr(w), _dtype_code(w), c_out, c_in, ld_w, gsw,
+                          None if Hc is None else _ptr(Hc), gsh, _ptr(amax), _ptr(sel), n,
+                          _ptr(out["idx"]), _ptr(out["e1"]), _ptr(out["e2"]), _ptr(out["err"]),
+                          _ptr(out["amax"]))
     return out

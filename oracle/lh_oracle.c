@@ -331,3 +331,163 @@ void oracle_fake_quant(const void *w, int dtype, int64_t c_out, int64_t c_in, in
             code_out[n] = (uint8_t)(k + 1);
     }
 }
+
+/* ====================================================================== */
+/* Scale-rule variants: the methods [LHG] compares Local-Hessian with.     */
+/*   "What is Local-Hessian": max scaling takes the block scale from the   */
+/*   largest |w| of the 16 weights; Four-Over-Six picks one of two         */
+/*   candidate scales by the in-block error; the MSE method sweeps all 126 */
+/*   positive FP8 values by the weight error.                              */
+/*   "Entry API and calibration flow": with the 126-value sweep off, the   */
+/*   amax is searched from multiplier 0.25 to 4.0 in steps of 0.1.         */
+/* Readings:                                                               */
+/*   R6  a block scale wanted as the value t (in units of S_g) is stored   */
+/*       as the nearest positive finite E4M3 value, ties to the even code; */
+/*       values above 448 store 448 and values that round to zero store    */
+/*       the smallest candidate 2^-9.                                      */
+/*   R7  max scaling: t = fl32(fl32(amax_b / 6) / S_g), amax_b = max |w|   */
+/*       over the block.                                                   */
+/*   R8  Four-Over-Six: the two candidates map amax_b to 6 (R7) and to 4:  */
+/*       t = fl32(fl32(amax_b / 4) / S_g).                                 */
+/*   R9  amax search: multipliers m_i = fl32((25 + 10 i) / 100) for        */
+/*       i = 0..37 (0.25 .. 3.95; the stop value 4.0 is exclusive);        */
+/*       candidate i stores t = fl32(fl32(fl32(m_i amax_b) / 6) / S_g).    */
+/*   R10 objective: dw^T H dw with the block's local Hessian when one is   */
+/*       given, else the plain weight error sum_i dw_i^2 (H = I).  A rule  */
+/*       returns the best of its distinct candidates, lowest index on ties */
+/*       (R5); e2 is the best among its other distinct candidates.         */
+/*   R11 g = 0 (S_g = 0): every rule returns candidate 0 (all Q are 0).    */
+/* ====================================================================== */
+enum { ORACLE_RULE_SWEEP = 0, ORACLE_RULE_MAX = 1, ORACLE_RULE_FOUR_OVER_SIX = 2,
+       ORACLE_RULE_AMAX_SEARCH = 3 };
+
+/* R6: E4M3 byte (1..126) stored for the wanted scale value t > 0. */
+int oracle_e4m3_round_code(float t)
+{
+    if (!(t > 0.0f))
+        return 1;
+    int best = 0; /* code 0 is the value zero */
+    double bd = (double)t;
+    for (int code = 1; code <= 126; ++code) {
+        double d = fabs((double)t - oracle_e4m3_value(code));
+        if (d < bd || (d == bd && (code % 2) == 0)) {
+            best = code;
+            bd = d;
+        }
+    }
+    return best == 0 ? 1 : best;
+}
+
+/* R9: the i-th amax-search multiplier. */
+float oracle_amax_multiplier(int i) { return (float)((25.0 + 10.0 * i) / 100.0); }
+
+/* Distinct candidate indices (ascending) a rule considers for one block;
+ * returns their count. */
+int oracle_rule_candidates(int rule, const float *w16, float g, int *k_out /* [126] */)
+{
+    float Sg = g / 2688.0f;
+    int n = 0;
+    if (rule == ORACLE_RULE_SWEEP) {
+        for (int k = 0; k < 126; ++k)
+            k_out[n++] = k;
+        return n;
+    }
+    if (Sg == 0.0f) { /* R11 */
+        k_out[0] = 0;
+        return 1;
+    }
+    float ab = 0.0f;
+    for (int i = 0; i < 16; ++i)
+        if (fabsf(w16[i]) > ab)
+            ab = fabsf(w16[i]);
+    int want[38];
+    int nw = 0;
+    if (rule == ORACLE_RULE_MAX || rule == ORACLE_RULE_FOUR_OVER_SIX) {
+        float t6 = (ab / 6.0f) / Sg;
+        want[nw++] = oracle_e4m3_round_code(t6) - 1;
+        if (rule == ORACLE_RULE_FOUR_OVER_SIX) {
+            float t4 = (ab / 4.0f) / Sg;
+            want[nw++] = oracle_e4m3_round_code(t4) - 1;
+        }
+    } else if (rule == ORACLE_RULE_AMAX_SEARCH) {
+        for (int i = 0; i < 38; ++i) {
+            float a = oracle_amax_multiplier(i) * ab;
+            float t = (a / 6.0f) / Sg;
+            want[nw++] = oracle_e4m3_round_code(t) - 1;
+        }
+    } else {
+        return 0;
+    }
+    /* distinct, ascending */
+    for (int k = 0; k < 126; ++k)
+        for (int i = 0; i < nw; ++i)
+            if (want[i] == k) {
+                k_out[n++] = k;
+                break;
+            }
+    return n;
+}
+
+/* Errors of all 126 candidates of one block under the R10 objective. */
+static void block_errors_objective(const float *w, const float *H, float g, double *E)
+{
+    if (H) {
+        oracle_block_errors(w, H, g, E);
+        return;
+    }
+    float s[126];
+    oracle_candidate_scales(g, s);
+    for (int k = 0; k < 126; ++k) {
+        double e = 0.0;
+        for (int i = 0; i < 16; ++i) {
+            double dw = (double)oracle_quantize(w[i], s[k], 0) - (double)w[i];
+            e += dw * dw;
+        }
+        E[k] = e;
+    }
+}
+
+/* Scale selection by rule for the selected blocks (flat indices as in
+ * oracle_sweep).  H (nullable) is the fp32 Hessian tensor; outputs compact. */
+void oracle_select(int rule, const void *w, int dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
+                   int64_t gstride_w, const float *H, int64_t gstride_h, const float *amax,
+                   const int64_t *sel, int64_t n_sel, int32_t *idx_out, double *e1_out,
+                   double *e2_out, float *err_out, float *amax_out)
+{
+    const int64_t nb = c_in / 16;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < n_sel; ++n) {
+        const int64_t f = sel[n];
+        const int64_t b = f % nb;
+        const int64_t row = (f / nb) % c_out;
+        const int64_t g = f / (nb * c_out);
+        float wb[16];
+        for (int i = 0; i < 16; ++i)
+            wb[i] = widen_f32(w, dtype, g * gstride_w + row * ld_w + 16 * b + i);
+        double E[126];
+        block_errors_objective(wb, H ? H + g * gstride_h + b * 256 : 0, amax[g], E);
+        int ks[126];
+        int nk = oracle_rule_candidates(rule, wb, amax[g], ks);
+        int kb = ks[0];
+        for (int i = 1; i < nk; ++i)
+            if (E[ks[i]] < E[kb])
+                kb = ks[i];
+        double second = INFINITY;
+        for (int i = 0; i < nk; ++i)
+            if (ks[i] != kb && E[ks[i]] < second)
+                second = E[ks[i]];
+        if (idx_out)
+            idx_out[n] = kb;
+        if (e1_out)
+            e1_out[n] = E[kb];
+        if (e2_out)
+            e2_out[n] = second;
+        if (err_out)
+            err_out[n] = (float)E[kb];
+        if (amax_out) {
+            float s[126];
+            oracle_candidate_scales(amax[g], s);
+            amax_out[n] = 6.0f * s[kb];
+        }
+    }
+}
