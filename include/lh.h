@@ -81,6 +81,13 @@ typedef enum lh_layout {
     LH_LAYOUT_TOKEN_MAJOR = 1    /* x[t * ld_x + c]: X^T as [N][C_in] (hooked activations) */
 } lh_layout;
 
+typedef enum lh_rule {
+    LH_RULE_SWEEP = 0,         /* all 126 E4M3 candidates (the Local-Hessian sweep) */
+    LH_RULE_MAX = 1,           /* max scaling: the block's amax maps to 6           */
+    LH_RULE_FOUR_OVER_SIX = 2, /* best of amax -> 6 and amax -> 4                   */
+    LH_RULE_AMAX_SEARCH = 3    /* amax multipliers 0.25, 0.35, ..., 3.95            */
+} lh_rule;
+
 /* Library ABI version (this header describes version 1). */
 int lh_abi_version(void);
 
@@ -183,6 +190,43 @@ lh_status lh_scale_sweep(const void *w, int w_dtype, int64_t c_out, int64_t c_in
                          int64_t group_stride_h, const float *amax, uint8_t *best_idx,
                          float *best_err, float *best_amax, void *workspace,
                          size_t workspace_bytes, void *stream);
+
+/*
+ * Block-scale selection by rule: the scale rules the Local-Hessian guide
+ * compares against ("What is Local-Hessian": max scaling takes the block
+ * scale from the block's largest |w|; Four-Over-Six picks one of two
+ * candidate scales by the in-block error; the MSE method sweeps all 126
+ * positive FP8 values by the weight error; "Entry API and calibration
+ * flow": with the 126-value sweep off, the amax is searched from
+ * multiplier 0.25 to 4.0 in steps of 0.1).
+ *
+ * Objective: E_k = dw_k^T H_b dw_k when h is given (the local Hessian),
+ * else the plain weight error sum_i dw_i^2 (H = I, the "MSE" rule).
+ * Candidate set per block, with a = max |w_b| and S_g = fl32(amax[g]/2688);
+ * a wanted scale value t is stored as the nearest positive finite E4M3
+ * value (ties to the even code, above 448 -> 448, never zero):
+ *   LH_RULE_SWEEP          all 126 candidates (with h: identical to
+ *                          lh_scale_sweep; without h: the MSE sweep)
+ *   LH_RULE_MAX            t = fl32(fl32(a / 6) / S_g)
+ *   LH_RULE_FOUR_OVER_SIX  that t and t = fl32(fl32(a / 4) / S_g)
+ *   LH_RULE_AMAX_SEARCH    t_i = fl32(fl32(fl32(m_i a) / 6) / S_g),
+ *                          m_i = fl32((25 + 10 i) / 100), i = 0..37
+ * Each block gets the candidate of lowest E_k in its set, lowest index on
+ * ties; S_g = 0 gives candidate 0.  Outputs, layouts and arguments are
+ * those of lh_scale_sweep, except:
+ *   rule      an lh_rule value (else LH_ERR_ARG).
+ *   h         may be NULL (plain weight error); group_stride_h is then
+ *             ignored.
+ *   workspace used only by LH_RULE_SWEEP with a Hessian (same contract
+ *             as lh_scale_sweep); may be NULL/0.
+ * Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_WORKSPACE,
+ * LH_ERR_ARG, LH_ERR_HIP.
+ */
+lh_status lh_select_scales(int rule, const void *w, int w_dtype, int64_t c_out, int64_t c_in,
+                           int64_t ld_w, int64_t n_groups, int64_t group_stride_w,
+                           const float *h, int64_t group_stride_h, const float *amax,
+                           uint8_t *best_idx, float *best_err, float *best_amax, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /*
  * NVFP4 fake-quant with chosen block scales ("Algorithm principle":

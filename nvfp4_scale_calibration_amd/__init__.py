@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_PKG, "liblh.so")
 
 LH_DTYPE_F32, LH_DTYPE_BF16 = 0, 1
 LH_LAYOUT_CHANNEL_MAJOR, LH_LAYOUT_TOKEN_MAJOR = 0, 1
+LH_RULE_SWEEP, LH_RULE_MAX, LH_RULE_FOUR_OVER_SIX, LH_RULE_AMAX_SEARCH = 0, 1, 2, 3
 N_CANDIDATES = 126
 BLOCK = 16
 
@@ -55,6 +56,8 @@ def _load() -> ctypes.CDLL:
     lib.lh_sweep_workspace_bytes.restype = SZ
     lib.lh_scale_sweep.argtypes = [P, I, I64, I64, I64, I64, I64, P, I64, P, P, P, P, P, SZ, P]
     lib.lh_scale_sweep.restype = I
+    lib.lh_select_scales.argtypes = [I, P, I, I64, I64, I64, I64, I64, P, I64, P, P, P, P, P, SZ, P]
+    lib.lh_select_scales.restype = I
     lib.lh_fake_quant_nvfp4.argtypes = [P, I, I64, I64, I64, I64, I64, P, P, P, P, P, P, P]
     lib.lh_fake_quant_nvfp4.restype = I
     return lib
@@ -63,7 +66,7 @@ def _load() -> ctypes.CDLL:
 lib = _load()
 EXPORTS = ("lh_abi_version", "lh_status_string", "lh_last_error_message", "lh_absmax",
            "lh_hessian_workspace_bytes", "lh_accumulate_hessian", "lh_sweep_workspace_bytes", "lh_scale_sweep",
-           "lh_fake_quant_nvfp4")
+           "lh_select_scales", "lh_fake_quant_nvfp4")
 
 
 def _check(status: int) -> None:
@@ -176,15 +179,7 @@ def lh_sweep_workspace_bytes(c_in: int, n_groups: int = 1) -> int:
     return int(lib.lh_sweep_workspace_bytes(c_in, n_groups))
 
 
-def lh_scale_sweep(w: torch.Tensor, h: torch.Tensor, amax: torch.Tensor,
-                   best_idx: torch.Tensor | None = None, best_err: torch.Tensor | bool | None = True,
-                   best_amax: torch.Tensor | bool | None = True,
-                   workspace: torch.Tensor | bool | None = True):
-    """Per-block best candidate index (E4M3 code = idx + 1), its error
-    dw^T H_b dw and the per-block amax 6 * s_idx.  Returns (idx, err, amax);
-    err / amax are None when not requested (False/None).  workspace=True
-    allocates the certificate scratch the library asks for (faster skipping),
-    False/None runs without it, a device tensor is used as given."""
+def _select(rule, w, h, amax, best_idx, best_err, best_amax, workspace):
     _require_device(w, h, amax)
     w3 = _as3(w)
     if w3.stride(-1) != 1:
@@ -201,18 +196,45 @@ def lh_scale_sweep(w: torch.Tensor, h: torch.Tensor, amax: torch.Tensor,
         best_amax = torch.empty(shape, dtype=torch.float32, device=dev)
     best_err = best_err if isinstance(best_err, torch.Tensor) else None
     best_amax = best_amax if isinstance(best_amax, torch.Tensor) else None
-    h_gstride = h.stride(0) if h.dim() == 4 and h.shape[0] > 1 else 0
+    h_gstride = h.stride(0) if h is not None and h.dim() == 4 and h.shape[0] > 1 else 0
     ws, ws_bytes = None, 0
     if workspace is True:
-        ws_bytes = lh_sweep_workspace_bytes(c_in, g)
+        ws_bytes = lh_sweep_workspace_bytes(c_in, g) if h is not None and rule == LH_RULE_SWEEP else 0
         if ws_bytes:
             ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     elif isinstance(workspace, torch.Tensor):
         ws, ws_bytes = workspace, workspace.numel() * workspace.element_size()
-    _check(lib.lh_scale_sweep(_ptr(w3), _dtype(w3), c_out, c_in, _ld(w3), g, _group_stride(w3),
-                              _ptr(h), h_gstride, _ptr(amax), _ptr(best_idx), _ptr(best_err),
-                              _ptr(best_amax), _ptr(ws), ws_bytes, _stream(w)))
+    args = (_ptr(w3), _dtype(w3), c_out, c_in, _ld(w3), g, _group_stride(w3), _ptr(h), h_gstride, _ptr(amax),
+            _ptr(best_idx), _ptr(best_err), _ptr(best_amax), _ptr(ws), ws_bytes, _stream(w))
+    if rule is None:
+        _check(lib.lh_scale_sweep(*args))
+    else:
+        _check(lib.lh_select_scales(int(rule), *args))
     return best_idx, best_err, best_amax
+
+
+def lh_scale_sweep(w: torch.Tensor, h: torch.Tensor, amax: torch.Tensor,
+                   best_idx: torch.Tensor | None = None, best_err: torch.Tensor | bool | None = True,
+                   best_amax: torch.Tensor | bool | None = True,
+                   workspace: torch.Tensor | bool | None = True):
+    """Per-block best candidate index (E4M3 code = idx + 1), its error
+    dw^T H_b dw and the per-block amax 6 * s_idx.  Returns (idx, err, amax);
+    err / amax are None when not requested (False/None).  workspace=True
+    allocates the certificate scratch the library asks for (faster skipping),
+    False/None runs without it, a device tensor is used as given."""
+    if h is None:
+        raise ValueError("lh_scale_sweep needs a Hessian (lh_select_scales takes h=None)")
+    return _select(None, w, h, amax, best_idx, best_err, best_amax, workspace)
+
+
+def lh_select_scales(rule: int, w: torch.Tensor, h: torch.Tensor | None, amax: torch.Tensor,
+                     best_idx: torch.Tensor | None = None, best_err: torch.Tensor | bool | None = True,
+                     best_amax: torch.Tensor | bool | None = True,
+                     workspace: torch.Tensor | bool | None = True):
+    """Block scales by rule (LH_RULE_SWEEP / MAX / FOUR_OVER_SIX /
+    AMAX_SEARCH) under dw^T H_b dw, or the plain weight error when h is
+    None.  Same outputs as lh_scale_sweep."""
+    return _select(rule, w, h, amax, best_idx, best_err, best_amax, workspace)
 
 
 def lh_fake_quant_nvfp4(w: torch.Tensor, best_idx: torch.Tensor, amax: torch.Tensor,

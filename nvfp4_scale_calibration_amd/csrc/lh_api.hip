@@ -110,24 +110,29 @@ size_t lh_sweep_workspace_bytes(int64_t c_in, int64_t n_groups) {
   return lh::sweep_ws_bytes(c_in, n_groups);
 }
 
-lh_status lh_scale_sweep(const void* w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
-                         int64_t n_groups, int64_t group_stride_w, const float* h,
-                         int64_t group_stride_h, const float* amax, uint8_t* best_idx,
-                         float* best_err, float* best_amax, void* workspace, size_t workspace_bytes,
-                         void* stream) {
-  const char* fn = "lh_scale_sweep";
+}  // extern "C"
+
+namespace {
+
+// Shared by lh_scale_sweep (rule 0, Hessian required) and lh_select_scales.
+lh_status select_common(const char* fn, int rule, bool h_required, const void* w, int w_dtype, int64_t c_out,
+                        int64_t c_in, int64_t ld_w, int64_t n_groups, int64_t group_stride_w, const float* h,
+                        int64_t group_stride_h, const float* amax, uint8_t* best_idx, float* best_err,
+                        float* best_amax, void* workspace, size_t workspace_bytes, void* stream) {
   g_msg[0] = '\0';
+  if (rule < 0 || rule > 3) return fail(LH_ERR_ARG, "%s: rule must be 0..3", fn);
   if (!valid_dtype(w_dtype)) return fail(LH_ERR_DTYPE, "%s: w_dtype must be 0 (f32) or 1 (bf16)", fn);
   if (c_out < 0 || c_in < 0 || n_groups < 0 || group_stride_w < 0 || group_stride_h < 0)
     return fail(LH_ERR_SHAPE, "%s: negative size or stride", fn);
   if (c_in % 16 != 0) return fail(LH_ERR_SHAPE, "%s: c_in must be a multiple of 16", fn);
   if (ld_w < c_in) return fail(LH_ERR_SHAPE, "%s: ld_w < c_in", fn);
   const bool work = n_groups > 0 && c_out > 0 && c_in > 0;
-  if (work && (w == nullptr || h == nullptr || amax == nullptr || best_idx == nullptr))
-    return fail(LH_ERR_NULL, "%s: w, h, amax and best_idx are required", fn);
+  if (work && (w == nullptr || (h_required && h == nullptr) || amax == nullptr || best_idx == nullptr))
+    return fail(LH_ERR_NULL, h_required ? "%s: w, h, amax and best_idx are required"
+                                        : "%s: w, amax and best_idx are required", fn);
   if (!aligned(w, elem_size(w_dtype)) || !aligned(amax, 4) || !aligned(best_err, 4) || !aligned(best_amax, 4))
     return fail(LH_ERR_ARG, "%s: pointer not aligned to its element size", fn);
-  if (!aligned(h, 16) || group_stride_h % 4 != 0)
+  if (h != nullptr && (!aligned(h, 16) || group_stride_h % 4 != 0))
     return fail(LH_ERR_ARG, "%s: h must be 16-byte aligned and group_stride_h a multiple of 4", fn);
   if (workspace == nullptr && workspace_bytes > 0) return fail(LH_ERR_NULL, "%s: workspace is NULL but workspace_bytes > 0", fn);
   if (!aligned(workspace, 4)) return fail(LH_ERR_ARG, "%s: workspace not 4-byte aligned", fn);
@@ -135,9 +140,30 @@ lh_status lh_scale_sweep(const void* w, int w_dtype, int64_t c_out, int64_t c_in
     return fail(LH_ERR_WORKSPACE, "%s: workspace smaller than lh_sweep_workspace_bytes()", fn);
   if (!work) return LH_OK;
   lh::SweepArgs a{w, w_dtype, c_out, c_in, ld_w, n_groups, group_stride_w, h, group_stride_h, amax,
-                  best_idx, best_err, best_amax, workspace, workspace_bytes};
+                  best_idx, best_err, best_amax, workspace, workspace_bytes, rule};
   hipError_t e = lh::launch_sweep(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LH_OK : hip_fail(e, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+lh_status lh_scale_sweep(const void* w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
+                         int64_t n_groups, int64_t group_stride_w, const float* h,
+                         int64_t group_stride_h, const float* amax, uint8_t* best_idx,
+                         float* best_err, float* best_amax, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return select_common("lh_scale_sweep", 0, true, w, w_dtype, c_out, c_in, ld_w, n_groups, group_stride_w, h,
+                       group_stride_h, amax, best_idx, best_err, best_amax, workspace, workspace_bytes, stream);
+}
+
+lh_status lh_select_scales(int rule, const void* w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
+                           int64_t n_groups, int64_t group_stride_w, const float* h, int64_t group_stride_h,
+                           const float* amax, uint8_t* best_idx, float* best_err, float* best_amax,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return select_common("lh_select_scales", rule, false, w, w_dtype, c_out, c_in, ld_w, n_groups, group_stride_w,
+                       h, group_stride_h, amax, best_idx, best_err, best_amax, workspace, workspace_bytes, stream);
 }
 
 lh_status lh_fake_quant_nvfp4(const void* w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,

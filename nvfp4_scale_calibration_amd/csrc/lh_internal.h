@@ -34,7 +34,7 @@ struct SweepArgs {
   const void* w;
   int dtype;
   int64_t c_out, c_in, ld_w, n_groups, gstride_w;
-  const float* h;
+  const float* h;  // nullptr: plain weight error (H = I)
   int64_t gstride_h;
   const float* amax;
   uint8_t* idx;
@@ -42,6 +42,7 @@ struct SweepArgs {
   float* best_amax;
   void* ws;       // nullable: per-block skip certificates
   size_t ws_bytes;
+  int rule;       // 0: 126-value sweep, 1: max, 2: Four-Over-Six, 3: amax search
 };
 size_t sweep_ws_bytes(int64_t c_in, int64_t n_groups);
 hipError_t launch_sweep(const SweepArgs& a, hipStream_t stream);

@@ -52,11 +52,13 @@
 // the lane's max-scaling candidate with the same arithmetic as the loop, so
 // the bound has a good incumbent from the start.
 //
-// Units: the lane works in units of 2^e with e = ilogb(S_g): w' = w 2^-e and
+// Units: each row works in units of 2^e with e = ilogb(S_g): w' = w 2^-e and
 // sigma' = sigma 2^-e are exact, so every Q', dw' = dw 2^-e and the error
 // E' = E 2^-2e are the same fp32 numbers scaled by a power of two (identical
-// argmin) while staying far from fp32 underflow for tiny amax.  The reported
-// error is ldexp(E', 2e).
+// argmin) while staying far from fp32 underflow for tiny amax.  When a row's
+// weights lie far from the amax (beyond 2^+-20 S_g), e follows the weights
+// instead, so that dw' and E' stay far from overflow and underflow.  The
+// reported error is ldexp(E', 2e).
 //
 // When S_g < 2^-117 some candidate scales are subnormal and the identities
 // above can fail, so the kernel divides per candidate and rounds in software
@@ -97,10 +99,18 @@ struct SkipSet {
   bool on;         // this lane's gamma allows skipping
 };
 
-// E = dw^T H dw = sum_i dw_i (H_ii dw_i + sum_{j>i} (H_ij + H_ji) dw_j)
+// E = dw^T H dw = sum_i dw_i (H_ii dw_i + sum_{j>i} (H_ij + H_ji) dw_j), or
+// the plain weight error sum_i dw_i^2 (H = I) when kMse.
+template <bool kMse>
 __device__ __forceinline__ float quad_form(const float (&diag)[16], const float (&sym)[120],
                                            const float (&dw)[16]) {
   float e = 0.0f;
+  if constexpr (kMse) {
+    e = dw[0] * dw[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) e = __builtin_fmaf(dw[i], dw[i], e);
+    return e;
+  }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     float y = diag[i] * dw[i];
@@ -131,6 +141,7 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 // p_i = fl32(w_i / sigma) (signed).  The eight FP4 pairs are packed into the
 // four bytes of two dwords (byte select 0..3); `pk` carries them from one
 // candidate to the next so no register has to be cleared first.
+template <bool kMse>
 __device__ __forceinline__ void eval_scaled(Best& best, int k, int j, float sigma, const float (&p)[16],
                                             const float (&w)[16], const float (&diag)[16],
                                             const float (&sym)[120], uint32_t (&pk)[2]) {
@@ -156,17 +167,22 @@ __device__ __forceinline__ void eval_scaled(Best& best, int k, int j, float sigm
   float dw[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) dw[i] = r[i] * s - w[i];  // Q = fl32(r * s), then Q - w
-  keep_best(best, quad_form(diag, sym, dw), k);
+  keep_best(best, quad_form<kMse>(diag, sym, dw), k);
 }
 
 // eval_scaled with a second skip test after the cast: E >= gamma *
 // sum_i H_ii dw_i^2 over all 16 weights, which reuses the products H_ii dw_i
 // that start the rows of the quadratic form; the rest of the form runs only
 // if some lane of the wave still needs it.  Bit-identical E when it runs.
+template <bool kMse>
 __device__ __forceinline__ void eval_scaled_skip(Best& best, const SkipSet& t, int k, int j, float sigma,
                                                  const float (&p)[16], const float (&w)[16],
                                                  const float (&diag)[16], const float (&sym)[120],
                                                  uint32_t (&pk)[2]) {
+  if constexpr (kMse) {  // the diagonal bound is the whole error here
+    eval_scaled<true>(best, k, j, sigma, p, w, diag, sym, pk);
+    return;
+  }
   const float s = ldexpf(sigma, j);
   const float pow2j = __uint_as_float((uint32_t)(127 + j) << 23);
 #pragma unroll
@@ -202,6 +218,7 @@ __device__ __forceinline__ void eval_scaled_skip(Best& best, const SkipSet& t, i
 
 // Candidate k straight from the definition: x = fl32(|w| / s), software
 // rounding to the grid, Q = fl32(sign(w) r s), dw = Q - w, then dw 2^-e.
+template <bool kMse>
 __device__ __forceinline__ void eval_direct(Best& best, int k, float Sg, int e, const float (&w)[16],
                                             const float (&diag)[16], const float (&sym)[120]) {
   const float s = e4m3_candidate(k) * Sg;
@@ -212,7 +229,7 @@ __device__ __forceinline__ void eval_direct(Best& best, int k, float Sg, int e, 
     const float q = copysignf(e2m1_round_mag(x) * s, w[i]);
     dw[i] = ldexpf(q - w[i], -e);
   }
-  keep_best(best, quad_form(diag, sym, dw), k);
+  keep_best(best, quad_form<kMse>(diag, sym, dw), k);
 }
 
 // True when this lane cannot prove the candidate worse than its incumbent.
@@ -233,15 +250,16 @@ __device__ __forceinline__ bool needs_eval(SkipSet& t, const Best& best, int j, 
 
 // All candidates of mantissa class m (mu = 1 + m/8), in increasing index.
 // Evaluates candidate (k, j) unless every lane of the wave can skip it.
+template <bool kMse>
 __device__ __forceinline__ void try_scaled(Best& best, SkipSet& t, int k, int j, float sigma, const float (&p)[16],
                                            const float (&w)[16], const float (&diag)[16],
                                            const float (&sym)[120], uint32_t (&pk)[2]) {
   const bool need = needs_eval(t, best, j, ldexpf(sigma, j));
-  if (__ballot(need) != 0) eval_scaled_skip(best, t, k, j, sigma, p, w, diag, sym, pk);
+  if (__ballot(need) != 0) eval_scaled_skip<kMse>(best, t, k, j, sigma, p, w, diag, sym, pk);
 }
 
 // All candidates of mantissa class m (mu = 1 + m/8), in increasing index.
-template <int m>
+template <int m, bool kMse>
 __device__ __forceinline__ void sweep_mantissa(Best& best, SkipSet& t, float Sg, const float (&w)[16],
                                                const float (&diag)[16], const float (&sym)[120],
                                                uint32_t (&pk)[2]) {
@@ -253,20 +271,20 @@ __device__ __forceinline__ void sweep_mantissa(Best& best, SkipSet& t, float Sg,
   for (int e = 0; e < 4; ++e) t.p[e] = t.w[e] / sigma;  // same operation on the same bits as p[idx]
   // subnormal E4M3 codes that share this mantissa: code = 1..7 -> k = code-1
   if constexpr (m == 0) {
-    try_scaled(best, t, 0, -9, sigma, p, w, diag, sym, pk);   // 1 * 2^-9
-    try_scaled(best, t, 1, -8, sigma, p, w, diag, sym, pk);   // 2 * 2^-9
-    try_scaled(best, t, 3, -7, sigma, p, w, diag, sym, pk);   // 4 * 2^-9
+    try_scaled<kMse>(best, t, 0, -9, sigma, p, w, diag, sym, pk);   // 1 * 2^-9
+    try_scaled<kMse>(best, t, 1, -8, sigma, p, w, diag, sym, pk);   // 2 * 2^-9
+    try_scaled<kMse>(best, t, 3, -7, sigma, p, w, diag, sym, pk);   // 4 * 2^-9
   } else if constexpr (m == 2) {
-    try_scaled(best, t, 4, -7, sigma, p, w, diag, sym, pk);   // 5 * 2^-9
+    try_scaled<kMse>(best, t, 4, -7, sigma, p, w, diag, sym, pk);   // 5 * 2^-9
   } else if constexpr (m == 4) {
-    try_scaled(best, t, 2, -8, sigma, p, w, diag, sym, pk);   // 3 * 2^-9
-    try_scaled(best, t, 5, -7, sigma, p, w, diag, sym, pk);   // 6 * 2^-9
+    try_scaled<kMse>(best, t, 2, -8, sigma, p, w, diag, sym, pk);   // 3 * 2^-9
+    try_scaled<kMse>(best, t, 5, -7, sigma, p, w, diag, sym, pk);   // 6 * 2^-9
   } else if constexpr (m == 6) {
-    try_scaled(best, t, 6, -7, sigma, p, w, diag, sym, pk);   // 7 * 2^-9
+    try_scaled<kMse>(best, t, 6, -7, sigma, p, w, diag, sym, pk);   // 7 * 2^-9
   }
   // normal codes 8E + m (E = 1..15; code 0x7F is NaN): value mu * 2^(E-7)
   constexpr int emax = (m == 7) ? 14 : 15;
-  for (int E = 1; E <= emax; ++E) try_scaled(best, t, 8 * E + m - 1, E - 7, sigma, p, w, diag, sym, pk);
+  for (int E = 1; E <= emax; ++E) try_scaled<kMse>(best, t, 8 * E + m - 1, E - 7, sigma, p, w, diag, sym, pk);
 }
 
 // Mantissa class and power of two of candidate k: c_k = (1 + m/8) 2^j.
@@ -306,6 +324,43 @@ __device__ __forceinline__ int max_scaling_candidate(const float (&w)[16], float
   }
   code = code < 1 ? 1 : (code > kCandidates ? kCandidates : code);
   return code - 1;
+}
+
+// Working exponent of one row (see "Units"): that of S_g (e_g) while the
+// row's largest |w| is within 2^+-20 of S_g, else that of the largest |w|
+// itself, kept within e_g +- 100 so that S_g 2^-e times every candidate stays
+// a normal fp32 number.
+__device__ __forceinline__ int row_exponent(int e_g, const float (&w)[16]) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(w[i]));
+  if (!(a > 0.0f)) return e_g;
+  const int d = ilogbf(a) - e_g;
+  if (d >= -20 && d <= 20) return e_g;
+  return e_g + (d > 100 ? 100 : (d < -100 ? -100 : d));
+}
+
+// H_b (16x16 row-major, 16-byte aligned) as its diagonal and the symmetrised
+// strict upper triangle H_ij + H_ji.
+__device__ __forceinline__ void load_hessian(const float* hb, float (&diag)[16], float (&sym)[120]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float r[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = reinterpret_cast<const float4*>(hb + 16 * i)[q];
+      r[4 * q] = f.x;
+      r[4 * q + 1] = f.y;
+      r[4 * q + 2] = f.z;
+      r[4 * q + 3] = f.w;
+    }
+    diag[i] = r[i];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j > i) sym[tri(i, j)] = r[j];
+      if (j < i) sym[tri(j, i)] += r[j];
+    }
+  }
 }
 
 template <typename T, bool kVec>
@@ -451,7 +506,7 @@ __global__ __launch_bounds__(kThreads) void sweep_certificate_kernel(const float
 // Two waves per SIMD: the allocator then spills ~14 row-setup values to
 // scratch (none inside the candidate loop), which costs far less than the
 // latency a single wave per SIMD leaves exposed.
-template <typename T, bool kVec>
+template <typename T, bool kVec, bool kMse>
 __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const T* __restrict__ wt, int64_t c_out,
                                                          int64_t ld_w, int64_t gstride_w, int64_t nb,
                                                          int64_t rows_step, int64_t lanes,
@@ -470,57 +525,45 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const T* __restrict_
   const int64_t b = rem - row0 * nb;
 
   float diag[16], sym[120];
-  {
-    const float* hb = h + grp * gstride_h + b * 256;
+  if constexpr (kMse) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float r[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 f = reinterpret_cast<const float4*>(hb + 16 * i)[q];
-        r[4 * q] = f.x;
-        r[4 * q + 1] = f.y;
-        r[4 * q + 2] = f.z;
-        r[4 * q + 3] = f.w;
-      }
-      diag[i] = r[i];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (j > i) sym[tri(i, j)] = r[j];
-        if (j < i) sym[tri(j, i)] += r[j];
-      }
-    }
+    for (int i = 0; i < 16; ++i) diag[i] = 1.0f;
+  } else {
+    load_hessian(h + grp * gstride_h + b * 256, diag, sym);
   }
 
   // Skip certificate: from the pre-pass when given, else scaled Gershgorin
   // gamma = 1 - max_i sum_{j != i} |S_ij| / (2 sqrt(H_ii H_jj)), less 1e-3 for
   // the rounding of this estimate, used only when >= 0.1 (then the fp32 error
   // of E is below 35u * 19).
-  float gamma;
-  if (cert) {
-    gamma = cert[grp * nb + b];
-  } else {
-    bool pos = true;
-    float rs[16], rho[16];
+  // H = I: C = I and tau = 1 exactly; E = sum dw^2 is accurate to 16u.
+  float gamma = 1.0f;
+  if constexpr (!kMse) {
+    if (cert) {
+      gamma = cert[grp * nb + b];
+    } else {
+      bool pos = true;
+      float rs[16], rho[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      pos = pos && (diag[i] > 0.0f) && (diag[i] < INFINITY);
-      rs[i] = diag[i] > 0.0f ? 1.0f / sqrtf(diag[i]) : 0.0f;
-      rho[i] = 0.0f;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-#pragma unroll
-      for (int j = i + 1; j < 16; ++j) {
-        const float c = fabsf(sym[tri(i, j)]) * 0.5f * rs[i] * rs[j];
-        rho[i] += c;
-        rho[j] += c;
+      for (int i = 0; i < 16; ++i) {
+        pos = pos && (diag[i] > 0.0f) && (diag[i] < INFINITY);
+        rs[i] = diag[i] > 0.0f ? 1.0f / sqrtf(diag[i]) : 0.0f;
+        rho[i] = 0.0f;
       }
-    float mx = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, rho[i]);
-    gamma = 1.0f - mx - 1e-3f;
-    if (!pos || !(gamma >= 0.1f)) gamma = 0.0f;
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int j = i + 1; j < 16; ++j) {
+          const float c = fabsf(sym[tri(i, j)]) * 0.5f * rs[i] * rs[j];
+          rho[i] += c;
+          rho[j] += c;
+        }
+      float mx = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, rho[i]);
+      gamma = 1.0f - mx - 1e-3f;
+      if (!pos || !(gamma >= 0.1f)) gamma = 0.0f;
+    }
   }
   // Per-lane scratch in LDS, element-major so that 64 lanes hit 64 consecutive
   // words: the diagonal (fixed) and the current row's prescaled weights.
@@ -533,12 +576,13 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const T* __restrict_
   const float g = amax[grp];
   const float Sg = g / kAmaxDivisor;
   const bool fast = (Sg >= 0x1p-117f) && (Sg <= 0x1p127f);
-  const int e = (Sg > 0.0f && Sg <= 0x1p127f) ? ilogbf(Sg) : 0;
-  const float Su = ldexpf(Sg, -e);  // S_g in units of 2^e: [1, 2)
+  const int e_g = (Sg > 0.0f && Sg <= 0x1p127f) ? ilogbf(Sg) : 0;
 
   for (int64_t row = row0; row < c_out; row += rows_step) {
     float w[16];
     load_block<T, kVec>(wt + grp * gstride_w + row * ld_w + 16 * b, w);
+    const int e = row_exponent(e_g, w);
+    const float Su = ldexpf(Sg, -e);  // S_g in units of 2^e: [1, 2) unless the weights moved e
     Best best{INFINITY, kCandidates};
     uint32_t pk[2] = {0u, 0u};
     if (fast) {
@@ -581,18 +625,128 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const T* __restrict_
         float p0[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) p0[i] = w[i] / sigma0;
-        eval_scaled(best, k0, j0, sigma0, p0, w, diag, sym, pk);
+        eval_scaled<kMse>(best, k0, j0, sigma0, p0, w, diag, sym, pk);
       }
-      sweep_mantissa<0>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<1>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<2>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<3>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<4>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<5>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<6>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<7>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<0, kMse>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<1, kMse>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<2, kMse>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<3, kMse>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<4, kMse>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<5, kMse>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<6, kMse>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<7, kMse>(best, t, Su, w, diag, sym, pk);
     } else {
-      for (int k = 0; k < kCandidates; ++k) eval_direct(best, k, Sg, e, w, diag, sym);
+      for (int k = 0; k < kCandidates; ++k) eval_direct<kMse>(best, k, Sg, e, w, diag, sym);
+    }
+    const int k = best.k < kCandidates ? best.k : 0;  // NaN errors only
+    const int64_t o = (grp * c_out + row) * nb + b;
+    idx_out[o] = (uint8_t)k;
+    if (err_out) err_out[o] = ldexpf(best.err, 2 * e);
+    if (amax_out) amax_out[o] = 6.0f * (e4m3_candidate(k) * Sg);
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Scale rules other than the 126-value sweep ("Local-Hessian weight-scale
+// guide", "What is Local-Hessian": max scaling from the block's largest |w|,
+// Four-Over-Six choosing between two candidate scales by the in-block error;
+// "Entry API and calibration flow": the amax search from multiplier 0.25 to
+// 4.0 in steps of 0.1).  A wanted block scale t (in units of S_g) is stored
+// as the nearest positive finite E4M3 value, ties to the even code,
+// saturating at 448 and never zero.  Candidates: max t = fl32(fl32(a/6)/S_g)
+// with a = max|w|; Four-Over-Six adds t = fl32(fl32(a/4)/S_g); the amax
+// search takes a_i = fl32(m_i a), m_i = fl32((25 + 10 i) / 100), i < 38.
+// The objective is dw^T H dw, or sum dw^2 without a Hessian.  S_g = 0
+// selects candidate 0 (every Q is 0).
+// ---------------------------------------------------------------------------
+
+// E4M3 byte (1..126) stored for a wanted positive scale value t.
+__device__ __forceinline__ int e4m3_store_code(float t) {
+  if (!(t > 0.0f)) return 1;
+  if (t >= 448.0f) return 126;
+  int code;
+  if (t < 0x1p-6f) {
+    code = (int)rintf(t * 512.0f);  // subnormal step 2^-9; ties to the even code
+  } else {
+    const int E = ilogbf(t);                  // -6 .. 8
+    const float mfrac = ldexpf(t, -E) - 1.0f;  // [0, 1), exact
+    code = (E + 7) * 8 + (int)rintf(mfrac * 8.0f);  // a rounded-up 8 carries into the next binade
+  }
+  return code < 1 ? 1 : (code > kCandidates ? kCandidates : code);
+}
+
+// Candidate set of one block as a 128-bit mask (bit k = candidate k).
+__device__ __forceinline__ void rule_mask(int rule, float a, float Sg, uint64_t (&mask)[2]) {
+  mask[0] = mask[1] = 0;
+  auto add = [&](int k) {
+    if (k < 64) mask[0] |= 1ull << k;
+    else mask[1] |= 1ull << (k - 64);
+  };
+  if (!(Sg > 0.0f)) {
+    add(0);
+    return;
+  }
+  if (rule == 3) {
+    for (int i = 0; i < 38; ++i) {
+      const float m = (float)((double)(25 + 10 * i) / 100.0);
+      add(e4m3_store_code((m * a / 6.0f) / Sg) - 1);
+    }
+    return;
+  }
+  add(e4m3_store_code((a / 6.0f) / Sg) - 1);
+  if (rule == 2) add(e4m3_store_code((a / 4.0f) / Sg) - 1);
+}
+
+template <typename T, bool kVec, bool kMse>
+__global__ __launch_bounds__(kThreads) void select_kernel(int rule, const T* __restrict__ wt, int64_t c_out,
+                                                          int64_t ld_w, int64_t gstride_w, int64_t nb,
+                                                          int64_t rows_step, int64_t lanes,
+                                                          const float* __restrict__ h, int64_t gstride_h,
+                                                          const float* __restrict__ amax,
+                                                          uint8_t* __restrict__ idx_out,
+                                                          float* __restrict__ err_out,
+                                                          float* __restrict__ amax_out) {
+  const int64_t L = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (L >= lanes) return;
+  const int64_t per_group = nb * rows_step;
+  const int64_t grp = L / per_group;
+  const int64_t rem = L - grp * per_group;
+  const int64_t row0 = rem / nb;
+  const int64_t b = rem - row0 * nb;
+
+  float diag[16], sym[120];
+  if constexpr (kMse) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) diag[i] = 1.0f;
+  } else {
+    load_hessian(h + grp * gstride_h + b * 256, diag, sym);
+  }
+  const float g = amax[grp];
+  const float Sg = g / kAmaxDivisor;
+  const int e_g = (Sg > 0.0f && Sg <= 0x1p127f) ? ilogbf(Sg) : 0;
+
+  for (int64_t row = row0; row < c_out; row += rows_step) {
+    float w[16];
+    load_block<T, kVec>(wt + grp * gstride_w + row * ld_w + 16 * b, w);
+    const int e = row_exponent(e_g, w);
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(w[i]));
+    uint64_t mask[2];
+    rule_mask(rule, a, Sg, mask);
+    Best best{INFINITY, kCandidates};
+    // ascending candidate order; lanes leave the loop when their mask is empty
+    while ((mask[0] | mask[1]) != 0) {
+      int k;
+      if (mask[0] != 0) {
+        k = __builtin_ctzll(mask[0]);
+        mask[0] &= mask[0] - 1;
+      } else {
+        k = 64 + __builtin_ctzll(mask[1]);
+        mask[1] &= mask[1] - 1;
+      }
+      eval_direct<kMse>(best, k, Sg, e, w, diag, sym);
     }
     const int k = best.k < kCandidates ? best.k : 0;  // NaN errors only
     const int64_t o = (grp * c_out + row) * nb + b;
@@ -615,6 +769,24 @@ hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
   k = (a.c_out + rows_per_lane - 1) / rows_per_lane;
   const int64_t lanes = per_k * k;
   const int64_t grid = (lanes + kThreads - 1) / kThreads;
+  const bool mse = a.h == nullptr;
+  if (a.rule != 0) {
+    if (mse)
+      select_kernel<T, kVec, true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+          a.rule, static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, k, lanes, nullptr, 0, a.amax,
+          a.idx, a.err, a.best_amax);
+    else
+      select_kernel<T, kVec, false><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+          a.rule, static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, k, lanes, a.h, a.gstride_h,
+          a.amax, a.idx, a.err, a.best_amax);
+    return hipGetLastError();
+  }
+  if (mse) {
+    sweep_kernel<T, kVec, true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+        static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, k, lanes, nullptr, 0, a.amax, a.idx, a.err,
+        a.best_amax, nullptr);
+    return hipGetLastError();
+  }
   float* cert = nullptr;
   if (a.ws != nullptr && a.ws_bytes >= sweep_ws_bytes(a.c_in, a.n_groups)) {
     cert = static_cast<float*>(a.ws);
@@ -623,7 +795,7 @@ hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  sweep_kernel<T, kVec><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+  sweep_kernel<T, kVec, false><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
       static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, k, lanes, a.h, a.gstride_h, a.amax,
       a.idx, a.err, a.best_amax, cert);
   return hipGetLastError();
@@ -641,7 +813,7 @@ hipError_t launch_sweep(const SweepArgs& a, hipStream_t stream) {
   const int64_t epv = 16 / esz;
   const bool aligned = (reinterpret_cast<uintptr_t>(a.w) % 16 == 0) && (a.ld_w % epv == 0) &&
                        (a.gstride_w % epv == 0);
-  const bool h_aligned = (reinterpret_cast<uintptr_t>(a.h) % 16 == 0) && (a.gstride_h % 4 == 0);
+  const bool h_aligned = a.h == nullptr || ((reinterpret_cast<uintptr_t>(a.h) % 16 == 0) && (a.gstride_h % 4 == 0));
   if (!h_aligned) return hipErrorInvalidValue;  // rejected earlier by the front end
   if (a.dtype == 1)
     return aligned ? launch_sweep_typed<uint16_t, true>(a, stream) : launch_sweep_typed<uint16_t, false>(a, stream);

@@ -137,3 +137,23 @@ def fake_quant_against_oracle(w_np, idx_full, amax_np, c_out, c_in, n_groups, se
         assert np.array_equal(got, fq["packed"]), "%s packed nibbles differ" % what
     if "scale_e4m3" in gpu:
         assert np.array_equal(gpu["scale_e4m3"].reshape(-1)[sel], fq["code"]), "%s E4M3 codes differ" % what
+
+
+def select_against_oracle(rule, w_np, h_np, amax_np, c_out, c_in, n_groups, sel, gpu_idx_full, gpu_err_full,
+                          gpu_amax_full, what=""):
+    """Scale selection by rule (h_np None = plain weight error) against the
+    oracle on `sel`, with the sweep's rules; S uses H = I without a Hessian."""
+    nb = c_in // 16
+    res = oracle.select(rule, w_np, h_np, amax_np, c_out, c_in, n_groups=n_groups, sel=sel)
+    idx_full = np.zeros(n_groups * c_out * nb, np.uint8)
+    idx_full[sel] = res["idx"].astype(np.uint8)
+    fq = oracle.fake_quant(w_np, idx_full, amax_np, c_out, c_in, n_groups=n_groups, sel=sel)
+    if h_np is None:
+        hb = np.broadcast_to(np.eye(16, dtype=np.float32), (len(sel), 16, 16))
+    else:
+        grp = sel // (c_out * nb)
+        hb = h_np.reshape(n_groups, nb, 16, 16)[grp, sel % nb]
+    S = abs_form(block_rows(w_np, sel, c_out, c_in), fq["q"], hb)
+    ge = None if gpu_err_full is None else gpu_err_full.reshape(-1)[sel]
+    ga = None if gpu_amax_full is None else gpu_amax_full.reshape(-1)[sel]
+    return check_sweep(gpu_idx_full.reshape(-1)[sel], ge, ga, res, S, what)

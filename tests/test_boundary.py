@@ -138,3 +138,32 @@ def test_workspace_plan_is_host_logic(lib):
     assert ws(17408, 16384, 1) >= 0
     # depends only on its three arguments
     assert ws(4096, 4096, 1) == ws(4096, 4096, 1)
+
+
+def test_select_validation(lib):
+    P = ctypes.c_void_p
+    ok = dict(rule=1, w=P(FAKE), dt=1, c_out=4, c_in=32, ld=32, g=1, gs=0, h=None, hs=0, amax=P(FAKE),
+              idx=P(FAKE), err=None, am=None, ws=None, wsb=0, st=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.lh_select_scales(a["rule"], a["w"], a["dt"], a["c_out"], a["c_in"], a["ld"], a["g"], a["gs"],
+                                    a["h"], a["hs"], a["amax"], a["idx"], a["err"], a["am"], a["ws"], a["wsb"],
+                                    a["st"])
+
+    assert call(rule=4) == ARG and "rule" in _msg(lib)
+    assert call(rule=-1) == ARG
+    assert call(dt=5) == DTYPE
+    assert call(c_in=20) == SHAPE
+    assert call(w=None) == NULL
+    assert call(amax=None) == NULL
+    assert call(idx=None) == NULL
+    assert call(h=P(FAKE + 8)) == ARG            # a given Hessian must be 16-byte aligned
+    assert call(err=P(FAKE + 2)) == ARG
+    assert call(ws=None, wsb=4) == NULL
+    # empty problems are valid no-ops, with or without a Hessian
+    assert call(c_out=0, w=None, idx=None) == OK
+    assert call(g=0, h=P(FAKE)) == OK
+    # lh_scale_sweep still requires its Hessian
+    assert lib.lh_scale_sweep(P(FAKE), 1, 4, 32, 32, 1, 0, None, 0, P(FAKE), P(FAKE), None, None, None, 0,
+                              None) == NULL
