@@ -71,6 +71,7 @@ def _load():
     lib.oracle_rule_candidates.argtypes = [I32, P, F, P]
     lib.oracle_rule_candidates.restype = I32
     lib.oracle_select.argtypes = [I32, P, I32, I64, I64, I64, I64, P, I64, P, P, I64, P, P, P, P, P]
+    lib.oracle_hessian_ragged.argtypes = [P, I32, I64, I64, P, I64, P, P, I64, P, P, P]
     lib.oracle_num_threads.restype = I32
     lib.oracle_set_num_threads.argtypes = [I32]
     _lib = lib
@@ -249,3 +250,29 @@ def select(rule: int, w: np.ndarray, H, amax: np.ndarray, c_out: int, c_in: int,
                           _ptr(out["idx"]), _ptr(out["e1"]), _ptr(out["e2"]), _ptr(out["err"]),
                           _ptr(out["amax"]))
     return out
+
+
+def hessian_ragged(x: np.ndarray, c_in: int, offsets, h_old: np.ndarray, counts=None, ld_x: int | None = None,
+                   sel: np.ndarray | None = None):
+    """Per-group Hessians of token-major x [rows][ld_x] whose rows
+    offsets[g] .. offsets[g+1]-1 belong to group g.  h_old is the previous
+    fp32 Hessian tensor [n_groups][c_in/16][16][16]; without counts each
+    group with tokens gets S_g / n_g, with counts the running mean
+    (n_old H + S_g) / (n_old + n_g); groups without tokens keep h_old.
+    Returns (h64, h32) compact over the selected flat blocks, and the
+    updated counts (or None)."""
+    x = np.ascontiguousarray(x)
+    offsets = np.ascontiguousarray(offsets, np.int64)
+    n_groups = len(offsets) - 1
+    nb = c_in // 16
+    ld_x = c_in if ld_x is None else ld_x
+    sel = np.arange(n_groups * nb, dtype=np.int64) if sel is None else np.ascontiguousarray(sel, np.int64)
+    hold = np.ascontiguousarray(np.asarray(h_old, np.float32).reshape(n_groups * nb, 256)[sel])
+    cnt = None if counts is None else np.ascontiguousarray(counts, np.int64)
+    h64 = np.zeros((len(sel), 16, 16), np.float64)
+    h32 = np.zeros((len(sel), 16, 16), np.float32)
+    _load().oracle_hessian_ragged(_ptr(x), _dtype_code(x), c_in, ld_x, _ptr(offsets), n_groups,
+                                  None if cnt is None else _ptr(cnt), _ptr(sel), len(sel), _ptr(hold),
+                                  _ptr(h64), _ptr(h32))
+    new_counts = None if cnt is None else cnt + np.diff(offsets)
+    return h64, h32, new_counts

@@ -491,3 +491,54 @@ void oracle_select(int rule, const void *w, int dtype, int64_t c_out, int64_t c_
         }
     }
 }
+
+/* ====================================================================== */
+/* Ragged / streaming Hessian accumulation ([LHG] "Entry API and          */
+/* calibration flow", phase 2: forward hooks capture each linear layer's  */
+/* inputs batch by batch and accumulate X^T X per module; MoE experts see  */
+/* only the tokens routed to them, so their token counts differ and may   */
+/* be zero; phase 3 uses the per-block Hessian normalised by the tokens).  */
+/* Readings:                                                               */
+/*   R12 x is token-major, rows offsets[g] .. offsets[g+1]-1 belong to     */
+/*       group g (expert g); n_g = offsets[g+1] - offsets[g].              */
+/*   R13 without counts: H_g = S_g / n_g, S_g = sum over the group's rows   */
+/*       of x_t x_t^T (block diagonal); a group with n_g = 0 keeps its old */
+/*       H (the caller's fallback, e.g. the identity = plain MSE).         */
+/*   R14 with counts (a running mean over batches): n_old = counts[g],     */
+/*       H_g = (n_old H_g + S_g) / (n_old + n_g), counts[g] = n_old + n_g; */
+/*       unchanged while n_old + n_g = 0.                                  */
+/* Outputs are compact per selected flat block g * (c_in/16) + b; h_old    */
+/* (compact, fp32) is the previous H of those blocks.                      */
+/* ====================================================================== */
+void oracle_hessian_ragged(const void *x, int dtype, int64_t c_in, int64_t ld_x,
+                           const int64_t *offsets, int64_t n_groups, const int64_t *counts,
+                           const int64_t *sel, int64_t n_sel, const float *h_old, double *h64,
+                           float *h32)
+{
+    const int64_t nb = c_in / 16;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t n = 0; n < n_sel; ++n) {
+        const int64_t g = sel[n] / nb, b = sel[n] % nb;
+        const int64_t r0 = offsets[g], r1 = offsets[g + 1];
+        const int64_t ng = r1 - r0;
+        const int64_t nold = counts ? counts[g] : 0;
+        for (int i = 0; i < 16; ++i)
+            for (int j = 0; j < 16; ++j) {
+                const int64_t ci = 16 * b + i, cj = 16 * b + j;
+                double acc = 0.0;
+                for (int64_t t = r0; t < r1; ++t)
+                    acc += widen(x, dtype, t * ld_x + ci) * widen(x, dtype, t * ld_x + cj);
+                const double old = (double)h_old[n * 256 + i * 16 + j];
+                double v;
+                if (nold + ng == 0 || (!counts && ng == 0))
+                    v = old;
+                else if (counts)
+                    v = ((double)nold * old + acc) / (double)(nold + ng);
+                else
+                    v = acc / (double)ng;
+                if (h64)
+                    h64[n * 256 + i * 16 + j] = v;
+                h32[n * 256 + i * 16 + j] = (float)v;
+            }
+    }
+}
