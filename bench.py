@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--workload", type=int, default=2, help="named workload 1..5 (default: dense-4096)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the cold-cache Hessian timing and the scale-rule variants")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 256 MiB device copy 5 times (HBM counter calibration)")
     return p.parse_args()
@@ -84,6 +86,81 @@ def traffic_from_profiles(kernel: str, workload: str, src_hash: str):
     if not ent or ent.get("source_hash") != src_hash:
         return None
     return ent.get("bytes_per_launch")
+
+
+def timed(fn, stream, reps: int, before=None):
+    """Per-rep durations (ms) of fn() with HIP events on `stream`; before()
+    runs outside the bracket."""
+    import torch
+    out = []
+    for _ in range(reps):
+        if before is not None:
+            before()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        out.append(e0.elapsed_time(e1))
+    return out
+
+
+def pct(v, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(v), q))
+
+
+def extras(lh, work, w, x, h, amax, idx, err, bam, ws, ws_bytes, stream) -> dict:
+    """Outside the timed steps: (1) the Hessian pass with the last-level
+    cache flushed before every rep (a 512 MiB scratch write), median and
+    p10/p90; (2) every scale rule of lh_select_scales on the same layer,
+    with the local Hessian and with the plain weight error."""
+    import torch
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=w.device)
+    cold = timed(lambda: lh.lh_accumulate_hessian(x, h=h, workspace=ws if ws_bytes else None), stream, 15,
+                 before=lambda: scratch.fill_(1))
+    del scratch
+    blocks = work.n_blocks
+    rules = {}
+    names = {0: "sweep126", 1: "max", 2: "four_over_six", 3: "amax_search"}
+    for rule in (0, 1, 2, 3):
+        for weighted in (True, False):
+            hh = h if weighted else None
+            fn = (lambda r=rule, hh=hh: lh.lh_select_scales(r, w, hh, amax, best_idx=idx, best_err=err,
+                                                              best_amax=bam))
+            fn()
+            t = timed(fn, stream, 5)
+            ms = sorted(t)[len(t) // 2]
+            rules["%s/%s" % (names[rule], "hessian" if weighted else "mse")] = {
+                "ms": ms, "blocks_per_s": blocks / (ms / 1e3)}
+    # ragged / streaming Hessian on the MoE layer's capture (skewed routing)
+    import lh_workloads as wl
+    cap = wl.make_ragged_moe()
+    xr = cap.x.to(w.device)
+    off = torch.from_numpy(cap.offsets).to(w.device)
+    hr = torch.zeros((cap.n_groups, cap.c_in // 16, 16, 16), dtype=torch.float32, device=w.device)
+    cnt = torch.zeros(cap.n_groups, dtype=torch.int64, device=w.device)
+    rb = lh.lh_hessian_ragged_workspace_bytes(cap.c_in, xr.shape[0], cap.n_groups)
+    rws = torch.empty(max(rb, 1), dtype=torch.uint8, device=w.device)
+    fn = (lambda: lh.lh_accumulate_hessian_ragged(xr, off, h=hr, counts=cnt, workspace=rws if rb else None))
+    fn()
+    warm = timed(fn, stream, 15)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=w.device)
+    rcold = timed(fn, stream, 15, before=lambda: scratch.fill_(1))
+    del scratch
+    counts = cap.offsets[1:] - cap.offsets[:-1]
+    xb = work.x_bytes
+    return {"hessian_cold": {"median_ms": pct(cold, 50), "p10_ms": pct(cold, 10), "p90_ms": pct(cold, 90),
+                             "gbps_median": xb / (pct(cold, 50) / 1e3) / 1e9,
+                             "flush": "512 MiB device write before every rep"},
+            "hessian_ragged": {"workload": cap.description, "x_bytes": cap.x_bytes,
+                               "max_group_rows": int(counts.max()), "empty_groups": int((counts == 0).sum()),
+                               "running_mean": True,
+                               "warm_median_ms": pct(warm, 50), "warm_gbps": cap.x_bytes / (pct(warm, 50) / 1e3) / 1e9,
+                               "cold_median_ms": pct(rcold, 50), "cold_p10_ms": pct(rcold, 10),
+                               "cold_p90_ms": pct(rcold, 90),
+                               "cold_gbps": cap.x_bytes / (pct(rcold, 50) / 1e3) / 1e9},
+            "scale_rules": rules}
 
 
 def cpu_baseline(work, budget_s: float) -> dict:
@@ -234,6 +311,8 @@ def main():
                     "x_bytes": work.x_bytes, "warm": True},
         "source_hash": src_hash,
     }
+    if not args.no_extras:
+        out["extras"] = extras(lh, work, w, x, h, amax, idx, err, bam, ws, ws_bytes, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(work, args.cpu_seconds)
     print(json.dumps(out), flush=True)

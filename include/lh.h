@@ -149,6 +149,50 @@ lh_status lh_accumulate_hessian(const void *x, int x_dtype, int layout, int64_t 
                                 void *stream);
 
 /*
+ * Scratch bytes lh_accumulate_hessian_ragged can use for its deterministic
+ * split of each group's rows (0 = it runs one pass per block).  Depends only
+ * on the arguments.
+ */
+size_t lh_hessian_ragged_workspace_bytes(int64_t c_in, int64_t n_rows, int64_t n_groups);
+
+/*
+ * Ragged / streaming local Hessians ("Entry API and calibration flow",
+ * phase 2: forward hooks capture each layer's token-major inputs batch by
+ * batch and accumulate X^T X; MoE experts receive only their routed tokens,
+ * so their token counts differ and may be zero; phase 3 normalises by the
+ * token count).
+ *
+ * x is token-major, x[t * ld_x + c] for rows t < n_rows; rows
+ * token_offsets[g] .. token_offsets[g+1]-1 belong to group g (expert g),
+ * n_g = their count.  With S_g[b] = sum over those rows of x_b x_b^T:
+ *   token_counts == NULL:  h[g] = S_g / n_g for groups with n_g > 0.
+ *   token_counts != NULL:  running mean over calls,
+ *                          h[g] = (n_old h[g] + S_g) / (n_old + n_g),
+ *                          n_old = token_counts[g]; then token_counts[g] += n_g.
+ * A group that receives no row keeps h[g] unchanged (the caller's fallback,
+ * e.g. the identity, which makes the sweep the plain weight-error sweep).
+ *   x             fp32 or bf16 (x_dtype), ld_x >= c_in.
+ *   token_offsets device int64 [n_groups + 1], 8-byte aligned; expected
+ *                 non-decreasing within [0, n_rows].  Offsets are clamped to
+ *                 [0, n_rows] and a decreasing pair gives an empty group, so
+ *                 no offset can make the kernels read outside x.
+ *   h             fp32 [n_groups][c_in/16][16][16], group stride
+ *                 group_stride_h (>= (c_in/16)*256 when n_groups > 1).
+ *   token_counts  NULL, or device int64 [n_groups] (8-byte aligned), read
+ *                 and updated on the stream.
+ *   workspace     NULL/0, or at least lh_hessian_ragged_workspace_bytes(c_in,
+ *                 n_rows, n_groups) bytes (4-byte aligned).
+ * Results are deterministic (fixed reduction order).
+ * Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_WORKSPACE,
+ * LH_ERR_ARG, LH_ERR_HIP.
+ */
+lh_status lh_accumulate_hessian_ragged(const void *x, int x_dtype, int64_t c_in, int64_t ld_x,
+                                       int64_t n_rows, const int64_t *token_offsets,
+                                       int64_t n_groups, float *h, int64_t group_stride_h,
+                                       int64_t *token_counts, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
+/*
  * Scratch bytes that let lh_scale_sweep skip provably worse candidates with a
  * tight per-block certificate (a lower bound on the smallest eigenvalue of
  * the block's correlation matrix, one fp32 per block).  0 bytes is always

@@ -165,3 +165,53 @@ def make_custom(c_out: int, c_in: int, n_tok: int, n_groups: int = 1, dtype: str
         raise ValueError(x_dist)
     return Workload("custom-%dx%dx%dx%d" % (n_groups, c_out, c_in, n_tok), "custom", c_out, c_in,
                     n_tok, n_groups, dtype, _store(w, dtype), _store(x, dtype))
+
+
+@dataclass
+class RaggedCapture:
+    """Token-major activations of several groups (MoE experts) in one buffer:
+    rows offsets[g] .. offsets[g+1]-1 belong to group g."""
+    name: str
+    description: str
+    c_in: int
+    dtype: str
+    x: torch.Tensor          # [n_rows, c_in], CPU, token-major
+    offsets: np.ndarray      # int64 [n_groups + 1]
+
+    @property
+    def n_groups(self) -> int:
+        return len(self.offsets) - 1
+
+    @property
+    def x_bytes(self) -> int:
+        return self.x.numel() * self.x.element_size()
+
+
+def make_ragged(n_groups: int, c_in: int, n_rows: int, dtype: str = BF16, seed: int = 0,
+                concentration: float = 0.3, n_empty: int = 0) -> RaggedCapture:
+    """Skewed routing: group shares ~ Dirichlet(concentration) (small values
+    give a few heavy experts and many light ones), `n_empty` groups forced to
+    zero rows, counts rounded so they sum to n_rows; rows ~ N(0, 1) with a
+    log-normal scale per channel.  Streams: SeedSequence(seed).spawn(3) for
+    the shares, the empty picks and the values."""
+    s_share, s_empty, s_val = [np.random.default_rng(q) for q in np.random.SeedSequence(seed).spawn(3)]
+    share = s_share.dirichlet(np.full(n_groups, concentration))
+    if n_empty:
+        share[s_empty.choice(n_groups, n_empty, replace=False)] = 0.0
+        share /= share.sum()
+    counts = np.floor(share * n_rows).astype(np.int64)
+    rest = n_rows - int(counts.sum())
+    order = np.argsort(-(share * n_rows - counts))  # largest remainders first
+    counts[order[:rest]] += 1
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    x = _normal(s_val, (n_rows, c_in)) * np.exp(s_val.standard_normal(c_in)).astype(np.float32)
+    desc = ("ragged capture: %d groups, X[%d tokens x %d] %s token-major, Dirichlet(%g) routing shares, "
+            "%d empty groups, channel scales exp(N(0,1))" % (n_groups, n_rows, c_in, dtype, concentration, n_empty))
+    return RaggedCapture("ragged-%dx%d" % (n_groups, c_in), desc, c_in, dtype, _store(x, dtype), offsets)
+
+
+def make_ragged_moe() -> RaggedCapture:
+    """The MoE layer's activations as hooks would capture them: 64 experts,
+    C_in 2048, the 32768 routed tokens (64 x 512 on average) split by skewed
+    routing, 4 experts without tokens."""
+    return make_ragged(64, 2048, 64 * 512, BF16, seed=2004, concentration=0.3, n_empty=4)

@@ -52,6 +52,10 @@ def _load() -> ctypes.CDLL:
     lib.lh_hessian_workspace_bytes.restype = SZ
     lib.lh_accumulate_hessian.argtypes = [P, I, I, I64, I64, I64, I64, I64, F, F, P, I64, P, SZ, P]
     lib.lh_accumulate_hessian.restype = I
+    lib.lh_hessian_ragged_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.lh_hessian_ragged_workspace_bytes.restype = SZ
+    lib.lh_accumulate_hessian_ragged.argtypes = [P, I, I64, I64, I64, P, I64, P, I64, P, P, SZ, P]
+    lib.lh_accumulate_hessian_ragged.restype = I
     lib.lh_sweep_workspace_bytes.argtypes = [I64, I64]
     lib.lh_sweep_workspace_bytes.restype = SZ
     lib.lh_scale_sweep.argtypes = [P, I, I64, I64, I64, I64, I64, P, I64, P, P, P, P, P, SZ, P]
@@ -65,7 +69,8 @@ def _load() -> ctypes.CDLL:
 
 lib = _load()
 EXPORTS = ("lh_abi_version", "lh_status_string", "lh_last_error_message", "lh_absmax",
-           "lh_hessian_workspace_bytes", "lh_accumulate_hessian", "lh_sweep_workspace_bytes", "lh_scale_sweep",
+           "lh_hessian_workspace_bytes", "lh_accumulate_hessian", "lh_hessian_ragged_workspace_bytes",
+           "lh_accumulate_hessian_ragged", "lh_sweep_workspace_bytes", "lh_scale_sweep",
            "lh_select_scales", "lh_fake_quant_nvfp4")
 
 
@@ -172,6 +177,43 @@ def lh_accumulate_hessian(x: torch.Tensor, layout: str = "channel", alpha: float
     _check(lib.lh_accumulate_hessian(_ptr(x3), _dtype(x3), lay, c_in, n_tok, _ld(x3), g,
                                      _group_stride(x3), float(alpha), float(beta), _ptr(h), h_gstride,
                                      _ptr(ws), ws_bytes, _stream(x)))
+    return h
+
+
+def lh_hessian_ragged_workspace_bytes(c_in: int, n_rows: int, n_groups: int) -> int:
+    return int(lib.lh_hessian_ragged_workspace_bytes(c_in, n_rows, n_groups))
+
+
+def lh_accumulate_hessian_ragged(x: torch.Tensor, offsets: torch.Tensor, h: torch.Tensor | None = None,
+                                 counts: torch.Tensor | None = None,
+                                 workspace: torch.Tensor | bool | None = True) -> torch.Tensor:
+    """Per-group Hessians of token-major x [n_rows, c_in] whose rows
+    offsets[g] .. offsets[g+1]-1 (device int64 [n_groups + 1]) belong to
+    group g.  Without counts each group with tokens gets S_g / n_g; with a
+    device int64 counts tensor the running mean (n_old H + S_g) / (n_old +
+    n_g) is kept and counts is advanced.  Groups without tokens keep h (a
+    new h starts at zero)."""
+    _require_device(x, offsets, h, counts)
+    if x.dim() != 2 or x.stride(-1) != 1:
+        raise ValueError("x must be a 2-D token-major tensor with contiguous rows")
+    if offsets.dtype != torch.int64 or counts is not None and counts.dtype != torch.int64:
+        raise TypeError("offsets and counts must be int64")
+    n_rows, c_in = x.shape
+    g = offsets.numel() - 1
+    nb = c_in // BLOCK
+    if h is None:
+        h = torch.zeros((g, nb, BLOCK, BLOCK), dtype=torch.float32, device=x.device)
+    ws, ws_bytes = None, 0
+    if workspace is True:
+        ws_bytes = lh_hessian_ragged_workspace_bytes(c_in, n_rows, g)
+        if ws_bytes:
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    elif isinstance(workspace, torch.Tensor):
+        ws, ws_bytes = workspace, workspace.numel() * workspace.element_size()
+    h_gstride = h.stride(0) if h.dim() == 4 and h.shape[0] > 1 else 0
+    ld = x.stride(0) if n_rows > 1 else c_in
+    _check(lib.lh_accumulate_hessian_ragged(_ptr(x), _dtype(x), c_in, ld, n_rows, _ptr(offsets), g, _ptr(h),
+                                            h_gstride, _ptr(counts), _ptr(ws), ws_bytes, _stream(x)))
     return h
 
 

@@ -105,6 +105,45 @@ lh_status lh_accumulate_hessian(const void* x, int x_dtype, int layout, int64_t 
   return e == hipSuccess ? LH_OK : hip_fail(e, fn);
 }
 
+size_t lh_hessian_ragged_workspace_bytes(int64_t c_in, int64_t n_rows, int64_t n_groups) {
+  if (c_in <= 0 || n_rows <= 0 || n_groups <= 0 || c_in % 16 != 0) return 0;
+  return lh::hessian_ragged_ws_bytes(c_in, n_rows, n_groups);
+}
+
+lh_status lh_accumulate_hessian_ragged(const void* x, int x_dtype, int64_t c_in, int64_t ld_x, int64_t n_rows,
+                                       const int64_t* token_offsets, int64_t n_groups, float* h,
+                                       int64_t group_stride_h, int64_t* token_counts, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  const char* fn = "lh_accumulate_hessian_ragged";
+  g_msg[0] = '\0';
+  if (!valid_dtype(x_dtype)) return fail(LH_ERR_DTYPE, "%s: x_dtype must be 0 (f32) or 1 (bf16)", fn);
+  if (c_in < 0 || n_rows < 0 || n_groups < 0 || group_stride_h < 0)
+    return fail(LH_ERR_SHAPE, "%s: negative size or stride", fn);
+  if (c_in % 16 != 0) return fail(LH_ERR_SHAPE, "%s: c_in must be a multiple of 16", fn);
+  if (ld_x < c_in || ld_x < 1) return fail(LH_ERR_SHAPE, "%s: ld_x < c_in", fn);
+  const int64_t nb = c_in / 16;
+  if (n_groups > 1 && group_stride_h < nb * 256)
+    return fail(LH_ERR_SHAPE, "%s: group_stride_h < (c_in/16)*256 would overlap outputs", fn);
+  const bool work = n_groups > 0 && nb > 0;
+  if (work && (h == nullptr || token_offsets == nullptr))
+    return fail(LH_ERR_NULL, "%s: h and token_offsets are required", fn);
+  if (work && n_rows > 0 && x == nullptr) return fail(LH_ERR_NULL, "%s: x is NULL", fn);
+  if (workspace == nullptr && workspace_bytes > 0) return fail(LH_ERR_NULL, "%s: workspace is NULL but workspace_bytes > 0", fn);
+  if (!aligned(x, elem_size(x_dtype)) || !aligned(h, 4) || !aligned(workspace, 4) || !aligned(token_offsets, 8) ||
+      !aligned(token_counts, 8))
+    return fail(LH_ERR_ARG, "%s: pointer not aligned to its element size", fn);
+  if (workspace != nullptr && workspace_bytes > 0 && work) {
+    const size_t need = lh::hessian_ragged_ws_bytes(c_in, n_rows, n_groups);
+    if (workspace_bytes < need)
+      return fail(LH_ERR_WORKSPACE, "%s: workspace smaller than lh_hessian_ragged_workspace_bytes()", fn);
+  }
+  if (!work) return LH_OK;
+  lh::HessianRaggedArgs a{x, x_dtype, c_in, ld_x, n_rows, token_offsets, n_groups, h, group_stride_h,
+                          token_counts, workspace, workspace_bytes};
+  hipError_t e = lh::launch_hessian_ragged(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LH_OK : hip_fail(e, fn);
+}
+
 size_t lh_sweep_workspace_bytes(int64_t c_in, int64_t n_groups) {
   if (c_in <= 0 || n_groups <= 0 || c_in % 16 != 0) return 0;
   return lh::sweep_ws_bytes(c_in, n_groups);

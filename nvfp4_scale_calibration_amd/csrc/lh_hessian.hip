@@ -150,42 +150,28 @@ __global__ __launch_bounds__(kThreads) void hessian_cm_kernel(const T* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Token-major kernel: x[t * ld + 16b + c].  Each wave stages a 64-token x
-// 16-channel tile in LDS (row = one token, 16 values, no padding) and lane
-// (ch, kg) reads tokens kg, kg+4, ..., kg+60 of column ch: for bf16 the 64
-// lanes touch 32 distinct words in 32 distinct banks, for fp32 every bank
-// serves exactly two lanes (the minimum for 64 four-byte reads).
-// The trip count is uniform over the workgroup (slabs past the end load
-// zeros), so the barriers are reached by every wave.
+// Token-major accumulation: x[t * ld + 16b + c] for tokens [t0, t1).  Each
+// wave stages a 64-token x 16-channel tile in LDS (row = one token, 16
+// values, no padding) and lane (ch, kg) reads tokens kg, kg+4, ..., kg+60 of
+// column ch: for bf16 the 64 lanes touch 32 distinct words in 32 distinct
+// banks, for fp32 every bank serves exactly two lanes (the minimum for 64
+// four-byte reads).  The trip count is uniform over the workgroup (slabs
+// past the end load zeros), so the barriers are reached by every wave.
+// `base` points at channel 16b of token 0.
 // ---------------------------------------------------------------------------
 template <typename T, bool kVec>
-__global__ __launch_bounds__(kThreads) void hessian_tm_kernel(const T* __restrict__ x, int64_t n_tok,
-                                                              int64_t ld, int64_t gstride, int64_t nb,
-                                                              int64_t n_groups, int64_t nsplit,
-                                                              int64_t chunk, float alpha, float beta,
-                                                              float* __restrict__ h, int64_t h_gstride,
-                                                              float* __restrict__ ws) {
+__device__ __forceinline__ f32x4_t tm_accumulate(const T* __restrict__ base, int64_t ld, int64_t t0, int64_t t1,
+                                                 T* my, int wave, int lane) {
   constexpr int kElemsPer16B = 16 / sizeof(T);          // 8 bf16 or 4 fp32
   constexpr int kLanesPerTok = 16 / kElemsPer16B;       // 2 or 4
   constexpr int kToksPerLoad = 64 / kLanesPerTok;       // 32 or 16
   constexpr int kLoads = kSlab / kToksPerLoad;          // 2 or 4
-  __shared__ __attribute__((aligned(16))) T tile[4][kSlab * 16];
-  __shared__ float red[4][256];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ch = lane & 15, kg = lane >> 4;
-  int64_t id = blockIdx.x;
-  const int64_t s = id % nsplit;
-  id /= nsplit;
-  const int64_t b = id % nb, grp = id / nb;
-  const int64_t t0 = s * chunk;
-  const int64_t t1 = min(n_tok, t0 + chunk);
-  const T* base = x + grp * gstride + 16 * b;
-  T* my = tile[wave];
   const int ltok = lane / kLanesPerTok;                 // token within a load
   const int lcol = (lane % kLanesPerTok) * kElemsPer16B;  // first channel
 
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  const int64_t rounds = (t1 - t0 + kRound - 1) / kRound;
+  const int64_t rounds = t1 > t0 ? (t1 - t0 + kRound - 1) / kRound : 0;
   for (int64_t r = 0; r < rounds; ++r) {
     const int64_t t = t0 + r * kRound + wave * kSlab;
 #pragma unroll
@@ -219,18 +205,129 @@ __global__ __launch_bounds__(kThreads) void hessian_tm_kernel(const T* __restric
     __syncthreads();
     acc = mfma_accumulate(v, acc);
   }
+  return acc;
+}
 
+// Fixed-order sum of the four waves' 16x16 results; thread e gets entry e.
+__device__ __forceinline__ float reduce_waves(f32x4_t acc, float (&red)[4][256], int wave, int lane) {
+  const int ch = lane & 15, kg = lane >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) red[wave][(4 * kg + i) * 16 + ch] = acc[i];
   __syncthreads();
   const int e = threadIdx.x;
-  const float v = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+  return ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+}
+
+template <typename T, bool kVec>
+__global__ __launch_bounds__(kThreads) void hessian_tm_kernel(const T* __restrict__ x, int64_t n_tok,
+                                                              int64_t ld, int64_t gstride, int64_t nb,
+                                                              int64_t n_groups, int64_t nsplit,
+                                                              int64_t chunk, float alpha, float beta,
+                                                              float* __restrict__ h, int64_t h_gstride,
+                                                              float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) T tile[4][kSlab * 16];
+  __shared__ float red[4][256];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int64_t id = blockIdx.x;
+  const int64_t s = id % nsplit;
+  id /= nsplit;
+  const int64_t b = id % nb, grp = id / nb;
+  const int64_t t0 = s * chunk;
+  const int64_t t1 = min(n_tok, t0 + chunk);
+  const f32x4_t acc = tm_accumulate<T, kVec>(x + grp * gstride + 16 * b, ld, t0, t1, tile[wave], wave, lane);
+  const float v = reduce_waves(acc, red, wave, lane);
+  const int e = threadIdx.x;
   if (nsplit == 1) {
     float* hp = h + grp * h_gstride + b * 256 + e;
     *hp = (beta == 0.0f) ? alpha * v : beta * (*hp) + alpha * v;
   } else {
     ws[((s * n_groups + grp) * nb + b) * 256 + e] = v;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Ragged groups ("Entry API and calibration flow", phase 2: hooks capture
+// token-major inputs per batch; MoE experts receive different, possibly
+// zero, numbers of tokens).  Group g owns rows offsets[g] .. offsets[g+1]-1
+// of x (clamped to [0, n_rows], so no offset can move a read outside the
+// buffer).  Without counts: H_g = S_g / n_g.  With counts (running mean over
+// batches): H_g = (n_old H_g + S_g) / (n_old + n_g).  A group whose token
+// total is still zero keeps its H (the caller's fallback).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void ragged_range(const int64_t* __restrict__ offsets, int64_t grp, int64_t n_rows,
+                                             int64_t& r0, int64_t& r1) {
+  int64_t a = offsets[grp], z = offsets[grp + 1];
+  a = a < 0 ? 0 : (a > n_rows ? n_rows : a);
+  z = z < a ? a : (z > n_rows ? n_rows : z);
+  r0 = a;
+  r1 = z;
+}
+
+__device__ __forceinline__ void ragged_store(float* hp, float v, int64_t n_g, const int64_t* __restrict__ counts,
+                                             int64_t grp) {
+  if (n_g == 0) return;  // no new tokens: H stays as it is
+  if (counts) {
+    const int64_t n_old = counts[grp];
+    *hp = ((float)n_old * (*hp) + v) / (float)(n_old + n_g);
+  } else {
+    *hp = v / (float)n_g;
+  }
+}
+
+template <typename T, bool kVec>
+__global__ __launch_bounds__(kThreads) void hessian_ragged_kernel(const T* __restrict__ x, int64_t ld,
+                                                                  int64_t n_rows,
+                                                                  const int64_t* __restrict__ offsets,
+                                                                  int64_t nb, int64_t n_groups, int64_t nsplit,
+                                                                  float* __restrict__ h, int64_t h_gstride,
+                                                                  const int64_t* __restrict__ counts,
+                                                                  float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) T tile[4][kSlab * 16];
+  __shared__ float red[4][256];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int64_t id = blockIdx.x;
+  const int64_t s = id % nsplit;
+  id /= nsplit;
+  const int64_t b = id % nb, grp = id / nb;
+  int64_t r0, r1;
+  ragged_range(offsets, grp, n_rows, r0, r1);
+  // slice s of the group's rows: equal whole rounds of 256 tokens
+  const int64_t per = ((r1 - r0 + nsplit - 1) / nsplit + kRound - 1) / kRound * kRound;
+  const int64_t t0 = min(r1, r0 + s * per);
+  const int64_t t1 = min(r1, t0 + per);
+  const f32x4_t acc = tm_accumulate<T, kVec>(x + 16 * b, ld, t0, t1, tile[wave], wave, lane);
+  const float v = reduce_waves(acc, red, wave, lane);
+  const int e = threadIdx.x;
+  if (nsplit == 1)
+    ragged_store(h + grp * h_gstride + b * 256 + e, v, r1 - r0, counts, grp);
+  else
+    ws[((s * n_groups + grp) * nb + b) * 256 + e] = v;
+}
+
+__global__ __launch_bounds__(kThreads) void hessian_ragged_finalize_kernel(
+    const float* __restrict__ ws, int64_t nsplit, int64_t n_groups, int64_t nb, int64_t n_rows,
+    const int64_t* __restrict__ offsets, const int64_t* __restrict__ counts, float* __restrict__ h,
+    int64_t h_gstride) {
+  const int64_t blk = blockIdx.x;  // grp * nb + b
+  const int64_t grp = blk / nb, b = blk % nb;
+  const int e = threadIdx.x;
+  const int64_t per_split = n_groups * nb * 256;
+  float v = ws[blk * 256 + e];
+  for (int64_t s = 1; s < nsplit; ++s) v += ws[s * per_split + blk * 256 + e];
+  int64_t r0, r1;
+  ragged_range(offsets, grp, n_rows, r0, r1);
+  ragged_store(h + grp * h_gstride + b * 256 + e, v, r1 - r0, counts, grp);
+}
+
+// counts[g] += n_g, after every block of the group has read the old count.
+__global__ __launch_bounds__(kThreads) void hessian_ragged_counts_kernel(const int64_t* __restrict__ offsets,
+                                                                         int64_t n_groups, int64_t n_rows,
+                                                                         int64_t* __restrict__ counts) {
+  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (g >= n_groups) return;
+  int64_t r0, r1;
+  ragged_range(offsets, g, n_rows, r0, r1);
+  counts[g] += r1 - r0;
 }
 
 // Sum of the token slices in slice order, then h = beta * h + alpha * sum.
@@ -279,7 +376,60 @@ hipError_t launch_typed(const HessianArgs& a, const HessianPlan& p, hipStream_t 
   return hipGetLastError();
 }
 
+template <typename T, bool kVec>
+hipError_t launch_ragged_typed(const HessianRaggedArgs& a, int64_t nsplit, hipStream_t stream) {
+  const int64_t nb = a.c_in / 16;
+  const int64_t grid = a.n_groups * nb * nsplit;
+  float* ws = nsplit > 1 ? static_cast<float*>(a.ws) : nullptr;
+  hessian_ragged_kernel<T, kVec><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+      static_cast<const T*>(a.x), a.ld, a.n_rows, a.offsets, nb, a.n_groups, nsplit, a.h, a.h_gstride, a.counts, ws);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (nsplit > 1) {
+    hessian_ragged_finalize_kernel<<<dim3((unsigned)(a.n_groups * nb)), dim3(kThreads), 0, stream>>>(
+        ws, nsplit, a.n_groups, nb, a.n_rows, a.offsets, a.counts, a.h, a.h_gstride);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (a.counts) {
+    hessian_ragged_counts_kernel<<<dim3((unsigned)((a.n_groups + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                                   stream>>>(a.offsets, a.n_groups, a.n_rows, a.counts);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
 }  // namespace
+
+// Ragged slices per group: planned from the average rows per group (the
+// per-group counts live on the device), ~1024 rows per slice, at most 16.
+int64_t hessian_ragged_nsplit(int64_t c_in, int64_t n_rows, int64_t n_groups, bool have_ws) {
+  if (!have_ws || n_groups <= 0 || c_in < 16) return 1;
+  const int64_t avg = n_rows / n_groups;
+  if (avg < 2048) return 1;
+  const int64_t ns = avg / 1024;
+  return ns > 16 ? 16 : ns;
+}
+
+size_t hessian_ragged_ws_bytes(int64_t c_in, int64_t n_rows, int64_t n_groups) {
+  const int64_t ns = hessian_ragged_nsplit(c_in, n_rows, n_groups, true);
+  if (ns <= 1) return 0;
+  return (size_t)ns * (size_t)n_groups * (size_t)(c_in / 16) * 256u * sizeof(float);
+}
+
+hipError_t launch_hessian_ragged(const HessianRaggedArgs& a, hipStream_t stream) {
+  const int64_t nb = a.c_in / 16;
+  if (a.n_groups == 0 || nb == 0) return hipSuccess;
+  const size_t need = hessian_ragged_ws_bytes(a.c_in, a.n_rows, a.n_groups);
+  const bool have_ws = a.ws != nullptr && need > 0 && a.ws_bytes >= need;
+  const int64_t nsplit = hessian_ragged_nsplit(a.c_in, a.n_rows, a.n_groups, have_ws);
+  const int64_t epv = a.dtype == 1 ? 8 : 4;
+  const bool aligned = (reinterpret_cast<uintptr_t>(a.x) % 16 == 0) && (a.ld % epv == 0);
+  if (a.dtype == 1)
+    return aligned ? launch_ragged_typed<uint16_t, true>(a, nsplit, stream)
+                   : launch_ragged_typed<uint16_t, false>(a, nsplit, stream);
+  return aligned ? launch_ragged_typed<float, true>(a, nsplit, stream) : launch_ragged_typed<float, false>(a, nsplit, stream);
+}
 
 // Token slices per block.  Measured on MI355X (17408 x 16384 bf16 X): the
 // pass streams best with ~1024-token slices (16 slices: 5.7 TB/s, vs 4.7 TB/s

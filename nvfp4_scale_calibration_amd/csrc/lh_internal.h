@@ -30,6 +30,22 @@ HessianPlan hessian_plan(int64_t c_in, int64_t n_tok, int64_t n_groups, bool hav
 size_t hessian_ws_bytes(int64_t c_in, int64_t n_tok, int64_t n_groups);
 hipError_t launch_hessian(const HessianArgs& a, hipStream_t stream);
 
+struct HessianRaggedArgs {
+  const void* x;          // token-major [n_rows][ld]
+  int dtype;              // 0 fp32, 1 bf16
+  int64_t c_in, ld, n_rows;
+  const int64_t* offsets; // device [n_groups + 1]
+  int64_t n_groups;
+  float* h;
+  int64_t h_gstride;
+  int64_t* counts;        // nullable device [n_groups]: running mean
+  void* ws;               // nullable
+  size_t ws_bytes;
+};
+int64_t hessian_ragged_nsplit(int64_t c_in, int64_t n_rows, int64_t n_groups, bool have_ws);
+size_t hessian_ragged_ws_bytes(int64_t c_in, int64_t n_rows, int64_t n_groups);
+hipError_t launch_hessian_ragged(const HessianRaggedArgs& a, hipStream_t stream);
+
 struct SweepArgs {
   const void* w;
   int dtype;

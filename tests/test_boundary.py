@@ -167,3 +167,31 @@ def test_select_validation(lib):
     # lh_scale_sweep still requires its Hessian
     assert lib.lh_scale_sweep(P(FAKE), 1, 4, 32, 32, 1, 0, None, 0, P(FAKE), P(FAKE), None, None, None, 0,
                               None) == NULL
+
+
+def test_ragged_hessian_validation(lib):
+    P = ctypes.c_void_p
+    ok = dict(x=P(FAKE), dt=1, c_in=32, ld=32, rows=100, off=P(FAKE), g=3, h=P(FAKE), hs=512, cnt=None,
+              ws=None, wsb=0, st=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.lh_accumulate_hessian_ragged(a["x"], a["dt"], a["c_in"], a["ld"], a["rows"], a["off"], a["g"],
+                                                a["h"], a["hs"], a["cnt"], a["ws"], a["wsb"], a["st"])
+
+    assert call(dt=3) == DTYPE
+    assert call(c_in=40) == SHAPE
+    assert call(ld=16) == SHAPE
+    assert call(rows=-1) == SHAPE
+    assert call(hs=100) == SHAPE                 # groups would overlap
+    assert call(off=None) == NULL
+    assert call(h=None) == NULL
+    assert call(x=None) == NULL
+    assert call(off=P(FAKE + 4)) == ARG          # int64 offsets need 8-byte alignment
+    assert call(cnt=P(FAKE + 4)) == ARG
+    assert call(ws=None, wsb=8) == NULL
+    big = lib.lh_hessian_ragged_workspace_bytes(4096, 1 << 16, 2)
+    assert big > 0 and big % (256 * 4) == 0
+    assert call(c_in=4096, ld=4096, rows=1 << 16, g=2, hs=256 * 256, ws=P(FAKE), wsb=big - 4) == WORKSPACE
+    assert lib.lh_hessian_ragged_workspace_bytes(2048, 32768, 64) == 0   # ~512 rows per group: one pass
+    assert call(g=0) == OK and call(c_in=0) == OK
