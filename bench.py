@@ -105,6 +105,28 @@ def timed(fn, stream, reps: int, before=None):
     return out
 
 
+def graph_time(fn, reps: int = 20) -> float:
+    """GPU time (ms) of one fn() launch: `reps` launches captured back to
+    back in one HIP graph and replayed between two events, so host-side
+    launch overhead does not leave the GPU idle between short kernels.
+    fn must not allocate (buffers are passed in)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def pct(v, q):
     import numpy as np
     return float(np.percentile(np.asarray(v), q))
@@ -145,6 +167,7 @@ def extras(lh, work, w, x, h, amax, idx, err, bam, ws, ws_bytes, stream) -> dict
     fn = (lambda: lh.lh_accumulate_hessian_ragged(xr, off, h=hr, counts=cnt, workspace=rws if rb else None))
     fn()
     warm = timed(fn, stream, 15)
+    launch_ms = graph_time(fn)
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device=w.device)
     rcold = timed(fn, stream, 15, before=lambda: scratch.fill_(1))
     del scratch
@@ -156,6 +179,7 @@ def extras(lh, work, w, x, h, amax, idx, err, bam, ws, ws_bytes, stream) -> dict
             "hessian_ragged": {"workload": cap.description, "x_bytes": cap.x_bytes,
                                "max_group_rows": int(counts.max()), "empty_groups": int((counts == 0).sum()),
                                "running_mean": True,
+                               "launch_ms": launch_ms, "launch_gbps": cap.x_bytes / (launch_ms / 1e3) / 1e9,
                                "warm_median_ms": pct(warm, 50), "warm_gbps": cap.x_bytes / (pct(warm, 50) / 1e3) / 1e9,
                                "cold_median_ms": pct(rcold, 50), "cold_p10_ms": pct(rcold, 10),
                                "cold_p90_ms": pct(rcold, 90),
@@ -281,6 +305,15 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_kernel_ms = {nm: sum(e[i].elapsed_time(e[i + 1]) for e in events) / args.steps for i, nm in enumerate(names)}
+    # per-launch GPU time of each call, free of host launch overhead
+    launch_ms = {
+        "absmax": graph_time(lambda: lh.lh_absmax(w, out=amax)),
+        "hessian": graph_time(lambda: lh.lh_accumulate_hessian(x, h=h, workspace=ws if ws_bytes else None)),
+        "sweep": graph_time(lambda: lh.lh_scale_sweep(w, h, amax, best_idx=idx, best_err=err, best_amax=bam,
+                                                      workspace=sws), reps=5),
+        "fake_quant": graph_time(lambda: lh.lh_fake_quant_nvfp4(w, idx, amax, w_q=wq, packed=packed,
+                                                                scale_e4m3=codes, global_scale=gscale)),
+    }
     ms_per_step = wall * 1e3 / args.steps
     sweep_s = per_kernel_ms["sweep"] / 1e3
     hess_s = per_kernel_ms["hessian"] / 1e3
@@ -305,9 +338,12 @@ def main():
         "roofline": {"bound": "alu", "achieved": achieved_tflops, "peak": FP32_VECTOR_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": traffic},
         "kernels_ms": per_kernel_ms,
+        "launch_ms": launch_ms,
         "sweep": {"blocks_per_s": blocks / sweep_s, "tflops": achieved_tflops,
                   "frac_nonpacked_fp32": achieved_tflops / FP32_NONPACKED_TFLOPS},
         "hessian": {"gbps": work.x_bytes / hess_s / 1e9, "frac_hbm": work.x_bytes / hess_s / 1e9 / HBM_PEAK_GBPS,
+                    "launch_gbps": work.x_bytes / (launch_ms["hessian"] / 1e3) / 1e9,
+                    "launch_frac_hbm": work.x_bytes / (launch_ms["hessian"] / 1e3) / 1e9 / HBM_PEAK_GBPS,
                     "x_bytes": work.x_bytes, "warm": True},
         "source_hash": src_hash,
     }

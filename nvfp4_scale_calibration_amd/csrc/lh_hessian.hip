@@ -150,102 +150,6 @@ __global__ __launch_bounds__(kThreads) void hessian_cm_kernel(const T* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Token-major accumulation: x[t * ld + 16b + c] for tokens [t0, t1).  Each
-// wave stages a 64-token x 16-channel tile in LDS (row = one token, 16
-// values, no padding) and lane (ch, kg) reads tokens kg, kg+4, ..., kg+60 of
-// column ch: for bf16 the 64 lanes touch 32 distinct words in 32 distinct
-// banks, for fp32 every bank serves exactly two lanes (the minimum for 64
-// four-byte reads).  The trip count is uniform over the workgroup (slabs
-// past the end load zeros), so the barriers are reached by every wave.
-// `base` points at channel 16b of token 0.
-// ---------------------------------------------------------------------------
-template <typename T, bool kVec>
-__device__ __forceinline__ f32x4_t tm_accumulate(const T* __restrict__ base, int64_t ld, int64_t t0, int64_t t1,
-                                                 T* my, int wave, int lane) {
-  constexpr int kElemsPer16B = 16 / sizeof(T);          // 8 bf16 or 4 fp32
-  constexpr int kLanesPerTok = 16 / kElemsPer16B;       // 2 or 4
-  constexpr int kToksPerLoad = 64 / kLanesPerTok;       // 32 or 16
-  constexpr int kLoads = kSlab / kToksPerLoad;          // 2 or 4
-  const int ch = lane & 15, kg = lane >> 4;
-  const int ltok = lane / kLanesPerTok;                 // token within a load
-  const int lcol = (lane % kLanesPerTok) * kElemsPer16B;  // first channel
-
-  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  const int64_t rounds = t1 > t0 ? (t1 - t0 + kRound - 1) / kRound : 0;
-  for (int64_t r = 0; r < rounds; ++r) {
-    const int64_t t = t0 + r * kRound + wave * kSlab;
-#pragma unroll
-    for (int q = 0; q < kLoads; ++q) {
-      const int trow = q * kToksPerLoad + ltok;
-      const int64_t tok = t + trow;
-      T* dst = my + trow * 16 + lcol;
-      if (kVec && tok < t1) {
-        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(base + tok * ld + lcol);
-      } else {
-#pragma unroll
-        for (int c = 0; c < kElemsPer16B; ++c) dst[c] = (tok < t1) ? base[tok * ld + lcol + c] : T(0);
-      }
-    }
-    __syncthreads();
-    Vals16<T> v;
-    if constexpr (sizeof(T) == 2) {
-      uint32_t w[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t lo = my[(kg + 4 * (2 * i)) * 16 + ch];
-        const uint32_t hi = my[(kg + 4 * (2 * i + 1)) * 16 + ch];
-        w[i] = lo | (hi << 16);
-      }
-      v.u[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      v.u[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v.f[i] = my[(kg + 4 * i) * 16 + ch];
-    }
-    __syncthreads();
-    acc = mfma_accumulate(v, acc);
-  }
-  return acc;
-}
-
-// Fixed-order sum of the four waves' 16x16 results; thread e gets entry e.
-__device__ __forceinline__ float reduce_waves(f32x4_t acc, float (&red)[4][256], int wave, int lane) {
-  const int ch = lane & 15, kg = lane >> 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) red[wave][(4 * kg + i) * 16 + ch] = acc[i];
-  __syncthreads();
-  const int e = threadIdx.x;
-  return ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
-}
-
-template <typename T, bool kVec>
-__global__ __launch_bounds__(kThreads) void hessian_tm_kernel(const T* __restrict__ x, int64_t n_tok,
-                                                              int64_t ld, int64_t gstride, int64_t nb,
-                                                              int64_t n_groups, int64_t nsplit,
-                                                              int64_t chunk, float alpha, float beta,
-                                                              float* __restrict__ h, int64_t h_gstride,
-                                                              float* __restrict__ ws) {
-  __shared__ __attribute__((aligned(16))) T tile[4][kSlab * 16];
-  __shared__ float red[4][256];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int64_t id = blockIdx.x;
-  const int64_t s = id % nsplit;
-  id /= nsplit;
-  const int64_t b = id % nb, grp = id / nb;
-  const int64_t t0 = s * chunk;
-  const int64_t t1 = min(n_tok, t0 + chunk);
-  const f32x4_t acc = tm_accumulate<T, kVec>(x + grp * gstride + 16 * b, ld, t0, t1, tile[wave], wave, lane);
-  const float v = reduce_waves(acc, red, wave, lane);
-  const int e = threadIdx.x;
-  if (nsplit == 1) {
-    float* hp = h + grp * h_gstride + b * 256 + e;
-    *hp = (beta == 0.0f) ? alpha * v : beta * (*hp) + alpha * v;
-  } else {
-    ws[((s * n_groups + grp) * nb + b) * 256 + e] = v;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Ragged groups ("Entry API and calibration flow", phase 2: hooks capture
 // token-major inputs per batch; MoE experts receive different, possibly
 // zero, numbers of tokens).  Group g owns rows offsets[g] .. offsets[g+1]-1
@@ -274,34 +178,175 @@ __device__ __forceinline__ void ragged_store(float* hp, float v, int64_t n_g, co
   }
 }
 
+// ---------------------------------------------------------------------------
+// Token-major kernel: x[t * ld + c].  A workgroup owns four consecutive
+// blocks (64 channels: one 128-byte bf16 row segment per token) and a slice
+// of tokens; wave w accumulates block 4q + w over the whole slice, so no
+// cross-wave reduction is needed.  Each round the 256 threads copy a
+// kTok-token x 64-channel tile into LDS (16-byte loads, rows padded to 80
+// elements) and every wave reads its 16-channel column in the MFMA operand
+// layout: lane (ch, kg) takes tokens kg, kg+4, ...  With the 80-element
+// pitch the four kg rows of one read fall on disjoint banks (bf16: 8 banks
+// apart; fp32: two lanes per bank, the minimum for 64 four-byte reads).
+// The tile is double-buffered and the next round's global loads are in
+// flight while the current round is multiplied: one barrier per round.
+// The trip count is uniform over the workgroup (rows past the slice load
+// zeros), so every wave reaches every barrier.
+// ---------------------------------------------------------------------------
+constexpr int kPitch = 80;  // LDS row pitch in elements (64 channels + 16 pad)
+
+template <typename T>
+struct TmShape {
+  static constexpr int kEP = 16 / sizeof(T);                // elements per 16-byte chunk
+  static constexpr int kCPR = 64 / kEP;                     // chunks per 64-channel row
+  static constexpr int kRowsPerPass = kThreads / kCPR;      // rows one pass of loads covers
+  static constexpr int kTok = sizeof(T) == 2 ? 128 : 64;    // tokens per round
+  static constexpr int kPasses = kTok / kRowsPerPass;       // 16-byte loads per thread per round
+  static constexpr int kVecs = kTok / 64;                   // Vals16 per lane per round
+};
+
 template <typename T, bool kVec>
-__global__ __launch_bounds__(kThreads) void hessian_ragged_kernel(const T* __restrict__ x, int64_t ld,
-                                                                  int64_t n_rows,
-                                                                  const int64_t* __restrict__ offsets,
-                                                                  int64_t nb, int64_t n_groups, int64_t nsplit,
-                                                                  float* __restrict__ h, int64_t h_gstride,
-                                                                  const int64_t* __restrict__ counts,
-                                                                  float* __restrict__ ws) {
-  __shared__ __attribute__((aligned(16))) T tile[4][kSlab * 16];
-  __shared__ float red[4][256];
+struct TmLoader {
+  using S = TmShape<T>;
+  uint4 r[S::kPasses];
+  // Rows [t, t + kTok) of the 64-channel segment at `seg` (row stride ld),
+  // rows at or past t1 and chunks at or past the last channel read as zero.
+  __device__ __forceinline__ void load(const T* __restrict__ seg, int64_t ld, int64_t t, int64_t t1, int crow,
+                                       int ccol, bool col_ok) {
+#pragma unroll
+    for (int p = 0; p < S::kPasses; ++p) {
+      const int64_t tok = t + p * S::kRowsPerPass + crow;
+      const bool ok = col_ok && tok < t1;
+      if (kVec) {
+        r[p] = ok ? *reinterpret_cast<const uint4*>(seg + tok * ld + ccol) : make_uint4(0u, 0u, 0u, 0u);
+      } else {
+        T v[S::kEP];
+#pragma unroll
+        for (int c = 0; c < S::kEP; ++c) v[c] = ok ? seg[tok * ld + ccol + c] : T(0);
+        r[p] = __builtin_bit_cast(uint4, v);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(T* buf, int crow, int ccol) const {
+#pragma unroll
+    for (int p = 0; p < S::kPasses; ++p)
+      *reinterpret_cast<uint4*>(buf + (p * S::kRowsPerPass + crow) * kPitch + ccol) = r[p];
+  }
+};
+
+// Channel column 16 w + ch of an LDS tile, tokens kg + 4 i, as MFMA operands.
+template <typename T>
+__device__ __forceinline__ f32x4_t tile_mfma(const T* buf, int wave, int lane, f32x4_t acc) {
+  const int ch = lane & 15, kg = lane >> 4;
+  const T* col = buf + 16 * wave + ch;
+#pragma unroll
+  for (int q = 0; q < TmShape<T>::kVecs; ++q) {
+    Vals16<T> v;
+    const int tb = 64 * q + kg;
+    if constexpr (sizeof(T) == 2) {
+      uint32_t w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = col[(tb + 4 * (2 * i)) * kPitch];
+        const uint32_t hi = col[(tb + 4 * (2 * i + 1)) * kPitch];
+        w[i] = lo | (hi << 16);
+      }
+      v.u[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      v.u[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v.f[i] = col[(tb + 4 * i) * kPitch];
+    }
+    acc = mfma_accumulate(v, acc);
+  }
+  return acc;
+}
+
+template <typename T, bool kVec, bool kRagged>
+__global__ __launch_bounds__(kThreads) void hessian_tm_kernel(const T* __restrict__ x, int64_t ld, int64_t gstride,
+                                                              int64_t n_tok, int64_t n_rows,
+                                                              const int64_t* __restrict__ offsets, int64_t c_in,
+                                                              int64_t nb, int64_t n_groups, int64_t nsplit,
+                                                              int64_t chunk, float alpha, float beta,
+                                                              float* __restrict__ h, int64_t h_gstride,
+                                                              const int64_t* __restrict__ counts,
+                                                              float* __restrict__ ws) {
+  using S = TmShape<T>;
+  __shared__ __attribute__((aligned(16))) T tile[2][S::kTok * kPitch];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t quads = (nb + 3) / 4;
   int64_t id = blockIdx.x;
   const int64_t s = id % nsplit;
   id /= nsplit;
-  const int64_t b = id % nb, grp = id / nb;
-  int64_t r0, r1;
-  ragged_range(offsets, grp, n_rows, r0, r1);
-  // slice s of the group's rows: equal whole rounds of 256 tokens
-  const int64_t per = ((r1 - r0 + nsplit - 1) / nsplit + kRound - 1) / kRound * kRound;
-  const int64_t t0 = min(r1, r0 + s * per);
-  const int64_t t1 = min(r1, t0 + per);
-  const f32x4_t acc = tm_accumulate<T, kVec>(x + 16 * b, ld, t0, t1, tile[wave], wave, lane);
-  const float v = reduce_waves(acc, red, wave, lane);
-  const int e = threadIdx.x;
-  if (nsplit == 1)
-    ragged_store(h + grp * h_gstride + b * 256 + e, v, r1 - r0, counts, grp);
-  else
-    ws[((s * n_groups + grp) * nb + b) * 256 + e] = v;
+  const int64_t q = id % quads, grp = id / quads;
+
+  int64_t t0, t1, r0 = 0, r1 = 0;
+  const T* seg;
+  if constexpr (kRagged) {
+    ragged_range(offsets, grp, n_rows, r0, r1);
+    // slice s of the group's rows: whole rounds
+    const int64_t per = ((r1 - r0 + nsplit - 1) / nsplit + S::kTok - 1) / S::kTok * S::kTok;
+    t0 = min(r1, r0 + s * per);
+    t1 = min(r1, t0 + per);
+    seg = x + 64 * q;
+  } else {
+    t0 = s * chunk;
+    t1 = min(n_tok, t0 + chunk);
+    seg = x + grp * gstride + 64 * q;
+  }
+  const int crow = threadIdx.x / S::kCPR;
+  const int ccol = (threadIdx.x % S::kCPR) * S::kEP;
+  const bool col_ok = 64 * q + ccol < c_in;  // chunks never straddle c_in (c_in % 16 == 0)
+
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int64_t rounds = t1 > t0 ? (t1 - t0 + S::kTok - 1) / S::kTok : 0;
+  TmLoader<T, kVec> ld_regs;
+  if (rounds > 0) {
+    ld_regs.load(seg, ld, t0, t1, crow, ccol, col_ok);
+    ld_regs.store(tile[0], crow, ccol);
+  }
+  __syncthreads();
+  for (int64_t r = 0; r < rounds; ++r) {
+    const int buf = (int)(r & 1);
+    const bool more = r + 1 < rounds;
+    if (more) ld_regs.load(seg, ld, t0 + (r + 1) * S::kTok, t1, crow, ccol, col_ok);
+    acc = tile_mfma<T>(tile[buf], wave, lane, acc);
+    if (more) ld_regs.store(tile[buf ^ 1], crow, ccol);
+    __syncthreads();
+  }
+
+  const int64_t b = 4 * q + wave;
+  if (b >= nb) return;
+  const int ch = lane & 15, kg = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = (4 * kg + i) * 16 + ch;
+    const float v = acc[i];
+    if (nsplit > 1) {
+      ws[((s * n_groups + grp) * nb + b) * 256 + e] = v;
+    } else if constexpr (kRagged) {
+      ragged_store(h + grp * h_gstride + b * 256 + e, v, r1 - r0, counts, grp);
+    } else {
+      float* hp = h + grp * h_gstride + b * 256 + e;
+      *hp = (beta == 0.0f) ? alpha * v : beta * (*hp) + alpha * v;
+    }
+  }
+}
+
+// p[0] + p[stride] + ... + p[(n-1) stride], added in slice order; eight
+// loads are issued ahead of their adds.
+__device__ __forceinline__ float sum_slices(const float* __restrict__ p, int64_t stride, int64_t n) {
+  float v = p[0];
+  int64_t s = 1;
+  for (; s + 8 <= n; s += 8) {
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = p[(s + i) * stride];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v += t[i];
+  }
+  for (; s < n; ++s) v += p[s * stride];
+  return v;
 }
 
 __global__ __launch_bounds__(kThreads) void hessian_ragged_finalize_kernel(
@@ -311,9 +356,7 @@ __global__ __launch_bounds__(kThreads) void hessian_ragged_finalize_kernel(
   const int64_t blk = blockIdx.x;  // grp * nb + b
   const int64_t grp = blk / nb, b = blk % nb;
   const int e = threadIdx.x;
-  const int64_t per_split = n_groups * nb * 256;
-  float v = ws[blk * 256 + e];
-  for (int64_t s = 1; s < nsplit; ++s) v += ws[s * per_split + blk * 256 + e];
+  const float v = sum_slices(ws + blk * 256 + e, n_groups * nb * 256, nsplit);
   int64_t r0, r1;
   ragged_range(offsets, grp, n_rows, r0, r1);
   ragged_store(h + grp * h_gstride + b * 256 + e, v, r1 - r0, counts, grp);
@@ -339,9 +382,7 @@ __global__ __launch_bounds__(kThreads) void hessian_finalize_kernel(const float*
   const int64_t blk = blockIdx.x;  // grp * nb + b
   const int64_t grp = blk / nb, b = blk % nb;
   const int e = threadIdx.x;
-  const int64_t per_split = n_groups * nb * 256;
-  float v = ws[blk * 256 + e];
-  for (int64_t s = 1; s < nsplit; ++s) v += ws[s * per_split + blk * 256 + e];
+  const float v = sum_slices(ws + blk * 256 + e, n_groups * nb * 256, nsplit);
   float* hp = h + grp * h_gstride + b * 256 + e;
   *hp = (beta == 0.0f) ? alpha * v : beta * (*hp) + alpha * v;
 }
@@ -358,17 +399,19 @@ __global__ __launch_bounds__(kThreads) void hessian_scale_kernel(float beta, flo
 template <typename T, bool kVec>
 hipError_t launch_typed(const HessianArgs& a, const HessianPlan& p, hipStream_t stream) {
   const int64_t nb = a.c_in / 16;
-  const int64_t grid = a.n_groups * nb * p.nsplit;
   float* ws = p.nsplit > 1 ? static_cast<float*>(a.ws) : nullptr;
   const T* x = static_cast<const T*>(a.x);
-  if (a.layout == 0)
+  if (a.layout == 0) {
+    const int64_t grid = a.n_groups * nb * p.nsplit;
     hessian_cm_kernel<T, kVec><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
         x, a.n_tok, a.ld, a.gstride, nb, a.n_groups, p.nsplit, p.chunk, a.alpha, a.beta, a.h,
         a.h_gstride, ws);
-  else
-    hessian_tm_kernel<T, kVec><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
-        x, a.n_tok, a.ld, a.gstride, nb, a.n_groups, p.nsplit, p.chunk, a.alpha, a.beta, a.h,
-        a.h_gstride, ws);
+  } else {
+    const int64_t grid = a.n_groups * ((nb + 3) / 4) * p.nsplit;
+    hessian_tm_kernel<T, kVec, false><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+        x, a.ld, a.gstride, a.n_tok, 0, nullptr, a.c_in, nb, a.n_groups, p.nsplit, p.chunk, a.alpha, a.beta,
+        a.h, a.h_gstride, nullptr, ws);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.nsplit == 1) return err;
   hessian_finalize_kernel<<<dim3((unsigned)(a.n_groups * nb)), dim3(kThreads), 0, stream>>>(
@@ -379,10 +422,11 @@ hipError_t launch_typed(const HessianArgs& a, const HessianPlan& p, hipStream_t 
 template <typename T, bool kVec>
 hipError_t launch_ragged_typed(const HessianRaggedArgs& a, int64_t nsplit, hipStream_t stream) {
   const int64_t nb = a.c_in / 16;
-  const int64_t grid = a.n_groups * nb * nsplit;
+  const int64_t grid = a.n_groups * ((nb + 3) / 4) * nsplit;
   float* ws = nsplit > 1 ? static_cast<float*>(a.ws) : nullptr;
-  hessian_ragged_kernel<T, kVec><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
-      static_cast<const T*>(a.x), a.ld, a.n_rows, a.offsets, nb, a.n_groups, nsplit, a.h, a.h_gstride, a.counts, ws);
+  hessian_tm_kernel<T, kVec, true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+      static_cast<const T*>(a.x), a.ld, 0, 0, a.n_rows, a.offsets, a.c_in, nb, a.n_groups, nsplit, 0, 1.0f, 0.0f,
+      a.h, a.h_gstride, a.counts, ws);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (nsplit > 1) {
@@ -399,16 +443,25 @@ hipError_t launch_ragged_typed(const HessianRaggedArgs& a, int64_t nsplit, hipSt
   return err;
 }
 
+// Token-major slices: enough workgroups of four blocks to keep ~16 per CU
+// busy (4096), slices of at least 512 tokens, at most 64 slices.
+int64_t tm_nsplit(int64_t c_in, int64_t tokens_per_group, int64_t n_groups) {
+  const int64_t wgs = n_groups * ((c_in / 16 + 3) / 4);
+  if (wgs <= 0) return 1;
+  int64_t ns = (4096 + wgs - 1) / wgs;
+  int64_t cap = tokens_per_group / 512;
+  if (cap > 64) cap = 64;
+  if (ns > cap) ns = cap;
+  return ns < 1 ? 1 : ns;
+}
+
 }  // namespace
 
-// Ragged slices per group: planned from the average rows per group (the
-// per-group counts live on the device), ~1024 rows per slice, at most 16.
+// Ragged slices per group, planned from the average rows per group (the
+// per-group counts live on the device).
 int64_t hessian_ragged_nsplit(int64_t c_in, int64_t n_rows, int64_t n_groups, bool have_ws) {
   if (!have_ws || n_groups <= 0 || c_in < 16) return 1;
-  const int64_t avg = n_rows / n_groups;
-  if (avg < 2048) return 1;
-  const int64_t ns = avg / 1024;
-  return ns > 16 ? 16 : ns;
+  return tm_nsplit(c_in, n_rows / n_groups, n_groups);
 }
 
 size_t hessian_ragged_ws_bytes(int64_t c_in, int64_t n_rows, int64_t n_groups) {
@@ -431,16 +484,25 @@ hipError_t launch_hessian_ragged(const HessianRaggedArgs& a, hipStream_t stream)
   return aligned ? launch_ragged_typed<float, true>(a, nsplit, stream) : launch_ragged_typed<float, false>(a, nsplit, stream);
 }
 
-// Token slices per block.  Measured on MI355X (17408 x 16384 bf16 X): the
-// pass streams best with ~1024-token slices (16 slices: 5.7 TB/s, vs 4.7 TB/s
-// for 2 slices, whose 2176 workgroups leave a nearly empty second wave of
-// workgroups), so slices are ~1024 tokens, at most 16 of them.
-HessianPlan hessian_plan(int64_t c_in, int64_t n_tok, int64_t n_groups, bool have_ws) {
+// Token slices per block.  Channel-major, measured on MI355X (17408 x 16384
+// bf16 X): the pass streams best with ~1024-token slices (16 slices:
+// 5.7 TB/s, vs 4.7 TB/s for 2 slices, whose 2176 workgroups leave a nearly
+// empty second wave of workgroups), so slices are ~1024 tokens, at most 16
+// of them.  Token-major workgroups cover four blocks: see tm_nsplit.
+// Chunks are whole multiples of 256 tokens (both kernels' rounds divide it).
+HessianPlan hessian_plan(int64_t c_in, int64_t n_tok, int64_t n_groups, int layout, bool have_ws) {
   HessianPlan p{1, ((n_tok + kRound - 1) / kRound) * kRound};
   const int64_t blocks = n_groups * (c_in / 16);
-  if (!have_ws || blocks <= 0 || n_tok < 2048) return p;
-  int64_t ns = n_tok / 1024;
-  if (ns > 16) ns = 16;
+  if (!have_ws || blocks <= 0) return p;
+  int64_t ns;
+  if (layout == 0) {
+    if (n_tok < 2048) return p;
+    ns = n_tok / 1024;
+    if (ns > 16) ns = 16;
+  } else {
+    ns = tm_nsplit(c_in, n_tok, n_groups);
+  }
+  if (ns <= 1) return p;
   int64_t chunk = (n_tok + ns - 1) / ns;
   chunk = ((chunk + kRound - 1) / kRound) * kRound;
   p.chunk = chunk;
@@ -449,10 +511,15 @@ HessianPlan hessian_plan(int64_t c_in, int64_t n_tok, int64_t n_groups, bool hav
   return p;
 }
 
+// Enough for either layout's plan.
 size_t hessian_ws_bytes(int64_t c_in, int64_t n_tok, int64_t n_groups) {
-  const HessianPlan p = hessian_plan(c_in, n_tok, n_groups, true);
-  if (p.nsplit <= 1) return 0;
-  return (size_t)p.nsplit * (size_t)n_groups * (size_t)(c_in / 16) * 256u * sizeof(float);
+  int64_t ns = 1;
+  for (int layout = 0; layout < 2; ++layout) {
+    const HessianPlan p = hessian_plan(c_in, n_tok, n_groups, layout, true);
+    if (p.nsplit > ns) ns = p.nsplit;
+  }
+  if (ns <= 1) return 0;
+  return (size_t)ns * (size_t)n_groups * (size_t)(c_in / 16) * 256u * sizeof(float);
 }
 
 hipError_t launch_hessian(const HessianArgs& a, hipStream_t stream) {
@@ -466,7 +533,7 @@ hipError_t launch_hessian(const HessianArgs& a, hipStream_t stream) {
   }
   const size_t need = hessian_ws_bytes(a.c_in, a.n_tok, a.n_groups);
   const bool have_ws = a.ws != nullptr && need > 0 && a.ws_bytes >= need;
-  const HessianPlan p = hessian_plan(a.c_in, a.n_tok, a.n_groups, have_ws);
+  const HessianPlan p = hessian_plan(a.c_in, a.n_tok, a.n_groups, a.layout, have_ws);
   const size_t esz = a.dtype == 1 ? 2 : 4;
   const int64_t epv = 16 / (int64_t)esz;  // elements per 16-byte vector
   const bool aligned = (reinterpret_cast<uintptr_t>(a.x) % 16 == 0) && (a.ld % epv == 0) &&

@@ -26,7 +26,7 @@ struct HessianPlan {
   int64_t nsplit;
   int64_t chunk;
 };
-HessianPlan hessian_plan(int64_t c_in, int64_t n_tok, int64_t n_groups, bool have_ws);
+HessianPlan hessian_plan(int64_t c_in, int64_t n_tok, int64_t n_groups, int layout, bool have_ws);
 size_t hessian_ws_bytes(int64_t c_in, int64_t n_tok, int64_t n_groups);
 hipError_t launch_hessian(const HessianArgs& a, hipStream_t stream);
 
