@@ -72,6 +72,9 @@ def _load():
     lib.oracle_rule_candidates.restype = I32
     lib.oracle_select.argtypes = [I32, P, I32, I64, I64, I64, I64, P, I64, P, P, I64, P, P, P, P, P]
     lib.oracle_hessian_ragged.argtypes = [P, I32, I64, I64, P, I64, P, P, I64, P, P, P]
+    lib.oracle_full_hessian.argtypes = [P, I32, I64, I64, I64, D, P]
+    lib.oracle_output_error.argtypes = [P, I32, P, I64, I64, I64, P, P, I64, P]
+    lib.oracle_scaled_histogram.argtypes = [P, I32, I64, I64, I64, P, F, I32, F, P]
     lib.oracle_num_threads.restype = I32
     lib.oracle_set_num_threads.argtypes = [I32]
     _lib = lib
@@ -276,3 +279,44 @@ def hessian_ragged(x: np.ndarray, c_in: int, offsets, h_old: np.ndarray, counts=
                                   _ptr(h64), _ptr(h32))
     new_counts = None if cnt is None else cnt + np.diff(offsets)
     return h64, h32, new_counts
+
+
+def full_hessian(x: np.ndarray, c_in: int, n_tok: int, ld_x: int | None = None, alpha: float | None = None):
+    """Full C_in x C_in Hessian alpha X X^T (fp64) of one channel-major group
+    (alpha defaults to 1/N)."""
+    x = np.ascontiguousarray(x)
+    ld_x = n_tok if ld_x is None else ld_x
+    alpha = (1.0 / n_tok if n_tok else 0.0) if alpha is None else alpha
+    h = np.zeros((c_in, c_in), np.float64)
+    _load().oracle_full_hessian(_ptr(x), _dtype_code(x), c_in, n_tok, ld_x, float(alpha), _ptr(h))
+    return h
+
+
+def output_error(w: np.ndarray, q: np.ndarray, h: np.ndarray, c_in: int, rows: np.ndarray | None = None,
+                 ld_w: int | None = None, ld_q: int | None = None) -> np.ndarray:
+    """(q - w) H (q - w)^T per selected row of one group (fp64), with the
+    fp32 full Hessian h [c_in][c_in]."""
+    w = np.ascontiguousarray(w)
+    q = np.ascontiguousarray(q, np.float32)
+    h = np.ascontiguousarray(h, np.float32)
+    n = w.shape[0] if w.ndim == 2 else w.size // (ld_w or c_in)
+    rows = np.arange(n, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
+    ld_w = c_in if ld_w is None else ld_w
+    ld_q = c_in if ld_q is None else ld_q
+    e = np.zeros(len(rows), np.float64)
+    _load().oracle_output_error(_ptr(w), _dtype_code(w), _ptr(q), c_in, ld_w, ld_q, _ptr(h), _ptr(rows),
+                                len(rows), _ptr(e))
+    return e
+
+
+def scaled_histogram(w: np.ndarray, idx: np.ndarray, g: float, c_out: int, c_in: int, n_bins: int,
+                     bins_per_unit: float, ld_w: int | None = None) -> np.ndarray:
+    """Counts [n_bins + 1] of x = fl32(|w| / s_k) over one group (bin
+    floor(fl32(x * bins_per_unit)), last bin = overflow)."""
+    w = np.ascontiguousarray(w)
+    idx = np.ascontiguousarray(idx, np.uint8)
+    ld_w = c_in if ld_w is None else ld_w
+    counts = np.zeros(n_bins + 1, np.uint64)
+    _load().oracle_scaled_histogram(_ptr(w), _dtype_code(w), c_out, c_in, ld_w, _ptr(idx), float(g), int(n_bins),
+                                    float(bins_per_unit), _ptr(counts))
+    return counts

@@ -542,3 +542,79 @@ void oracle_hessian_ragged(const void *x, int dtype, int64_t c_in, int64_t ld_x,
             }
     }
 }
+
+/* ====================================================================== */
+/* Approximation diagnostics ([LHG] "Algorithm principle": the layer's    */
+/* output error is E = ||Delta X||_F^2 = tr(Delta X X^T Delta^T); Local-  */
+/* Hessian keeps only the 16x16 diagonal blocks of X X^T.  "How scaling   */
+/* reshapes the weight distribution": the histogram of W/s, the values    */
+/* fed to the E2M1 rounding, per scale rule).                             */
+/* Readings:                                                               */
+/*   R15 full Hessian H = alpha X X^T (C_in x C_in), alpha = 1/N, so that  */
+/*       (q - w) H (q - w)^T summed over rows is ||Delta X||_F^2 / N, the  */
+/*       normalisation of the local Hessians.                              */
+/*   R16 histogram value x = fl32(|w| / s_k) with the block's chosen k (the */
+/*       cast's own quotient); bin = floor(fl32(x * bins_per_unit)), values */
+/*       at or past n_bins go to one overflow bin n_bins; s = 0 gives x = 0.*/
+/* ====================================================================== */
+
+/* Full Hessian of one group, channel-major x[c * ld_x + t], fp64:
+ * h[i * c_in + j] = alpha * sum_t x[i][t] x[j][t]. */
+void oracle_full_hessian(const void *x, int dtype, int64_t c_in, int64_t n_tok, int64_t ld_x,
+                         double alpha, double *h)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < c_in; ++i)
+        for (int64_t j = 0; j < c_in; ++j) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < n_tok; ++t)
+                acc += widen(x, dtype, i * ld_x + t) * widen(x, dtype, j * ld_x + t);
+            h[i * c_in + j] = alpha * acc;
+        }
+}
+
+/* Output error of the selected rows of one group: e[n] = d H d^T with
+ * d = q_row - w_row (fp64 from the fp32 q and the widened w) and the fp32
+ * full Hessian h [c_in][c_in]. */
+void oracle_output_error(const void *w, int dtype, const float *q, int64_t c_in, int64_t ld_w,
+                         int64_t ld_q, const float *h, const int64_t *rows, int64_t n_rows,
+                         double *e)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t n = 0; n < n_rows; ++n) {
+        const int64_t r = rows[n];
+        double acc = 0.0;
+        for (int64_t i = 0; i < c_in; ++i) {
+            const double di = (double)q[r * ld_q + i] - widen(w, dtype, r * ld_w + i);
+            if (di == 0.0)
+                continue;
+            double row = 0.0;
+            for (int64_t j = 0; j < c_in; ++j) {
+                const double dj = (double)q[r * ld_q + j] - widen(w, dtype, r * ld_w + j);
+                row += (double)h[i * c_in + j] * dj;
+            }
+            acc += di * row;
+        }
+        e[n] = acc;
+    }
+}
+
+/* Histogram of x = fl32(|w| / s_k) over one group's weights with the given
+ * per-block candidate indices; counts [n_bins + 1] are added to. */
+void oracle_scaled_histogram(const void *w, int dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
+                             const uint8_t *idx, float g, int32_t n_bins, float bins_per_unit,
+                             uint64_t *counts)
+{
+    float s[126];
+    oracle_candidate_scales(g, s);
+    const int64_t nb = c_in / 16;
+    for (int64_t r = 0; r < c_out; ++r)
+        for (int64_t c = 0; c < c_in; ++c) {
+            const float sk = s[idx[r * nb + c / 16]];
+            const float a = fabsf(widen_f32(w, dtype, r * ld_w + c));
+            const float x = (sk == 0.0f) ? 0.0f : a / sk;
+            const float y = x * bins_per_unit;
+            int64_t bin = (y >= (float)n_bins) ? n_bins : (int64_t)floorf(y);
+            counts[bin] += 1;
+        }
+}
