@@ -294,6 +294,65 @@ lh_status lh_fake_quant_nvfp4(const void *w, int w_dtype, int64_t c_out, int64_t
                               uint8_t *packed_e2m1, uint8_t *scale_e4m3, float *global_scale,
                               void *stream);
 
+/*
+ * ---------------------------------------------------------------------------
+ * Approximation diagnostics ("Algorithm principle": the layer's output error
+ * is ||Delta X||_F^2 = tr(Delta X X^T Delta^T), and Local-Hessian keeps only
+ * the 16 x 16 diagonal blocks of X X^T; "How scaling reshapes the weight
+ * distribution": the histogram of W/s, the values fed to the E2M1 rounding).
+ * ---------------------------------------------------------------------------
+ */
+
+/*
+ * Full Hessian h_full[g] = alpha * X_g X_g^T (C_in x C_in, fp32 accumulation
+ * on matrix cores), X channel-major x[g][c * ld_x + t] (fp32 or bf16),
+ * h_full[g][i * ld_h + j], ld_h >= c_in, group strides >= 0 (h groups must not
+ * overlap).  With alpha = 1/N its diagonal 16 x 16 blocks are the local
+ * Hessians.  n_tokens = 0 writes zeros.
+ * Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_ARG, LH_ERR_HIP.
+ */
+lh_status lh_full_hessian(const void *x, int x_dtype, int64_t c_in, int64_t n_tokens, int64_t ld_x,
+                          int64_t n_groups, int64_t group_stride_x, float alpha, float *h_full,
+                          int64_t ld_h, int64_t group_stride_h, void *stream);
+
+/* Scratch bytes lh_output_error needs (one fp32 per row and 64-column tile). */
+size_t lh_output_error_workspace_bytes(int64_t c_out, int64_t c_in, int64_t n_groups);
+
+/*
+ * Layer output error per output row with quantised weights w_q:
+ *   err[g][r] = d H d^T,  d = w_q[g][r] - w[g][r] (fp32),  H = h_full[g]
+ * (fp32 matrix cores; the row dot and the sum over column tiles run in a
+ * fixed order, so results are deterministic).  With h_full = X X^T / N the
+ * sum over rows is ||(W_q - W) X||_F^2 / N, to compare with the sum of the
+ * sweep's block errors (the block-diagonal part).  H is used as given and
+ * must be symmetric (h_full[j][i] stands in for h_full[i][j]).
+ *   w (w_dtype, ld_w), w_q fp32 (ld_q), both [n_groups][c_out][.] with group
+ *   strides; h_full [n_groups][c_in][ld_h]; err fp32 [n_groups][c_out].
+ *   workspace: at least lh_output_error_workspace_bytes(c_out, c_in,
+ *   n_groups) bytes, 4-byte aligned, required when there is work.
+ * Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_WORKSPACE,
+ * LH_ERR_ARG, LH_ERR_HIP.
+ */
+lh_status lh_output_error(const void *w, int w_dtype, const float *w_q, int64_t c_out, int64_t c_in,
+                          int64_t ld_w, int64_t ld_q, int64_t n_groups, int64_t group_stride_w,
+                          int64_t group_stride_q, const float *h_full, int64_t ld_h,
+                          int64_t group_stride_h, float *err, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
+ * Histogram of W/s: for every weight, x = fl32(|w| / s_k) with its block's
+ * candidate k = best_idx (the quotient the cast rounds) and s_k from
+ * amax[g]; bin = floor(fl32(x * bins_per_unit)), values at or beyond n_bins
+ * go to the overflow bin n_bins; s = 0 gives x = 0.  counts (uint64
+ * [n_groups][n_bins + 1], 8-byte aligned) is overwritten.  n_bins in
+ * [1, 4096], bins_per_unit positive and finite.
+ * Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_ARG, LH_ERR_HIP.
+ */
+lh_status lh_scaled_histogram(const void *w, int w_dtype, int64_t c_out, int64_t c_in,
+                              int64_t ld_w, int64_t n_groups, int64_t group_stride_w,
+                              const uint8_t *best_idx, const float *amax, int n_bins,
+                              float bins_per_unit, uint64_t *counts, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

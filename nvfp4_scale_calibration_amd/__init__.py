@@ -62,6 +62,14 @@ def _load() -> ctypes.CDLL:
     lib.lh_scale_sweep.restype = I
     lib.lh_select_scales.argtypes = [I, P, I, I64, I64, I64, I64, I64, P, I64, P, P, P, P, P, SZ, P]
     lib.lh_select_scales.restype = I
+    lib.lh_full_hessian.argtypes = [P, I, I64, I64, I64, I64, I64, F, P, I64, I64, P]
+    lib.lh_full_hessian.restype = I
+    lib.lh_output_error_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.lh_output_error_workspace_bytes.restype = SZ
+    lib.lh_output_error.argtypes = [P, I, P, I64, I64, I64, I64, I64, I64, I64, P, I64, I64, P, P, SZ, P]
+    lib.lh_output_error.restype = I
+    lib.lh_scaled_histogram.argtypes = [P, I, I64, I64, I64, I64, I64, P, P, I, F, P, P]
+    lib.lh_scaled_histogram.restype = I
     lib.lh_fake_quant_nvfp4.argtypes = [P, I, I64, I64, I64, I64, I64, P, P, P, P, P, P, P]
     lib.lh_fake_quant_nvfp4.restype = I
     return lib
@@ -71,7 +79,8 @@ lib = _load()
 EXPORTS = ("lh_abi_version", "lh_status_string", "lh_last_error_message", "lh_absmax",
            "lh_hessian_workspace_bytes", "lh_accumulate_hessian", "lh_hessian_ragged_workspace_bytes",
            "lh_accumulate_hessian_ragged", "lh_sweep_workspace_bytes", "lh_scale_sweep",
-           "lh_select_scales", "lh_fake_quant_nvfp4")
+           "lh_select_scales", "lh_fake_quant_nvfp4", "lh_full_hessian", "lh_output_error_workspace_bytes",
+           "lh_output_error", "lh_scaled_histogram")
 
 
 def _check(status: int) -> None:
@@ -307,3 +316,60 @@ def lh_fake_quant_nvfp4(w: torch.Tensor, best_idx: torch.Tensor, amax: torch.Ten
                                    _ptr(best_idx), _ptr(amax), _ptr(res["w_q"]), _ptr(res["packed"]),
                                    _ptr(res["scale_e4m3"]), _ptr(res["global_scale"]), _stream(w)))
     return {k: v for k, v in res.items() if v is not None}
+
+
+def lh_full_hessian(x: torch.Tensor, alpha: float | None = None, h: torch.Tensor | None = None) -> torch.Tensor:
+    """Full C_in x C_in Hessian alpha X X^T of channel-major x [.., c_in, N]
+    (alpha defaults to 1/N)."""
+    _require_device(x, h)
+    x3 = _as3(x)
+    g, c_in, n = x3.shape
+    if n > 0 and x3.stride(-1) != 1:
+        raise ValueError("last dim of x must be contiguous")
+    if alpha is None:
+        alpha = 1.0 / n if n > 0 else 0.0
+    if h is None:
+        h = torch.empty((g, c_in, c_in), dtype=torch.float32, device=x.device)
+    h3 = _as3(h)
+    ld = _ld(x3) if n > 0 else 1  # no token: nothing is read
+    _check(lib.lh_full_hessian(_ptr(x3), _dtype(x3), c_in, n, ld, g, _group_stride(x3), float(alpha),
+                               _ptr(h3), _ld(h3), _group_stride(h3), _stream(x)))
+    return h
+
+
+def lh_output_error_workspace_bytes(c_out: int, c_in: int, n_groups: int = 1) -> int:
+    return int(lib.lh_output_error_workspace_bytes(c_out, c_in, n_groups))
+
+
+def lh_output_error(w: torch.Tensor, w_q: torch.Tensor, h_full: torch.Tensor, err: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Per-row d H d^T with d = w_q - w ([n_groups, c_out])."""
+    _require_device(w, w_q, h_full, err, workspace)
+    w3, q3, h3 = _as3(w), _as3(w_q), _as3(h_full)
+    if q3.dtype != torch.float32 or h3.dtype != torch.float32:
+        raise TypeError("w_q and h_full must be float32")
+    g, c_out, c_in = w3.shape
+    if err is None:
+        err = torch.empty((g, c_out), dtype=torch.float32, device=w.device)
+    if workspace is None:
+        workspace = torch.empty(max(lh_output_error_workspace_bytes(c_out, c_in, g), 4), dtype=torch.uint8,
+                                device=w.device)
+    _check(lib.lh_output_error(_ptr(w3), _dtype(w3), _ptr(q3), c_out, c_in, _ld(w3), _ld(q3), g,
+                               _group_stride(w3), _group_stride(q3), _ptr(h3), _ld(h3), _group_stride(h3),
+                               _ptr(err), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(w)))
+    return err
+
+
+def lh_scaled_histogram(w: torch.Tensor, best_idx: torch.Tensor, amax: torch.Tensor, n_bins: int = 160,
+                        bins_per_unit: float = 20.0, counts: torch.Tensor | None = None) -> torch.Tensor:
+    """Counts [n_groups, n_bins + 1] (int64 storage of uint64 counts) of
+    W/s = fl32(|w| / s_k), bins of width 1/bins_per_unit, last = overflow."""
+    _require_device(w, best_idx, amax, counts)
+    w3 = _as3(w)
+    g, c_out, c_in = w3.shape
+    if counts is None:
+        counts = torch.empty((g, n_bins + 1), dtype=torch.int64, device=w.device)
+    _check(lib.lh_scaled_histogram(_ptr(w3), _dtype(w3), c_out, c_in, _ld(w3), g, _group_stride(w3),
+                                   _ptr(best_idx), _ptr(amax), int(n_bins), float(bins_per_unit), _ptr(counts),
+                                   _stream(w)))
+    return counts

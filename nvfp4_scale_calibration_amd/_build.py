@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblh.so")
-SOURCES = ["lh_api.hip", "lh_hessian.hip", "lh_sweep.hip", "lh_quant.hip"]
+SOURCES = ["lh_api.hip", "lh_hessian.hip", "lh_sweep.hip", "lh_quant.hip", "lh_dense.hip"]
 HEADERS = ["lh_device.h", "lh_internal.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

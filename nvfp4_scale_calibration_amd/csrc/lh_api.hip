@@ -7,6 +7,7 @@
 
 #include "lh.h"
 #include "lh_internal.h"
+#include <math.h>
 
 namespace {
 
@@ -229,6 +230,90 @@ lh_status lh_fake_quant_nvfp4(const void* w, int w_dtype, int64_t c_out, int64_t
   lh::FakeQuantArgs a{w, w_dtype, c_out, c_in, ld_w, n_groups, group_stride_w, best_idx, amax,
                       w_q, packed_e2m1, scale_e4m3, global_scale};
   hipError_t e = lh::launch_fake_quant(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LH_OK : hip_fail(e, fn);
+}
+
+size_t lh_output_error_workspace_bytes(int64_t c_out, int64_t c_in, int64_t n_groups) {
+  if (c_out <= 0 || c_in <= 0 || n_groups <= 0 || c_in % 16 != 0) return 0;
+  return lh::output_error_ws_bytes(c_out, c_in, n_groups);
+}
+
+lh_status lh_full_hessian(const void* x, int x_dtype, int64_t c_in, int64_t n_tokens, int64_t ld_x, int64_t n_groups,
+                          int64_t group_stride_x, float alpha, float* h_full, int64_t ld_h, int64_t group_stride_h,
+                          void* stream) {
+  const char* fn = "lh_full_hessian";
+  g_msg[0] = '\0';
+  if (!valid_dtype(x_dtype)) return fail(LH_ERR_DTYPE, "%s: x_dtype must be 0 (f32) or 1 (bf16)", fn);
+  if (c_in < 0 || n_tokens < 0 || n_groups < 0 || group_stride_x < 0 || group_stride_h < 0)
+    return fail(LH_ERR_SHAPE, "%s: negative size or stride", fn);
+  if (c_in % 16 != 0) return fail(LH_ERR_SHAPE, "%s: c_in must be a multiple of 16", fn);
+  if (ld_x < n_tokens || ld_x < 1) return fail(LH_ERR_SHAPE, "%s: ld_x < n_tokens", fn);
+  if (ld_h < c_in || ld_h < 1) return fail(LH_ERR_SHAPE, "%s: ld_h < c_in", fn);
+  if (n_groups > 1 && group_stride_h < c_in * ld_h)
+    return fail(LH_ERR_SHAPE, "%s: group_stride_h < c_in * ld_h would overlap outputs", fn);
+  const bool work = n_groups > 0 && c_in > 0;
+  if (work && h_full == nullptr) return fail(LH_ERR_NULL, "%s: h_full is NULL", fn);
+  if (work && n_tokens > 0 && x == nullptr) return fail(LH_ERR_NULL, "%s: x is NULL", fn);
+  if (!aligned(x, elem_size(x_dtype)) || !aligned(h_full, 4))
+    return fail(LH_ERR_ARG, "%s: pointer not aligned to its element size", fn);
+  if (!work) return LH_OK;
+  lh::FullHessianArgs a{x, x_dtype, c_in, n_tokens, ld_x, group_stride_x, n_groups, alpha, h_full, ld_h,
+                        group_stride_h};
+  hipError_t e = lh::launch_full_hessian(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LH_OK : hip_fail(e, fn);
+}
+
+lh_status lh_output_error(const void* w, int w_dtype, const float* w_q, int64_t c_out, int64_t c_in, int64_t ld_w,
+                          int64_t ld_q, int64_t n_groups, int64_t group_stride_w, int64_t group_stride_q,
+                          const float* h_full, int64_t ld_h, int64_t group_stride_h, float* err, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  const char* fn = "lh_output_error";
+  g_msg[0] = '\0';
+  if (!valid_dtype(w_dtype)) return fail(LH_ERR_DTYPE, "%s: w_dtype must be 0 (f32) or 1 (bf16)", fn);
+  if (c_out < 0 || c_in < 0 || n_groups < 0 || group_stride_w < 0 || group_stride_q < 0 || group_stride_h < 0)
+    return fail(LH_ERR_SHAPE, "%s: negative size or stride", fn);
+  if (c_in % 16 != 0) return fail(LH_ERR_SHAPE, "%s: c_in must be a multiple of 16", fn);
+  if (ld_w < c_in || ld_q < c_in || ld_h < c_in) return fail(LH_ERR_SHAPE, "%s: a leading dimension < c_in", fn);
+  const bool work = n_groups > 0 && c_out > 0 && c_in > 0;
+  if (work && (w == nullptr || w_q == nullptr || h_full == nullptr || err == nullptr))
+    return fail(LH_ERR_NULL, "%s: w, w_q, h_full and err are required", fn);
+  if (work && workspace == nullptr) return fail(LH_ERR_NULL, "%s: workspace is required", fn);
+  if (!aligned(w, elem_size(w_dtype)) || !aligned(w_q, 4) || !aligned(h_full, 4) || !aligned(err, 4) ||
+      !aligned(workspace, 4))
+    return fail(LH_ERR_ARG, "%s: pointer not aligned to its element size", fn);
+  if (work && workspace_bytes < lh::output_error_ws_bytes(c_out, c_in, n_groups))
+    return fail(LH_ERR_WORKSPACE, "%s: workspace smaller than lh_output_error_workspace_bytes()", fn);
+  if (!work) return LH_OK;
+  lh::OutputErrorArgs a{w, w_dtype, w_q, c_out, c_in, ld_w, ld_q, group_stride_w, group_stride_q, n_groups,
+                        h_full, ld_h, group_stride_h, err, workspace};
+  hipError_t e = lh::launch_output_error(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LH_OK : hip_fail(e, fn);
+}
+
+lh_status lh_scaled_histogram(const void* w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
+                              int64_t n_groups, int64_t group_stride_w, const uint8_t* best_idx, const float* amax,
+                              int n_bins, float bins_per_unit, uint64_t* counts, void* stream) {
+  const char* fn = "lh_scaled_histogram";
+  g_msg[0] = '\0';
+  if (!valid_dtype(w_dtype)) return fail(LH_ERR_DTYPE, "%s: w_dtype must be 0 (f32) or 1 (bf16)", fn);
+  if (c_out < 0 || c_in < 0 || n_groups < 0 || group_stride_w < 0)
+    return fail(LH_ERR_SHAPE, "%s: negative size or stride", fn);
+  if (c_in % 16 != 0) return fail(LH_ERR_SHAPE, "%s: c_in must be a multiple of 16", fn);
+  if (ld_w < c_in) return fail(LH_ERR_SHAPE, "%s: ld_w < c_in", fn);
+  if (n_bins < 1 || n_bins > lh::histogram_max_bins())
+    return fail(LH_ERR_ARG, "%s: n_bins must be in [1, 4096]", fn);
+  if (!(bins_per_unit > 0.0f) || !(bins_per_unit < INFINITY))
+    return fail(LH_ERR_ARG, "%s: bins_per_unit must be positive and finite", fn);
+  const bool blocks = n_groups > 0 && c_out > 0 && c_in > 0;
+  if (n_groups > 0 && (counts == nullptr || amax == nullptr))
+    return fail(LH_ERR_NULL, "%s: counts and amax are required", fn);
+  if (blocks && (w == nullptr || best_idx == nullptr)) return fail(LH_ERR_NULL, "%s: w and best_idx are required", fn);
+  if (!aligned(w, elem_size(w_dtype)) || !aligned(amax, 4) || !aligned(counts, 8))
+    return fail(LH_ERR_ARG, "%s: pointer not aligned to its element size", fn);
+  if (n_groups == 0) return LH_OK;
+  lh::HistogramArgs a{w, w_dtype, c_out, c_in, ld_w, group_stride_w, n_groups, best_idx, amax, n_bins,
+                      bins_per_unit, reinterpret_cast<unsigned long long*>(counts)};
+  hipError_t e = lh::launch_histogram(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LH_OK : hip_fail(e, fn);
 }
 

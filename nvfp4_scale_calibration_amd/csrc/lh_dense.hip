@@ -1,0 +1,361 @@
+// lh_dense.hip - dense C_in x C_in work on CDNA4 matrix cores: the full
+// Hessian X X^T, the layer output error (q - w) H (q - w)^T, and the W/s
+// histogram.
+//
+// "Local-Hessian weight-scale guide" (xxmr.cn/news/266017), "Algorithm
+// principle": the layer's output error is ||Delta X||_F^2 =
+// tr(Delta X X^T Delta^T); Local-Hessian keeps only the 16 x 16 diagonal
+// blocks of X X^T.  These kernels measure what that approximation leaves
+// out, on the same inputs.  "How scaling reshapes the weight distribution":
+// the histogram of W/s, the values the E2M1 rounding receives.
+//
+// GEMM design: C[m][n] = sum_k A[m][k] B[n][k] ("NT": both operands
+// K-contiguous, which is how X [C_in][N] feeds X X^T and how the symmetric
+// H feeds D H).  A 256-thread workgroup owns a 64 x 64 tile of C; its four
+// waves own 32 x 32 quadrants as 2 x 2 MFMA tiles (v_mfma_f32_16x16x32_bf16
+// for bf16 operands, v_mfma_f32_16x16x4_f32 for fp32), fp32 accumulation.
+// K advances in 128-byte chunks staged through LDS (rows padded by 16 bytes)
+// with the next chunk's global loads in flight during the MFMAs.  Operand
+// loaders are plug-ins (plain, or q - w formed on the fly); epilogues are a
+// scaled store or a fixed-order row dot with D (for the output error).
+#include "lh_device.h"
+#include "lh_internal.h"
+
+namespace lh {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int kTile = 64;
+
+// Operand element type on the MFMA side and the K chunk (128 bytes per row).
+template <typename T>
+struct Mfma;
+template <>
+struct Mfma<uint16_t> {
+  static constexpr int kKc = 64;   // bf16 elements per chunk
+  static constexpr int kEP = 8;    // elements per 16 bytes
+};
+template <>
+struct Mfma<float> {
+  static constexpr int kKc = 32;
+  static constexpr int kEP = 4;
+};
+
+// Plain operand: rows of T with leading dimension ld.  The 16-byte chunk at
+// (row, k) with k % kEP == 0; rows >= rows_end or k >= k_end read as zero.
+template <typename T, bool kVec>
+struct PlainLoader {
+  const T* p;
+  int64_t ld;
+  int64_t gs;  // group stride (elements)
+  __device__ __forceinline__ void group(int64_t g) { p += g * gs; }
+  __device__ __forceinline__ uint4 chunk(int64_t row, int64_t k, int64_t rows_end, int64_t k_end) const {
+    constexpr int EP = Mfma<T>::kEP;
+    if (row >= rows_end || k >= k_end) return make_uint4(0u, 0u, 0u, 0u);
+    if (kVec && k + EP <= k_end) return *reinterpret_cast<const uint4*>(p + row * ld + k);
+    T v[EP];
+#pragma unroll
+    for (int i = 0; i < EP; ++i) v[i] = (k + i < k_end) ? p[row * ld + k + i] : T(0);
+    return __builtin_bit_cast(uint4, v);
+  }
+};
+
+// fp32 operand D = q - w (q fp32, w of type TW), formed while loading.
+template <typename TW>
+struct DiffLoader {
+  const float* q;
+  int64_t ldq;
+  const TW* w;
+  int64_t ldw;
+  int64_t gsq, gsw;  // group strides (elements)
+  __device__ __forceinline__ void group(int64_t g) {
+    q += g * gsq;
+    w += g * gsw;
+  }
+  __device__ __forceinline__ float value(int64_t row, int64_t k) const {
+    return q[row * ldq + k] - load_as_f32<TW>(w, row * ldw + k);
+  }
+  __device__ __forceinline__ uint4 chunk(int64_t row, int64_t k, int64_t rows_end, int64_t k_end) const {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (row < rows_end && k + i < k_end) ? value(row, k + i) : 0.0f;
+    return __builtin_bit_cast(uint4, v);
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ f32x4_t mfma_step(const T* a, const T* b, f32x4_t acc);
+template <>
+__device__ __forceinline__ f32x4_t mfma_step<uint16_t>(const uint16_t* a, const uint16_t* b, f32x4_t acc) {
+  const bf16x8_t av = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(a));
+  const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(b));
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4_t mfma_step<float>(const float* a, const float* b, f32x4_t acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(*a, *b, acc, 0, 0, 0);
+}
+
+enum Epi { kEpiStore = 0, kEpiRowDot = 1 };
+
+struct GemmArgs {
+  int64_t M, N, K;
+  float alpha, beta;         // kEpiStore: C = alpha * acc + beta * C (beta == 0: C not read)
+  float* c;                  // kEpiStore output
+  int64_t ldc, sc;
+  float* part;               // kEpiRowDot: partial[g][m][n-tile]
+};
+
+// One workgroup: C tile (blockIdx.y, blockIdx.x) of group blockIdx.z.
+template <typename T, typename LA, typename LB, int kEpi>
+__global__ __launch_bounds__(kThreads) void gemm_nt_kernel(LA la, LB lb, GemmArgs g) {
+  constexpr int kKc = Mfma<T>::kKc;
+  constexpr int kEP = Mfma<T>::kEP;
+  constexpr int kPitch = kKc + kEP;            // +16 bytes per row
+  constexpr int kCPR = kKc / kEP;              // 16-byte chunks per row (8)
+  constexpr int kLoads = kTile * kCPR / kThreads;  // per operand per thread (2)
+  __shared__ __attribute__((aligned(16))) T as[2][kTile * kPitch];
+  __shared__ __attribute__((aligned(16))) T bs[2][kTile * kPitch];
+
+  const int64_t grp = blockIdx.z;
+  la.group(grp);
+  lb.group(grp);
+  const int64_t m0 = (int64_t)blockIdx.y * kTile, n0 = (int64_t)blockIdx.x * kTile;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  uint4 ra[kLoads], rb[kLoads];
+  auto gload = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int c = tid + kThreads * i;
+      const int row = c / kCPR, col = (c % kCPR) * kEP;
+      ra[i] = la.chunk(m0 + row, k0 + col, g.M, g.K);
+      rb[i] = lb.chunk(n0 + row, k0 + col, g.N, g.K);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int c = tid + kThreads * i;
+      const int row = c / kCPR, col = (c % kCPR) * kEP;
+      *reinterpret_cast<uint4*>(&as[buf][row * kPitch + col]) = ra[i];
+      *reinterpret_cast<uint4*>(&bs[buf][row * kPitch + col]) = rb[i];
+    }
+  };
+
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int64_t chunks = (g.K + kKc - 1) / kKc;
+  if (chunks > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  const int r16 = lane & 15, kg = lane >> 4;
+  for (int64_t ck = 0; ck < chunks; ++ck) {
+    const int buf = (int)(ck & 1);
+    const bool more = ck + 1 < chunks;
+    if (more) gload((ck + 1) * kKc);
+    const T* A = as[buf];
+    const T* B = bs[buf];
+    // bf16: K step 32, lane takes 8 consecutive k at 8 * kg; fp32: K step 4, lane takes k = kg
+    constexpr int kStep = sizeof(T) == 2 ? 32 : 4;
+    constexpr int kLaneK = sizeof(T) == 2 ? 8 : 1;
+#pragma unroll
+    for (int ks = 0; ks < kKc; ks += kStep) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const T* arow = A + (32 * wm + 16 * i + r16) * kPitch + ks + kLaneK * kg;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const T* brow = B + (32 * wn + 16 * j + r16) * kPitch + ks + kLaneK * kg;
+          acc[i][j] = mfma_step<T>(arow, brow, acc[i][j]);
+        }
+      }
+    }
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // lane holds C[32 wm + 16 i + 4 kg + r][32 wn + 16 j + r16]
+  if constexpr (kEpi == kEpiStore) {
+    float* C = g.c + grp * g.sc;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t m = m0 + 32 * wm + 16 * i + 4 * kg + r;
+          const int64_t n = n0 + 32 * wn + 16 * j + r16;
+          if (m < g.M && n < g.N) {
+            float* cp = C + m * g.ldc + n;
+            *cp = (g.beta == 0.0f) ? g.alpha * acc[i][j][r] : g.alpha * acc[i][j][r] + g.beta * (*cp);
+          }
+        }
+  } else {
+    // row dot with D = A-source over this tile's 64 columns (K == N here):
+    // lane sums its two columns, then the 16 lanes of a row group (xor
+    // shuffles), then the two column waves in LDS, all in a fixed order.
+    __shared__ float rowsum[2][kTile];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + 32 * wm + 16 * i + 4 * kg + r;
+        float v = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int64_t n = n0 + 32 * wn + 16 * j + r16;
+          const float d = (m < g.M && n < g.N) ? la.value(m, n) : 0.0f;
+          v = __builtin_fmaf(acc[i][j][r], d, v);
+        }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, 16);
+        if (r16 == 0) rowsum[wn][32 * wm + 16 * i + 4 * kg + r] = v;
+      }
+    __syncthreads();
+    if (tid < kTile) {
+      const int64_t m = m0 + tid;
+      if (m < g.M) g.part[(grp * g.M + m) * gridDim.x + blockIdx.x] = rowsum[0][tid] + rowsum[1][tid];
+    }
+  }
+}
+
+// e[g][m] = sum over n-tiles of part, in tile order.
+__global__ __launch_bounds__(kThreads) void rowdot_reduce_kernel(const float* __restrict__ part, int64_t rows,
+                                                                 int64_t tiles, float* __restrict__ e) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= rows) return;
+  float v = 0.0f;
+  for (int64_t t = 0; t < tiles; ++t) v += part[i * tiles + t];
+  e[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+// W/s histogram: x = fl32(|w| / s_k) with the block's chosen k (the cast's
+// own quotient); bin = floor(fl32(x * bins_per_unit)), values at or past
+// n_bins count in the overflow bin n_bins.  Per-workgroup LDS counts, then
+// one 64-bit atomic add per non-empty bin: integer sums, so the result does
+// not depend on the order.
+// ---------------------------------------------------------------------------
+constexpr int kMaxBins = 4096;
+
+__global__ __launch_bounds__(kThreads) void zero_counts_kernel(unsigned long long* __restrict__ c, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) c[i] = 0ull;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void histogram_kernel(const T* __restrict__ w, int64_t c_out, int64_t c_in,
+                                                             int64_t ld_w, int64_t gstride_w,
+                                                             const uint8_t* __restrict__ idx,
+                                                             const float* __restrict__ amax, int n_bins,
+                                                             float bins_per_unit,
+                                                             unsigned long long* __restrict__ counts) {
+  __shared__ unsigned int local[kMaxBins + 1];
+  for (int i = threadIdx.x; i <= n_bins; i += kThreads) local[i] = 0u;
+  __syncthreads();
+  const int64_t grp = blockIdx.y;
+  const float Sg = amax[grp] / kAmaxDivisor;
+  const int64_t nb = c_in / 16;
+  const int64_t total = c_out * c_in;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total; e += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = e / c_in, c = e - r * c_in;
+    const int k = idx[(grp * c_out + r) * nb + c / 16];
+    const float s = e4m3_candidate(k) * Sg;
+    const float a = fabsf(load_as_f32<T>(w, grp * gstride_w + r * ld_w + c));
+    const float x = (s == 0.0f) ? 0.0f : a / s;
+    const float y = x * bins_per_unit;
+    const int bin = (y >= (float)n_bins) ? n_bins : (int)floorf(y);
+    atomicAdd(&local[bin], 1u);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i <= n_bins; i += kThreads)
+    if (local[i]) atomicAdd(&counts[grp * (n_bins + 1) + i], (unsigned long long)local[i]);
+}
+
+template <typename T, bool kVec>
+hipError_t launch_full_hessian_typed(const FullHessianArgs& a, hipStream_t stream) {
+  PlainLoader<T, kVec> L{static_cast<const T*>(a.x), a.ld_x, a.gstride_x};
+  GemmArgs g{a.c_in, a.c_in, a.n_tok, a.alpha, 0.0f, a.h, a.ld_h, a.gstride_h, nullptr};
+  const dim3 grid((unsigned)((a.c_in + kTile - 1) / kTile), (unsigned)((a.c_in + kTile - 1) / kTile),
+                  (unsigned)a.n_groups);
+  gemm_nt_kernel<T, PlainLoader<T, kVec>, PlainLoader<T, kVec>, kEpiStore><<<grid, dim3(kThreads), 0, stream>>>(L, L, g);
+  return hipGetLastError();
+}
+
+template <typename TW, bool kVecH>
+hipError_t launch_output_error_typed(const OutputErrorArgs& a, hipStream_t stream) {
+  DiffLoader<TW> D{a.q, a.ld_q, static_cast<const TW*>(a.w), a.ld_w, a.gstride_q, a.gstride_w};
+  PlainLoader<float, kVecH> H{a.h, a.ld_h, a.gstride_h};
+  const int64_t tiles = (a.c_in + kTile - 1) / kTile;
+  float* part = static_cast<float*>(a.ws);
+  GemmArgs g{a.c_out, a.c_in, a.c_in, 1.0f, 0.0f, nullptr, 0, 0, part};
+  const dim3 grid((unsigned)tiles, (unsigned)((a.c_out + kTile - 1) / kTile), (unsigned)a.n_groups);
+  gemm_nt_kernel<float, DiffLoader<TW>, PlainLoader<float, kVecH>, kEpiRowDot><<<grid, dim3(kThreads), 0, stream>>>(
+      D, H, g);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t rows = a.n_groups * a.c_out;
+  rowdot_reduce_kernel<<<dim3((unsigned)((rows + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream>>>(
+      part, rows, tiles, a.err);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t output_error_ws_bytes(int64_t c_out, int64_t c_in, int64_t n_groups) {
+  return (size_t)n_groups * (size_t)c_out * (size_t)((c_in + kTile - 1) / kTile) * sizeof(float);
+}
+
+int histogram_max_bins() { return kMaxBins; }
+
+hipError_t launch_full_hessian(const FullHessianArgs& a, hipStream_t stream) {
+  if (a.n_groups == 0 || a.c_in == 0) return hipSuccess;
+  const int64_t ep = a.dtype == 1 ? 8 : 4;
+  const bool vec = reinterpret_cast<uintptr_t>(a.x) % 16 == 0 && a.ld_x % ep == 0 && a.gstride_x % ep == 0;
+  if (a.dtype == 1)
+    return vec ? launch_full_hessian_typed<uint16_t, true>(a, stream) : launch_full_hessian_typed<uint16_t, false>(a, stream);
+  return vec ? launch_full_hessian_typed<float, true>(a, stream) : launch_full_hessian_typed<float, false>(a, stream);
+}
+
+hipError_t launch_output_error(const OutputErrorArgs& a, hipStream_t stream) {
+  if (a.n_groups == 0 || a.c_out == 0) return hipSuccess;
+  const bool vh = reinterpret_cast<uintptr_t>(a.h) % 16 == 0 && a.ld_h % 4 == 0 && a.gstride_h % 4 == 0;
+  if (a.dtype == 1)
+    return vh ? launch_output_error_typed<uint16_t, true>(a, stream) : launch_output_error_typed<uint16_t, false>(a, stream);
+  return vh ? launch_output_error_typed<float, true>(a, stream) : launch_output_error_typed<float, false>(a, stream);
+}
+
+hipError_t launch_histogram(const HistogramArgs& a, hipStream_t stream) {
+  if (a.n_groups == 0) return hipSuccess;
+  const int64_t nc = a.n_groups * (a.n_bins + 1);
+  zero_counts_kernel<<<dim3((unsigned)((nc + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream>>>(a.counts, nc);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || a.c_out == 0 || a.c_in == 0) return err;
+  const int64_t total = a.c_out * a.c_in;
+  int64_t blocks = (total + kThreads * 16 - 1) / (kThreads * 16);
+  if (blocks > 1024) blocks = 1024;
+  if (blocks < 1) blocks = 1;
+  const dim3 grid((unsigned)blocks, (unsigned)a.n_groups);
+  if (a.dtype == 1)
+    histogram_kernel<uint16_t><<<grid, dim3(kThreads), 0, stream>>>(
+        static_cast<const uint16_t*>(a.w), a.c_out, a.c_in, a.ld_w, a.gstride_w, a.idx, a.amax, a.n_bins,
+        a.bins_per_unit, a.counts);
+  else
+    histogram_kernel<float><<<grid, dim3(kThreads), 0, stream>>>(
+        static_cast<const float*>(a.w), a.c_out, a.c_in, a.ld_w, a.gstride_w, a.idx, a.amax, a.n_bins,
+        a.bins_per_unit, a.counts);
+  return hipGetLastError();
+}
+
+}  // namespace lh

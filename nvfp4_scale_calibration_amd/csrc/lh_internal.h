@@ -84,4 +84,40 @@ struct AbsmaxArgs {
 };
 hipError_t launch_absmax(const AbsmaxArgs& a, hipStream_t stream);
 
+struct FullHessianArgs {
+  const void* x;        // channel-major [n_groups][c_in][ld_x]
+  int dtype;
+  int64_t c_in, n_tok, ld_x, gstride_x, n_groups;
+  float alpha;
+  float* h;             // [n_groups][c_in][ld_h]
+  int64_t ld_h, gstride_h;
+};
+hipError_t launch_full_hessian(const FullHessianArgs& a, hipStream_t stream);
+
+struct OutputErrorArgs {
+  const void* w;
+  int dtype;
+  const float* q;
+  int64_t c_out, c_in, ld_w, ld_q, gstride_w, gstride_q, n_groups;
+  const float* h;
+  int64_t ld_h, gstride_h;
+  float* err;           // [n_groups][c_out]
+  void* ws;             // output_error_ws_bytes
+};
+size_t output_error_ws_bytes(int64_t c_out, int64_t c_in, int64_t n_groups);
+hipError_t launch_output_error(const OutputErrorArgs& a, hipStream_t stream);
+
+struct HistogramArgs {
+  const void* w;
+  int dtype;
+  int64_t c_out, c_in, ld_w, gstride_w, n_groups;
+  const uint8_t* idx;
+  const float* amax;
+  int n_bins;
+  float bins_per_unit;
+  unsigned long long* counts;  // [n_groups][n_bins + 1]
+};
+int histogram_max_bins();
+hipError_t launch_histogram(const HistogramArgs& a, hipStream_t stream);
+
 }  // namespace lh

@@ -1,0 +1,128 @@
+"""GPU parity of the approximation diagnostics (lh_full_hessian,
+lh_output_error, lh_scaled_histogram) against the CPU oracle, on ragged
+shapes, several groups, both dtypes, and the dense-4096 layer (sampled rows).
+
+Tolerances (derived from the fp32 arithmetic):
+  * full Hessian: each entry is an fp32 sum of N exact bf16/fp32 products,
+    |dH_ij| <= N u sum_t |x_it x_jt| <= N u sqrt(H_ii H_jj) * N/N, so the
+    Hessian rule |dH| <= 1e-3 sqrt(H_ii H_jj) holds for N up to ~16k;
+  * output error: T = d H (fp32, K = c_in terms) then a 64-term row dot
+    and an ordered sum over c_in/64 tiles: |de| <= (c_in + 64 + c_in/64) u S
+    with S = sum |d_n| |H_nk| |d_k|;
+  * histogram: integer counts, bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lh_workloads as wl
+import oracle
+import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+U = 2.0 ** -24
+
+
+@pytest.fixture(scope="module")
+def lh():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import nvfp4_scale_calibration_amd as m
+    return m
+
+
+def check_full_hessian(h_gpu, x_np_g, c_in, n, rows=None):
+    if rows is None:
+        ref = oracle.full_hessian(x_np_g, c_in, n)
+        got = h_gpu
+    else:
+        xv = x_np_g if x_np_g.dtype == np.float32 else (x_np_g.astype(np.uint32) << 16).view(np.float32)
+        x64 = xv.astype(np.float64)
+        ref = x64[rows] @ x64.T / n
+        got = h_gpu[rows]
+        dref = np.einsum("ij,ij->i", x64, x64) / n
+        scale = np.sqrt(np.abs(dref[rows]))[:, None] * np.sqrt(np.abs(dref))[None, :]
+        bad = np.abs(got - ref) > 1e-3 * scale + 1e-30
+        assert not bad.any(), "full Hessian mismatch in sampled rows: %d entries" % bad.sum()
+        return
+    d = np.sqrt(np.abs(np.diag(ref)))
+    bad = np.abs(got - ref) > 1e-3 * d[:, None] * d[None, :] + 1e-30
+    assert not bad.any(), "full Hessian mismatch: %d entries, first %s" % (bad.sum(), np.argwhere(bad)[0])
+
+
+def check_output_error(err_gpu, w_np_g, q_np_g, h32, c_in, rows):
+    e = oracle.output_error(w_np_g, q_np_g, h32, c_in, rows=rows)
+    wv = w_np_g if w_np_g.dtype == np.float32 else (w_np_g.astype(np.uint32) << 16).view(np.float32)
+    d = np.abs(q_np_g[rows].astype(np.float64) - wv[rows].astype(np.float64))
+    S = np.einsum("ri,ij,rj->r", d, np.abs(h32.astype(np.float64)), d)
+    tol = (c_in + 64 + c_in // 64 + 8) * U * S + 1e-30
+    bad = np.abs(err_gpu[rows] - e) > tol
+    assert not bad.any(), "output error mismatch at rows %s: gpu %s oracle %s tol %s" % (
+        rows[bad][:4], err_gpu[rows][bad][:4], e[bad][:4], tol[bad][:4])
+    return e
+
+
+def run_layer(lh, work):
+    wd, xd = work.w.to(DEV), work.x.to(DEV)
+    amax = lh.lh_absmax(wd)
+    h = lh.lh_accumulate_hessian(xd)
+    idx, err, _ = lh.lh_scale_sweep(wd, h, amax)
+    q = lh.lh_fake_quant_nvfp4(wd, idx, amax, w_q=True)["w_q"]
+    hf = lh.lh_full_hessian(xd)
+    e_full = lh.lh_output_error(wd, q, hf)
+    counts = lh.lh_scaled_histogram(wd, idx, amax)
+    torch.cuda.synchronize()
+    return dict(amax=amax.cpu().numpy(), h=h.cpu().numpy(), idx=idx.cpu().numpy(), err=err.cpu().numpy(),
+                q=q.cpu().numpy(), hf=hf.cpu().numpy(), e_full=e_full.cpu().numpy(), counts=counts.cpu().numpy())
+
+
+@pytest.mark.parametrize("G,c_out,c_in,n,dtype", [(2, 37, 48, 77, "f32"), (1, 129, 272, 300, "bf16"),
+                                                   (3, 70, 1040, 130, "bf16")])
+def test_diagnostics_ragged(lh, G, c_out, c_in, n, dtype):
+    work = wl.make_custom(c_out, c_in, n, n_groups=G, dtype=dtype, seed=c_in + n, w_dist="t3", x_dist="lognormal")
+    print("case diag G=%d %dx%d N=%d %s" % (G, c_out, c_in, n, dtype), flush=True)
+    got = run_layer(lh, work)
+    w_np, x_np = wl.np_bits(work.w), wl.np_bits(work.x)
+    for g in range(G):
+        check_full_hessian(got["hf"][g], x_np[g], c_in, n)
+        # its diagonal blocks are the local Hessians
+        for b in range(c_in // 16):
+            blk = got["hf"][g][16 * b:16 * b + 16, 16 * b:16 * b + 16]
+            d = np.sqrt(np.abs(np.diag(blk)))
+            assert np.all(np.abs(blk - got["h"][g, b]) <= 2e-3 * d[:, None] * d[None, :] + 1e-30)
+        check_output_error(got["e_full"][g], w_np[g], got["q"][g], got["hf"][g], c_in, np.arange(c_out))
+        counts = oracle.scaled_histogram(w_np[g], got["idx"][g], float(got["amax"][g]), c_out, c_in, 160, 20.0)
+        np.testing.assert_array_equal(got["counts"][g].astype(np.uint64), counts)
+
+
+def test_diagnostics_zero_weights_and_no_tokens(lh):
+    work = wl.make_custom(16, 32, 0, dtype="f32", seed=1, w_dist="zeros")
+    wd = work.w.to(DEV)
+    amax = lh.lh_absmax(wd)
+    idx, _, _ = lh.lh_scale_sweep(wd, torch.eye(16, device=DEV).expand(1, 2, 16, 16).contiguous(), amax)
+    hf = lh.lh_full_hessian(work.x.to(DEV))
+    q = lh.lh_fake_quant_nvfp4(wd, idx, amax, w_q=True)["w_q"]
+    e = lh.lh_output_error(wd, q, hf)
+    counts = lh.lh_scaled_histogram(wd, idx, amax)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(hf) == 0 and torch.count_nonzero(e) == 0
+    assert counts[0, 0].item() == 16 * 32 and counts.sum().item() == 16 * 32
+
+
+def test_diagnostics_dense_4096_sampled(lh):
+    work = wl.make(2)
+    c_in, n = work.c_in, work.n_tok
+    print("case diag dense-4096", flush=True)
+    got = run_layer(lh, work)
+    w_np, x_np = wl.np_bits(work.w)[0], wl.np_bits(work.x)[0]
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(c_in, 12, replace=False))
+    check_full_hessian(got["hf"][0], x_np, c_in, n, rows=rows)
+    orows = np.sort(rng.choice(work.c_out, 8, replace=False))
+    e = check_output_error(got["e_full"][0], w_np, got["q"][0], got["hf"][0], c_in, orows)
+    # the block-diagonal part the sweep minimised is a share of the full error
+    e_bd = got["err"][0].astype(np.float64).sum(axis=1)
+    print("  rows %s: full %s block-diagonal %s" % (orows[:4], e[:4], e_bd[orows][:4]), flush=True)
+    counts = oracle.scaled_histogram(w_np, got["idx"][0], float(got["amax"][0]), work.c_out, c_in, 160, 20.0)
+    np.testing.assert_array_equal(got["counts"][0].astype(np.uint64), counts)
