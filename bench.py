@@ -172,6 +172,7 @@ def extras(lh, work, w, x, h, amax, idx, err, bam, ws, ws_bytes, stream) -> dict
     rcold = timed(fn, stream, 15, before=lambda: scratch.fill_(1))
     del scratch
     counts = cap.offsets[1:] - cap.offsets[:-1]
+    diag = diagnostics(lh, work, w, x, h, amax, idx, err, bam)
     xb = work.x_bytes
     return {"hessian_cold": {"median_ms": pct(cold, 50), "p10_ms": pct(cold, 10), "p90_ms": pct(cold, 90),
                              "gbps_median": xb / (pct(cold, 50) / 1e3) / 1e9,
@@ -184,7 +185,53 @@ def extras(lh, work, w, x, h, amax, idx, err, bam, ws, ws_bytes, stream) -> dict
                                "cold_median_ms": pct(rcold, 50), "cold_p10_ms": pct(rcold, 10),
                                "cold_p90_ms": pct(rcold, 90),
                                "cold_gbps": cap.x_bytes / (pct(rcold, 50) / 1e3) / 1e9},
-            "scale_rules": rules}
+            "scale_rules": rules,
+            "diagnostics": diag}
+
+
+def diagnostics(lh, work, w, x, h, amax, idx, err, bam) -> dict:
+    """How much of the layer's output error the block-diagonal objective
+    sees, per scale rule: the full error sum_r (q-w) H_full (q-w)^T (H_full =
+    X X^T / N on matrix cores) against the sweep's block errors, and where
+    the W/s values fall relative to the E2M1 grid.  Timed: the full Hessian
+    (bf16 MFMA, 2 C_in^2 N flop) and the output error (fp32 MFMA, 2 C_out
+    C_in^2 flop)."""
+    import torch
+    G, c_out, c_in, n = work.n_groups, work.c_out, work.c_in, work.n_tok
+    if G != 1:
+        return {"skipped": "grouped layers: per-expert full Hessians not measured here"}
+    hf = torch.empty((1, c_in, c_in), dtype=torch.float32, device=w.device)
+    t_hf = graph_time(lambda: lh.lh_full_hessian(x, h=hf), reps=3)
+    wq = torch.empty((1, c_out, c_in), dtype=torch.float32, device=w.device)
+    e = torch.empty((1, c_out), dtype=torch.float32, device=w.device)
+    ows = torch.empty(max(lh.lh_output_error_workspace_bytes(c_out, c_in, 1), 4), dtype=torch.uint8, device=w.device)
+    counts = torch.empty((1, 161), dtype=torch.int64, device=w.device)
+    grid = torch.tensor([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=torch.float64)
+    centers = (torch.arange(160, dtype=torch.float64) + 0.5) / 20.0
+    near_grid = (centers[:, None] - grid[None, :]).abs().min(1).values < 0.05
+    out = {"full_hessian_ms": t_hf, "full_hessian_tflops": 2.0 * c_in * c_in * n / (t_hf / 1e3) / 1e12}
+    rules = {"local_hessian": (0, h), "mse": (0, None), "max": (1, h), "four_over_six": (2, None)}
+    for name, (rule, hh) in rules.items():
+        ri, re_, _ = lh.lh_select_scales(rule, w, hh, amax, best_idx=torch.empty_like(idx), best_err=True,
+                                         best_amax=False)
+        lh.lh_fake_quant_nvfp4(w, ri, amax, w_q=wq)
+        fn = (lambda: lh.lh_output_error(w, wq, hf, err=e, workspace=ows))
+        t_e = graph_time(fn, reps=3) if name == "local_hessian" else None
+        fn()
+        lh.lh_scaled_histogram(w, ri, amax, counts=counts)
+        torch.cuda.synchronize()
+        c = counts[0].double().cpu()
+        tot = float(c.sum())
+        ent = {"output_error": float(e.double().sum()),
+               "w_over_s_near_grid": float(c[:160][near_grid].sum()) / tot,
+               "w_over_s_at_least_5_5": float(c[110:].sum()) / tot}
+        if rule == 0 and hh is not None:
+            ent["block_diagonal_error"] = float(re_.double().sum())
+        if t_e is not None:
+            out["output_error_ms"] = t_e
+            out["output_error_tflops"] = 2.0 * c_out * c_in * c_in / (t_e / 1e3) / 1e12
+        out[name] = ent
+    return out
 
 
 def cpu_baseline(work, budget_s: float) -> dict:
