@@ -75,6 +75,9 @@ def _load():
     lib.oracle_full_hessian.argtypes = [P, I32, I64, I64, I64, D, P]
     lib.oracle_output_error.argtypes = [P, I32, P, I64, I64, I64, P, P, I64, P]
     lib.oracle_scaled_histogram.argtypes = [P, I32, I64, I64, I64, P, F, I32, F, P]
+    lib.oracle_gptq_u.argtypes = [P, I64, D, P]
+    lib.oracle_gptq_u.restype = I32
+    lib.oracle_gptq_sweep.argtypes = [P, I32, I64, I64, P, F, P, P, I32, P, I64, P]
     lib.oracle_num_threads.restype = I32
     lib.oracle_set_num_threads.argtypes = [I32]
     _lib = lib
@@ -320,3 +323,34 @@ def scaled_histogram(w: np.ndarray, idx: np.ndarray, g: float, c_out: int, c_in:
     _load().oracle_scaled_histogram(_ptr(w), _dtype_code(w), c_out, c_in, ld_w, _ptr(idx), float(g), int(n_bins),
                                     float(bins_per_unit), _ptr(counts))
     return counts
+
+
+def gptq_u(h: np.ndarray, damp: float = 0.01) -> np.ndarray:
+    """Upper U (fp64) with (H + damp mean(diag H) I)^-1 = U^T U, from the fp32
+    full Hessian h [n][n]."""
+    h = np.ascontiguousarray(h, np.float32)
+    n = h.shape[0]
+    U = np.zeros((n, n), np.float64)
+    if _load().oracle_gptq_u(_ptr(h), n, float(damp), _ptr(U)) != 0:
+        raise ValueError("damped Hessian is not positive definite")
+    return U
+
+
+def gptq_sweep(w: np.ndarray, idx: np.ndarray, g: float, c_in: int, U32: np.ndarray | None = None,
+               U64: np.ndarray | None = None, rows: np.ndarray | None = None, ld_w: int | None = None) -> np.ndarray:
+    """GPTQ rounding of the selected rows of one group with fixed block
+    scales.  With U32 (fp32) the fp32 sweep (fused multiply-adds in column
+    order), with U64 the fp64 sweep.  Returns q [n_rows][c_in] fp32."""
+    w = np.ascontiguousarray(w)
+    idx = np.ascontiguousarray(idx, np.uint8)
+    ld_w = c_in if ld_w is None else ld_w
+    n_all = w.size // ld_w
+    rows = np.arange(n_all, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
+    prec = 32 if U32 is not None else 64
+    u32 = None if U32 is None else np.ascontiguousarray(U32, np.float32)
+    u64 = None if U64 is None else np.ascontiguousarray(U64, np.float64)
+    q = np.zeros((len(rows), c_in), np.float32)
+    _load().oracle_gptq_sweep(_ptr(w), _dtype_code(w), c_in, ld_w, _ptr(idx), float(g),
+                              None if u32 is None else _ptr(u32), None if u64 is None else _ptr(u64), prec,
+                              _ptr(rows), len(rows), _ptr(q))
+    return q

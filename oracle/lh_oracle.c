@@ -46,6 +46,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #ifdef _OPENMP
@@ -617,4 +618,127 @@ void oracle_scaled_histogram(const void *w, int dtype, int64_t c_out, int64_t c_
             int64_t bin = (y >= (float)n_bins) ? n_bins : (int64_t)floorf(y);
             counts[bin] += 1;
         }
+}
+
+/* ====================================================================== */
+/* GPTQ rounding with fixed Local-Hessian scales ([LHG] "Combining with    */
+/* GPTQ": Local-Hessian chooses the block scales, GPTQ then replaces the   */
+/* round-to-nearest step to minimise the layer output error; the two are   */
+/* orthogonal).  The GPTQ steps follow the published method (Frantar et    */
+/* al., ICLR 2023): columns are quantised in order and each column's       */
+/* rounding error is fed to the not-yet-quantised columns through the      */
+/* upper Cholesky factor U of the inverse Hessian (H^-1 = U^T U).          */
+/* Readings:                                                               */
+/*   R17 H = the full Hessian X X^T / N (any positive factor gives the same */
+/*       result), damped: H' = H + 0.01 * mean(diag H) * I, or I when the  */
+/*       diagonal is all zero.                                             */
+/*   R18 per output row, for i = 0 .. C_in-1: x = w_i (the running value),  */
+/*       q_i = Q(x, s) with the block's fixed scale (the cast of R3),       */
+/*       e = (x - q_i) / U_ii, and w_j -= e U_ij for j > i.  Each w_j thus  */
+/*       receives its updates in increasing i.                              */
+/*   R19 precision: the fp32 sweep (the kernel's precision, which decides   */
+/*       the codes) takes x, the cast and e in fp32 and each update as one  */
+/*       fused multiply-add w_j = fma(-e, U_ij, w_j) in increasing i, with  */
+/*       U given as fp32; the fp64 sweep does the same steps in fp64.       */
+/* ====================================================================== */
+
+/* U (fp64, upper, row-major n x n) with H'^-1 = U^T U from the fp32 full
+ * Hessian h (n x n row-major).  Uses H' = R R^T with R upper (a Cholesky
+ * factorisation taken from the last row and column backwards), then
+ * U = R^-1.  Returns 0, or -1 if H' is not positive definite. */
+int oracle_gptq_u(const float *h, int64_t n, double damp, double *U)
+{
+    double *Hp = (double *)calloc((size_t)(n * n), sizeof(double));
+    double *R = (double *)calloc((size_t)(n * n), sizeof(double));
+    if (!Hp || !R) {
+        free(Hp);
+        free(R);
+        return -1;
+    }
+    double mean = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        mean += (double)h[i * n + i];
+    mean /= (double)n;
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = 0; j < n; ++j)
+            Hp[i * n + j] = (mean == 0.0) ? (i == j ? 1.0 : 0.0) : (double)h[i * n + j];
+    if (mean != 0.0)
+        for (int64_t i = 0; i < n; ++i)
+            Hp[i * n + i] += damp * mean;
+    /* backward Cholesky: H' = R R^T, R upper */
+    for (int64_t j = n - 1; j >= 0; --j) {
+        double d = Hp[j * n + j];
+        for (int64_t k = j + 1; k < n; ++k)
+            d -= R[j * n + k] * R[j * n + k];
+        if (!(d > 0.0)) {
+            free(Hp);
+            free(R);
+            return -1;
+        }
+        const double rjj = sqrt(d);
+        R[j * n + j] = rjj;
+        for (int64_t i = 0; i < j; ++i) {
+            double v = Hp[i * n + j];
+            for (int64_t k = j + 1; k < n; ++k)
+                v -= R[i * n + k] * R[j * n + k];
+            R[i * n + j] = v / rjj;
+        }
+    }
+    /* U = R^-1 (upper): solve R U = I column by column, bottom-up */
+    memset(U, 0, sizeof(double) * (size_t)(n * n));
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t c = 0; c < n; ++c)
+        for (int64_t i = c; i >= 0; --i) {
+            double v = (i == c) ? 1.0 : 0.0;
+            for (int64_t k = i + 1; k <= c; ++k)
+                v -= R[i * n + k] * U[k * n + c];
+            U[i * n + c] = v / R[i * n + i];
+        }
+    free(Hp);
+    free(R);
+    return 0;
+}
+
+/* GPTQ sweep of the selected rows of one group with fixed per-block
+ * candidate indices idx [c_out][c_in/16] and global amax g.  U32 (fp32) is
+ * used by the fp32 sweep (precision 32), U64 (fp64) by the fp64 sweep
+ * (precision 64).  q_out [n_rows][c_in] fp32. */
+void oracle_gptq_sweep(const void *w, int dtype, int64_t c_in, int64_t ld_w, const uint8_t *idx,
+                       float g, const float *U32, const double *U64, int precision,
+                       const int64_t *rows, int64_t n_rows, float *q_out)
+{
+    float s[126];
+    oracle_candidate_scales(g, s);
+    const int64_t nb = c_in / 16;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t n = 0; n < n_rows; ++n) {
+        const int64_t r = rows[n];
+        if (precision == 32) {
+            float *wr = (float *)malloc(sizeof(float) * (size_t)c_in);
+            for (int64_t i = 0; i < c_in; ++i)
+                wr[i] = widen_f32(w, dtype, r * ld_w + i);
+            for (int64_t i = 0; i < c_in; ++i) {
+                const float x = wr[i];
+                const float q = oracle_quantize(x, s[idx[r * nb + i / 16]], 0);
+                q_out[n * c_in + i] = q;
+                const float e = (x - q) / U32[i * c_in + i];
+                for (int64_t j = i + 1; j < c_in; ++j)
+                    wr[j] = fmaf(-e, U32[i * c_in + j], wr[j]);
+            }
+            free(wr);
+        } else {
+            double *wr = (double *)malloc(sizeof(double) * (size_t)c_in);
+            for (int64_t i = 0; i < c_in; ++i)
+                wr[i] = widen(w, dtype, r * ld_w + i);
+            for (int64_t i = 0; i < c_in; ++i) {
+                const float x = (float)wr[i];
+                const float q = oracle_quantize(x, s[idx[r * nb + i / 16]], 0);
+                q_out[n * c_in + i] = q;
+                const double e = (wr[i] - (double)q) / U64[i * c_in + i];
+                for (int64_t j = i + 1; j < c_in; ++j)
+                    wr[j] -= e * U64[i * c_in + j];
+            }
+            free(wr);
+        }
+    }
 }
