@@ -353,6 +353,49 @@ lh_status lh_scaled_histogram(const void *w, int w_dtype, int64_t c_out, int64_t
                               const uint8_t *best_idx, const float *amax, int n_bins,
                               float bins_per_unit, uint64_t *counts, void *stream);
 
+/*
+ * ---------------------------------------------------------------------------
+ * GPTQ rounding with fixed Local-Hessian scales ("Combining with GPTQ":
+ * Local-Hessian sets the block scales, GPTQ then replaces round-to-nearest
+ * to minimise the layer output error).  The GPTQ steps are the published
+ * method's (Frantar et al., ICLR 2023).  One layer (group) per call.
+ * ---------------------------------------------------------------------------
+ */
+
+/* Scratch bytes for lh_gptq_prepare (c_in) and lh_gptq_quantize (c_out, c_in). */
+size_t lh_gptq_workspace_bytes(int64_t c_out, int64_t c_in);
+
+/*
+ * u = the upper Cholesky factor of H'^-1, H' = H + damp * mean(diag H) * I
+ * (the identity when the diagonal is all zero): H'^-1 = u^T u, u upper with
+ * a positive diagonal, zeros below.  h_full: fp32 [c_in][ld_h] (e.g. from
+ * lh_full_hessian; any positive factor gives the same rounding); u: fp32
+ * [c_in][ld_u].  The damped Hessian must be numerically positive definite,
+ * else u holds non-finite values.  damp = 0.01 is the method's usual value.
+ * workspace: lh_gptq_workspace_bytes(c_out, c_in) bytes, 16-byte aligned.
+ * Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_WORKSPACE, LH_ERR_ARG, LH_ERR_HIP.
+ */
+lh_status lh_gptq_prepare(const float *h_full, int64_t c_in, int64_t ld_h, float damp, float *u,
+                          int64_t ld_u, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * GPTQ quantisation of w [c_out][ld_w] (w_dtype) with the fixed block scales
+ * best_idx [c_out][c_in/16] (candidate indices, e.g. from lh_scale_sweep)
+ * and the global amax (device fp32 scalar): per row, for i = 0..c_in-1,
+ *   q_i = Q(w_i, s_block(i))  (the cast of lh_fake_quant_nvfp4),
+ *   e = (w_i - q_i) / u_ii,   w_j = fma(-e, u_ij, w_j) for j > i (fp32),
+ * each w_j receiving its updates in increasing i.  w_q [c_out][ld_q] fp32
+ * receives the q_i (dequantised values on each block's E2M1 grid; their
+ * codes are what lh_fake_quant_nvfp4 would pack).  w is not modified.
+ * workspace: lh_gptq_workspace_bytes(c_out, c_in) bytes, 16-byte aligned.
+ * Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_WORKSPACE,
+ * LH_ERR_ARG, LH_ERR_HIP.
+ */
+lh_status lh_gptq_quantize(const void *w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
+                           const uint8_t *best_idx, const float *amax, const float *u,
+                           int64_t ld_u, float *w_q, int64_t ld_q, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

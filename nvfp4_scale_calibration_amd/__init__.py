@@ -70,6 +70,12 @@ def _load() -> ctypes.CDLL:
     lib.lh_output_error.restype = I
     lib.lh_scaled_histogram.argtypes = [P, I, I64, I64, I64, I64, I64, P, P, I, F, P, P]
     lib.lh_scaled_histogram.restype = I
+    lib.lh_gptq_workspace_bytes.argtypes = [I64, I64]
+    lib.lh_gptq_workspace_bytes.restype = SZ
+    lib.lh_gptq_prepare.argtypes = [P, I64, I64, F, P, I64, P, SZ, P]
+    lib.lh_gptq_prepare.restype = I
+    lib.lh_gptq_quantize.argtypes = [P, I, I64, I64, I64, P, P, P, I64, P, I64, P, SZ, P]
+    lib.lh_gptq_quantize.restype = I
     lib.lh_fake_quant_nvfp4.argtypes = [P, I, I64, I64, I64, I64, I64, P, P, P, P, P, P, P]
     lib.lh_fake_quant_nvfp4.restype = I
     return lib
@@ -80,7 +86,8 @@ EXPORTS = ("lh_abi_version", "lh_status_string", "lh_last_error_message", "lh_ab
            "lh_hessian_workspace_bytes", "lh_accumulate_hessian", "lh_hessian_ragged_workspace_bytes",
            "lh_accumulate_hessian_ragged", "lh_sweep_workspace_bytes", "lh_scale_sweep",
            "lh_select_scales", "lh_fake_quant_nvfp4", "lh_full_hessian", "lh_output_error_workspace_bytes",
-           "lh_output_error", "lh_scaled_histogram")
+           "lh_output_error", "lh_scaled_histogram", "lh_gptq_workspace_bytes", "lh_gptq_prepare",
+           "lh_gptq_quantize")
 
 
 def _check(status: int) -> None:
@@ -373,3 +380,48 @@ def lh_scaled_histogram(w: torch.Tensor, best_idx: torch.Tensor, amax: torch.Ten
                                    _ptr(best_idx), _ptr(amax), int(n_bins), float(bins_per_unit), _ptr(counts),
                                    _stream(w)))
     return counts
+
+
+def lh_gptq_workspace_bytes(c_out: int, c_in: int) -> int:
+    return int(lib.lh_gptq_workspace_bytes(c_out, c_in))
+
+
+def _gptq_ws(c_out, c_in, device, workspace):
+    if workspace is not None:
+        return workspace
+    return torch.empty(max(lh_gptq_workspace_bytes(c_out, c_in), 16), dtype=torch.uint8, device=device)
+
+
+def lh_gptq_prepare(h_full: torch.Tensor, damp: float = 0.01, u: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Upper u with (H + damp mean(diag H) I)^-1 = u^T u, from one layer's
+    full Hessian [c_in, c_in] (fp32)."""
+    _require_device(h_full, u, workspace)
+    h2 = h_full.reshape(h_full.shape[-2], h_full.shape[-1])
+    c_in = h2.shape[0]
+    if u is None:
+        u = torch.empty((c_in, c_in), dtype=torch.float32, device=h_full.device)
+    ws = _gptq_ws(0, c_in, h_full.device, workspace)
+    _check(lib.lh_gptq_prepare(_ptr(h2), c_in, h2.stride(0), float(damp), _ptr(u), u.stride(0), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(h_full)))
+    return u
+
+
+def lh_gptq_quantize(w: torch.Tensor, best_idx: torch.Tensor, amax: torch.Tensor, u: torch.Tensor,
+                     w_q: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """GPTQ rounding of one layer's w [c_out, c_in] with fixed block scales
+    (best_idx [c_out, c_in/16], global amax device scalar); returns the
+    dequantised fp32 weights."""
+    _require_device(w, best_idx, amax, u, w_q, workspace)
+    w2 = w.reshape(w.shape[-2], w.shape[-1])
+    if w2.stride(-1) != 1:
+        raise ValueError("last dim of w must be contiguous")
+    c_out, c_in = w2.shape
+    if w_q is None:
+        w_q = torch.empty((c_out, c_in), dtype=torch.float32, device=w.device)
+    ws = _gptq_ws(c_out, c_in, w.device, workspace)
+    ld_w = w2.stride(0) if c_out > 1 else c_in
+    _check(lib.lh_gptq_quantize(_ptr(w2), _dtype(w2), c_out, c_in, ld_w, _ptr(best_idx), _ptr(amax), _ptr(u),
+                                u.stride(0), _ptr(w_q), w_q.stride(0) if c_out > 1 else c_in, _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(w)))
+    return w_q

@@ -317,4 +317,52 @@ lh_status lh_scaled_histogram(const void* w, int w_dtype, int64_t c_out, int64_t
   return e == hipSuccess ? LH_OK : hip_fail(e, fn);
 }
 
+size_t lh_gptq_workspace_bytes(int64_t c_out, int64_t c_in) {
+  if (c_out < 0 || c_in <= 0 || c_in % 16 != 0) return 0;
+  const size_t a = lh::gptq_prepare_ws_bytes(c_in), b = lh::gptq_quantize_ws_bytes(c_out, c_in);
+  return a > b ? a : b;
+}
+
+lh_status lh_gptq_prepare(const float* h_full, int64_t c_in, int64_t ld_h, float damp, float* u, int64_t ld_u,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "lh_gptq_prepare";
+  g_msg[0] = '\0';
+  if (c_in < 0) return fail(LH_ERR_SHAPE, "%s: negative size", fn);
+  if (c_in % 16 != 0) return fail(LH_ERR_SHAPE, "%s: c_in must be a multiple of 16", fn);
+  if (ld_h < c_in || ld_u < c_in) return fail(LH_ERR_SHAPE, "%s: a leading dimension < c_in", fn);
+  if (!(damp >= 0.0f) || !(damp < INFINITY)) return fail(LH_ERR_ARG, "%s: damp must be finite and >= 0", fn);
+  if (c_in == 0) return LH_OK;
+  if (h_full == nullptr || u == nullptr || workspace == nullptr)
+    return fail(LH_ERR_NULL, "%s: h_full, u and workspace are required", fn);
+  if (!aligned(h_full, 4) || !aligned(u, 4) || !aligned(workspace, 16))
+    return fail(LH_ERR_ARG, "%s: h_full and u need 4-byte, workspace 16-byte alignment", fn);
+  if (workspace_bytes < lh::gptq_prepare_ws_bytes(c_in))
+    return fail(LH_ERR_WORKSPACE, "%s: workspace smaller than lh_gptq_workspace_bytes()", fn);
+  lh::GptqPrepareArgs a{h_full, c_in, ld_h, damp, u, ld_u, workspace};
+  hipError_t e = lh::launch_gptq_prepare(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LH_OK : hip_fail(e, fn);
+}
+
+lh_status lh_gptq_quantize(const void* w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
+                           const uint8_t* best_idx, const float* amax, const float* u, int64_t ld_u, float* w_q,
+                           int64_t ld_q, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "lh_gptq_quantize";
+  g_msg[0] = '\0';
+  if (!valid_dtype(w_dtype)) return fail(LH_ERR_DTYPE, "%s: w_dtype must be 0 (f32) or 1 (bf16)", fn);
+  if (c_out < 0 || c_in < 0) return fail(LH_ERR_SHAPE, "%s: negative size", fn);
+  if (c_in % 16 != 0) return fail(LH_ERR_SHAPE, "%s: c_in must be a multiple of 16", fn);
+  if (ld_w < c_in || ld_u < c_in || ld_q < c_in) return fail(LH_ERR_SHAPE, "%s: a leading dimension < c_in", fn);
+  if (c_out == 0 || c_in == 0) return LH_OK;
+  if (!w || !best_idx || !amax || !u || !w_q || !workspace)
+    return fail(LH_ERR_NULL, "%s: w, best_idx, amax, u, w_q and workspace are required", fn);
+  if (!aligned(w, elem_size(w_dtype)) || !aligned(amax, 4) || !aligned(u, 4) || !aligned(w_q, 4) ||
+      !aligned(workspace, 16))
+    return fail(LH_ERR_ARG, "%s: pointer not aligned to its element size (workspace: 16 bytes)", fn);
+  if (workspace_bytes < lh::gptq_quantize_ws_bytes(c_out, c_in))
+    return fail(LH_ERR_WORKSPACE, "%s: workspace smaller than lh_gptq_workspace_bytes()", fn);
+  lh::GptqQuantizeArgs a{w, w_dtype, c_out, c_in, ld_w, best_idx, amax, u, ld_u, w_q, ld_q, workspace};
+  hipError_t e = lh::launch_gptq_quantize(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LH_OK : hip_fail(e, fn);
+}
+
 }  // extern "C"

@@ -103,7 +103,8 @@ enum Epi { kEpiStore = 0, kEpiRowDot = 1 };
 
 struct GemmArgs {
   int64_t M, N, K;
-  float alpha, beta;         // kEpiStore: C = alpha * acc + beta * C (beta == 0: C not read)
+  float alpha, beta;
+  int lower_only;            // skip tiles strictly above the diagonal (square M == N)         // kEpiStore: C = alpha * acc + beta * C (beta == 0: C not read)
   float* c;                  // kEpiStore output
   int64_t ldc, sc;
   float* part;               // kEpiRowDot: partial[g][m][n-tile]
@@ -120,6 +121,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(LA la, LB lb, GemmArg
   __shared__ __attribute__((aligned(16))) T as[2][kTile * kPitch];
   __shared__ __attribute__((aligned(16))) T bs[2][kTile * kPitch];
 
+  if (g.lower_only && blockIdx.x > blockIdx.y) return;  // whole workgroup: no barrier is skipped
   const int64_t grp = blockIdx.z;
   la.group(grp);
   lb.group(grp);
@@ -283,10 +285,259 @@ __global__ __launch_bounds__(kThreads) void histogram_kernel(const T* __restrict
     if (local[i]) atomicAdd(&counts[grp * (n_bins + 1) + i], (unsigned long long)local[i]);
 }
 
+
+// ---------------------------------------------------------------------------
+// GPTQ rounding with fixed Local-Hessian scales ("Combining with GPTQ":
+// Local-Hessian chooses the block scales, GPTQ then replaces the
+// round-to-nearest step).  The steps follow the published GPTQ method
+// (Frantar et al., ICLR 2023):
+//   H' = H + damp * mean(diag H) * I  (I when the diagonal is all zero),
+//   U  = the upper Cholesky factor of H'^-1 (H'^-1 = U^T U),
+//   per row, for i = 0 .. C_in-1:  q_i = Q(w_i, s_block);
+//     e = (w_i - q_i) / U_ii;  w_j = fma(-e, U_ij, w_j) for j > i.
+// Every w_j receives its updates in increasing i, one fused multiply-add
+// each, whichever kernel applies them: the panel kernel for j inside the
+// current 128-column block, the trailing kernel for the columns after it.
+// So the result does not depend on the blocking.
+//
+// U without forming H'^-1: with P the index reversal, A = P H' P = L L^T
+// (lower Cholesky, blocked: 64 x 64 diagonal factor in LDS, panel solve,
+// trailing update on the matrix-core GEMM), then H' = R R^T with R = P L P
+// upper, and U = R^-1 = P L^-1 P.  L^-1 is formed by block rows:
+// X_i = L_ii^-1 (E_i - L_i,<i X_<i), the product on the GEMM (with X stored
+// transposed so that both operands are K-contiguous), the 64 x 64 solve
+// per column in a small kernel.
+// ---------------------------------------------------------------------------
+constexpr int kCb = 64;     // Cholesky / inverse block
+constexpr int kGb = 128;    // GPTQ column block
+
+// ws layout (floats): A/L [n][n] | Y = (L^-1)^T [n][n] | T [64][n] | scalar
+__global__ __launch_bounds__(kThreads) void gptq_damp_kernel(const float* __restrict__ h, int64_t n, int64_t ld_h,
+                                                             float damp, float* __restrict__ out) {
+  __shared__ float part[kThreads];
+  float v = 0.0f;
+  for (int64_t i = threadIdx.x; i < n; i += kThreads) v += h[i * ld_h + i];
+  part[threadIdx.x] = v;
+  __syncthreads();
+  for (int off = kThreads / 2; off > 0; off >>= 1) {
+    if (threadIdx.x < off) part[threadIdx.x] += part[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float mean = part[0] / (float)n;
+    out[0] = mean;                // 0: no signal, use the identity
+    out[1] = damp * mean;
+  }
+}
+
+// A[i][j] = H'[n-1-i][n-1-j]; Y = 0.
+__global__ __launch_bounds__(kThreads) void gptq_reverse_kernel(const float* __restrict__ h, int64_t n, int64_t ld_h,
+                                                                const float* __restrict__ dm, float* __restrict__ A,
+                                                                float* __restrict__ Y) {
+  const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (e >= n * n) return;
+  const int64_t i = e / n, j = e - i * n;
+  const float mean = dm[0], add = dm[1];
+  float v;
+  if (mean == 0.0f) v = (i == j) ? 1.0f : 0.0f;
+  else v = h[(n - 1 - i) * ld_h + (n - 1 - j)] + (i == j ? add : 0.0f);
+  A[e] = v;
+  Y[e] = 0.0f;
+}
+
+// In-place lower Cholesky of the bs x bs diagonal block at (k0, k0) of A.
+__global__ __launch_bounds__(kThreads) void chol_diag_kernel(float* __restrict__ A, int64_t n, int64_t k0, int bs) {
+  __shared__ float a[kCb][kCb + 1];
+  for (int e = threadIdx.x; e < bs * bs; e += kThreads) a[e / bs][e % bs] = A[(k0 + e / bs) * n + k0 + e % bs];
+  __syncthreads();
+  for (int j = 0; j < bs; ++j) {
+    if (threadIdx.x == 0) a[j][j] = sqrtf(a[j][j]);
+    __syncthreads();
+    const float d = a[j][j];
+    for (int i = j + 1 + threadIdx.x; i < bs; i += kThreads) a[i][j] /= d;
+    __syncthreads();
+    // rank-1 update of the lower part of the remaining sub-block
+    for (int e = threadIdx.x; e < (bs - j - 1) * (bs - j - 1); e += kThreads) {
+      const int i = j + 1 + e / (bs - j - 1), c = j + 1 + e % (bs - j - 1);
+      if (c <= i) a[i][c] = __builtin_fmaf(-a[i][j], a[c][j], a[i][c]);
+    }
+    __syncthreads();
+  }
+  for (int e = threadIdx.x; e < bs * bs; e += kThreads) {
+    const int i = e / bs, c = e % bs;
+    A[(k0 + i) * n + k0 + c] = c <= i ? a[i][c] : 0.0f;
+  }
+}
+
+// Panel below the diagonal block: row r of A[k0+bs:, k0:k0+bs] := solve of
+// L_kk x = a (forward substitution; one thread per row).
+__global__ __launch_bounds__(kThreads) void chol_panel_kernel(float* __restrict__ A, int64_t n, int64_t k0, int bs) {
+  __shared__ float l[kCb][kCb + 1];
+  for (int e = threadIdx.x; e < bs * bs; e += kThreads) l[e / bs][e % bs] = A[(k0 + e / bs) * n + k0 + e % bs];
+  __syncthreads();
+  const int64_t r = k0 + bs + (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (r >= n) return;
+  float* row = A + r * n + k0;
+  float x[kCb];
+#pragma unroll
+  for (int j = 0; j < kCb; ++j) {
+    if (j < bs) {
+      float v = row[j];
+      for (int c = 0; c < j; ++c) v = __builtin_fmaf(-l[j][c], x[c], v);
+      x[j] = v / l[j][j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kCb; ++j)
+    if (j < bs) row[j] = x[j];
+}
+
+// Block row ib of X = L^-1, stored transposed (Y[j][i0 + a] = X[i0 + a][j]):
+// for every column j < i0 + bs, y = L_ii^-1 (e_j - T[:, j]).
+__global__ __launch_bounds__(kThreads) void tri_inv_solve_kernel(const float* __restrict__ L, const float* __restrict__ T,
+                                                                 float* __restrict__ Y, int64_t n, int64_t i0, int bs) {
+  __shared__ float l[kCb][kCb + 1];
+  for (int e = threadIdx.x; e < bs * bs; e += kThreads) l[e / bs][e % bs] = L[(i0 + e / bs) * n + i0 + e % bs];
+  __syncthreads();
+  const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (j >= i0 + bs) return;
+  float y[kCb];
+#pragma unroll
+  for (int a = 0; a < kCb; ++a) {
+    if (a < bs) {
+      float v = ((j == i0 + a) ? 1.0f : 0.0f) - (i0 > 0 ? T[(int64_t)a * n + j] : 0.0f);
+      for (int c = 0; c < a; ++c) v = __builtin_fmaf(-l[a][c], y[c], v);
+      y[a] = v / l[a][a];
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < kCb; ++a)
+    if (a < bs) Y[j * n + i0 + a] = y[a];
+}
+
+// U[i][j] = X[n-1-i][n-1-j] = Y[n-1-j][n-1-i] (upper; zero below), through
+// 32 x 32 LDS tiles.
+__global__ __launch_bounds__(kThreads) void gptq_u_kernel(const float* __restrict__ Y, int64_t n, float* __restrict__ U,
+                                                          int64_t ld_u) {
+  __shared__ float t[32][33];
+  const int64_t bi = (int64_t)blockIdx.y * 32, bj = (int64_t)blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  for (int r = ty; r < 32; r += 8) {
+    // tile element (i = bi + r, j = bj + tx) needs Y[n-1-j][n-1-i]; read it row-wise
+    const int64_t yr = n - 1 - (bj + r), yc = n - 1 - (bi + tx);
+    t[r][tx] = (yr >= 0 && yr < n && yc >= 0 && yc < n) ? Y[yr * n + yc] : 0.0f;
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    const int64_t i = bi + r, j = bj + tx;
+    if (i < n && j < n) U[i * ld_u + j] = (j >= i) ? t[tx][r] : 0.0f;
+  }
+}
+
+// Running fp32 weights.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void gptq_copy_kernel(const T* __restrict__ w, int64_t c_out, int64_t c_in,
+                                                             int64_t ld_w, float* __restrict__ wf) {
+  const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (e >= c_out * c_in) return;
+  const int64_t r = e / c_in, c = e - r * c_in;
+  wf[e] = load_as_f32<T>(w, r * ld_w + c);
+}
+
+// Q(x, s) of the cast: x' = fl32(|x| / s) (IEEE), nearest E2M1 value (ties
+// to the even code, saturating), q = fl32(sign(x) r s), -0 -> +0.
+__device__ __forceinline__ float cast_q(float x, float s) {
+  const float r = (s == 0.0f) ? 0.0f : e2m1_round_mag(fabsf(x) / s);
+  return copysignf(r * s, x) + 0.0f;
+}
+
+// Panel: one lane per output row quantises columns b0 .. b0+width-1 in
+// order, feeding each error to the block's later columns (held in
+// registers); writes Q and the errors E[row][i].
+__global__ __launch_bounds__(kThreads) void gptq_panel_kernel(float* __restrict__ wf, int64_t c_out, int64_t c_in,
+                                                              int64_t b0, int width, const float* __restrict__ U,
+                                                              int64_t ld_u, const uint8_t* __restrict__ idx,
+                                                              const float* __restrict__ amax, float* __restrict__ q,
+                                                              int64_t ld_q, float* __restrict__ E) {
+  __shared__ float u[kGb][kGb + 1];
+  for (int e = threadIdx.x; e < width * width; e += kThreads)
+    u[e / width][e % width] = U[(b0 + e / width) * ld_u + b0 + e % width];
+  __syncthreads();
+  const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (r >= c_out) return;
+  const float Sg = amax[0] / kAmaxDivisor;
+  const int64_t nb = c_in / 16;
+  float w[kGb];
+#pragma unroll
+  for (int i = 0; i < kGb; ++i) w[i] = i < width ? wf[r * c_in + b0 + i] : 0.0f;
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kGb; ++i) {
+    if (i < width) {
+      if (i % 16 == 0) s = e4m3_candidate(idx[r * nb + (b0 + i) / 16]) * Sg;
+      const float x = w[i];
+      const float qi = cast_q(x, s);
+      q[r * ld_q + b0 + i] = qi;
+      const float e = (x - qi) / u[i][i];
+      E[r * kGb + i] = e;
+#pragma unroll
+      for (int j = i + 1; j < kGb; ++j) w[j] = __builtin_fmaf(-e, u[i][j], w[j]);
+    }
+  }
+}
+
+// Trailing columns: wf[r][j] for j >= b0 + width, updates from the block's
+// columns i in increasing order.  64 x 64 tile per workgroup, 4 x 4 per
+// thread; E and U rows staged in LDS.
+__global__ __launch_bounds__(kThreads) void gptq_trailing_kernel(float* __restrict__ wf, int64_t c_out, int64_t c_in,
+                                                                 int64_t b0, int width, const float* __restrict__ U,
+                                                                 int64_t ld_u, const float* __restrict__ E) {
+  __shared__ float es[kTile][kGb + 1];
+  __shared__ float us[kGb][kTile + 4];
+  const int64_t j0 = b0 + width + (int64_t)blockIdx.x * kTile;
+  const int64_t r0 = (int64_t)blockIdx.y * kTile;
+  for (int e = threadIdx.x; e < kTile * kGb; e += kThreads) {
+    const int rr = e / kGb, i = e % kGb;
+    es[rr][i] = (r0 + rr < c_out && i < width) ? E[(r0 + rr) * kGb + i] : 0.0f;
+  }
+  for (int e = threadIdx.x; e < kGb * kTile; e += kThreads) {
+    const int i = e / kTile, jj = e % kTile;
+    us[i][jj] = (i < width && j0 + jj < c_in) ? U[(b0 + i) * ld_u + j0 + jj] : 0.0f;
+  }
+  __syncthreads();
+  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;  // 16 x 16 threads, 4 x 4 each
+  float acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int64_t r = r0 + 4 * tr + a, j = j0 + 4 * tc + b;
+      acc[a][b] = (r < c_out && j < c_in) ? wf[r * c_in + j] : 0.0f;
+    }
+  for (int i = 0; i < width; ++i) {
+    float ev[4], uv[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) ev[a] = es[4 * tr + a][i];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) uv[b] = us[i][4 * tc + b];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fmaf(-ev[a], uv[b], acc[a][b]);
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int64_t r = r0 + 4 * tr + a, j = j0 + 4 * tc + b;
+      if (r < c_out && j < c_in) wf[r * c_in + j] = acc[a][b];
+    }
+}
+
 template <typename T, bool kVec>
 hipError_t launch_full_hessian_typed(const FullHessianArgs& a, hipStream_t stream) {
   PlainLoader<T, kVec> L{static_cast<const T*>(a.x), a.ld_x, a.gstride_x};
-  GemmArgs g{a.c_in, a.c_in, a.n_tok, a.alpha, 0.0f, a.h, a.ld_h, a.gstride_h, nullptr};
+  GemmArgs g{a.c_in, a.c_in, a.n_tok, a.alpha, 0.0f, 0, a.h, a.ld_h, a.gstride_h, nullptr};
   const dim3 grid((unsigned)((a.c_in + kTile - 1) / kTile), (unsigned)((a.c_in + kTile - 1) / kTile),
                   (unsigned)a.n_groups);
   gemm_nt_kernel<T, PlainLoader<T, kVec>, PlainLoader<T, kVec>, kEpiStore><<<grid, dim3(kThreads), 0, stream>>>(L, L, g);
@@ -299,7 +550,7 @@ hipError_t launch_output_error_typed(const OutputErrorArgs& a, hipStream_t strea
   PlainLoader<float, kVecH> H{a.h, a.ld_h, a.gstride_h};
   const int64_t tiles = (a.c_in + kTile - 1) / kTile;
   float* part = static_cast<float*>(a.ws);
-  GemmArgs g{a.c_out, a.c_in, a.c_in, 1.0f, 0.0f, nullptr, 0, 0, part};
+  GemmArgs g{a.c_out, a.c_in, a.c_in, 1.0f, 0.0f, 0, nullptr, 0, 0, part};
   const dim3 grid((unsigned)tiles, (unsigned)((a.c_out + kTile - 1) / kTile), (unsigned)a.n_groups);
   gemm_nt_kernel<float, DiffLoader<TW>, PlainLoader<float, kVecH>, kEpiRowDot><<<grid, dim3(kThreads), 0, stream>>>(
       D, H, g);
@@ -312,6 +563,92 @@ hipError_t launch_output_error_typed(const OutputErrorArgs& a, hipStream_t strea
 }
 
 }  // namespace
+
+
+size_t gptq_prepare_ws_bytes(int64_t n) {
+  return ((size_t)2 * n * n + (size_t)kCb * n + 64) * sizeof(float);
+}
+
+size_t gptq_quantize_ws_bytes(int64_t c_out, int64_t c_in) {
+  return ((size_t)c_out * c_in + (size_t)c_out * kGb) * sizeof(float);
+}
+
+hipError_t launch_gptq_prepare(const GptqPrepareArgs& a, hipStream_t stream) {
+  const int64_t n = a.n;
+  if (n == 0) return hipSuccess;
+  float* ws = static_cast<float*>(a.ws);
+  float* A = ws;
+  float* Y = A + n * n;
+  float* T = Y + n * n;
+  float* dm = T + kCb * n;
+  gptq_damp_kernel<<<dim3(1), dim3(kThreads), 0, stream>>>(a.h, n, a.ld_h, a.damp, dm);
+  gptq_reverse_kernel<<<dim3((unsigned)((n * n + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream>>>(
+      a.h, n, a.ld_h, dm, A, Y);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // blocked lower Cholesky of A
+  for (int64_t k0 = 0; k0 < n; k0 += kCb) {
+    const int bs = (int)(n - k0 < kCb ? n - k0 : kCb);
+    chol_diag_kernel<<<dim3(1), dim3(kThreads), 0, stream>>>(A, n, k0, bs);
+    const int64_t rest = n - k0 - bs;
+    if (rest > 0) {
+      chol_panel_kernel<<<dim3((unsigned)((rest + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream>>>(A, n, k0, bs);
+      PlainLoader<float, true> P{A + (k0 + bs) * n + k0, n, 0};
+      GemmArgs g{rest, rest, bs, -1.0f, 1.0f, 1, A + (k0 + bs) * n + k0 + bs, n, 0, nullptr};
+      const unsigned tiles = (unsigned)((rest + kTile - 1) / kTile);
+      gemm_nt_kernel<float, PlainLoader<float, true>, PlainLoader<float, true>, kEpiStore>
+          <<<dim3(tiles, tiles, 1), dim3(kThreads), 0, stream>>>(P, P, g);
+    }
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  // X = L^-1 by block rows, stored transposed in Y
+  for (int64_t i0 = 0; i0 < n; i0 += kCb) {
+    const int bs = (int)(n - i0 < kCb ? n - i0 : kCb);
+    if (i0 > 0) {
+      // T[a][j] = sum_{k < i0} L[i0 + a][k] Y[j][k], j < i0 + bs
+      PlainLoader<float, true> La{A + i0 * n, n, 0};
+      PlainLoader<float, true> Yb{Y, n, 0};
+      GemmArgs g{bs, i0 + bs, i0, 1.0f, 0.0f, 0, T, n, 0, nullptr};
+      gemm_nt_kernel<float, PlainLoader<float, true>, PlainLoader<float, true>, kEpiStore>
+          <<<dim3((unsigned)((i0 + bs + kTile - 1) / kTile), 1, 1), dim3(kThreads), 0, stream>>>(La, Yb, g);
+    }
+    tri_inv_solve_kernel<<<dim3((unsigned)((i0 + bs + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream>>>(
+        A, T, Y, n, i0, bs);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  const unsigned t32 = (unsigned)((n + 31) / 32);
+  gptq_u_kernel<<<dim3(t32, t32), dim3(kThreads), 0, stream>>>(Y, n, a.u, a.ld_u);
+  return hipGetLastError();
+}
+
+hipError_t launch_gptq_quantize(const GptqQuantizeArgs& a, hipStream_t stream) {
+  if (a.c_out == 0 || a.c_in == 0) return hipSuccess;
+  float* wf = static_cast<float*>(a.ws);
+  float* E = wf + a.c_out * a.c_in;
+  const unsigned ge = (unsigned)((a.c_out * a.c_in + kThreads - 1) / kThreads);
+  if (a.dtype == 1)
+    gptq_copy_kernel<uint16_t><<<dim3(ge), dim3(kThreads), 0, stream>>>(static_cast<const uint16_t*>(a.w), a.c_out,
+                                                                        a.c_in, a.ld_w, wf);
+  else
+    gptq_copy_kernel<float><<<dim3(ge), dim3(kThreads), 0, stream>>>(static_cast<const float*>(a.w), a.c_out, a.c_in,
+                                                                     a.ld_w, wf);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  for (int64_t b0 = 0; b0 < a.c_in; b0 += kGb) {
+    const int width = (int)(a.c_in - b0 < kGb ? a.c_in - b0 : kGb);
+    gptq_panel_kernel<<<dim3((unsigned)((a.c_out + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream>>>(
+        wf, a.c_out, a.c_in, b0, width, a.u, a.ld_u, a.idx, a.amax, a.q, a.ld_q, E);
+    const int64_t rest = a.c_in - b0 - width;
+    if (rest > 0)
+      gptq_trailing_kernel<<<dim3((unsigned)((rest + kTile - 1) / kTile), (unsigned)((a.c_out + kTile - 1) / kTile)),
+                             dim3(kThreads), 0, stream>>>(wf, a.c_out, a.c_in, b0, width, a.u, a.ld_u, E);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
 
 size_t output_error_ws_bytes(int64_t c_out, int64_t c_in, int64_t n_groups) {
   return (size_t)n_groups * (size_t)c_out * (size_t)((c_in + kTile - 1) / kTile) * sizeof(float);

@@ -120,4 +120,30 @@ struct HistogramArgs {
 int histogram_max_bins();
 hipError_t launch_histogram(const HistogramArgs& a, hipStream_t stream);
 
+struct GptqPrepareArgs {
+  const float* h;       // full Hessian [n][ld_h]
+  int64_t n, ld_h;
+  float damp;
+  float* u;             // [n][ld_u]
+  int64_t ld_u;
+  void* ws;             // gptq_prepare_ws_bytes(n)
+};
+size_t gptq_prepare_ws_bytes(int64_t n);
+hipError_t launch_gptq_prepare(const GptqPrepareArgs& a, hipStream_t stream);
+
+struct GptqQuantizeArgs {
+  const void* w;
+  int dtype;
+  int64_t c_out, c_in, ld_w;
+  const uint8_t* idx;   // [c_out][c_in/16]
+  const float* amax;    // device scalar
+  const float* u;
+  int64_t ld_u;
+  float* q;             // [c_out][ld_q]
+  int64_t ld_q;
+  void* ws;             // gptq_quantize_ws_bytes(c_out, c_in)
+};
+size_t gptq_quantize_ws_bytes(int64_t c_out, int64_t c_in);
+hipError_t launch_gptq_quantize(const GptqQuantizeArgs& a, hipStream_t stream);
+
 }  // namespace lh
