@@ -231,6 +231,21 @@ def diagnostics(lh, work, w, x, h, amax, idx, err, bam) -> dict:
             out["output_error_ms"] = t_e
             out["output_error_tflops"] = 2.0 * c_out * c_in * c_in / (t_e / 1e3) / 1e12
         out[name] = ent
+    # GPTQ rounding with fixed scales (Local-Hessian and max), on the same layer
+    gws = torch.empty(max(lh.lh_gptq_workspace_bytes(c_out, c_in), 16), dtype=torch.uint8, device=w.device)
+    u = torch.empty((c_in, c_in), dtype=torch.float32, device=w.device)
+    gq = torch.empty((c_out, c_in), dtype=torch.float32, device=w.device)
+    t_prep = graph_time(lambda: lh.lh_gptq_prepare(hf, u=u, workspace=gws), reps=1)
+    for name, (rule, hh) in (("local_hessian_gptq", (0, h)), ("max_gptq", (1, h))):
+        ri, _, _ = lh.lh_select_scales(rule, w, hh, amax, best_idx=torch.empty_like(idx), best_err=False,
+                                       best_amax=False)
+        fn = (lambda ri=ri: lh.lh_gptq_quantize(w, ri, amax, u, w_q=gq, workspace=gws))
+        t_q = graph_time(fn, reps=1)
+        fn()
+        lh.lh_output_error(w, gq.view(1, c_out, c_in), hf, err=e, workspace=ows)
+        torch.cuda.synchronize()
+        out[name] = {"output_error": float(e.double().sum()), "quantize_ms": t_q}
+    out["gptq_prepare_ms"] = t_prep
     return out
 
 
