@@ -64,8 +64,10 @@ __global__ __launch_bounds__(kThreads) void fake_quant_kernel(const T* __restric
                                                               const float* __restrict__ amax,
                                                               float* __restrict__ wq,
                                                               uint8_t* __restrict__ packed,
-                                                              uint8_t* __restrict__ codes) {
+                                                              uint8_t* __restrict__ codes,
+                                                              float* __restrict__ gscale, int64_t n_groups) {
   const int64_t f = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (gscale && f < n_groups) gscale[f] = amax[f] / kAmaxDivisor;  // S_g, written once per group
   if (f >= total) return;
   const int64_t b = f % nb;
   const int64_t rg = f / nb;  // grp * c_out + row
@@ -122,12 +124,13 @@ hipError_t launch_fq_typed(const FakeQuantArgs& a, hipStream_t stream) {
   const int64_t nb = a.c_in / 16;
   const int64_t total = a.n_groups * a.c_out * nb;
   if (total > 0 && (a.wq || a.packed || a.codes)) {
-    const int64_t grid = (total + kThreads - 1) / kThreads;
+    // threads f < n_groups also write S_g, so the grid covers both
+    const int64_t n = total > a.n_groups ? total : a.n_groups;
+    const int64_t grid = (n + kThreads - 1) / kThreads;
     fake_quant_kernel<T, kVec><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
         static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, total, a.idx, a.amax, a.wq, a.packed,
-        a.codes);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+        a.codes, a.gscale, a.n_groups);
+    return hipGetLastError();
   }
   if (a.gscale && a.n_groups > 0) {
     global_scale_kernel<<<dim3((unsigned)((a.n_groups + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream>>>(
@@ -211,7 +214,11 @@ __global__ __launch_bounds__(kThreads) void absmax_kernel(const T* __restrict__ 
     uint32_t t = part[0];
 #pragma unroll
     for (int i = 1; i < kThreads / 64; ++i) t = max(t, part[i]);
-    atomicMax(reinterpret_cast<unsigned int*>(out + grp), t);
+    // Atomics on one address serialise in L2; the stored value only grows, so
+    // a workgroup whose maximum does not exceed what it reads (possibly a
+    // stale, smaller value) has nothing to add.
+    unsigned int* o = reinterpret_cast<unsigned int*>(out + grp);
+    if (t > __atomic_load_n(o, __ATOMIC_RELAXED)) atomicMax(o, t);
   }
 }
 

@@ -137,6 +137,19 @@ __device__ __forceinline__ float quad_form_from(const float (&yd)[16], const flo
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
+// RN(a / b) given rb = RN(1 / b): q = RN(a rb), r = a - b q (exact by fma),
+// q' = RN(q + r rb).  Markstein's theorem makes q' the correctly rounded
+// quotient when no step overflows and the quotient is normal; the fast path
+// guarantees the range (row working exponent), and a subnormal quotient
+// rounds to E2M1 zero either way.  Checked against IEEE division on the host
+// over every divisor significand.  Three instructions instead of the ~10 of
+// a full IEEE division sequence.
+__device__ __forceinline__ float div_rn(float a, float b, float rb) {
+  const float q = a * rb;
+  const float r = __builtin_fmaf(-q, b, a);
+  return __builtin_fmaf(r, rb, q);
+}
+
 // Candidate k with scale s = 2^j * sigma, from the per-mantissa quotients
 // p_i = fl32(w_i / sigma) (signed).  The eight FP4 pairs are packed into the
 // four bytes of two dwords (byte select 0..3); `pk` carries them from one
@@ -264,11 +277,12 @@ __device__ __forceinline__ void sweep_mantissa(Best& best, SkipSet& t, float Sg,
                                                const float (&diag)[16], const float (&sym)[120],
                                                uint32_t (&pk)[2]) {
   const float sigma = (1.0f + 0.125f * (float)m) * Sg;  // fl32(mu * S_g)
+  const float rs = 1.0f / sigma;                        // IEEE division, once per class
   float p[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) p[i] = w[i] / sigma;  // IEEE division
+  for (int i = 0; i < 16; ++i) p[i] = div_rn(w[i], sigma, rs);  // = fl32(w / sigma)
 #pragma unroll
-  for (int e = 0; e < 4; ++e) t.p[e] = t.w[e] / sigma;  // same operation on the same bits as p[idx]
+  for (int e = 0; e < 4; ++e) t.p[e] = div_rn(t.w[e], sigma, rs);  // same operation on the same bits as p[idx]
   // subnormal E4M3 codes that share this mantissa: code = 1..7 -> k = code-1
   if constexpr (m == 0) {
     try_scaled<kMse>(best, t, 0, -9, sigma, p, w, diag, sym, pk);   // 1 * 2^-9
@@ -622,9 +636,10 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const T* __restrict_
         int m0, j0;
         candidate_class(k0, m0, j0);
         const float sigma0 = (1.0f + 0.125f * (float)m0) * Su;
+        const float rs0 = 1.0f / sigma0;
         float p0[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) p0[i] = w[i] / sigma0;
+        for (int i = 0; i < 16; ++i) p0[i] = div_rn(w[i], sigma0, rs0);
         eval_scaled<kMse>(best, k0, j0, sigma0, p0, w, diag, sym, pk);
       }
       sweep_mantissa<0, kMse>(best, t, Su, w, diag, sym, pk);
