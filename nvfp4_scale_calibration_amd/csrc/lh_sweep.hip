@@ -261,17 +261,21 @@ __device__ __forceinline__ bool needs_eval(SkipSet& t, const Best& best, int j, 
   return !(t.on && lb > best.err * kSkipMargin);
 }
 
-// All candidates of mantissa class m (mu = 1 + m/8), in increasing index.
-// Evaluates candidate (k, j) unless every lane of the wave can skip it.
-template <bool kMse>
-__device__ __forceinline__ void try_scaled(Best& best, SkipSet& t, int k, int j, float sigma, const float (&p)[16],
-                                           const float (&w)[16], const float (&diag)[16],
-                                           const float (&sym)[120], uint32_t (&pk)[2]) {
-  const bool need = needs_eval(t, best, j, ldexpf(sigma, j));
-  if (__ballot(need) != 0) eval_scaled_skip<kMse>(best, t, k, j, sigma, p, w, diag, sym, pk);
+// E4M3 code of mantissa class m at power j (value (1 + m/8) 2^j): normal
+// codes 8 (j + 7) + m for j >= -6, subnormal codes (8 + m) 2^(j + 9) / 8
+// below (e.g. 3 * 2^-9 = 1.5 * 2^-8).
+__device__ __forceinline__ int class_code(int m, int j) {
+  return j >= -6 ? 8 * (j + 7) + m : ((8 + m) << (j + 9)) >> 3;
 }
 
-// All candidates of mantissa class m (mu = 1 + m/8), in increasing index.
+// All candidates of mantissa class m (mu = 1 + m/8): powers j in
+// [jmin, jmax] (codes 1..126 only; 0x7F is NaN).  First every lane runs the
+// level-1 test on every candidate of the class against its incumbent at the
+// class start and keeps a mask of the candidates it cannot rule out; then
+// each lane evaluates its own candidates in increasing index while any lane
+// of the wave has one left.  A wave therefore costs the largest per-lane
+// count rather than the union over its lanes, and every candidate a lane
+// skips is still certified worse than that lane's incumbent.
 template <int m, bool kMse>
 __device__ __forceinline__ void sweep_mantissa(Best& best, SkipSet& t, float Sg, const float (&w)[16],
                                                const float (&diag)[16], const float (&sym)[120],
@@ -283,22 +287,19 @@ __device__ __forceinline__ void sweep_mantissa(Best& best, SkipSet& t, float Sg,
   for (int i = 0; i < 16; ++i) p[i] = div_rn(w[i], sigma, rs);  // = fl32(w / sigma)
 #pragma unroll
   for (int e = 0; e < 4; ++e) t.p[e] = div_rn(t.w[e], sigma, rs);  // same operation on the same bits as p[idx]
-  // subnormal E4M3 codes that share this mantissa: code = 1..7 -> k = code-1
-  if constexpr (m == 0) {
-    try_scaled<kMse>(best, t, 0, -9, sigma, p, w, diag, sym, pk);   // 1 * 2^-9
-    try_scaled<kMse>(best, t, 1, -8, sigma, p, w, diag, sym, pk);   // 2 * 2^-9
-    try_scaled<kMse>(best, t, 3, -7, sigma, p, w, diag, sym, pk);   // 4 * 2^-9
-  } else if constexpr (m == 2) {
-    try_scaled<kMse>(best, t, 4, -7, sigma, p, w, diag, sym, pk);   // 5 * 2^-9
-  } else if constexpr (m == 4) {
-    try_scaled<kMse>(best, t, 2, -8, sigma, p, w, diag, sym, pk);   // 3 * 2^-9
-    try_scaled<kMse>(best, t, 5, -7, sigma, p, w, diag, sym, pk);   // 6 * 2^-9
-  } else if constexpr (m == 6) {
-    try_scaled<kMse>(best, t, 6, -7, sigma, p, w, diag, sym, pk);   // 7 * 2^-9
+  constexpr int jmin = (m == 0) ? -9 : (m == 4) ? -8 : (m == 2 || m == 6) ? -7 : -6;
+  constexpr int jmax = (m == 7) ? 7 : 8;
+  uint32_t need = 0;
+#pragma unroll
+  for (int c = 0; c <= jmax - jmin; ++c)
+    if (needs_eval(t, best, jmin + c, ldexpf(sigma, jmin + c))) need |= 1u << c;
+  while (__ballot(need != 0) != 0) {
+    if (need != 0) {
+      const int j = jmin + __builtin_ctz(need);
+      need &= need - 1;
+      eval_scaled_skip<kMse>(best, t, class_code(m, j) - 1, j, sigma, p, w, diag, sym, pk);
+    }
   }
-  // normal codes 8E + m (E = 1..15; code 0x7F is NaN): value mu * 2^(E-7)
-  constexpr int emax = (m == 7) ? 14 : 15;
-  for (int E = 1; E <= emax; ++E) try_scaled<kMse>(best, t, 8 * E + m - 1, E - 7, sigma, p, w, diag, sym, pk);
 }
 
 // Mantissa class and power of two of candidate k: c_k = (1 + m/8) 2^j.
