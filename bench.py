@@ -64,10 +64,15 @@ def copy_probe() -> None:
     print(json.dumps({"copy_probe_bytes_per_launch": n}), flush=True)
 
 
+SWEEP_SOURCES = ("lh_device.h", "lh_sweep.hip")   # the sources the sweep kernel is built from
+
+
 def kernel_source_hash() -> str:
+    """Hash of the sweep kernel's sources: counter readings taken on other
+    sources no longer describe the kernel and are not reported."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nvfp4_scale_calibration_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in SWEEP_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]

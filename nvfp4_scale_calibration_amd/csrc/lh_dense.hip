@@ -345,27 +345,33 @@ __global__ __launch_bounds__(kThreads) void gptq_reverse_kernel(const float* __r
   Y[e] = 0.0f;
 }
 
-// In-place lower Cholesky of the bs x bs diagonal block at (k0, k0) of A.
-__global__ __launch_bounds__(kThreads) void chol_diag_kernel(float* __restrict__ A, int64_t n, int64_t k0, int bs) {
-  __shared__ float a[kCb][kCb + 1];
-  for (int e = threadIdx.x; e < bs * bs; e += kThreads) a[e / bs][e % bs] = A[(k0 + e / bs) * n + k0 + e % bs];
-  __syncthreads();
-  for (int j = 0; j < bs; ++j) {
-    if (threadIdx.x == 0) a[j][j] = sqrtf(a[j][j]);
-    __syncthreads();
-    const float d = a[j][j];
-    for (int i = j + 1 + threadIdx.x; i < bs; i += kThreads) a[i][j] /= d;
-    __syncthreads();
-    // rank-1 update of the lower part of the remaining sub-block
-    for (int e = threadIdx.x; e < (bs - j - 1) * (bs - j - 1); e += kThreads) {
-      const int i = j + 1 + e / (bs - j - 1), c = j + 1 + e % (bs - j - 1);
-      if (c <= i) a[i][c] = __builtin_fmaf(-a[i][j], a[c][j], a[i][c]);
-    }
-    __syncthreads();
+// In-place lower Cholesky of the bs x bs diagonal block at (k0, k0) of A,
+// by one wave: lane i keeps row i in registers (padded with the identity
+// beyond bs), and column j's entries reach the other lanes through
+// v_readlane at compile-time lane indices.  Lane i's lower entries only ever
+// combine lower entries (a[c] -= a[j] l_cj with j < c <= i), so whatever the
+// upper part holds is never used; it is written back as zeros.
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__global__ __launch_bounds__(64) void chol_diag_kernel(float* __restrict__ A, int64_t n, int64_t k0, int bs) {
+  const int i = threadIdx.x;
+  float a[kCb];
+#pragma unroll
+  for (int c = 0; c < kCb; ++c) a[c] = (i < bs && c < bs) ? A[(k0 + i) * n + k0 + c] : (c == i ? 1.0f : 0.0f);
+#pragma unroll
+  for (int j = 0; j < kCb; ++j) {
+    const float ljj = sqrtf(lane_value(a[j], j));
+    const float inv = 1.0f / ljj;
+    a[j] = (i == j) ? ljj : a[j] * inv;
+#pragma unroll
+    for (int c = j + 1; c < kCb; ++c) a[c] = __builtin_fmaf(-a[j], lane_value(a[j], c), a[c]);
   }
-  for (int e = threadIdx.x; e < bs * bs; e += kThreads) {
-    const int i = e / bs, c = e % bs;
-    A[(k0 + i) * n + k0 + c] = c <= i ? a[i][c] : 0.0f;
+  if (i < bs) {
+#pragma unroll
+    for (int c = 0; c < kCb; ++c)
+      if (c < bs) A[(k0 + i) * n + k0 + c] = c <= i ? a[c] : 0.0f;
   }
 }
 
@@ -589,7 +595,7 @@ hipError_t launch_gptq_prepare(const GptqPrepareArgs& a, hipStream_t stream) {
   // blocked lower Cholesky of A
   for (int64_t k0 = 0; k0 < n; k0 += kCb) {
     const int bs = (int)(n - k0 < kCb ? n - k0 : kCb);
-    chol_diag_kernel<<<dim3(1), dim3(kThreads), 0, stream>>>(A, n, k0, bs);
+    chol_diag_kernel<<<dim3(1), dim3(64), 0, stream>>>(A, n, k0, bs);
     const int64_t rest = n - k0 - bs;
     if (rest > 0) {
       chol_panel_kernel<<<dim3((unsigned)((rest + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream>>>(A, n, k0, bs);
