@@ -167,9 +167,11 @@ def extras(lh, work, w, x, h, amax, idx, err, bam, ws, ws_bytes, stream) -> dict
     off = torch.from_numpy(cap.offsets).to(w.device)
     hr = torch.zeros((cap.n_groups, cap.c_in // 16, 16, 16), dtype=torch.float32, device=w.device)
     cnt = torch.zeros(cap.n_groups, dtype=torch.int64, device=w.device)
-    rb = lh.lh_hessian_ragged_workspace_bytes(cap.c_in, xr.shape[0], cap.n_groups)
+    largest = int((cap.offsets[1:] - cap.offsets[:-1]).max())   # known where the tokens were routed
+    rb = lh.lh_hessian_ragged_workspace_bytes(cap.c_in, xr.shape[0], cap.n_groups, largest)
     rws = torch.empty(max(rb, 1), dtype=torch.uint8, device=w.device)
-    fn = (lambda: lh.lh_accumulate_hessian_ragged(xr, off, h=hr, counts=cnt, workspace=rws if rb else None))
+    fn = (lambda: lh.lh_accumulate_hessian_ragged(xr, off, h=hr, counts=cnt, workspace=rws if rb else None,
+                                                  max_group_rows=largest))
     fn()
     warm = timed(fn, stream, 15)
     launch_ms = graph_time(fn)

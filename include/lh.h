@@ -151,9 +151,10 @@ lh_status lh_accumulate_hessian(const void *x, int x_dtype, int layout, int64_t 
 /*
  * Scratch bytes lh_accumulate_hessian_ragged can use for its deterministic
  * split of each group's rows (0 = it runs one pass per block).  Depends only
- * on the arguments.
+ * on the arguments (max_group_rows as passed to the accumulation).
  */
-size_t lh_hessian_ragged_workspace_bytes(int64_t c_in, int64_t n_rows, int64_t n_groups);
+size_t lh_hessian_ragged_workspace_bytes(int64_t c_in, int64_t n_rows, int64_t n_groups,
+                                         int64_t max_group_rows);
 
 /*
  * Ragged / streaming local Hessians ("Entry API and calibration flow",
@@ -178,17 +179,23 @@ size_t lh_hessian_ragged_workspace_bytes(int64_t c_in, int64_t n_rows, int64_t n
  *                 no offset can make the kernels read outside x.
  *   h             fp32 [n_groups][c_in/16][16][16], group stride
  *                 group_stride_h (>= (c_in/16)*256 when n_groups > 1).
+ *   max_group_rows  host-side bound on any group's row count, or 0 if
+ *                 unknown.  It only shapes the work split (with it, the rows
+ *                 of the largest group spread over many workgroups in 1024-row
+ *                 slices; without it, the split follows the average group);
+ *                 results are correct whatever it is.
  *   token_counts  NULL, or device int64 [n_groups] (8-byte aligned), read
  *                 and updated on the stream.
  *   workspace     NULL/0, or at least lh_hessian_ragged_workspace_bytes(c_in,
- *                 n_rows, n_groups) bytes (4-byte aligned).
+ *                 n_rows, n_groups, max_group_rows) bytes (4-byte aligned).
  * Results are deterministic (fixed reduction order).
  * Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_WORKSPACE,
  * LH_ERR_ARG, LH_ERR_HIP.
  */
 lh_status lh_accumulate_hessian_ragged(const void *x, int x_dtype, int64_t c_in, int64_t ld_x,
                                        int64_t n_rows, const int64_t *token_offsets,
-                                       int64_t n_groups, float *h, int64_t group_stride_h,
+                                       int64_t n_groups, int64_t max_group_rows, float *h,
+                                       int64_t group_stride_h,
                                        int64_t *token_counts, void *workspace,
                                        size_t workspace_bytes, void *stream);
 

@@ -52,9 +52,9 @@ def _load() -> ctypes.CDLL:
     lib.lh_hessian_workspace_bytes.restype = SZ
     lib.lh_accumulate_hessian.argtypes = [P, I, I, I64, I64, I64, I64, I64, F, F, P, I64, P, SZ, P]
     lib.lh_accumulate_hessian.restype = I
-    lib.lh_hessian_ragged_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.lh_hessian_ragged_workspace_bytes.argtypes = [I64, I64, I64, I64]
     lib.lh_hessian_ragged_workspace_bytes.restype = SZ
-    lib.lh_accumulate_hessian_ragged.argtypes = [P, I, I64, I64, I64, P, I64, P, I64, P, P, SZ, P]
+    lib.lh_accumulate_hessian_ragged.argtypes = [P, I, I64, I64, I64, P, I64, I64, P, I64, P, P, SZ, P]
     lib.lh_accumulate_hessian_ragged.restype = I
     lib.lh_sweep_workspace_bytes.argtypes = [I64, I64]
     lib.lh_sweep_workspace_bytes.restype = SZ
@@ -196,13 +196,14 @@ def lh_accumulate_hessian(x: torch.Tensor, layout: str = "channel", alpha: float
     return h
 
 
-def lh_hessian_ragged_workspace_bytes(c_in: int, n_rows: int, n_groups: int) -> int:
-    return int(lib.lh_hessian_ragged_workspace_bytes(c_in, n_rows, n_groups))
+def lh_hessian_ragged_workspace_bytes(c_in: int, n_rows: int, n_groups: int, max_group_rows: int = 0) -> int:
+    return int(lib.lh_hessian_ragged_workspace_bytes(c_in, n_rows, n_groups, max_group_rows))
 
 
 def lh_accumulate_hessian_ragged(x: torch.Tensor, offsets: torch.Tensor, h: torch.Tensor | None = None,
                                  counts: torch.Tensor | None = None,
-                                 workspace: torch.Tensor | bool | None = True) -> torch.Tensor:
+                                 workspace: torch.Tensor | bool | None = True,
+                                 max_group_rows: int = 0) -> torch.Tensor:
     """Per-group Hessians of token-major x [n_rows, c_in] whose rows
     offsets[g] .. offsets[g+1]-1 (device int64 [n_groups + 1]) belong to
     group g.  Without counts each group with tokens gets S_g / n_g; with a
@@ -221,14 +222,15 @@ def lh_accumulate_hessian_ragged(x: torch.Tensor, offsets: torch.Tensor, h: torc
         h = torch.zeros((g, nb, BLOCK, BLOCK), dtype=torch.float32, device=x.device)
     ws, ws_bytes = None, 0
     if workspace is True:
-        ws_bytes = lh_hessian_ragged_workspace_bytes(c_in, n_rows, g)
+        ws_bytes = lh_hessian_ragged_workspace_bytes(c_in, n_rows, g, max_group_rows)
         if ws_bytes:
             ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
     elif isinstance(workspace, torch.Tensor):
         ws, ws_bytes = workspace, workspace.numel() * workspace.element_size()
     h_gstride = h.stride(0) if h.dim() == 4 and h.shape[0] > 1 else 0
     ld = x.stride(0) if n_rows > 1 else c_in
-    _check(lib.lh_accumulate_hessian_ragged(_ptr(x), _dtype(x), c_in, ld, n_rows, _ptr(offsets), g, _ptr(h),
+    _check(lib.lh_accumulate_hessian_ragged(_ptr(x), _dtype(x), c_in, ld, n_rows, _ptr(offsets), g,
+                                            int(max_group_rows), _ptr(h),
                                             h_gstride, _ptr(counts), _ptr(ws), ws_bytes, _stream(x)))
     return h
 

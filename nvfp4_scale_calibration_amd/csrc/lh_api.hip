@@ -106,19 +106,19 @@ lh_status lh_accumulate_hessian(const void* x, int x_dtype, int layout, int64_t 
   return e == hipSuccess ? LH_OK : hip_fail(e, fn);
 }
 
-size_t lh_hessian_ragged_workspace_bytes(int64_t c_in, int64_t n_rows, int64_t n_groups) {
-  if (c_in <= 0 || n_rows <= 0 || n_groups <= 0 || c_in % 16 != 0) return 0;
-  return lh::hessian_ragged_ws_bytes(c_in, n_rows, n_groups);
+size_t lh_hessian_ragged_workspace_bytes(int64_t c_in, int64_t n_rows, int64_t n_groups, int64_t max_group_rows) {
+  if (c_in <= 0 || n_rows <= 0 || n_groups <= 0 || c_in % 16 != 0 || max_group_rows < 0) return 0;
+  return lh::hessian_ragged_ws_bytes(c_in, n_rows, n_groups, max_group_rows);
 }
 
 lh_status lh_accumulate_hessian_ragged(const void* x, int x_dtype, int64_t c_in, int64_t ld_x, int64_t n_rows,
-                                       const int64_t* token_offsets, int64_t n_groups, float* h,
-                                       int64_t group_stride_h, int64_t* token_counts, void* workspace,
+                                       const int64_t* token_offsets, int64_t n_groups, int64_t max_group_rows,
+                                       float* h, int64_t group_stride_h, int64_t* token_counts, void* workspace,
                                        size_t workspace_bytes, void* stream) {
   const char* fn = "lh_accumulate_hessian_ragged";
   g_msg[0] = '\0';
   if (!valid_dtype(x_dtype)) return fail(LH_ERR_DTYPE, "%s: x_dtype must be 0 (f32) or 1 (bf16)", fn);
-  if (c_in < 0 || n_rows < 0 || n_groups < 0 || group_stride_h < 0)
+  if (c_in < 0 || n_rows < 0 || n_groups < 0 || group_stride_h < 0 || max_group_rows < 0)
     return fail(LH_ERR_SHAPE, "%s: negative size or stride", fn);
   if (c_in % 16 != 0) return fail(LH_ERR_SHAPE, "%s: c_in must be a multiple of 16", fn);
   if (ld_x < c_in || ld_x < 1) return fail(LH_ERR_SHAPE, "%s: ld_x < c_in", fn);
@@ -134,13 +134,13 @@ lh_status lh_accumulate_hessian_ragged(const void* x, int x_dtype, int64_t c_in,
       !aligned(token_counts, 8))
     return fail(LH_ERR_ARG, "%s: pointer not aligned to its element size", fn);
   if (workspace != nullptr && workspace_bytes > 0 && work) {
-    const size_t need = lh::hessian_ragged_ws_bytes(c_in, n_rows, n_groups);
+    const size_t need = lh::hessian_ragged_ws_bytes(c_in, n_rows, n_groups, max_group_rows);
     if (workspace_bytes < need)
       return fail(LH_ERR_WORKSPACE, "%s: workspace smaller than lh_hessian_ragged_workspace_bytes()", fn);
   }
   if (!work) return LH_OK;
   lh::HessianRaggedArgs a{x, x_dtype, c_in, ld_x, n_rows, token_offsets, n_groups, h, group_stride_h,
-                          token_counts, workspace, workspace_bytes};
+                          token_counts, max_group_rows, workspace, workspace_bytes};
   hipError_t e = lh::launch_hessian_ragged(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LH_OK : hip_fail(e, fn);
 }

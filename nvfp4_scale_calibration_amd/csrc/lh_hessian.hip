@@ -31,6 +31,7 @@ namespace {
 
 constexpr int kSlab = 64;                 // tokens per wave per step
 constexpr int kRound = kSlab * 4;         // tokens per workgroup per step
+constexpr int64_t kRaggedSlice = 1024;    // rows per ragged slice when the largest group is known
 
 // Sixteen token values of one channel, in the lane's register layout.
 template <typename T>
@@ -178,6 +179,16 @@ __device__ __forceinline__ void ragged_store(float* hp, float v, int64_t n_g, co
   }
 }
 
+// Rows per slice of a group of n_g rows split nsplit ways: an even split, or
+// fixed slices of slice_rows where those cover the group (the plan sizes
+// nsplit for the largest group); whole multiples of 256 rows.  Slice s holds
+// rows [s per, (s + 1) per); the group uses ceil(n_g / per) slices.
+__device__ __forceinline__ int64_t ragged_per(int64_t n_g, int64_t nsplit, int64_t slice_rows) {
+  int64_t per = (n_g + nsplit - 1) / nsplit;
+  if (slice_rows > per) per = slice_rows;
+  return (per + kRound - 1) / kRound * kRound;
+}
+
 // ---------------------------------------------------------------------------
 // Token-major kernel: x[t * ld + c].  A workgroup owns four consecutive
 // blocks (64 channels: one 128-byte bf16 row segment per token) and a slice
@@ -267,7 +278,8 @@ __global__ __launch_bounds__(kThreads) void hessian_tm_kernel(const T* __restric
                                                               int64_t n_tok, int64_t n_rows,
                                                               const int64_t* __restrict__ offsets, int64_t c_in,
                                                               int64_t nb, int64_t n_groups, int64_t nsplit,
-                                                              int64_t chunk, float alpha, float beta,
+                                                              int64_t chunk, int64_t slice_rows, float alpha,
+                                                              float beta,
                                                               float* __restrict__ h, int64_t h_gstride,
                                                               const int64_t* __restrict__ counts,
                                                               float* __restrict__ ws) {
@@ -284,9 +296,10 @@ __global__ __launch_bounds__(kThreads) void hessian_tm_kernel(const T* __restric
   const T* seg;
   if constexpr (kRagged) {
     ragged_range(offsets, grp, n_rows, r0, r1);
-    // slice s of the group's rows: whole rounds
-    const int64_t per = ((r1 - r0 + nsplit - 1) / nsplit + S::kTok - 1) / S::kTok * S::kTok;
-    t0 = min(r1, r0 + s * per);
+    const int64_t per = ragged_per(r1 - r0, nsplit, slice_rows);
+    t0 = r0 + s * per;
+    if (nsplit > 1 && t0 >= r1) return;  // unused slice: the finalize kernel skips it (whole workgroup)
+    t0 = min(r1, t0);
     t1 = min(r1, t0 + per);
     seg = x + 64 * q;
   } else {
@@ -300,18 +313,27 @@ __global__ __launch_bounds__(kThreads) void hessian_tm_kernel(const T* __restric
 
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
   const int64_t rounds = t1 > t0 ? (t1 - t0 + S::kTok - 1) / S::kTok : 0;
-  TmLoader<T, kVec> ld_regs;
+  // Two register sets keep the loads of the next two rounds in flight while a
+  // round is multiplied (twice the bytes in flight of one set, no more LDS).
+  TmLoader<T, kVec> ra, rb;
   if (rounds > 0) {
-    ld_regs.load(seg, ld, t0, t1, crow, ccol, col_ok);
-    ld_regs.store(tile[0], crow, ccol);
+    ra.load(seg, ld, t0, t1, crow, ccol, col_ok);
+    ra.store(tile[0], crow, ccol);
   }
+  if (rounds > 1) ra.load(seg, ld, t0 + S::kTok, t1, crow, ccol, col_ok);
+  if (rounds > 2) rb.load(seg, ld, t0 + 2 * S::kTok, t1, crow, ccol, col_ok);
   __syncthreads();
-  for (int64_t r = 0; r < rounds; ++r) {
-    const int buf = (int)(r & 1);
-    const bool more = r + 1 < rounds;
-    if (more) ld_regs.load(seg, ld, t0 + (r + 1) * S::kTok, t1, crow, ccol, col_ok);
-    acc = tile_mfma<T>(tile[buf], wave, lane, acc);
-    if (more) ld_regs.store(tile[buf ^ 1], crow, ccol);
+  for (int64_t r = 0; r < rounds; r += 2) {
+    // even round r: tile[0]; ra holds round r+1, rb round r+2
+    acc = tile_mfma<T>(tile[0], wave, lane, acc);
+    if (r + 1 < rounds) ra.store(tile[1], crow, ccol);
+    if (r + 3 < rounds) ra.load(seg, ld, t0 + (r + 3) * S::kTok, t1, crow, ccol, col_ok);
+    __syncthreads();
+    if (r + 1 >= rounds) break;
+    // odd round r+1: tile[1]; rb holds round r+2, ra round r+3
+    acc = tile_mfma<T>(tile[1], wave, lane, acc);
+    if (r + 2 < rounds) rb.store(tile[0], crow, ccol);
+    if (r + 4 < rounds) rb.load(seg, ld, t0 + (r + 4) * S::kTok, t1, crow, ccol, col_ok);
     __syncthreads();
   }
 
@@ -350,16 +372,19 @@ __device__ __forceinline__ float sum_slices(const float* __restrict__ p, int64_t
 }
 
 __global__ __launch_bounds__(kThreads) void hessian_ragged_finalize_kernel(
-    const float* __restrict__ ws, int64_t nsplit, int64_t n_groups, int64_t nb, int64_t n_rows,
+    const float* __restrict__ ws, int64_t nsplit, int64_t slice_rows, int64_t n_groups, int64_t nb, int64_t n_rows,
     const int64_t* __restrict__ offsets, const int64_t* __restrict__ counts, float* __restrict__ h,
     int64_t h_gstride) {
   const int64_t blk = blockIdx.x;  // grp * nb + b
   const int64_t grp = blk / nb, b = blk % nb;
   const int e = threadIdx.x;
-  const float v = sum_slices(ws + blk * 256 + e, n_groups * nb * 256, nsplit);
   int64_t r0, r1;
   ragged_range(offsets, grp, n_rows, r0, r1);
-  ragged_store(h + grp * h_gstride + b * 256 + e, v, r1 - r0, counts, grp);
+  const int64_t n_g = r1 - r0;
+  const int64_t per = ragged_per(n_g, nsplit, slice_rows);
+  const int64_t used = n_g > 0 ? (n_g + per - 1) / per : 0;  // slices the group wrote, in order
+  const float v = used > 0 ? sum_slices(ws + blk * 256 + e, n_groups * nb * 256, used) : 0.0f;
+  ragged_store(h + grp * h_gstride + b * 256 + e, v, n_g, counts, grp);
 }
 
 // counts[g] += n_g, after every block of the group has read the old count.
@@ -409,7 +434,7 @@ hipError_t launch_typed(const HessianArgs& a, const HessianPlan& p, hipStream_t 
   } else {
     const int64_t grid = a.n_groups * ((nb + 3) / 4) * p.nsplit;
     hessian_tm_kernel<T, kVec, false><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
-        x, a.ld, a.gstride, a.n_tok, 0, nullptr, a.c_in, nb, a.n_groups, p.nsplit, p.chunk, a.alpha, a.beta,
+        x, a.ld, a.gstride, a.n_tok, 0, nullptr, a.c_in, nb, a.n_groups, p.nsplit, p.chunk, 0, a.alpha, a.beta,
         a.h, a.h_gstride, nullptr, ws);
   }
   hipError_t err = hipGetLastError();
@@ -420,18 +445,19 @@ hipError_t launch_typed(const HessianArgs& a, const HessianPlan& p, hipStream_t 
 }
 
 template <typename T, bool kVec>
-hipError_t launch_ragged_typed(const HessianRaggedArgs& a, int64_t nsplit, hipStream_t stream) {
+hipError_t launch_ragged_typed(const HessianRaggedArgs& a, const RaggedPlan& p, hipStream_t stream) {
   const int64_t nb = a.c_in / 16;
+  const int64_t nsplit = p.nsplit;
   const int64_t grid = a.n_groups * ((nb + 3) / 4) * nsplit;
   float* ws = nsplit > 1 ? static_cast<float*>(a.ws) : nullptr;
   hessian_tm_kernel<T, kVec, true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
-      static_cast<const T*>(a.x), a.ld, 0, 0, a.n_rows, a.offsets, a.c_in, nb, a.n_groups, nsplit, 0, 1.0f, 0.0f,
-      a.h, a.h_gstride, a.counts, ws);
+      static_cast<const T*>(a.x), a.ld, 0, 0, a.n_rows, a.offsets, a.c_in, nb, a.n_groups, nsplit, 0, p.slice_rows,
+      1.0f, 0.0f, a.h, a.h_gstride, a.counts, ws);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (nsplit > 1) {
     hessian_ragged_finalize_kernel<<<dim3((unsigned)(a.n_groups * nb)), dim3(kThreads), 0, stream>>>(
-        ws, nsplit, a.n_groups, nb, a.n_rows, a.offsets, a.counts, a.h, a.h_gstride);
+        ws, nsplit, p.slice_rows, a.n_groups, nb, a.n_rows, a.offsets, a.counts, a.h, a.h_gstride);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -457,31 +483,46 @@ int64_t tm_nsplit(int64_t c_in, int64_t tokens_per_group, int64_t n_groups) {
 
 }  // namespace
 
-// Ragged slices per group, planned from the average rows per group (the
-// per-group counts live on the device).
-int64_t hessian_ragged_nsplit(int64_t c_in, int64_t n_rows, int64_t n_groups, bool have_ws) {
-  if (!have_ws || n_groups <= 0 || c_in < 16) return 1;
-  return tm_nsplit(c_in, n_rows / n_groups, n_groups);
+// Ragged slices.  The per-group counts live on the device, so the plan uses
+// what the host knows: with a bound on the largest group, fixed 1024-row
+// slices (the largest group gets all the workgroups it can use and unused
+// slices of smaller groups exit at once); otherwise an even split planned
+// from the average rows per group.
+RaggedPlan hessian_ragged_plan(int64_t c_in, int64_t n_rows, int64_t n_groups, int64_t max_group_rows,
+                               bool have_ws) {
+  RaggedPlan p{1, 0};
+  if (!have_ws || n_groups <= 0 || c_in < 16) return p;
+  if (max_group_rows > 0) {
+    int64_t ns = (max_group_rows + kRaggedSlice - 1) / kRaggedSlice;
+    if (ns > 64) ns = 64;
+    if (ns > 1) {
+      p.nsplit = ns;
+      p.slice_rows = kRaggedSlice;
+    }
+    return p;
+  }
+  p.nsplit = tm_nsplit(c_in, n_rows / n_groups, n_groups);
+  return p;
 }
 
-size_t hessian_ragged_ws_bytes(int64_t c_in, int64_t n_rows, int64_t n_groups) {
-  const int64_t ns = hessian_ragged_nsplit(c_in, n_rows, n_groups, true);
-  if (ns <= 1) return 0;
-  return (size_t)ns * (size_t)n_groups * (size_t)(c_in / 16) * 256u * sizeof(float);
+size_t hessian_ragged_ws_bytes(int64_t c_in, int64_t n_rows, int64_t n_groups, int64_t max_group_rows) {
+  const RaggedPlan p = hessian_ragged_plan(c_in, n_rows, n_groups, max_group_rows, true);
+  if (p.nsplit <= 1) return 0;
+  return (size_t)p.nsplit * (size_t)n_groups * (size_t)(c_in / 16) * 256u * sizeof(float);
 }
 
 hipError_t launch_hessian_ragged(const HessianRaggedArgs& a, hipStream_t stream) {
   const int64_t nb = a.c_in / 16;
   if (a.n_groups == 0 || nb == 0) return hipSuccess;
-  const size_t need = hessian_ragged_ws_bytes(a.c_in, a.n_rows, a.n_groups);
+  const size_t need = hessian_ragged_ws_bytes(a.c_in, a.n_rows, a.n_groups, a.max_group_rows);
   const bool have_ws = a.ws != nullptr && need > 0 && a.ws_bytes >= need;
-  const int64_t nsplit = hessian_ragged_nsplit(a.c_in, a.n_rows, a.n_groups, have_ws);
+  const RaggedPlan p = hessian_ragged_plan(a.c_in, a.n_rows, a.n_groups, a.max_group_rows, have_ws);
   const int64_t epv = a.dtype == 1 ? 8 : 4;
   const bool aligned = (reinterpret_cast<uintptr_t>(a.x) % 16 == 0) && (a.ld % epv == 0);
   if (a.dtype == 1)
-    return aligned ? launch_ragged_typed<uint16_t, true>(a, nsplit, stream)
-                   : launch_ragged_typed<uint16_t, false>(a, nsplit, stream);
-  return aligned ? launch_ragged_typed<float, true>(a, nsplit, stream) : launch_ragged_typed<float, false>(a, nsplit, stream);
+    return aligned ? launch_ragged_typed<uint16_t, true>(a, p, stream)
+                   : launch_ragged_typed<uint16_t, false>(a, p, stream);
+  return aligned ? launch_ragged_typed<float, true>(a, p, stream) : launch_ragged_typed<float, false>(a, p, stream);
 }
 
 // Token slices per block.  Channel-major, measured on MI355X (17408 x 16384

@@ -39,11 +39,17 @@ struct HessianRaggedArgs {
   float* h;
   int64_t h_gstride;
   int64_t* counts;        // nullable device [n_groups]: running mean
+  int64_t max_group_rows; // host bound on any group's rows (0: unknown)
   void* ws;               // nullable
   size_t ws_bytes;
 };
-int64_t hessian_ragged_nsplit(int64_t c_in, int64_t n_rows, int64_t n_groups, bool have_ws);
-size_t hessian_ragged_ws_bytes(int64_t c_in, int64_t n_rows, int64_t n_groups);
+struct RaggedPlan {
+  int64_t nsplit;
+  int64_t slice_rows;     // 0: even split per group
+};
+RaggedPlan hessian_ragged_plan(int64_t c_in, int64_t n_rows, int64_t n_groups, int64_t max_group_rows,
+                               bool have_ws);
+size_t hessian_ragged_ws_bytes(int64_t c_in, int64_t n_rows, int64_t n_groups, int64_t max_group_rows);
 hipError_t launch_hessian_ragged(const HessianRaggedArgs& a, hipStream_t stream);
 
 struct SweepArgs {

@@ -171,13 +171,13 @@ def test_select_validation(lib):
 
 def test_ragged_hessian_validation(lib):
     P = ctypes.c_void_p
-    ok = dict(x=P(FAKE), dt=1, c_in=32, ld=32, rows=100, off=P(FAKE), g=3, h=P(FAKE), hs=512, cnt=None,
+    ok = dict(x=P(FAKE), dt=1, c_in=32, ld=32, rows=100, off=P(FAKE), g=3, mx=0, h=P(FAKE), hs=512, cnt=None,
               ws=None, wsb=0, st=None)
 
     def call(**kw):
         a = dict(ok, **kw)
         return lib.lh_accumulate_hessian_ragged(a["x"], a["dt"], a["c_in"], a["ld"], a["rows"], a["off"], a["g"],
-                                                a["h"], a["hs"], a["cnt"], a["ws"], a["wsb"], a["st"])
+                                                a["mx"], a["h"], a["hs"], a["cnt"], a["ws"], a["wsb"], a["st"])
 
     assert call(dt=3) == DTYPE
     assert call(c_in=40) == SHAPE
@@ -190,8 +190,12 @@ def test_ragged_hessian_validation(lib):
     assert call(off=P(FAKE + 4)) == ARG          # int64 offsets need 8-byte alignment
     assert call(cnt=P(FAKE + 4)) == ARG
     assert call(ws=None, wsb=8) == NULL
-    big = lib.lh_hessian_ragged_workspace_bytes(4096, 1 << 16, 2)
+    assert call(mx=-1) == SHAPE
+    big = lib.lh_hessian_ragged_workspace_bytes(4096, 1 << 16, 2, 0)
     assert big > 0 and big % (256 * 4) == 0
     assert call(c_in=4096, ld=4096, rows=1 << 16, g=2, hs=256 * 256, ws=P(FAKE), wsb=big - 4) == WORKSPACE
-    assert lib.lh_hessian_ragged_workspace_bytes(2048, 32768, 64) == 0   # ~512 rows per group: one pass
+    assert lib.lh_hessian_ragged_workspace_bytes(2048, 32768, 64, 0) == 0   # ~512 rows per group: one pass
+    # a known largest group (4230 rows): five 1024-row slices per group
+    assert lib.lh_hessian_ragged_workspace_bytes(2048, 32768, 64, 4230) == 5 * 64 * 128 * 256 * 4
+    assert lib.lh_hessian_ragged_workspace_bytes(2048, 32768, 64, 1000) == 0
     assert call(g=0) == OK and call(c_in=0) == OK

@@ -23,14 +23,14 @@ def lh():
     return m
 
 
-def run(lh, cap, h0, counts=None, workspace=True, ld_pad=0):
+def run(lh, cap, h0, counts=None, workspace=True, ld_pad=0, max_group_rows=0):
     xd = cap.x.to(DEV)
     if ld_pad:  # rows padded in memory: a view with row stride c_in + ld_pad
         xd = torch.cat([xd, torch.zeros((xd.shape[0], ld_pad), dtype=xd.dtype, device=DEV)], 1)[:, :cap.c_in]
     off = torch.from_numpy(cap.offsets).to(DEV)
     h = torch.from_numpy(h0.copy()).to(DEV)
     cnt = None if counts is None else torch.from_numpy(counts.copy()).to(DEV)
-    lh.lh_accumulate_hessian_ragged(xd, off, h=h, counts=cnt, workspace=workspace)
+    lh.lh_accumulate_hessian_ragged(xd, off, h=h, counts=cnt, workspace=workspace, max_group_rows=max_group_rows)
     torch.cuda.synchronize()
     return h.cpu().numpy(), (None if cnt is None else cnt.cpu().numpy())
 
@@ -109,8 +109,27 @@ def test_ragged_moe_capture_full_size_sampled(lh):
     G, nb = cap.n_groups, cap.c_in // 16
     print("case ragged MoE capture rows=%d" % cap.x.shape[0], flush=True)
     h0 = np.zeros((G, nb, 16, 16), np.float32)
-    h, _ = run(lh, cap, h0)
+    h, _ = run(lh, cap, h0, max_group_rows=int(np.diff(cap.offsets).max()))  # as the benchmark runs it
     rng = np.random.default_rng(0)
     heavy = int(np.argmax(np.diff(cap.offsets)))
     sel = np.unique(np.concatenate([rng.choice(G * nb, 40, replace=False), heavy * nb + np.arange(4)]))
     check(cap, h, h0, sel=sel, what="moe-capture")
+
+
+@pytest.mark.parametrize("hint", ["exact", "too small", "none"])
+def test_ragged_largest_group_hint(lh, hint):
+    """With a bound on the largest group the rows are cut into 1024-row
+    slices (unused slices skipped by the finalize kernel); a bound that is
+    too small only changes the split.  Results match the oracle either way
+    and reruns are bit-identical."""
+    cap = wl.make_ragged(12, 128, 20000, dtype="bf16", seed=77, concentration=0.2, n_empty=3)
+    largest = int(np.diff(cap.offsets).max())
+    mx = {"exact": largest, "too small": max(1, largest // 5), "none": 0}[hint]
+    print("case ragged hint=%s largest=%d max_group_rows=%d" % (hint, largest, mx), flush=True)
+    h0 = np.full((12, 8, 16, 16), 2.0, np.float32)
+    counts = np.arange(12, dtype=np.int64) * 7      # running mean on top of earlier batches
+    a, ca = run(lh, cap, h0, counts=counts, max_group_rows=mx)
+    b, cb = run(lh, cap, h0, counts=counts, max_group_rows=mx)
+    assert np.array_equal(a, b) and np.array_equal(ca, cb)
+    want = check(cap, a, h0, counts=counts, what="hint %s" % hint)
+    np.testing.assert_array_equal(ca, want)
