@@ -93,6 +93,41 @@ def traffic_from_profiles(kernel: str, workload: str, src_hash: str):
     return ent.get("bytes_per_launch")
 
 
+def valu_from_profiles(workload: str, src_hash: str):
+    """The sweep kernel's executed VALU issue fraction from the committed
+    rocprofv3 counter summary (SQ_INSTS_VALU), if taken on these sources."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("sweep/%s" % workload, {}).get("source_hash") != src_hash:
+        return None
+    return data.get("valu", {}).get(workload)
+
+
+def copy_gbps(device) -> float:
+    """Bandwidth of a plain 256 MiB device copy (read + write), for the
+    'fraction of a measured copy' figures."""
+    import torch
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device=device).fill_(1)
+    b = torch.empty_like(a)
+    t = graph_time(lambda: b.copy_(a), reps=5)
+    return 2 * n / (t / 1e3) / 1e9
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def timed(fn, stream, reps: int, before=None):
     """Per-rep durations (ms) of fn() with HIP events on `stream`; before()
     runs outside the bracket."""
@@ -301,7 +336,7 @@ def cpu_baseline(work, budget_s: float) -> dict:
     blocks = G * c_out * nb
     step_s = t_amax + t_hess_total + ts / len(ssel) * blocks
     return {
-        "value": blocks / step_s, "unit": "blocks/s", "cores": threads, "kind": "oracle",
+        "value": blocks / step_s, "unit": "blocks/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
         "sample": "Hessians of %d of %d input blocks (all %d tokens) + sweep and fake-quant of the first %d of "
                   "%d blocks, per-unit times scaled to the whole step; global amax over the full tensor"
                   % (len(sel), G * nb, n, len(ssel), blocks),
@@ -389,6 +424,10 @@ def main():
     achieved_tflops = SWEEP_FLOP_PER_BLOCK * blocks / sweep_s / 1e12
     src_hash = kernel_source_hash()
     traffic = traffic_from_profiles("sweep", wl.SHORT_NAMES[args.workload], src_hash)
+    valu = valu_from_profiles(wl.SHORT_NAMES[args.workload], src_hash)
+    copy_bw = copy_gbps(dev)
+    # fake-quant: W + indices read, Q + nibbles + codes written (algorithmic bytes)
+    fq_bytes = work.w.numel() * work.w.element_size() + blocks + blocks * 16 * 4 + blocks * 8 + blocks
     out = {
         "metric": METRIC,
         "value": blocks / (ms_per_step / 1e3),
@@ -409,10 +448,15 @@ def main():
         "kernels_ms": per_kernel_ms,
         "launch_ms": launch_ms,
         "sweep": {"blocks_per_s": blocks / sweep_s, "tflops": achieved_tflops,
-                  "frac_nonpacked_fp32": achieved_tflops / FP32_NONPACKED_TFLOPS},
+                  "frac_nonpacked_fp32": achieved_tflops / FP32_NONPACKED_TFLOPS,
+                  "valu_issue_frac": None if valu is None else valu["issue_frac"],
+                  "valu_instr_per_block": None if valu is None else valu["valu_instr_per_block"]},
+        "fake_quant": {"gbps": fq_bytes / (launch_ms["fake_quant"] / 1e3) / 1e9, "bytes": fq_bytes},
+        "copy_gbps": copy_bw,
         "hessian": {"gbps": work.x_bytes / hess_s / 1e9, "frac_hbm": work.x_bytes / hess_s / 1e9 / HBM_PEAK_GBPS,
                     "launch_gbps": work.x_bytes / (launch_ms["hessian"] / 1e3) / 1e9,
                     "launch_frac_hbm": work.x_bytes / (launch_ms["hessian"] / 1e3) / 1e9 / HBM_PEAK_GBPS,
+                    "launch_frac_copy": work.x_bytes / (launch_ms["hessian"] / 1e3) / 1e9 / copy_bw,
                     "x_bytes": work.x_bytes, "warm": True},
         "source_hash": src_hash,
     }
