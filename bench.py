@@ -2,12 +2,12 @@
 """Benchmark of the Local-Hessian NVFP4 calibration hot path on one MI355X.
 
 One step = the whole path over one layer's synthetic inputs, inputs resident
-in HBM: global amax -> local Hessians -> 126-candidate scale sweep ->
-NVFP4 fake-quant (dequantised fp32 weights + packed E2M1 nibbles + E4M3
-scale codes).  W warm-up steps, then K timed steps between device
-synchronisations; every kernel is also timed with HIP events recorded on the
-stream it is launched on (the current torch stream, which the binding
-passes to the library).
+in HBM: global amax -> local Hessians -> 126-candidate scale sweep and
+NVFP4 fake-quant of its result (dequantised fp32 weights + packed E2M1
+nibbles + E4M3 scale codes + S_g) in one call.  W warm-up steps, then K
+timed steps between device synchronisations; every call is also timed with
+HIP events recorded on the stream it is launched on (the current torch
+stream, which the binding passes to the library).
 
 Prints ONE JSON line.  value = NVFP4 blocks scale-swept per second over the
 whole step; the line also carries the Hessian pass in GB/s, the sweep in
@@ -382,7 +382,7 @@ def main():
     codes = torch.empty((G, c_out, nb), dtype=torch.uint8, device=dev)
     gscale = torch.empty(G, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    names = ("absmax", "hessian", "sweep", "fake_quant")
+    names = ("absmax", "hessian", "sweep_fake_quant")
 
     def step(ev=None):
         def mark(i):
@@ -393,15 +393,14 @@ def main():
         mark(1)
         lh.lh_accumulate_hessian(x, h=h, workspace=ws if ws_bytes else None)
         mark(2)
-        lh.lh_scale_sweep(w, h, amax, best_idx=idx, best_err=err, best_amax=bam, workspace=sws)
+        lh.lh_scale_sweep_fake_quant(w, h, amax, best_idx=idx, best_err=err, best_amax=bam, w_q=wq, packed=packed,
+                                     scale_e4m3=codes, global_scale=gscale, workspace=sws)
         mark(3)
-        lh.lh_fake_quant_nvfp4(w, idx, amax, w_q=wq, packed=packed, scale_e4m3=codes, global_scale=gscale)
-        mark(4)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -410,16 +409,20 @@ def main():
     wall = time.perf_counter() - t0
     per_kernel_ms = {nm: sum(e[i].elapsed_time(e[i + 1]) for e in events) / args.steps for i, nm in enumerate(names)}
     # per-launch GPU time of each call, free of host launch overhead
+    # (the sweep and the fake-quant also as two separate calls, for comparison)
     launch_ms = {
         "absmax": graph_time(lambda: lh.lh_absmax(w, out=amax)),
         "hessian": graph_time(lambda: lh.lh_accumulate_hessian(x, h=h, workspace=ws if ws_bytes else None)),
+        "sweep_fake_quant": graph_time(lambda: lh.lh_scale_sweep_fake_quant(
+            w, h, amax, best_idx=idx, best_err=err, best_amax=bam, w_q=wq, packed=packed, scale_e4m3=codes,
+            global_scale=gscale, workspace=sws), reps=5),
         "sweep": graph_time(lambda: lh.lh_scale_sweep(w, h, amax, best_idx=idx, best_err=err, best_amax=bam,
                                                       workspace=sws), reps=5),
         "fake_quant": graph_time(lambda: lh.lh_fake_quant_nvfp4(w, idx, amax, w_q=wq, packed=packed,
                                                                 scale_e4m3=codes, global_scale=gscale)),
     }
     ms_per_step = wall * 1e3 / args.steps
-    sweep_s = per_kernel_ms["sweep"] / 1e3
+    sweep_s = per_kernel_ms["sweep_fake_quant"] / 1e3
     hess_s = per_kernel_ms["hessian"] / 1e3
     achieved_tflops = SWEEP_FLOP_PER_BLOCK * blocks / sweep_s / 1e12
     src_hash = kernel_source_hash()

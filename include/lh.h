@@ -243,6 +243,29 @@ lh_status lh_scale_sweep(const void *w, int w_dtype, int64_t c_out, int64_t c_in
                          size_t workspace_bytes, void *stream);
 
 /*
+ * The sweep and the fake-quant with its result in one pass ("Algorithm
+ * principle": the candidate scales are bit-consistent with fake-quant, and
+ * Q(W, s) = Cast(W / s) * s is the path's end product).  Writes exactly what
+ * lh_scale_sweep followed by lh_fake_quant_nvfp4 with the chosen indices
+ * writes, from one sweep launch that also emits the quantised blocks (each
+ * lane quantises the rows it has just swept, so the weights are read again
+ * from cache rather than by a second pass over the layer).
+ *   Arguments up to workspace_bytes: as lh_scale_sweep (best_idx required).
+ *   w_q, packed_e2m1, scale_e4m3, global_scale: as lh_fake_quant_nvfp4
+ *             (dense layouts, each optional; w_q 16-byte aligned,
+ *             packed_e2m1 8-byte aligned).
+ * Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_WORKSPACE,
+ * LH_ERR_ARG, LH_ERR_HIP.
+ */
+lh_status lh_scale_sweep_fake_quant(const void *w, int w_dtype, int64_t c_out, int64_t c_in,
+                                    int64_t ld_w, int64_t n_groups, int64_t group_stride_w,
+                                    const float *h, int64_t group_stride_h, const float *amax,
+                                    uint8_t *best_idx, float *best_err, float *best_amax,
+                                    float *w_q, uint8_t *packed_e2m1, uint8_t *scale_e4m3,
+                                    float *global_scale, void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+/*
  * Block-scale selection by rule: the scale rules the Local-Hessian guide
  * compares against ("What is Local-Hessian": max scaling takes the block
  * scale from the block's largest |w|; Four-Over-Six picks one of two

@@ -62,6 +62,9 @@ def _load() -> ctypes.CDLL:
     lib.lh_scale_sweep.restype = I
     lib.lh_select_scales.argtypes = [I, P, I, I64, I64, I64, I64, I64, P, I64, P, P, P, P, P, SZ, P]
     lib.lh_select_scales.restype = I
+    lib.lh_scale_sweep_fake_quant.argtypes = [P, I, I64, I64, I64, I64, I64, P, I64, P, P, P, P, P, P, P, P, P,
+                                              SZ, P]
+    lib.lh_scale_sweep_fake_quant.restype = I
     lib.lh_full_hessian.argtypes = [P, I, I64, I64, I64, I64, I64, F, P, I64, I64, P]
     lib.lh_full_hessian.restype = I
     lib.lh_output_error_workspace_bytes.argtypes = [I64, I64, I64]
@@ -85,7 +88,7 @@ lib = _load()
 EXPORTS = ("lh_abi_version", "lh_status_string", "lh_last_error_message", "lh_absmax",
            "lh_hessian_workspace_bytes", "lh_accumulate_hessian", "lh_hessian_ragged_workspace_bytes",
            "lh_accumulate_hessian_ragged", "lh_sweep_workspace_bytes", "lh_scale_sweep",
-           "lh_select_scales", "lh_fake_quant_nvfp4", "lh_full_hessian", "lh_output_error_workspace_bytes",
+           "lh_scale_sweep_fake_quant", "lh_select_scales", "lh_fake_quant_nvfp4", "lh_full_hessian", "lh_output_error_workspace_bytes",
            "lh_output_error", "lh_scaled_histogram", "lh_gptq_workspace_bytes", "lh_gptq_prepare",
            "lh_gptq_quantize")
 
@@ -239,7 +242,7 @@ def lh_sweep_workspace_bytes(c_in: int, n_groups: int = 1) -> int:
     return int(lib.lh_sweep_workspace_bytes(c_in, n_groups))
 
 
-def _select(rule, w, h, amax, best_idx, best_err, best_amax, workspace):
+def _select(rule, w, h, amax, best_idx, best_err, best_amax, workspace, quant=None):
     _require_device(w, h, amax)
     w3 = _as3(w)
     if w3.stride(-1) != 1:
@@ -266,7 +269,9 @@ def _select(rule, w, h, amax, best_idx, best_err, best_amax, workspace):
         ws, ws_bytes = workspace, workspace.numel() * workspace.element_size()
     args = (_ptr(w3), _dtype(w3), c_out, c_in, _ld(w3), g, _group_stride(w3), _ptr(h), h_gstride, _ptr(amax),
             _ptr(best_idx), _ptr(best_err), _ptr(best_amax), _ptr(ws), ws_bytes, _stream(w))
-    if rule is None:
+    if quant is not None:
+        _check(lib.lh_scale_sweep_fake_quant(*args[:13], *(_ptr(quant[k]) for k in _FQ_KEYS), *args[13:]))
+    elif rule is None:
         _check(lib.lh_scale_sweep(*args))
     else:
         _check(lib.lh_select_scales(int(rule), *args))
@@ -285,6 +290,43 @@ def lh_scale_sweep(w: torch.Tensor, h: torch.Tensor, amax: torch.Tensor,
     if h is None:
         raise ValueError("lh_scale_sweep needs a Hessian (lh_select_scales takes h=None)")
     return _select(None, w, h, amax, best_idx, best_err, best_amax, workspace)
+
+
+_FQ_KEYS = ("w_q", "packed", "scale_e4m3", "global_scale")
+
+
+def _fq_outputs(w3, w_q, packed, scale_e4m3, global_scale) -> dict:
+    g, c_out, c_in = w3.shape
+    dev = w3.device
+
+    def out(req, shape, dtype):
+        if isinstance(req, torch.Tensor):
+            return req
+        return torch.empty(shape, dtype=dtype, device=dev) if req else None
+
+    return dict(w_q=out(w_q, (g, c_out, c_in), torch.float32),
+                packed=out(packed, (g, c_out, c_in // 2), torch.uint8),
+                scale_e4m3=out(scale_e4m3, (g, c_out, c_in // BLOCK), torch.uint8),
+                global_scale=out(global_scale, (g,), torch.float32))
+
+
+def lh_scale_sweep_fake_quant(w: torch.Tensor, h: torch.Tensor, amax: torch.Tensor,
+                              best_idx: torch.Tensor | None = None, best_err: torch.Tensor | bool | None = True,
+                              best_amax: torch.Tensor | bool | None = True,
+                              w_q: bool | torch.Tensor = True, packed: bool | torch.Tensor = False,
+                              scale_e4m3: bool | torch.Tensor = False, global_scale: bool | torch.Tensor = False,
+                              workspace: torch.Tensor | bool | None = True) -> dict:
+    """lh_scale_sweep and lh_fake_quant_nvfp4 with its indices in one pass.
+    Returns a dict with idx, err, amax (as lh_scale_sweep; None when not
+    requested) and the requested fake-quant outputs (as lh_fake_quant_nvfp4)."""
+    if h is None:
+        raise ValueError("lh_scale_sweep_fake_quant needs a Hessian")
+    _require_device(w)
+    quant = _fq_outputs(_as3(w), w_q, packed, scale_e4m3, global_scale)
+    idx, err, bam = _select(None, w, h, amax, best_idx, best_err, best_amax, workspace, quant=quant)
+    res = dict(idx=idx, err=err, amax=bam)
+    res.update({k: v for k, v in quant.items() if v is not None})
+    return res
 
 
 def lh_select_scales(rule: int, w: torch.Tensor, h: torch.Tensor | None, amax: torch.Tensor,
@@ -310,17 +352,7 @@ def lh_fake_quant_nvfp4(w: torch.Tensor, best_idx: torch.Tensor, amax: torch.Ten
     if w3.stride(-1) != 1:
         raise ValueError("last dim of w must be contiguous")
     g, c_out, c_in = w3.shape
-    dev = w.device
-
-    def out(req, shape, dtype):
-        if isinstance(req, torch.Tensor):
-            return req
-        return torch.empty(shape, dtype=dtype, device=dev) if req else None
-
-    res = dict(w_q=out(w_q, (g, c_out, c_in), torch.float32),
-               packed=out(packed, (g, c_out, c_in // 2), torch.uint8),
-               scale_e4m3=out(scale_e4m3, (g, c_out, c_in // BLOCK), torch.uint8),
-               global_scale=out(global_scale, (g,), torch.float32))
+    res = _fq_outputs(w3, w_q, packed, scale_e4m3, global_scale)
     _check(lib.lh_fake_quant_nvfp4(_ptr(w3), _dtype(w3), c_out, c_in, _ld(w3), g, _group_stride(w3),
                                    _ptr(best_idx), _ptr(amax), _ptr(res["w_q"]), _ptr(res["packed"]),
                                    _ptr(res["scale_e4m3"]), _ptr(res["global_scale"]), _stream(w)))

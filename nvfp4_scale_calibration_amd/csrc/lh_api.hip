@@ -154,11 +154,21 @@ size_t lh_sweep_workspace_bytes(int64_t c_in, int64_t n_groups) {
 
 namespace {
 
-// Shared by lh_scale_sweep (rule 0, Hessian required) and lh_select_scales.
+// Fake-quant outputs of the fused sweep (all NULL for the plain calls).
+struct QuantPtrs {
+  float* w_q;
+  uint8_t* packed;
+  uint8_t* codes;
+  float* gscale;
+};
+
+// Shared by lh_scale_sweep (rule 0, Hessian required), lh_select_scales and
+// lh_scale_sweep_fake_quant (rule 0, Hessian required, fake-quant outputs).
 lh_status select_common(const char* fn, int rule, bool h_required, const void* w, int w_dtype, int64_t c_out,
                         int64_t c_in, int64_t ld_w, int64_t n_groups, int64_t group_stride_w, const float* h,
                         int64_t group_stride_h, const float* amax, uint8_t* best_idx, float* best_err,
-                        float* best_amax, void* workspace, size_t workspace_bytes, void* stream) {
+                        float* best_amax, void* workspace, size_t workspace_bytes, void* stream,
+                        QuantPtrs qp = QuantPtrs{nullptr, nullptr, nullptr, nullptr}) {
   g_msg[0] = '\0';
   if (rule < 0 || rule > 3) return fail(LH_ERR_ARG, "%s: rule must be 0..3", fn);
   if (!valid_dtype(w_dtype)) return fail(LH_ERR_DTYPE, "%s: w_dtype must be 0 (f32) or 1 (bf16)", fn);
@@ -178,9 +188,20 @@ lh_status select_common(const char* fn, int rule, bool h_required, const void* w
   if (!aligned(workspace, 4)) return fail(LH_ERR_ARG, "%s: workspace not 4-byte aligned", fn);
   if (workspace != nullptr && workspace_bytes > 0 && work && workspace_bytes < lh::sweep_ws_bytes(c_in, n_groups))
     return fail(LH_ERR_WORKSPACE, "%s: workspace smaller than lh_sweep_workspace_bytes()", fn);
-  if (!work) return LH_OK;
+  if (!aligned(qp.w_q, 16) || !aligned(qp.packed, 8) || !aligned(qp.gscale, 4))
+    return fail(LH_ERR_ARG, "%s: misaligned pointer (w_q needs 16 bytes, packed_e2m1 8, global_scale 4)", fn);
+  if (qp.gscale != nullptr && n_groups > 0 && amax == nullptr) return fail(LH_ERR_NULL, "%s: amax is NULL", fn);
+  if (!work) {
+    if (qp.gscale == nullptr || n_groups == 0) return LH_OK;
+    // no block, but S_g is still asked for
+    lh::FakeQuantArgs f{w, w_dtype, c_out, c_in, ld_w, n_groups, group_stride_w, nullptr, amax,
+                        nullptr, nullptr, nullptr, qp.gscale};
+    hipError_t e = lh::launch_fake_quant(f, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LH_OK : hip_fail(e, fn);
+  }
   lh::SweepArgs a{w, w_dtype, c_out, c_in, ld_w, n_groups, group_stride_w, h, group_stride_h, amax,
-                  best_idx, best_err, best_amax, workspace, workspace_bytes, rule};
+                  best_idx, best_err, best_amax, workspace, workspace_bytes, rule,
+                  qp.w_q, qp.packed, qp.codes, qp.gscale};
   hipError_t e = lh::launch_sweep(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LH_OK : hip_fail(e, fn);
 }
@@ -196,6 +217,17 @@ lh_status lh_scale_sweep(const void* w, int w_dtype, int64_t c_out, int64_t c_in
                          void* stream) {
   return select_common("lh_scale_sweep", 0, true, w, w_dtype, c_out, c_in, ld_w, n_groups, group_stride_w, h,
                        group_stride_h, amax, best_idx, best_err, best_amax, workspace, workspace_bytes, stream);
+}
+
+lh_status lh_scale_sweep_fake_quant(const void* w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
+                                    int64_t n_groups, int64_t group_stride_w, const float* h,
+                                    int64_t group_stride_h, const float* amax, uint8_t* best_idx,
+                                    float* best_err, float* best_amax, float* w_q, uint8_t* packed_e2m1,
+                                    uint8_t* scale_e4m3, float* global_scale, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return select_common("lh_scale_sweep_fake_quant", 0, true, w, w_dtype, c_out, c_in, ld_w, n_groups,
+                       group_stride_w, h, group_stride_h, amax, best_idx, best_err, best_amax, workspace,
+                       workspace_bytes, stream, QuantPtrs{w_q, packed_e2m1, scale_e4m3, global_scale});
 }
 
 lh_status lh_select_scales(int rule, const void* w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,

@@ -61,4 +61,60 @@ __device__ __forceinline__ float e2m1_round_mag(float x) {
   return (xc + magic) - magic;
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// NVFP4 cast of one 16-weight block with block scale s ("Algorithm
+// principle": Q(W, s) = Cast(W / s) * s).  x = fl32(w / s) by IEEE division
+// (0 when s == 0); v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds pairs of x
+// to signed E2M1 nibbles (nearest, ties to even, saturating at 6), packed
+// low nibble first into the bytes of pk[0] (weights 0-7) and pk[1] (8-15);
+// a sign on a zero magnitude is cleared, so -0 is written as +0.
+__device__ __forceinline__ void nvfp4_cast_block(const float (&w)[16], float s, uint32_t (&pk)[2]) {
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = (s == 0.0f) ? 0.0f : w[i] / s;  // IEEE division
+  pk[0] = pk[1] = 0u;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], x[8 * h + 0], x[8 * h + 1], 1.0f, 0);
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], x[8 * h + 2], x[8 * h + 3], 1.0f, 1);
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], x[8 * h + 4], x[8 * h + 5], 1.0f, 2);
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], x[8 * h + 6], x[8 * h + 7], 1.0f, 3);
+    // keep the sign bit (bit 3 of a nibble) only where the magnitude is non-zero
+    const uint32_t nz = (pk[h] | (pk[h] >> 1) | (pk[h] >> 2)) & 0x11111111u;
+    pk[h] &= 0x77777777u | (nz << 3);
+  }
+}
+
+// Dequantised block: v_cvt_scalef32_pk_f32_fp4 (scale 1) decodes the signed
+// grid values r and Q = fl32(r * s).
+__device__ __forceinline__ void nvfp4_decode_block(const uint32_t (&pk)[2], float s, float (&q)[16]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const f32x2_t r0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 0);
+    const f32x2_t r1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 1);
+    const f32x2_t r2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 2);
+    const f32x2_t r3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 3);
+    q[8 * h + 0] = r0.x * s; q[8 * h + 1] = r0.y * s; q[8 * h + 2] = r1.x * s; q[8 * h + 3] = r1.y * s;
+    q[8 * h + 4] = r2.x * s; q[8 * h + 5] = r2.y * s; q[8 * h + 6] = r3.x * s; q[8 * h + 7] = r3.y * s;
+  }
+}
+
+// The per-block outputs of the fake-quant for block (row rg, input block b)
+// of a dense [rows][nb] layout from its nibbles, each optional: 16 fp32
+// Q = fl32(r * s) values, 8 bytes of nibbles, the E4M3 code k + 1.
+__device__ __forceinline__ void nvfp4_emit_block(const uint32_t (&pk)[2], float s, int k, int64_t rg, int64_t b,
+                                                 int64_t nb, float* __restrict__ wq, uint8_t* __restrict__ packed,
+                                                 uint8_t* __restrict__ codes) {
+  if (wq) {
+    float q[16];
+    nvfp4_decode_block(pk, s, q);
+    float4* o = reinterpret_cast<float4*>(wq + rg * (nb * 16) + 16 * b);
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) o[qd] = make_float4(q[4 * qd], q[4 * qd + 1], q[4 * qd + 2], q[4 * qd + 3]);
+  }
+  if (packed) *reinterpret_cast<uint2*>(packed + rg * (nb * 8) + 8 * b) = make_uint2(pk[0], pk[1]);
+  if (codes) codes[rg * nb + b] = (uint8_t)(k + 1);
+}
+
 }  // namespace lh

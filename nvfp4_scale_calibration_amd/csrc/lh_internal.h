@@ -65,6 +65,11 @@ struct SweepArgs {
   void* ws;       // nullable: per-block skip certificates
   size_t ws_bytes;
   int rule;       // 0: 126-value sweep, 1: max, 2: Four-Over-Six, 3: amax search
+  // fused fake-quant outputs (rule 0 only; all nullptr: none), dense layouts
+  float* wq = nullptr;
+  uint8_t* packed = nullptr;
+  uint8_t* codes = nullptr;
+  float* gscale = nullptr;
 };
 size_t sweep_ws_bytes(int64_t c_in, int64_t n_groups);
 hipError_t launch_sweep(const SweepArgs& a, hipStream_t stream);

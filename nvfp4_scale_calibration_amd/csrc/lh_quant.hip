@@ -49,14 +49,9 @@ __device__ __forceinline__ void load16(const T* p, float (&w)[16]) {
   }
 }
 
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// One thread per 16-weight block.  Outputs are dense and each optional.
-// x = fl32(w / s) by IEEE division; v_cvt_scalef32_pk_fp4_f32 (scale 1)
-// rounds pairs of x to signed E2M1 nibbles (nearest, ties to even,
-// saturating), which is the packed output once a sign on a zero magnitude is
-// cleared (-0 is written as +0); v_cvt_scalef32_pk_f32_fp4 decodes them and
-// Q = fl32(r * s).  s == 0 (amax 0) gives x = 0 for every weight.
+// One thread per 16-weight block.  Outputs are dense and each optional; the
+// cast and the stores are nvfp4_cast_block / nvfp4_emit_block, which the
+// fused sweep uses too.  s == 0 (amax 0) gives x = 0 for every weight.
 template <typename T, bool kVec>
 __global__ __launch_bounds__(kThreads) void fake_quant_kernel(const T* __restrict__ wt, int64_t c_out,
                                                               int64_t ld_w, int64_t gstride_w, int64_t nb,
@@ -77,41 +72,9 @@ __global__ __launch_bounds__(kThreads) void fake_quant_kernel(const T* __restric
   const float s = e4m3_candidate(k) * Sg;
   float w[16];
   load16<T, kVec>(wt + grp * gstride_w + row * ld_w + 16 * b, w);
-  float x[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = (s == 0.0f) ? 0.0f : w[i] / s;  // IEEE division
-  uint32_t pk[2] = {0u, 0u};
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], x[8 * h + 0], x[8 * h + 1], 1.0f, 0);
-    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], x[8 * h + 2], x[8 * h + 3], 1.0f, 1);
-    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], x[8 * h + 4], x[8 * h + 5], 1.0f, 2);
-    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], x[8 * h + 6], x[8 * h + 7], 1.0f, 3);
-    // keep the sign bit (bit 3 of a nibble) only where the magnitude is non-zero
-    const uint32_t nz = (pk[h] | (pk[h] >> 1) | (pk[h] >> 2)) & 0x11111111u;
-    pk[h] &= 0x77777777u | (nz << 3);
-  }
-  if (wq) {
-    float q[16];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int byte = 0; byte < 4; ++byte) {
-        f32x2_t r;
-        if (byte == 0) r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 0);
-        else if (byte == 1) r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 1);
-        else if (byte == 2) r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 2);
-        else r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 3);
-        q[8 * h + 2 * byte] = r.x * s;       // Q = fl32(r * s)
-        q[8 * h + 2 * byte + 1] = r.y * s;
-      }
-    }
-    float4* o = reinterpret_cast<float4*>(wq + rg * (nb * 16) + 16 * b);
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd) o[qd] = make_float4(q[4 * qd], q[4 * qd + 1], q[4 * qd + 2], q[4 * qd + 3]);
-  }
-  if (packed) *reinterpret_cast<uint2*>(packed + rg * (nb * 8) + 8 * b) = make_uint2(pk[0], pk[1]);
-  if (codes) codes[f] = (uint8_t)(k + 1);
+  uint32_t pk[2];
+  nvfp4_cast_block(w, s, pk);
+  nvfp4_emit_block(pk, s, k, rg, b, nb, wq, packed, codes);
 }
 
 __global__ void global_scale_kernel(const float* __restrict__ amax, float* __restrict__ out, int64_t n) {

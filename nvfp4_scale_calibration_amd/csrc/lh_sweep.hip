@@ -74,6 +74,11 @@ namespace {
 // Index of (i, j), i < j, in the packed strict upper triangle (row-major).
 __host__ __device__ constexpr int tri(int i, int j) { return i * 15 - (i * (i - 1)) / 2 + (j - i - 1); }
 
+// Workgroup size of the sweep kernel: one wave, so that a finished wave's
+// slot is refilled at once (lanes do unequal work: a workgroup of several
+// waves holds its slots until its slowest wave ends).
+constexpr int kSweepThreads = 64;
+
 struct Best {
   float err;
   int k;
@@ -134,8 +139,6 @@ __device__ __forceinline__ float quad_form_from(const float (&yd)[16], const flo
   }
   return e;
 }
-
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // RN(a / b) given rb = RN(1 / b): q = RN(a rb), r = a - b q (exact by fma),
 // q' = RN(q + r rb).  Markstein's theorem makes q' the correctly rounded
@@ -246,19 +249,30 @@ __device__ __forceinline__ void eval_direct(Best& best, int k, float Sg, int e, 
 }
 
 // True when this lane cannot prove the candidate worse than its incumbent.
+// The bound over the two largest elements comes first; the other two are
+// added only when some lane of the wave survives it.  Terms are added in the
+// same order either way and adding a non-negative term never lowers a
+// rounded sum, so a lane stopped by the two-element bound would also be
+// stopped by the four-element one: the outcome is that of the four-element
+// test alone.
 __device__ __forceinline__ bool needs_eval(SkipSet& t, const Best& best, int j, float s) {
   const float pow2j = __uint_as_float((uint32_t)(127 + j) << 23);
+  const float thr = best.err * kSkipMargin;
   t.pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t.pk, t.p[0], t.p[1], pow2j, 0);
-  t.pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t.pk, t.p[2], t.p[3], pow2j, 1);
   const f32x2_t r01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.pk, 1.0f, 0);
-  const f32x2_t r23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.pk, 1.0f, 1);
   const float d0 = r01.x * s - t.w[0], d1 = r01.y * s - t.w[1];
-  const float d2 = r23.x * s - t.w[2], d3 = r23.y * s - t.w[3];
   float lb = (t.dg[0] * d0) * d0;
   lb = __builtin_fmaf(t.dg[1] * d1, d1, lb);
-  lb = __builtin_fmaf(t.dg[2] * d2, d2, lb);
-  lb = __builtin_fmaf(t.dg[3] * d3, d3, lb);
-  return !(t.on && lb > best.err * kSkipMargin);
+  bool need = !(t.on && lb > thr);
+  if (__ballot(need) != 0) {
+    t.pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t.pk, t.p[2], t.p[3], pow2j, 1);
+    const f32x2_t r23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.pk, 1.0f, 1);
+    const float d2 = r23.x * s - t.w[2], d3 = r23.y * s - t.w[3];
+    lb = __builtin_fmaf(t.dg[2] * d2, d2, lb);
+    lb = __builtin_fmaf(t.dg[3] * d3, d3, lb);
+    need = need && !(t.on && lb > thr);
+  }
+  return need;
 }
 
 // E4M3 code of mantissa class m at power j (value (1 + m/8) 2^j): normal
@@ -353,6 +367,47 @@ __device__ __forceinline__ int row_exponent(int e_g, const float (&w)[16]) {
   const int d = ilogbf(a) - e_g;
   if (d >= -20 && d <= 20) return e_g;
   return e_g + (d > 100 ? 100 : (d < -100 ? -100 : d));
+}
+
+// Nibbles of candidate k for a row in its working units (w and Su prescaled
+// by 2^-e), computed with the sweep's own arithmetic: p = fl32(w / sigma)
+// (div_rn) and the scaled FP4 conversion with scale 2^j.  When e is S_g's
+// own exponent every quantity involved is a normal fp32 number except
+// quotients that round to a zero nibble either way, so these are exactly
+// the nibbles of nvfp4_cast_block(w 2^e, s_k) (IEEE quotient fl32(w / s_k),
+// then the E2M1 rounding).  Signs on zero magnitudes are cleared as there.
+__device__ __forceinline__ void candidate_nibbles(int k, float Su, const float (&w)[16], uint32_t (&pk)[2]) {
+  int m, j;
+  candidate_class(k, m, j);
+  const float sigma = (1.0f + 0.125f * (float)m) * Su;
+  const float rs = 1.0f / sigma;
+  const float pow2j = __uint_as_float((uint32_t)(127 + j) << 23);
+  float p[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) p[i] = div_rn(w[i], sigma, rs);
+  pk[0] = pk[1] = 0u;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 0], p[8 * h + 1], pow2j, 0);
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 2], p[8 * h + 3], pow2j, 1);
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 4], p[8 * h + 5], pow2j, 2);
+    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 6], p[8 * h + 7], pow2j, 3);
+    const uint32_t nz = (pk[h] | (pk[h] >> 1) | (pk[h] >> 2)) & 0x11111111u;
+    pk[h] &= 0x77777777u | (nz << 3);
+  }
+}
+
+// The block's raw weights read again with relaxed atomic loads, which the
+// compiler does not merge with the row's first load (that would keep the raw
+// values live across the candidate loop); used only for rows whose working
+// exponent is not S_g's.
+template <typename T>
+__device__ __forceinline__ void reload_block(const T* p, float (&w)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if constexpr (sizeof(T) == 2) w[i] = bf16_bits_to_f32(__atomic_load_n(p + i, __ATOMIC_RELAXED));
+    else w[i] = __uint_as_float(__atomic_load_n(reinterpret_cast<const uint32_t*>(p) + i, __ATOMIC_RELAXED));
+  }
 }
 
 // H_b (16x16 row-major, 16-byte aligned) as its diagonal and the symmetrised
@@ -518,11 +573,24 @@ __global__ __launch_bounds__(kThreads) void sweep_certificate_kernel(const float
   if (live && q == 0) cert[t] = tau;
 }
 
+// Fake-quant outputs written by the fused sweep (each optional).
+struct QuantOut {
+  float* wq;
+  uint8_t* packed;
+  uint8_t* codes;
+  float* gscale;
+  int64_t n_groups;
+};
+
 // Two waves per SIMD: the allocator then spills ~14 row-setup values to
 // scratch (none inside the candidate loop), which costs far less than the
-// latency a single wave per SIMD leaves exposed.
-template <typename T, bool kVec, bool kMse>
-__global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const T* __restrict__ wt, int64_t c_out,
+// latency a single wave per SIMD leaves exposed.  With kQuant each row also
+// writes the fake-quant of its block with the index just chosen: the
+// nibbles come from candidate_nibbles on the row's working values (or
+// nvfp4_cast_block on the raw weights for the rare rows that need them),
+// the stores from nvfp4_emit_block, the standalone fake-quant's code.
+template <typename T, bool kVec, bool kMse, bool kQuant>
+__global__ __launch_bounds__(kSweepThreads, 2) void sweep_kernel(const T* __restrict__ wt, int64_t c_out,
                                                          int64_t ld_w, int64_t gstride_w, int64_t nb,
                                                          int64_t rows_step, int64_t lanes,
                                                          const float* __restrict__ h, int64_t gstride_h,
@@ -530,8 +598,8 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const T* __restrict_
                                                          uint8_t* __restrict__ idx_out,
                                                          float* __restrict__ err_out,
                                                          float* __restrict__ amax_out,
-                                                         const float* __restrict__ cert) {
-  const int64_t L = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+                                                         const float* __restrict__ cert, QuantOut qo) {
+  const int64_t L = (int64_t)blockIdx.x * kSweepThreads + threadIdx.x;
   if (L >= lanes) return;
   const int64_t per_group = nb * rows_step;
   const int64_t grp = L / per_group;
@@ -582,8 +650,8 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const T* __restrict_
   }
   // Per-lane scratch in LDS, element-major so that 64 lanes hit 64 consecutive
   // words: the diagonal (fixed) and the current row's prescaled weights.
-  __shared__ float lds_diag[16][kThreads];
-  __shared__ float lds_w[16][kThreads];
+  __shared__ float lds_diag[16][kSweepThreads];
+  __shared__ float lds_w[16][kSweepThreads];
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < 16; ++i) lds_diag[i][tid] = diag[i];
@@ -659,6 +727,20 @@ __global__ __launch_bounds__(kThreads, 2) void sweep_kernel(const T* __restrict_
     idx_out[o] = (uint8_t)k;
     if (err_out) err_out[o] = ldexpf(best.err, 2 * e);
     if (amax_out) amax_out[o] = 6.0f * (e4m3_candidate(k) * Sg);
+    if constexpr (kQuant) {
+      const float s = e4m3_candidate(k) * Sg;
+      uint32_t pk[2];
+      if (fast && e == e_g) {
+        candidate_nibbles(k, Su, w, pk);
+      } else {
+        if (fast) reload_block(wt + grp * gstride_w + row * ld_w + 16 * b, w);  // w was prescaled
+        nvfp4_cast_block(w, s, pk);
+      }
+      nvfp4_emit_block(pk, s, k, grp * c_out + row, b, nb, qo.wq, qo.packed, qo.codes);
+    }
+  }
+  if constexpr (kQuant) {
+    if (qo.gscale && L < qo.n_groups) qo.gscale[L] = amax[L] / kAmaxDivisor;  // S_g, once per group
   }
 }
 
@@ -776,13 +858,14 @@ template <typename T, bool kVec>
 hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
   const int64_t nb = a.c_in / 16;
   const int64_t per_k = a.n_groups * nb;
-  // Two rounds of lanes at two waves per SIMD on 256 CUs; rows split evenly.
-  const int64_t target = 256LL * 4 * 2 * 64 * 2;
-  int64_t k = (target + per_k - 1) / per_k;
-  if (k > a.c_out) k = a.c_out;
-  if (k < 1) k = 1;
-  const int64_t rows_per_lane = (a.c_out + k - 1) / k;
-  k = (a.c_out + rows_per_lane - 1) / rows_per_lane;
+  // About sixteen rounds of lanes at two waves per SIMD on 256 CUs, so that
+  // waves of unequal work pack well, but at least two rows per lane (its
+  // Hessian load and certificate are paid once per walk); rows split evenly.
+  const int64_t target = 256LL * 4 * 2 * 64 * 16;
+  int64_t rows_per_lane = (a.c_out * per_k + target - 1) / target;
+  if (rows_per_lane < 2) rows_per_lane = 2;
+  if (rows_per_lane > a.c_out) rows_per_lane = a.c_out;
+  const int64_t k = (a.c_out + rows_per_lane - 1) / rows_per_lane;
   const int64_t lanes = per_k * k;
   const int64_t grid = (lanes + kThreads - 1) / kThreads;
   const bool mse = a.h == nullptr;
@@ -797,10 +880,18 @@ hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
           a.amax, a.idx, a.err, a.best_amax);
     return hipGetLastError();
   }
+  const int64_t sgrid = (lanes + kSweepThreads - 1) / kSweepThreads;
+  const QuantOut qo{a.wq, a.packed, a.codes, a.gscale, a.n_groups};
+  const bool quant = a.wq || a.packed || a.codes || a.gscale;
   if (mse) {
-    sweep_kernel<T, kVec, true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
-        static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, k, lanes, nullptr, 0, a.amax, a.idx, a.err,
-        a.best_amax, nullptr);
+    if (quant)
+      sweep_kernel<T, kVec, true, true><<<dim3((unsigned)sgrid), dim3(kSweepThreads), 0, stream>>>(
+          static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, k, lanes, nullptr, 0, a.amax, a.idx,
+          a.err, a.best_amax, nullptr, qo);
+    else
+      sweep_kernel<T, kVec, true, false><<<dim3((unsigned)sgrid), dim3(kSweepThreads), 0, stream>>>(
+          static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, k, lanes, nullptr, 0, a.amax, a.idx,
+          a.err, a.best_amax, nullptr, qo);
     return hipGetLastError();
   }
   float* cert = nullptr;
@@ -811,9 +902,14 @@ hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  sweep_kernel<T, kVec, false><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
-      static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, k, lanes, a.h, a.gstride_h, a.amax,
-      a.idx, a.err, a.best_amax, cert);
+  if (quant)
+    sweep_kernel<T, kVec, false, true><<<dim3((unsigned)sgrid), dim3(kSweepThreads), 0, stream>>>(
+        static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, k, lanes, a.h, a.gstride_h, a.amax,
+        a.idx, a.err, a.best_amax, cert, qo);
+  else
+    sweep_kernel<T, kVec, false, false><<<dim3((unsigned)sgrid), dim3(kSweepThreads), 0, stream>>>(
+        static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, k, lanes, a.h, a.gstride_h, a.amax,
+        a.idx, a.err, a.best_amax, cert, qo);
   return hipGetLastError();
 }
 

@@ -169,6 +169,33 @@ def test_select_validation(lib):
                               None) == NULL
 
 
+def test_sweep_fake_quant_validation(lib):
+    P = ctypes.c_void_p
+    ok = dict(w=P(FAKE), dt=1, c_out=4, c_in=32, ld=32, g=1, gs=0, h=P(FAKE), hs=0, amax=P(FAKE), idx=P(FAKE),
+              err=None, am=None, wq=P(FAKE), pk=None, codes=None, gsc=None, ws=None, wsb=0, st=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.lh_scale_sweep_fake_quant(a["w"], a["dt"], a["c_out"], a["c_in"], a["ld"], a["g"], a["gs"],
+                                             a["h"], a["hs"], a["amax"], a["idx"], a["err"], a["am"], a["wq"],
+                                             a["pk"], a["codes"], a["gsc"], a["ws"], a["wsb"], a["st"])
+
+    assert call(dt=3) == DTYPE
+    assert call(c_in=24) == SHAPE
+    assert call(ld=16) == SHAPE
+    assert call(h=None) == NULL and "h" in _msg(lib)   # the Hessian is required
+    assert call(idx=None) == NULL
+    assert call(amax=None) == NULL
+    assert call(wq=P(FAKE + 4)) == ARG and "w_q" in _msg(lib)   # 16-byte alignment
+    assert call(pk=P(FAKE + 4)) == ARG                          # 8-byte alignment
+    assert call(gsc=P(FAKE + 2)) == ARG
+    assert call(ws=P(FAKE), wsb=1) == WORKSPACE
+    # empty problems: nothing to do unless S_g is asked for, which needs amax
+    assert call(c_out=0, w=None, idx=None) == OK
+    assert call(c_out=0, w=None, idx=None, gsc=P(FAKE), amax=None) == NULL
+    assert call(g=0, gsc=P(FAKE), amax=None) == OK
+
+
 def test_ragged_hessian_validation(lib):
     P = ctypes.c_void_p
     ok = dict(x=P(FAKE), dt=1, c_in=32, ld=32, rows=100, off=P(FAKE), g=3, mx=0, h=P(FAKE), hs=512, cnt=None,

@@ -1,7 +1,7 @@
-"""The whole path captured in one HIP graph: every replay, with eager work
-and synchronisations between replays, reproduces the eager results bit for
-bit (the library records only kernel launches: no memset, copy, sync or
-allocation)."""
+"""The whole path (and the fused sweep + fake-quant call) captured in one HIP
+graph: every replay, with eager work and synchronisations between replays,
+reproduces the eager results bit for bit (the library records only kernel
+launches: no memset, copy, sync or allocation)."""
 import pytest
 import torch
 
@@ -33,7 +33,9 @@ def test_path_in_hip_graph_replays_match_eager(lh):
                idx=torch.empty((G, c_out, nb), **u8), err=torch.empty((G, c_out, nb), **f32),
                bam=torch.empty((G, c_out, nb), **f32), idx4=torch.empty((G, c_out, nb), **u8),
                wq=torch.empty((G, c_out, c_in), **f32), packed=torch.empty((G, c_out, c_in // 2), **u8),
-               codes=torch.empty((G, c_out, nb), **u8), gs=torch.empty(G, **f32))
+               codes=torch.empty((G, c_out, nb), **u8), gs=torch.empty(G, **f32),
+               f_idx=torch.empty((G, c_out, nb), **u8), f_wq=torch.empty((G, c_out, c_in), **f32),
+               f_packed=torch.empty((G, c_out, c_in // 2), **u8), f_codes=torch.empty((G, c_out, nb), **u8))
     hws = torch.empty(max(lh.lh_hessian_workspace_bytes(c_in, n, G), 4), **u8)
     rws = torch.empty(max(lh.lh_hessian_ragged_workspace_bytes(c_in, 2 * n, 3), 4), **u8)
     sws = torch.empty(max(lh.lh_sweep_workspace_bytes(c_in, G), 4), **u8)
@@ -49,10 +51,15 @@ def test_path_in_hip_graph_replays_match_eager(lh):
                             best_err=False, best_amax=False)
         lh.lh_fake_quant_nvfp4(w, out["idx"], out["amax"], w_q=out["wq"], packed=out["packed"],
                                scale_e4m3=out["codes"], global_scale=out["gs"])
+        lh.lh_scale_sweep_fake_quant(w, out["h"], out["amax"], best_idx=out["f_idx"], best_err=False,
+                                     best_amax=False, w_q=out["f_wq"], packed=out["f_packed"],
+                                     scale_e4m3=out["f_codes"], workspace=sws)
 
     step()
     torch.cuda.synchronize()
     eager = {k: v.clone() for k, v in out.items()}
+    for k in ("idx", "wq", "packed", "codes"):     # the fused call writes what the two separate calls write
+        assert torch.equal(eager["f_" + k], eager[k]), k
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()
