@@ -469,17 +469,114 @@ __device__ __forceinline__ void load_block(const T* p, float (&w)[16]) {
 // ---------------------------------------------------------------------------
 // Skip certificate pre-pass.  With S = (H + H^T)/2, D = diag S and
 // C = D^-1/2 S D^-1/2 (unit diagonal), it finds a large tau with C - tau I
-// positive definite, testing each tau with an fp32 Cholesky factorisation: if every pivot is positive, the
+// positive definite, testing each tau with an fp32 Cholesky factorisation
+// (operations accurate to a few ulps): if every pivot is positive, the
 // computed factor is the exact factor of C - tau I + dA with
-// |dA| <= 17u |L||L^T| (Cholesky backward error), and |L||L^T| <= 1
-// entrywise, so lambda_min(C) >= tau - 16*17u.  The certificate stored is
-// tau - 2e-3.  It is zeroed (no skipping) when the diagonal is not positive
-// and finite, when it falls below 0.02, or when the fp32 error bound of the
-// quadratic form, 35u (1 + rho) / tau with rho the largest off-diagonal row
-// sum of |C| (so lambda_max(|C|) <= 1 + rho), would exceed 2^-11.
+// |dA| <= 20u |L||L^T| (Cholesky backward error), and |L||L^T| <= 1
+// entrywise, so lambda_min(C) >= tau - 16*20u.  The certificate stored is
+// tau - 2e-3, which also covers the rounding of C itself.  It is zeroed (no
+// skipping) when the diagonal is not positive and finite, when it falls
+// below 0.02, or when the fp32 error bound of the quadratic form,
+// 35u (1 + rho) / tau with rho the largest off-diagonal row sum of |C| (so
+// lambda_max(|C|) <= 1 + rho), would exceed 2^-11.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float sym_entry(const float* hb, const float (&rs)[16], int i, int j) {
-  return (i == j) ? hb[i * 17] * rs[i] * rs[i] : 0.5f * (hb[i * 16 + j] + hb[j * 16 + i]) * rs[i] * rs[j];
+
+// Up to this many blocks the team kernel (short dependency chains, 16 lanes
+// per factorisation) is faster; beyond it the lane kernel (one
+// factorisation per lane, 16x fewer instructions in total) is.
+constexpr int64_t kCertTeamMaxBlocks = 2048;
+
+// Value of lane k of this lane's 16-lane team (ds_swizzle bit mode within
+// 32-lane halves: new lane = (lane & 16) | k).
+template <int k>
+__device__ __forceinline__ float team_lane(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x10 | (k << 5)));
+}
+
+// A_ik -= l_ij l_kj for k = k0..15, l_kj from lane k of the team.
+template <int k0>
+__device__ __forceinline__ void team_column_update(float (&a)[16], float l) {
+  if constexpr (k0 < 16) {
+    a[k0] = __builtin_fmaf(-l, team_lane<k0>(l), a[k0]);
+    team_column_update<k0 + 1>(a, l);
+  }
+}
+
+// Columns j..15 of a right-looking Cholesky factorisation held one row per
+// lane (a = row i of the matrix): the pivot d = A_jj comes from lane j,
+// l_ij = A_ij / sqrt(d), then the trailing entries are updated.  Entries
+// above a lane's diagonal are updated too but never read by a valid step.
+// ok stays true while every pivot is positive.
+template <int j>
+__device__ __forceinline__ void team_cholesky(float (&a)[16], bool& ok) {
+  if constexpr (j < 16) {
+    const float d = team_lane<j>(a[j]);
+    ok = ok && (d > 0.0f);
+    const float l = a[j] * __builtin_amdgcn_rsqf(fmaxf(d, 0x1p-126f));
+    team_column_update<j + 1>(a, l);
+    team_cholesky<j + 1>(a, ok);
+  }
+}
+
+// For few blocks (latency-bound): one workgroup per block, team q (16
+// lanes) tests tau = q/16, team 0 the
+// Gershgorin bound (no factorisation); the block keeps the largest tau that
+// passes.  Lane i of a team holds row i of C - tau I and the team factorises
+// it column by column (right-looking: the pivot and then each entry of the
+// new column are broadcast within the team), so each lane does 16 steps of
+// a few operations instead of a whole factorisation.
+__global__ __launch_bounds__(kThreads) void sweep_certificate_team_kernel(const float* __restrict__ h, int64_t gstride_h,
+                                                                     int64_t nb, float* __restrict__ cert) {
+  __shared__ float hs[16][17];
+  __shared__ float taus[16];
+  const int64_t t = blockIdx.x;
+  const int q = threadIdx.x >> 4, i = threadIdx.x & 15;
+  const int64_t grp = t / nb, b = t - grp * nb;
+  hs[q][i] = h[grp * gstride_h + b * 256 + threadIdx.x];  // row q, column i
+  __syncthreads();
+  bool pos = true;
+  float rs[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float d = hs[j][j];
+    pos = pos && (d > 0.0f) && (d < INFINITY);
+    rs[j] = d > 0.0f ? __builtin_amdgcn_rsqf(d) : 0.0f;
+  }
+  // row i of C and its off-diagonal absolute sum
+  const float hii = hs[i][i];
+  const float ri = hii > 0.0f ? __builtin_amdgcn_rsqf(hii) : 0.0f;
+  float a[16];
+  float r = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    a[j] = (j == i) ? hii * ri * ri : 0.5f * (hs[i][j] + hs[j][i]) * ri * rs[j];
+    if (j != i) r += fabsf(a[j]);
+  }
+  float rho = pos ? r : 0.0f;
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) rho = fmaxf(rho, __shfl_xor(rho, off, 16));
+  float tau = 0.0f;
+  if (q == 0) {
+    tau = fmaxf(1.0f - rho - 1e-3f, 0.0f);
+  } else {
+    const float tq = (float)q * 0.0625f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j == i) a[j] -= tq;
+    bool ok = true;
+    team_cholesky<0>(a, ok);
+    tau = ok ? tq - 2e-3f : 0.0f;
+  }
+  if (i == 0) taus[q] = tau;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float best = taus[0];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) best = fmaxf(best, taus[k]);
+    const float err = 35.0f * 0x1p-24f * (1.0f + rho) / best;
+    if (!pos || !(best >= 0.02f) || !(err <= 0x1p-11f)) best = 0.0f;
+    cert[t] = best;
+  }
 }
 
 // In-place Cholesky of the packed lower triangle a (a[i (i + 1) / 2 + j],
@@ -505,33 +602,30 @@ __device__ bool cholesky_ok(float (&a)[136]) {
   return true;
 }
 
-// Sixteen lanes per block: lane q tests tau = q/16 (lane 0 tests the
-// Gershgorin bound, which needs no factorisation); the block keeps the
-// largest tau that passes.  The 16 lanes first stage the block's H in LDS
-// (one row each), so each factorisation reads LDS, not global memory.
-__global__ __launch_bounds__(kThreads) void sweep_certificate_kernel(const float* __restrict__ h, int64_t gstride_h,
+// For many blocks: sixteen lanes per block, lane q tests tau = q/16 (lane 0
+// the Gershgorin bound, which needs no factorisation) with a whole
+// factorisation of its own; the block keeps the largest tau that passes.  The 16 lanes stage the block's H in LDS (one
+// row each), then replace it by C (lane q computes row q and its
+// off-diagonal sum), so each lane only reads C's lower triangle before its
+// factorisation.
+__global__ __launch_bounds__(kThreads) void sweep_certificate_lane_kernel(const float* __restrict__ h, int64_t gstride_h,
                                                                      int64_t nb, int64_t total,
                                                                      float* __restrict__ cert) {
-  __shared__ float hs[kThreads / 16][257];  // +1 pad: rows of different blocks on different banks
+  constexpr int kPitch = 260;  // 16-byte aligned rows; the four teams of a wave start 4 banks apart
+  __shared__ __align__(16) float hs[kThreads / 16][kPitch];
   const int slot = threadIdx.x >> 4;
   const int64_t t = (int64_t)blockIdx.x * (kThreads / 16) + slot;
   const int q = threadIdx.x & 15;
   const bool live = t < total;  // all 16 lanes of a block share t
   const int64_t tc = live ? t : 0;
   const int64_t grp = tc / nb, b = tc - grp * nb;
+  float* hb = hs[slot];
   {
     const float4* src = reinterpret_cast<const float4*>(h + grp * gstride_h + b * 256 + q * 16);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float4 v = src[c];
-      hs[slot][q * 16 + 4 * c + 0] = v.x;
-      hs[slot][q * 16 + 4 * c + 1] = v.y;
-      hs[slot][q * 16 + 4 * c + 2] = v.z;
-      hs[slot][q * 16 + 4 * c + 3] = v.w;
-    }
+    for (int c = 0; c < 4; ++c) reinterpret_cast<float4*>(hb + q * 16)[c] = src[c];
   }
   __syncthreads();
-  const float* hb = hs[slot];
   float rs[16];
   bool pos = true;
 #pragma unroll
@@ -540,17 +634,26 @@ __global__ __launch_bounds__(kThreads) void sweep_certificate_kernel(const float
     pos = pos && (d > 0.0f) && (d < INFINITY);
     rs[i] = d > 0.0f ? 1.0f / sqrtf(d) : 0.0f;
   }
-  float rho = 0.0f;
-  if (pos) {
+  // row q of C = D^-1/2 S D^-1/2 (the same operations for entry (q, j) as
+  // for the lower-triangle entry the factorisation reads) and its
+  // off-diagonal absolute sum
+  const float hqq = hb[q * 17];
+  const float rq = hqq > 0.0f ? 1.0f / sqrtf(hqq) : 0.0f;
+  float crow[16];
+  float r = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float r = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (j != i) r += fabsf(sym_entry(hb, rs, i, j));
-      rho = fmaxf(rho, r);
-    }
+  for (int j = 0; j < 16; ++j) {
+    crow[j] = (j == q) ? hqq * rq * rq : 0.5f * (hb[q * 16 + j] + hb[j * 16 + q]) * rq * rs[j];
+    if (j != q) r += fabsf(crow[j]);
   }
+  __syncthreads();  // every lane has read H
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    reinterpret_cast<float4*>(hb + q * 16)[c] = make_float4(crow[4 * c], crow[4 * c + 1], crow[4 * c + 2], crow[4 * c + 3]);
+  float rho = pos ? r : 0.0f;
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) rho = fmaxf(rho, __shfl_xor(rho, off, 16));
+  __syncthreads();
   float tau = 0.0f;
   if (pos && live) {
     if (q == 0) {
@@ -559,9 +662,21 @@ __global__ __launch_bounds__(kThreads) void sweep_certificate_kernel(const float
       const float tq = (float)q * 0.0625f;
       float a[136];
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
+      for (int i = 0; i < 16; ++i) {
+        float row[16];
 #pragma unroll
-        for (int j = 0; j <= i; ++j) a[i * (i + 1) / 2 + j] = sym_entry(hb, rs, i, j) - (i == j ? tq : 0.0f);
+        for (int c = 0; c < 4; ++c) {
+          if (4 * c <= i) {
+            const float4 v = reinterpret_cast<const float4*>(hb + i * 16)[c];
+            row[4 * c] = v.x;
+            row[4 * c + 1] = v.y;
+            row[4 * c + 2] = v.z;
+            row[4 * c + 3] = v.w;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j <= i; ++j) a[i * (i + 1) / 2 + j] = row[j] - (i == j ? tq : 0.0f);
+      }
       tau = cholesky_ok(a) ? tq - 2e-3f : 0.0f;
     }
   }
@@ -897,8 +1012,11 @@ hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
   float* cert = nullptr;
   if (a.ws != nullptr && a.ws_bytes >= sweep_ws_bytes(a.c_in, a.n_groups)) {
     cert = static_cast<float*>(a.ws);
-    sweep_certificate_kernel<<<dim3((unsigned)((per_k + kThreads / 16 - 1) / (kThreads / 16))), dim3(kThreads), 0, stream>>>(
-        a.h, a.gstride_h, nb, per_k, cert);
+    if (per_k <= kCertTeamMaxBlocks)
+      sweep_certificate_team_kernel<<<dim3((unsigned)per_k), dim3(kThreads), 0, stream>>>(a.h, a.gstride_h, nb, cert);
+    else
+      sweep_certificate_lane_kernel<<<dim3((unsigned)((per_k + kThreads / 16 - 1) / (kThreads / 16))), dim3(kThreads), 0,
+                                      stream>>>(a.h, a.gstride_h, nb, per_k, cert);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -301,3 +301,50 @@ def test_skipping_never_changes_results(lh):
         parity.sweep_against_oracle(w_np, h.cpu().numpy(), amax.cpu().numpy(), c_out, c_in, 1, sel,
                                     outs[0][0].cpu().numpy(), outs[0][1].cpu().numpy(), outs[0][2].cpu().numpy(),
                                     name)
+
+
+@pytest.mark.parametrize("copies", [1, 7])   # 320 blocks (one workgroup per block), 2240 (one lane per tau)
+def test_certificate_is_a_valid_eigenvalue_bound(lh, copies):
+    """The per-block skip certificate left in the sweep's workspace is a
+    lower bound on the smallest eigenvalue of C = D^-1/2 S D^-1/2
+    (S = (H + H^T)/2, D = diag S), checked in fp64 with numpy: 0 where no
+    bound is certified (singular, indefinite, zero diagonal), else at least
+    0.02 and within 1/16 + 2e-3 below the best grid value q/16 that the
+    exact eigenvalue allows (or at the Gershgorin bound)."""
+    rng = np.random.default_rng(26)
+    hs = []
+    for n_tok in (2000, 100, 40, 17, 3):
+        x = rng.standard_normal((64 * 16, n_tok)) * np.exp(rng.standard_normal((64 * 16, 1)))
+        hs.append(oracle.hessian(x.astype(np.float32), 64 * 16, n_tok)[1].reshape(64, 16, 16))
+    h = np.concatenate(hs)
+    h[3, 5, 5] = -h[3, 5, 5]            # indefinite
+    h[7, 2, :] = h[7, :, 2] = 0.0       # zero row: diagonal not positive
+    h[9] *= np.float32(2.0 ** 60)       # scale leaves C unchanged
+    h[11, 0, 1] += np.float32(0.3) * np.sqrt(h[11, 0, 0] * h[11, 1, 1])   # non-symmetric
+    h = np.ascontiguousarray(np.tile(h, (copies, 1, 1)))
+    nb = h.shape[0]
+    c_in = nb * 16
+    w = torch.from_numpy((rng.standard_normal((4, c_in)) * 0.02).astype(np.float32)).to(DEV)
+    hd = torch.from_numpy(h).reshape(1, nb, 16, 16).to(DEV)
+    amax = lh.lh_absmax(w)
+    ws = torch.full((lh.lh_sweep_workspace_bytes(c_in, 1) // 4,), -1.0, dtype=torch.float32, device=DEV)
+    lh.lh_scale_sweep(w, hd, amax, workspace=ws.view(torch.uint8))
+    torch.cuda.synchronize()
+    cert = ws.cpu().numpy()
+    n_pos = 0
+    for b in range(nb):
+        s = (h[b].astype(np.float64) + h[b].T.astype(np.float64)) / 2
+        d = np.diag(s)
+        if not np.all(d > 0):
+            assert cert[b] == 0.0, b
+            continue
+        c = s / np.sqrt(np.outer(d, d))
+        lam = np.linalg.eigvalsh(c).min()
+        assert cert[b] == 0.0 or 0.02 <= cert[b] <= lam, (b, cert[b], lam)
+        rho = (np.abs(c).sum(1) - 1).max()
+        best = max(np.floor(16 * lam - 1e-3) / 16, 1 - rho - 1e-3)   # what the grid and Gershgorin allow
+        if best >= 0.1 and 35 * 2.0 ** -24 * (1 + rho) / best <= 2.0 ** -12:
+            assert cert[b] >= best - 1 / 16 - 2e-3, (b, cert[b], lam)
+        n_pos += cert[b] > 0
+    print("  %d of %d blocks certified" % (n_pos, nb), flush=True)
+    assert n_pos > nb // 4
