@@ -973,18 +973,17 @@ template <typename T, bool kVec>
 hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
   const int64_t nb = a.c_in / 16;
   const int64_t per_k = a.n_groups * nb;
-  // About sixteen rounds of lanes at two waves per SIMD on 256 CUs, so that
-  // waves of unequal work pack well, but at least two rows per lane (its
-  // Hessian load and certificate are paid once per walk); rows split evenly.
-  const int64_t target = 256LL * 4 * 2 * 64 * 16;
-  int64_t rows_per_lane = (a.c_out * per_k + target - 1) / target;
-  if (rows_per_lane < 2) rows_per_lane = 2;
-  if (rows_per_lane > a.c_out) rows_per_lane = a.c_out;
-  const int64_t k = (a.c_out + rows_per_lane - 1) / rows_per_lane;
-  const int64_t lanes = per_k * k;
-  const int64_t grid = (lanes + kThreads - 1) / kThreads;
   const bool mse = a.h == nullptr;
   if (a.rule != 0) {
+    // Few candidates per row: two rounds of lanes at two waves per SIMD, so
+    // that each lane's Hessian load serves as many rows as possible.
+    const int64_t target = 256LL * 4 * 2 * 64 * 2;
+    int64_t k = (target + per_k - 1) / per_k;
+    if (k > a.c_out) k = a.c_out;
+    const int64_t rows_per_lane = (a.c_out + k - 1) / k;
+    k = (a.c_out + rows_per_lane - 1) / rows_per_lane;
+    const int64_t lanes = per_k * k;
+    const int64_t grid = (lanes + kThreads - 1) / kThreads;
     if (mse)
       select_kernel<T, kVec, true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
           a.rule, static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, k, lanes, nullptr, 0, a.amax,
@@ -995,6 +994,16 @@ hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
           a.amax, a.idx, a.err, a.best_amax);
     return hipGetLastError();
   }
+  // The 126-value sweep: about sixteen rounds of lanes at two waves per SIMD
+  // on 256 CUs, so that waves of unequal work pack well, but at least two
+  // rows per lane (its Hessian load and certificate are paid once per walk);
+  // rows split evenly.
+  const int64_t target = 256LL * 4 * 2 * 64 * 16;
+  int64_t rows_per_lane = (a.c_out * per_k + target - 1) / target;
+  if (rows_per_lane < 2) rows_per_lane = 2;
+  if (rows_per_lane > a.c_out) rows_per_lane = a.c_out;
+  const int64_t k = (a.c_out + rows_per_lane - 1) / rows_per_lane;
+  const int64_t lanes = per_k * k;
   const int64_t sgrid = (lanes + kSweepThreads - 1) / kSweepThreads;
   const QuantOut qo{a.wq, a.packed, a.codes, a.gscale, a.n_groups};
   const bool quant = a.wq || a.packed || a.codes || a.gscale;
