@@ -457,87 +457,190 @@ __device__ __forceinline__ float cast_q(float x, float s) {
   return copysignf(r * s, x) + 0.0f;
 }
 
-// Panel: one lane per output row quantises columns b0 .. b0+width-1 in
-// order, feeding each error to the block's later columns (held in
-// registers); writes Q and the errors E[row][i].
+// Value held by lane o of this lane's group of eight (ds_swizzle bit mode
+// within 32-lane halves: new lane = (lane & 24) | o).
+template <int o>
+__device__ __forceinline__ float group8_lane(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x18 | (o << 5)));
+}
+
+constexpr int kPanelChunk = 20;  // LDS floats per 16-column chunk: 8 chunks start on 8 disjoint bank quads
+
+// Steps for the columns owned by lanes o .. 7 of each group (see
+// gptq_panel_kernel): for each of owner o's sixteen columns, the owner
+// quantises, the error is broadcast, and every lane updates its columns.
+template <int o>
+__device__ __forceinline__ void panel_steps(float (&w)[16], float (&qv)[16], float (&ev)[16], float s, int g,
+                                            int width, const float (*u)[8 * kPanelChunk]) {
+  if constexpr (o < 8) {
+    if (16 * o >= width) return;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int i = 16 * o + c;
+      float e = 0.0f;
+      if (g == o) {
+        const float x = w[c];
+        const float qi = cast_q(x, s);
+        qv[c] = qi;
+        e = (x - qi) / u[i][o * kPanelChunk + c];
+        ev[c] = e;
+      }
+      e = group8_lane<o>(e);
+      const float4* ur = reinterpret_cast<const float4*>(&u[i][g * kPanelChunk]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 v = ur[k];
+        w[4 * k] = __builtin_fmaf(-e, v.x, w[4 * k]);
+        w[4 * k + 1] = __builtin_fmaf(-e, v.y, w[4 * k + 1]);
+        w[4 * k + 2] = __builtin_fmaf(-e, v.z, w[4 * k + 2]);
+        w[4 * k + 3] = __builtin_fmaf(-e, v.w, w[4 * k + 3]);
+      }
+    }
+    panel_steps<o + 1>(w, qv, ev, s, g, width, u);
+  }
+}
+
+// Panel: eight lanes per output row, lane g owning the block's columns
+// 16g .. 16g+15 (one NVFP4 block, so one block scale per lane).  Column i is
+// quantised by its owner; the error e_i = (w_i - q_i) / U_ii reaches the
+// row's other lanes by a broadcast within the group of eight, and every lane
+// applies w_j -= e_i U_ij (one fused multiply-add) to its sixteen columns.
+// U_ij = 0 for j < i, so the columns already quantised (never read again)
+// are the only ones an update may touch besides j > i, and each w_j with
+// j > i receives exactly the sequential chain of updates in increasing i.
+// Writes Q and the errors, transposed: E[i][row].
 __global__ __launch_bounds__(kThreads) void gptq_panel_kernel(float* __restrict__ wf, int64_t c_out, int64_t c_in,
                                                               int64_t b0, int width, const float* __restrict__ U,
                                                               int64_t ld_u, const uint8_t* __restrict__ idx,
                                                               const float* __restrict__ amax, float* __restrict__ q,
                                                               int64_t ld_q, float* __restrict__ E) {
-  __shared__ float u[kGb][kGb + 1];
-  for (int e = threadIdx.x; e < width * width; e += kThreads)
-    u[e / width][e % width] = U[(b0 + e / width) * ld_u + b0 + e % width];
+  __shared__ __attribute__((aligned(16))) float u[kGb][8 * kPanelChunk];
+  // staging: sixteen loads in flight per thread before their LDS writes
+  for (int base = 0; base < kGb * kGb / kThreads; base += 16) {
+    float v[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int e = (base + t) * kThreads + threadIdx.x;
+      const int i = e / kGb, j = e % kGb;
+      v[t] = (i < width && j < width) ? U[(b0 + i) * ld_u + b0 + j] : 0.0f;
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int e = (base + t) * kThreads + threadIdx.x;
+      const int i = e / kGb, j = e % kGb;
+      u[i][(j >> 4) * kPanelChunk + (j & 15)] = v[t];
+    }
+  }
   __syncthreads();
-  const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (r >= c_out) return;
+  const int g = threadIdx.x & 7;
+  const int64_t r = (int64_t)blockIdx.x * (kThreads / 8) + (threadIdx.x >> 3);
+  if (r >= c_out) return;  // whole groups of eight leave together
+  const bool mine = 16 * g < width;
+  float w[16];
+  if (mine) {
+    const float4* src = reinterpret_cast<const float4*>(wf + r * c_in + b0 + 16 * g);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 v = src[k];
+      w[4 * k] = v.x;
+      w[4 * k + 1] = v.y;
+      w[4 * k + 2] = v.z;
+      w[4 * k + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) w[k] = 0.0f;
+  }
   const float Sg = amax[0] / kAmaxDivisor;
-  const int64_t nb = c_in / 16;
-  float w[kGb];
+  const float s = mine ? e4m3_candidate(idx[r * (c_in / 16) + (b0 >> 4) + g]) * Sg : 0.0f;
+  float qv[16], ev[16];
+  panel_steps<0>(w, qv, ev, s, g, width, u);
+  if (mine) {
 #pragma unroll
-  for (int i = 0; i < kGb; ++i) w[i] = i < width ? wf[r * c_in + b0 + i] : 0.0f;
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kGb; ++i) {
-    if (i < width) {
-      if (i % 16 == 0) s = e4m3_candidate(idx[r * nb + (b0 + i) / 16]) * Sg;
-      const float x = w[i];
-      const float qi = cast_q(x, s);
-      q[r * ld_q + b0 + i] = qi;
-      const float e = (x - qi) / u[i][i];
-      E[r * kGb + i] = e;
-#pragma unroll
-      for (int j = i + 1; j < kGb; ++j) w[j] = __builtin_fmaf(-e, u[i][j], w[j]);
+    for (int c = 0; c < 16; ++c) {
+      q[r * ld_q + b0 + 16 * g + c] = qv[c];
+      E[(int64_t)(16 * g + c) * c_out + r] = ev[c];
     }
   }
 }
 
-// Trailing columns: wf[r][j] for j >= b0 + width, updates from the block's
-// columns i in increasing order.  64 x 64 tile per workgroup, 4 x 4 per
-// thread; E and U rows staged in LDS.
+// Trailing columns j >= b0 + width: wf[r][j] receives the block's updates
+// -E[i][r] U[b0+i][j] as fused multiply-adds in increasing i (the sequential
+// chain).  128 x 128 tile per workgroup, 8 x 8 per thread; E^T and the U
+// rows go through LDS 64 values of i at a time (67 KB, two workgroups per
+// CU).
+constexpr int kTrail = 128;
+constexpr int kTrailI = 64;
 __global__ __launch_bounds__(kThreads) void gptq_trailing_kernel(float* __restrict__ wf, int64_t c_out, int64_t c_in,
                                                                  int64_t b0, int width, const float* __restrict__ U,
                                                                  int64_t ld_u, const float* __restrict__ E) {
-  __shared__ float es[kTile][kGb + 1];
-  __shared__ float us[kGb][kTile + 4];
-  const int64_t j0 = b0 + width + (int64_t)blockIdx.x * kTile;
-  const int64_t r0 = (int64_t)blockIdx.y * kTile;
-  for (int e = threadIdx.x; e < kTile * kGb; e += kThreads) {
-    const int rr = e / kGb, i = e % kGb;
-    es[rr][i] = (r0 + rr < c_out && i < width) ? E[(r0 + rr) * kGb + i] : 0.0f;
-  }
-  for (int e = threadIdx.x; e < kGb * kTile; e += kThreads) {
-    const int i = e / kTile, jj = e % kTile;
-    us[i][jj] = (i < width && j0 + jj < c_in) ? U[(b0 + i) * ld_u + j0 + jj] : 0.0f;
-  }
-  __syncthreads();
-  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;  // 16 x 16 threads, 4 x 4 each
-  float acc[4][4];
+  constexpr int kP = kTrail + 4;
+  __shared__ __attribute__((aligned(16))) float es[kTrailI][kP];
+  __shared__ __attribute__((aligned(16))) float us[kTrailI][kP];
+  const int64_t j0 = b0 + width + (int64_t)blockIdx.x * kTrail;
+  const int64_t r0 = (int64_t)blockIdx.y * kTrail;
+  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
+  const int64_t jc = j0 + 8 * tc;
+  const bool cols = jc < c_in;  // c_in is a multiple of 16: all eight columns or none
+  float acc[8][8];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 8; ++a) {
+    const int64_t r = r0 + 8 * tr + a;
+    if (r < c_out && cols) {
+      const float4* src = reinterpret_cast<const float4*>(wf + r * c_in + jc);
+      const float4 v0 = src[0], v1 = src[1];
+      acc[a][0] = v0.x; acc[a][1] = v0.y; acc[a][2] = v0.z; acc[a][3] = v0.w;
+      acc[a][4] = v1.x; acc[a][5] = v1.y; acc[a][6] = v1.z; acc[a][7] = v1.w;
+    } else {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int64_t r = r0 + 4 * tr + a, j = j0 + 4 * tc + b;
-      acc[a][b] = (r < c_out && j < c_in) ? wf[r * c_in + j] : 0.0f;
+      for (int b = 0; b < 8; ++b) acc[a][b] = 0.0f;
     }
-  for (int i = 0; i < width; ++i) {
-    float ev[4], uv[4];
+  }
+  for (int i0 = 0; i0 < width; i0 += kTrailI) {
+    if (i0 > 0) __syncthreads();  // every thread is done with the previous chunk
+    // staging: sixteen loads of each array in flight per thread before their
+    // LDS writes
+    for (int base = 0; base < kTrailI * kTrail / kThreads; base += 16) {
+      float ve[16], vu[16];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) ev[a] = es[4 * tr + a][i];
+      for (int t = 0; t < 16; ++t) {
+        const int e = (base + t) * kThreads + threadIdx.x;
+        const int i = i0 + e / kTrail, x = e % kTrail;
+        ve[t] = (i < width && r0 + x < c_out) ? E[(int64_t)i * c_out + r0 + x] : 0.0f;
+        vu[t] = (i < width && j0 + x < c_in) ? U[(b0 + i) * ld_u + j0 + x] : 0.0f;
+      }
 #pragma unroll
-    for (int b = 0; b < 4; ++b) uv[b] = us[i][4 * tc + b];
+      for (int t = 0; t < 16; ++t) {
+        const int e = (base + t) * kThreads + threadIdx.x;
+        es[e / kTrail][e % kTrail] = ve[t];
+        us[e / kTrail][e % kTrail] = vu[t];
+      }
+    }
+    __syncthreads();
+    const int n = width - i0 < kTrailI ? width - i0 : kTrailI;
+#pragma unroll 2
+    for (int i = 0; i < n; ++i) {
+      const float4 e0 = *reinterpret_cast<const float4*>(&es[i][8 * tr]);
+      const float4 e1 = *reinterpret_cast<const float4*>(&es[i][8 * tr + 4]);
+      const float4 v0 = *reinterpret_cast<const float4*>(&us[i][8 * tc]);
+      const float4 v1 = *reinterpret_cast<const float4*>(&us[i][8 * tc + 4]);
+      const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+      const float uv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < 8; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fmaf(-ev[a], uv[b], acc[a][b]);
+        for (int b = 0; b < 8; ++b) acc[a][b] = __builtin_fmaf(-ev[a], uv[b], acc[a][b]);
+    }
   }
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int64_t r = r0 + 4 * tr + a, j = j0 + 4 * tc + b;
-      if (r < c_out && j < c_in) wf[r * c_in + j] = acc[a][b];
+  for (int a = 0; a < 8; ++a) {
+    const int64_t r = r0 + 8 * tr + a;
+    if (r < c_out && cols) {
+      float4* dst = reinterpret_cast<float4*>(wf + r * c_in + jc);
+      dst[0] = make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);
+      dst[1] = make_float4(acc[a][4], acc[a][5], acc[a][6], acc[a][7]);
     }
+  }
 }
 
 template <typename T, bool kVec>
@@ -644,11 +747,13 @@ hipError_t launch_gptq_quantize(const GptqQuantizeArgs& a, hipStream_t stream) {
   if (err != hipSuccess) return err;
   for (int64_t b0 = 0; b0 < a.c_in; b0 += kGb) {
     const int width = (int)(a.c_in - b0 < kGb ? a.c_in - b0 : kGb);
-    gptq_panel_kernel<<<dim3((unsigned)((a.c_out + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream>>>(
+    const int64_t rows_per_wg = kThreads / 8;  // eight lanes per row
+    gptq_panel_kernel<<<dim3((unsigned)((a.c_out + rows_per_wg - 1) / rows_per_wg)), dim3(kThreads), 0, stream>>>(
         wf, a.c_out, a.c_in, b0, width, a.u, a.ld_u, a.idx, a.amax, a.q, a.ld_q, E);
     const int64_t rest = a.c_in - b0 - width;
     if (rest > 0)
-      gptq_trailing_kernel<<<dim3((unsigned)((rest + kTile - 1) / kTile), (unsigned)((a.c_out + kTile - 1) / kTile)),
+      gptq_trailing_kernel<<<dim3((unsigned)((rest + kTrail - 1) / kTrail),
+                                  (unsigned)((a.c_out + kTrail - 1) / kTrail)),
                              dim3(kThreads), 0, stream>>>(wf, a.c_out, a.c_in, b0, width, a.u, a.ld_u, E);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
