@@ -86,6 +86,25 @@ struct DiffLoader {
   }
 };
 
+// fp32 operand I_shifted - T: element (row, k) = [row == off + k] - t[row][k]
+// (t may be null: the shifted identity alone), formed while loading.
+struct EyeMinusLoader {
+  const float* t;
+  int64_t ld;
+  int64_t off;
+  __device__ __forceinline__ void group(int64_t) {}
+  __device__ __forceinline__ uint4 chunk(int64_t row, int64_t k, int64_t rows_end, int64_t k_end) const {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool in = row < rows_end && k + i < k_end;
+      const float e = (row == off + k + i) ? 1.0f : 0.0f;
+      v[i] = in ? e - (t ? t[row * ld + k + i] : 0.0f) : 0.0f;
+    }
+    return __builtin_bit_cast(uint4, v);
+  }
+};
+
 template <typename T>
 __device__ __forceinline__ f32x4_t mfma_step(const T* a, const T* b, f32x4_t acc);
 template <>
@@ -301,17 +320,18 @@ __global__ __launch_bounds__(kThreads) void histogram_kernel(const T* __restrict
 // So the result does not depend on the blocking.
 //
 // U without forming H'^-1: with P the index reversal, A = P H' P = L L^T
-// (lower Cholesky, blocked: 64 x 64 diagonal factor in LDS, panel solve,
-// trailing update on the matrix-core GEMM), then H' = R R^T with R = P L P
-// upper, and U = R^-1 = P L^-1 P.  L^-1 is formed by block rows:
-// X_i = L_ii^-1 (E_i - L_i,<i X_<i), the product on the GEMM (with X stored
-// transposed so that both operands are K-contiguous), the 64 x 64 solve
-// per column in a small kernel.
+// (lower Cholesky, blocked by 64: one wave factorises the diagonal block in
+// registers and inverts it; the panel L_r = A_r L_kk^-T and the trailing
+// update A -= L_r L_r^T run on the matrix-core GEMM), then H' = R R^T with
+// R = P L P upper, and U = R^-1 = P L^-1 P.  L^-1 is formed by block rows,
+// X_i = L_ii^-1 (E_i - L_i,<i X_<i), both products on the GEMM (X stored
+// transposed so that every operand is K-contiguous).
 // ---------------------------------------------------------------------------
 constexpr int kCb = 64;     // Cholesky / inverse block
 constexpr int kGb = 128;    // GPTQ column block
 
-// ws layout (floats): A/L [n][n] | Y = (L^-1)^T [n][n] | T [64][n] | scalar
+// ws layout (floats): A/L [n][n] | Y = (L^-1)^T [n][n] | T [n][64] |
+// inverses of the diagonal blocks [blocks][64][64] | scalars
 __global__ __launch_bounds__(kThreads) void gptq_damp_kernel(const float* __restrict__ h, int64_t n, int64_t ld_h,
                                                              float damp, float* __restrict__ out) {
   __shared__ float part[kThreads];
@@ -346,79 +366,72 @@ __global__ __launch_bounds__(kThreads) void gptq_reverse_kernel(const float* __r
 }
 
 // In-place lower Cholesky of the bs x bs diagonal block at (k0, k0) of A,
-// by one wave: lane i keeps row i in registers (padded with the identity
-// beyond bs), and column j's entries reach the other lanes through
-// v_readlane at compile-time lane indices.  Lane i's lower entries only ever
-// combine lower entries (a[c] -= a[j] l_cj with j < c <= i), so whatever the
-// upper part holds is never used; it is written back as zeros.
+// by one wave, and the inverse of the factor into Li (64 x 64): lane i keeps
+// row i in registers (padded with the identity beyond bs); the pivot comes
+// from lane j by v_readlane and column j's entries reach the other lanes
+// through LDS.  Lane i's lower entries only ever combine lower entries
+// (a[c] -= a[j] l_cj with j < c <= i), so whatever the upper part holds is
+// never used; it is written back as zeros.
 __device__ __forceinline__ float lane_value(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-__global__ __launch_bounds__(64) void chol_diag_kernel(float* __restrict__ A, int64_t n, int64_t k0, int bs) {
+__global__ __launch_bounds__(64) void chol_diag_kernel(float* __restrict__ A, int64_t n, int64_t k0, int bs,
+                                                       float* __restrict__ Li) {
+  __shared__ __attribute__((aligned(16))) float col[kCb];
+  __shared__ __attribute__((aligned(16))) float l[kCb][kCb + 4];
   const int i = threadIdx.x;
   float a[kCb];
 #pragma unroll
   for (int c = 0; c < kCb; ++c) a[c] = (i < bs && c < bs) ? A[(k0 + i) * n + k0 + c] : (c == i ? 1.0f : 0.0f);
+  // right-looking: column j's entries l_cj reach every lane through LDS,
+  // four at a time
 #pragma unroll
   for (int j = 0; j < kCb; ++j) {
     const float ljj = sqrtf(lane_value(a[j], j));
     const float inv = 1.0f / ljj;
     a[j] = (i == j) ? ljj : a[j] * inv;
+    if (j + 1 < kCb) {
+      col[i] = a[j];
+      __syncthreads();
 #pragma unroll
-    for (int c = j + 1; c < kCb; ++c) a[c] = __builtin_fmaf(-a[j], lane_value(a[j], c), a[c]);
+      for (int c4 = ((j + 1) & ~3); c4 < kCb; c4 += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(&col[c4]);
+        const float vc[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (c4 + t > j) a[c4 + t] = __builtin_fmaf(-a[j], vc[t], a[c4 + t]);
+      }
+      __syncthreads();  // col is rewritten for the next column
+    }
   }
+#pragma unroll
+  for (int c = 0; c < kCb; ++c) l[i][c] = c <= i ? a[c] : 0.0f;
   if (i < bs) {
 #pragma unroll
     for (int c = 0; c < kCb; ++c)
       if (c < bs) A[(k0 + i) * n + k0 + c] = c <= i ? a[c] : 0.0f;
   }
-}
-
-// Panel below the diagonal block: row r of A[k0+bs:, k0:k0+bs] := solve of
-// L_kk x = a (forward substitution; one thread per row).
-__global__ __launch_bounds__(kThreads) void chol_panel_kernel(float* __restrict__ A, int64_t n, int64_t k0, int bs) {
-  __shared__ float l[kCb][kCb + 1];
-  for (int e = threadIdx.x; e < bs * bs; e += kThreads) l[e / bs][e % bs] = A[(k0 + e / bs) * n + k0 + e % bs];
   __syncthreads();
-  const int64_t r = k0 + bs + (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (r >= n) return;
-  float* row = A + r * n + k0;
+  // L^-1 (lower; the identity padding inverts to itself): lane j solves
+  // L x = e_j by forward substitution (four partial sums per row) and
+  // writes column j.
   float x[kCb];
 #pragma unroll
-  for (int j = 0; j < kCb; ++j) {
-    if (j < bs) {
-      float v = row[j];
-      for (int c = 0; c < j; ++c) v = __builtin_fmaf(-l[j][c], x[c], v);
-      x[j] = v / l[j][j];
+  for (int r = 0; r < kCb; ++r) {
+    float p[4] = {(r == i) ? 1.0f : 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c4 = 0; c4 < r; c4 += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(&l[r][c4]);
+      const float vc[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (c4 + t < r) p[t] = __builtin_fmaf(-vc[t], x[c4 + t], p[t]);
     }
+    x[r] = ((p[0] + p[1]) + (p[2] + p[3])) / l[r][r];
   }
 #pragma unroll
-  for (int j = 0; j < kCb; ++j)
-    if (j < bs) row[j] = x[j];
-}
-
-// Block row ib of X = L^-1, stored transposed (Y[j][i0 + a] = X[i0 + a][j]):
-// for every column j < i0 + bs, y = L_ii^-1 (e_j - T[:, j]).
-__global__ __launch_bounds__(kThreads) void tri_inv_solve_kernel(const float* __restrict__ L, const float* __restrict__ T,
-                                                                 float* __restrict__ Y, int64_t n, int64_t i0, int bs) {
-  __shared__ float l[kCb][kCb + 1];
-  for (int e = threadIdx.x; e < bs * bs; e += kThreads) l[e / bs][e % bs] = L[(i0 + e / bs) * n + i0 + e % bs];
-  __syncthreads();
-  const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (j >= i0 + bs) return;
-  float y[kCb];
-#pragma unroll
-  for (int a = 0; a < kCb; ++a) {
-    if (a < bs) {
-      float v = ((j == i0 + a) ? 1.0f : 0.0f) - (i0 > 0 ? T[(int64_t)a * n + j] : 0.0f);
-      for (int c = 0; c < a; ++c) v = __builtin_fmaf(-l[a][c], y[c], v);
-      y[a] = v / l[a][a];
-    }
-  }
-#pragma unroll
-  for (int a = 0; a < kCb; ++a)
-    if (a < bs) Y[j * n + i0 + a] = y[a];
+  for (int r = 0; r < kCb; ++r) Li[r * kCb + i] = x[r];
 }
 
 // U[i][j] = X[n-1-i][n-1-j] = Y[n-1-j][n-1-i] (upper; zero below), through
@@ -675,7 +688,8 @@ hipError_t launch_output_error_typed(const OutputErrorArgs& a, hipStream_t strea
 
 
 size_t gptq_prepare_ws_bytes(int64_t n) {
-  return ((size_t)2 * n * n + (size_t)kCb * n + 64) * sizeof(float);
+  const size_t nblk = (size_t)((n + kCb - 1) / kCb);
+  return ((size_t)2 * n * n + (size_t)kCb * n + nblk * kCb * kCb + 64) * sizeof(float);
 }
 
 size_t gptq_quantize_ws_bytes(int64_t c_out, int64_t c_in) {
@@ -688,42 +702,58 @@ hipError_t launch_gptq_prepare(const GptqPrepareArgs& a, hipStream_t stream) {
   float* ws = static_cast<float*>(a.ws);
   float* A = ws;
   float* Y = A + n * n;
-  float* T = Y + n * n;
-  float* dm = T + kCb * n;
+  float* T = Y + n * n;            // T^T of the block-row products, [n][64]
+  float* Li = T + kCb * n;         // inverses of the diagonal blocks, [blocks][64][64]
+  float* dm = Li + ((n + kCb - 1) / kCb) * kCb * kCb;
   gptq_damp_kernel<<<dim3(1), dim3(kThreads), 0, stream>>>(a.h, n, a.ld_h, a.damp, dm);
   gptq_reverse_kernel<<<dim3((unsigned)((n * n + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream>>>(
       a.h, n, a.ld_h, dm, A, Y);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // blocked lower Cholesky of A
+  // blocked lower Cholesky of A: diagonal block (and its inverse), panel
+  // L_r = A_r L_kk^-T in place on the GEMM, trailing A -= L_r L_r^T
   for (int64_t k0 = 0; k0 < n; k0 += kCb) {
     const int bs = (int)(n - k0 < kCb ? n - k0 : kCb);
-    chol_diag_kernel<<<dim3(1), dim3(64), 0, stream>>>(A, n, k0, bs);
+    float* lk = Li + (k0 / kCb) * kCb * kCb;
+    chol_diag_kernel<<<dim3(1), dim3(64), 0, stream>>>(A, n, k0, bs, lk);
     const int64_t rest = n - k0 - bs;
     if (rest > 0) {
-      chol_panel_kernel<<<dim3((unsigned)((rest + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream>>>(A, n, k0, bs);
+      const unsigned tiles = (unsigned)((rest + kTile - 1) / kTile);
+      {
+        // each workgroup reads its rows of the panel before writing them
+        PlainLoader<float, true> P{A + (k0 + bs) * n + k0, n, 0};
+        PlainLoader<float, true> Lb{lk, kCb, 0};
+        GemmArgs g{rest, bs, bs, 1.0f, 0.0f, 0, A + (k0 + bs) * n + k0, n, 0, nullptr};
+        gemm_nt_kernel<float, PlainLoader<float, true>, PlainLoader<float, true>, kEpiStore>
+            <<<dim3(1, tiles, 1), dim3(kThreads), 0, stream>>>(P, Lb, g);
+      }
       PlainLoader<float, true> P{A + (k0 + bs) * n + k0, n, 0};
       GemmArgs g{rest, rest, bs, -1.0f, 1.0f, 1, A + (k0 + bs) * n + k0 + bs, n, 0, nullptr};
-      const unsigned tiles = (unsigned)((rest + kTile - 1) / kTile);
       gemm_nt_kernel<float, PlainLoader<float, true>, PlainLoader<float, true>, kEpiStore>
           <<<dim3(tiles, tiles, 1), dim3(kThreads), 0, stream>>>(P, P, g);
     }
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  // X = L^-1 by block rows, stored transposed in Y
+  // X = L^-1 by block rows, stored transposed in Y: with
+  // T^T[j][c] = sum_{k < i0} Y[j][k] L[i0 + c][k],
+  // Y[j][i0 + a] = sum_c ([j == i0 + c] - T^T[j][c]) L_ii^-1[a][c], j < i0 + bs
   for (int64_t i0 = 0; i0 < n; i0 += kCb) {
     const int bs = (int)(n - i0 < kCb ? n - i0 : kCb);
+    const int64_t m = i0 + bs;
+    const unsigned tiles = (unsigned)((m + kTile - 1) / kTile);
     if (i0 > 0) {
-      // T[a][j] = sum_{k < i0} L[i0 + a][k] Y[j][k], j < i0 + bs
-      PlainLoader<float, true> La{A + i0 * n, n, 0};
-      PlainLoader<float, true> Yb{Y, n, 0};
-      GemmArgs g{bs, i0 + bs, i0, 1.0f, 0.0f, 0, T, n, 0, nullptr};
+      PlainLoader<float, true> Ya{Y, n, 0};
+      PlainLoader<float, true> Lb{A + i0 * n, n, 0};
+      GemmArgs g{m, bs, i0, 1.0f, 0.0f, 0, T, kCb, 0, nullptr};
       gemm_nt_kernel<float, PlainLoader<float, true>, PlainLoader<float, true>, kEpiStore>
-          <<<dim3((unsigned)((i0 + bs + kTile - 1) / kTile), 1, 1), dim3(kThreads), 0, stream>>>(La, Yb, g);
+          <<<dim3(1, tiles, 1), dim3(kThreads), 0, stream>>>(Ya, Lb, g);
     }
-    tri_inv_solve_kernel<<<dim3((unsigned)((i0 + bs + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream>>>(
-        A, T, Y, n, i0, bs);
+    EyeMinusLoader D{i0 > 0 ? T : nullptr, kCb, i0};
+    PlainLoader<float, true> Lb{Li + (i0 / kCb) * kCb * kCb, kCb, 0};
+    GemmArgs g{m, bs, bs, 1.0f, 0.0f, 0, Y + i0, n, 0, nullptr};
+    gemm_nt_kernel<float, EyeMinusLoader, PlainLoader<float, true>, kEpiStore>
+        <<<dim3(1, tiles, 1), dim3(kThreads), 0, stream>>>(D, Lb, g);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
