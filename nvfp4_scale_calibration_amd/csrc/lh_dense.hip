@@ -86,25 +86,6 @@ struct DiffLoader {
   }
 };
 
-// fp32 operand I_shifted - T: element (row, k) = [row == off + k] - t[row][k]
-// (t may be null: the shifted identity alone), formed while loading.
-struct EyeMinusLoader {
-  const float* t;
-  int64_t ld;
-  int64_t off;
-  __device__ __forceinline__ void group(int64_t) {}
-  __device__ __forceinline__ uint4 chunk(int64_t row, int64_t k, int64_t rows_end, int64_t k_end) const {
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool in = row < rows_end && k + i < k_end;
-      const float e = (row == off + k + i) ? 1.0f : 0.0f;
-      v[i] = in ? e - (t ? t[row * ld + k + i] : 0.0f) : 0.0f;
-    }
-    return __builtin_bit_cast(uint4, v);
-  }
-};
-
 template <typename T>
 __device__ __forceinline__ f32x4_t mfma_step(const T* a, const T* b, f32x4_t acc);
 template <>
@@ -330,8 +311,8 @@ __global__ __launch_bounds__(kThreads) void histogram_kernel(const T* __restrict
 constexpr int kCb = 64;     // Cholesky / inverse block
 constexpr int kGb = 128;    // GPTQ column block
 
-// ws layout (floats): A/L [n][n] | Y = (L^-1)^T [n][n] | T [n][64] |
-// inverses of the diagonal blocks [blocks][64][64] | scalars
+// ws layout (floats): A/L [n][n] | X = L^-1 [n][n] | Y = X^T [n][n] |
+// T [n^2 / 4] | scalars
 __global__ __launch_bounds__(kThreads) void gptq_damp_kernel(const float* __restrict__ h, int64_t n, int64_t ld_h,
                                                              float damp, float* __restrict__ out) {
   __shared__ float part[kThreads];
@@ -350,10 +331,10 @@ __global__ __launch_bounds__(kThreads) void gptq_damp_kernel(const float* __rest
   }
 }
 
-// A[i][j] = H'[n-1-i][n-1-j]; Y = 0.
+// A[i][j] = H'[n-1-i][n-1-j]; X = Y = 0.
 __global__ __launch_bounds__(kThreads) void gptq_reverse_kernel(const float* __restrict__ h, int64_t n, int64_t ld_h,
                                                                 const float* __restrict__ dm, float* __restrict__ A,
-                                                                float* __restrict__ Y) {
+                                                                float* __restrict__ X, float* __restrict__ Y) {
   const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (e >= n * n) return;
   const int64_t i = e / n, j = e - i * n;
@@ -362,11 +343,13 @@ __global__ __launch_bounds__(kThreads) void gptq_reverse_kernel(const float* __r
   if (mean == 0.0f) v = (i == j) ? 1.0f : 0.0f;
   else v = h[(n - 1 - i) * ld_h + (n - 1 - j)] + (i == j ? add : 0.0f);
   A[e] = v;
+  X[e] = 0.0f;
   Y[e] = 0.0f;
 }
 
 // In-place lower Cholesky of the bs x bs diagonal block at (k0, k0) of A,
-// by one wave, and the inverse of the factor into Li (64 x 64): lane i keeps
+// by one wave, and the inverse of the factor into the same block of X (and
+// transposed into Y): lane i keeps
 // row i in registers (padded with the identity beyond bs); the pivot comes
 // from lane j by v_readlane and column j's entries reach the other lanes
 // through LDS.  Lane i's lower entries only ever combine lower entries
@@ -377,7 +360,7 @@ __device__ __forceinline__ float lane_value(float v, int lane) {
 }
 
 __global__ __launch_bounds__(64) void chol_diag_kernel(float* __restrict__ A, int64_t n, int64_t k0, int bs,
-                                                       float* __restrict__ Li) {
+                                                       float* __restrict__ X, float* __restrict__ Y) {
   __shared__ __attribute__((aligned(16))) float col[kCb];
   __shared__ __attribute__((aligned(16))) float l[kCb][kCb + 4];
   const int i = threadIdx.x;
@@ -415,7 +398,7 @@ __global__ __launch_bounds__(64) void chol_diag_kernel(float* __restrict__ A, in
   __syncthreads();
   // L^-1 (lower; the identity padding inverts to itself): lane j solves
   // L x = e_j by forward substitution (four partial sums per row) and
-  // writes column j.
+  // writes column j of the block into X and row j into Y = X^T.
   float x[kCb];
 #pragma unroll
   for (int r = 0; r < kCb; ++r) {
@@ -430,26 +413,46 @@ __global__ __launch_bounds__(64) void chol_diag_kernel(float* __restrict__ A, in
     }
     x[r] = ((p[0] + p[1]) + (p[2] + p[3])) / l[r][r];
   }
+  __syncthreads();  // every lane is done reading l
 #pragma unroll
-  for (int r = 0; r < kCb; ++r) Li[r * kCb + i] = x[r];
+  for (int r = 0; r < kCb; ++r) l[r][i] = x[r];
+  __syncthreads();
+  if (i < bs) {
+    float* xp = X + k0 * n + k0 + i;  // X[k0 + r][k0 + i] = L^-1[r][i]
+    float* yp = Y + k0 * n + k0 + i;  // Y[k0 + r][k0 + i] = L^-1[i][r]
+    for (int r = 0; r < bs; ++r) {
+      xp[r * n] = l[r][i];
+      yp[r * n] = l[i][r];
+    }
+  }
 }
 
-// U[i][j] = X[n-1-i][n-1-j] = Y[n-1-j][n-1-i] (upper; zero below), through
-// 32 x 32 LDS tiles.
-__global__ __launch_bounds__(kThreads) void gptq_u_kernel(const float* __restrict__ Y, int64_t n, float* __restrict__ U,
+// U[i][j] = X[n-1-i][n-1-j] (upper; zero below).
+__global__ __launch_bounds__(kThreads) void gptq_u_kernel(const float* __restrict__ X, int64_t n, float* __restrict__ U,
                                                           int64_t ld_u) {
+  const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (e >= n * n) return;
+  const int64_t i = e / n, j = e - i * n;
+  U[i * ld_u + j] = (j >= i) ? X[(n - 1 - i) * n + (n - 1 - j)] : 0.0f;
+}
+
+// X21 = Y12^T for each pair of one level of the triangular inverse: pair z
+// has Y12 at Y[o][o + b] and X21 at X[o + b][o], o = o0 + z * 2b (b x s2
+// and s2 x b), through 32 x 32 LDS tiles.
+__global__ __launch_bounds__(kThreads) void gptq_transpose_kernel(const float* __restrict__ Y, float* __restrict__ X,
+                                                                  int64_t n, int64_t o0, int64_t b, int64_t s2) {
   __shared__ float t[32][33];
-  const int64_t bi = (int64_t)blockIdx.y * 32, bj = (int64_t)blockIdx.x * 32;
+  const int64_t o = o0 + (int64_t)blockIdx.z * 2 * b;
+  const int64_t m0 = (int64_t)blockIdx.y * 32, c0 = (int64_t)blockIdx.x * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
   for (int r = ty; r < 32; r += 8) {
-    // tile element (i = bi + r, j = bj + tx) needs Y[n-1-j][n-1-i]; read it row-wise
-    const int64_t yr = n - 1 - (bj + r), yc = n - 1 - (bi + tx);
-    t[r][tx] = (yr >= 0 && yr < n && yc >= 0 && yc < n) ? Y[yr * n + yc] : 0.0f;
+    const int64_t m = m0 + r, c = c0 + tx;
+    t[r][tx] = (m < b && c < s2) ? Y[(o + m) * n + o + b + c] : 0.0f;
   }
   __syncthreads();
   for (int r = ty; r < 32; r += 8) {
-    const int64_t i = bi + r, j = bj + tx;
-    if (i < n && j < n) U[i * ld_u + j] = (j >= i) ? t[tx][r] : 0.0f;
+    const int64_t c = c0 + r, m = m0 + tx;
+    if (m < b && c < s2) X[(o + b + c) * n + o + m] = t[tx][r];
   }
 }
 
@@ -688,8 +691,8 @@ hipError_t launch_output_error_typed(const OutputErrorArgs& a, hipStream_t strea
 
 
 size_t gptq_prepare_ws_bytes(int64_t n) {
-  const size_t nblk = (size_t)((n + kCb - 1) / kCb);
-  return ((size_t)2 * n * n + (size_t)kCb * n + nblk * kCb * kCb + 64) * sizeof(float);
+  // A, X, Y (n x n each), T (the products of one inverse level: at most n^2 / 4)
+  return ((size_t)3 * n * n + (size_t)n * n / 4 + 64) * sizeof(float);
 }
 
 size_t gptq_quantize_ws_bytes(int64_t c_out, int64_t c_in) {
@@ -700,29 +703,28 @@ hipError_t launch_gptq_prepare(const GptqPrepareArgs& a, hipStream_t stream) {
   const int64_t n = a.n;
   if (n == 0) return hipSuccess;
   float* ws = static_cast<float*>(a.ws);
-  float* A = ws;
-  float* Y = A + n * n;
-  float* T = Y + n * n;            // T^T of the block-row products, [n][64]
-  float* Li = T + kCb * n;         // inverses of the diagonal blocks, [blocks][64][64]
-  float* dm = Li + ((n + kCb - 1) / kCb) * kCb * kCb;
+  float* A = ws;                   // A, then L
+  float* X = A + n * n;            // L^-1
+  float* Y = X + n * n;            // (L^-1)^T
+  float* T = Y + n * n;            // products of one inverse level
+  float* dm = T + n * n / 4;
   gptq_damp_kernel<<<dim3(1), dim3(kThreads), 0, stream>>>(a.h, n, a.ld_h, a.damp, dm);
   gptq_reverse_kernel<<<dim3((unsigned)((n * n + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream>>>(
-      a.h, n, a.ld_h, dm, A, Y);
+      a.h, n, a.ld_h, dm, A, X, Y);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // blocked lower Cholesky of A: diagonal block (and its inverse), panel
-  // L_r = A_r L_kk^-T in place on the GEMM, trailing A -= L_r L_r^T
+  // blocked lower Cholesky of A: diagonal block (and its inverse, into X and
+  // Y), panel L_r = A_r L_kk^-T in place on the GEMM, trailing A -= L_r L_r^T
   for (int64_t k0 = 0; k0 < n; k0 += kCb) {
     const int bs = (int)(n - k0 < kCb ? n - k0 : kCb);
-    float* lk = Li + (k0 / kCb) * kCb * kCb;
-    chol_diag_kernel<<<dim3(1), dim3(64), 0, stream>>>(A, n, k0, bs, lk);
+    chol_diag_kernel<<<dim3(1), dim3(64), 0, stream>>>(A, n, k0, bs, X, Y);
     const int64_t rest = n - k0 - bs;
     if (rest > 0) {
       const unsigned tiles = (unsigned)((rest + kTile - 1) / kTile);
       {
         // each workgroup reads its rows of the panel before writing them
         PlainLoader<float, true> P{A + (k0 + bs) * n + k0, n, 0};
-        PlainLoader<float, true> Lb{lk, kCb, 0};
+        PlainLoader<float, true> Lb{X + k0 * n + k0, n, 0};
         GemmArgs g{rest, bs, bs, 1.0f, 0.0f, 0, A + (k0 + bs) * n + k0, n, 0, nullptr};
         gemm_nt_kernel<float, PlainLoader<float, true>, PlainLoader<float, true>, kEpiStore>
             <<<dim3(1, tiles, 1), dim3(kThreads), 0, stream>>>(P, Lb, g);
@@ -735,30 +737,44 @@ hipError_t launch_gptq_prepare(const GptqPrepareArgs& a, hipStream_t stream) {
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  // X = L^-1 by block rows, stored transposed in Y: with
-  // T^T[j][c] = sum_{k < i0} Y[j][k] L[i0 + c][k],
-  // Y[j][i0 + a] = sum_c ([j == i0 + c] - T^T[j][c]) L_ii^-1[a][c], j < i0 + bs
-  for (int64_t i0 = 0; i0 < n; i0 += kCb) {
-    const int bs = (int)(n - i0 < kCb ? n - i0 : kCb);
-    const int64_t m = i0 + bs;
-    const unsigned tiles = (unsigned)((m + kTile - 1) / kTile);
-    if (i0 > 0) {
-      PlainLoader<float, true> Ya{Y, n, 0};
-      PlainLoader<float, true> Lb{A + i0 * n, n, 0};
-      GemmArgs g{m, bs, i0, 1.0f, 0.0f, 0, T, kCb, 0, nullptr};
-      gemm_nt_kernel<float, PlainLoader<float, true>, PlainLoader<float, true>, kEpiStore>
-          <<<dim3(1, tiles, 1), dim3(kThreads), 0, stream>>>(Ya, Lb, g);
+  // X = L^-1 from the diagonal blocks' inverses by doubling: for each pair
+  // of neighbouring blocks [L11 0; L21 L22] of size b (the second possibly
+  // shorter, s2), X21 = -X22 L21 X11, computed as its transpose
+  // Y12 = -(Y11 L21^T) Y22 = -R X22^T with R = Y11 L21^T (both products on
+  // the GEMM with K-contiguous operands), then X21 = Y12^T.  All full pairs
+  // of a level go in one batched launch.
+  for (int64_t b = kCb; b < n; b *= 2) {
+    const int64_t full = n / (2 * b);                 // pairs of two full blocks
+    const int64_t tail_o = full * 2 * b;              // a last pair with a shorter second block
+    const int64_t tail_s2 = n - tail_o - b;           // > 0 when that pair exists
+    for (int part = 0; part < 2; ++part) {
+      const int64_t o0 = part == 0 ? 0 : tail_o;
+      const int64_t s2 = part == 0 ? b : tail_s2;
+      const int64_t groups = part == 0 ? full : (tail_s2 > 0 ? 1 : 0);
+      if (groups == 0 || s2 <= 0) continue;
+      const int64_t gs = 2 * b * (n + 1);             // one pair to the next along the diagonal
+      const unsigned tb = (unsigned)((b + kTile - 1) / kTile), ts = (unsigned)((s2 + kTile - 1) / kTile);
+      {
+        PlainLoader<float, true> Ya{Y + o0 * n + o0, n, gs};
+        PlainLoader<float, true> Lb{A + (o0 + b) * n + o0, n, gs};
+        GemmArgs g{b, s2, b, 1.0f, 0.0f, 0, T, s2, b * s2, nullptr};  // R: b x s2 per pair (<= n^2 / 4 in all)
+        gemm_nt_kernel<float, PlainLoader<float, true>, PlainLoader<float, true>, kEpiStore>
+            <<<dim3(ts, tb, (unsigned)groups), dim3(kThreads), 0, stream>>>(Ya, Lb, g);
+      }
+      {
+        PlainLoader<float, true> Ra{T, s2, b * s2};
+        PlainLoader<float, true> Xb{X + (o0 + b) * n + o0 + b, n, gs};
+        GemmArgs g{b, s2, s2, -1.0f, 0.0f, 0, Y + o0 * n + o0 + b, n, gs, nullptr};
+        gemm_nt_kernel<float, PlainLoader<float, true>, PlainLoader<float, true>, kEpiStore>
+            <<<dim3(ts, tb, (unsigned)groups), dim3(kThreads), 0, stream>>>(Ra, Xb, g);
+      }
+      gptq_transpose_kernel<<<dim3((unsigned)((s2 + 31) / 32), (unsigned)((b + 31) / 32), (unsigned)groups),
+                              dim3(kThreads), 0, stream>>>(Y, X, n, o0, b, s2);
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
     }
-    EyeMinusLoader D{i0 > 0 ? T : nullptr, kCb, i0};
-    PlainLoader<float, true> Lb{Li + (i0 / kCb) * kCb * kCb, kCb, 0};
-    GemmArgs g{m, bs, bs, 1.0f, 0.0f, 0, Y + i0, n, 0, nullptr};
-    gemm_nt_kernel<float, EyeMinusLoader, PlainLoader<float, true>, kEpiStore>
-        <<<dim3(1, tiles, 1), dim3(kThreads), 0, stream>>>(D, Lb, g);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
   }
-  const unsigned t32 = (unsigned)((n + 31) / 32);
-  gptq_u_kernel<<<dim3(t32, t32), dim3(kThreads), 0, stream>>>(Y, n, a.u, a.ld_u);
+  gptq_u_kernel<<<dim3((unsigned)((n * n + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream>>>(X, n, a.u, a.ld_u);
   return hipGetLastError();
 }
 
