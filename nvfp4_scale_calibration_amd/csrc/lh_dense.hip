@@ -366,14 +366,21 @@ __global__ __launch_bounds__(64) void chol_diag_kernel(float* __restrict__ A, in
   const int i = threadIdx.x;
   float a[kCb];
 #pragma unroll
-  for (int c = 0; c < kCb; ++c) a[c] = (i < bs && c < bs) ? A[(k0 + i) * n + k0 + c] : (c == i ? 1.0f : 0.0f);
+  for (int c4 = 0; c4 < kCb; c4 += 4) {  // bs is a multiple of 16
+    float4 v = make_float4(c4 == i, c4 + 1 == i, c4 + 2 == i, c4 + 3 == i);
+    if (i < bs && c4 < bs) v = *reinterpret_cast<const float4*>(A + (k0 + i) * n + k0 + c4);
+    a[c4] = v.x;
+    a[c4 + 1] = v.y;
+    a[c4 + 2] = v.z;
+    a[c4 + 3] = v.w;
+  }
   // right-looking: column j's entries l_cj reach every lane through LDS,
   // four at a time
 #pragma unroll
   for (int j = 0; j < kCb; ++j) {
-    const float ljj = sqrtf(lane_value(a[j], j));
-    const float inv = 1.0f / ljj;
-    a[j] = (i == j) ? ljj : a[j] * inv;
+    const float d = lane_value(a[j], j);
+    const float inv = __builtin_amdgcn_rsqf(d);  // 1/sqrt(d) to about an ulp
+    a[j] = (i == j) ? d * inv : a[j] * inv;
     if (j + 1 < kCb) {
       col[i] = a[j];
       __syncthreads();
@@ -411,7 +418,7 @@ __global__ __launch_bounds__(64) void chol_diag_kernel(float* __restrict__ A, in
       for (int t = 0; t < 4; ++t)
         if (c4 + t < r) p[t] = __builtin_fmaf(-vc[t], x[c4 + t], p[t]);
     }
-    x[r] = ((p[0] + p[1]) + (p[2] + p[3])) / l[r][r];
+    x[r] = ((p[0] + p[1]) + (p[2] + p[3])) * (1.0f / l[r][r]);  // the reciprocal is off the chain
   }
   __syncthreads();  // every lane is done reading l
 #pragma unroll
