@@ -2,12 +2,13 @@
 """Benchmark of the Local-Hessian NVFP4 calibration hot path on one MI355X.
 
 One step = the whole path over one layer's synthetic inputs, inputs resident
-in HBM: global amax -> local Hessians -> 126-candidate scale sweep and
-NVFP4 fake-quant of its result (dequantised fp32 weights + packed E2M1
-nibbles + E4M3 scale codes + S_g) in one call.  W warm-up steps, then K
-timed steps between device synchronisations; every call is also timed with
-HIP events recorded on the stream it is launched on (the current torch
-stream, which the binding passes to the library).
+in HBM: global amax and local Hessians (lh_calibrate_prologue), then the
+126-candidate scale sweep and the NVFP4 fake-quant of its result
+(dequantised fp32 weights + packed E2M1 nibbles + E4M3 scale codes + S_g,
+lh_calibrate_sweep).  W warm-up steps, then K timed steps between device
+synchronisations; the sweep's launch is also timed with HIP events recorded
+on the stream it is launched on (the current torch stream, which the binding
+passes to the library).
 
 Prints ONE JSON line.  value = NVFP4 blocks scale-swept per second over the
 whole step; the line also carries the Hessian pass in GB/s, the sweep in
@@ -372,6 +373,7 @@ def main():
     amax = torch.empty(G, dtype=torch.float32, device=dev)
     h = torch.empty((G, nb, 16, 16), dtype=torch.float32, device=dev)
     ws_bytes = lh.lh_hessian_workspace_bytes(c_in, n, G)
+    cws = torch.empty(lh.lh_calibrate_workspace_bytes(c_out, c_in, n, G), dtype=torch.uint8, device=dev)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     sws = torch.empty(max(lh.lh_sweep_workspace_bytes(c_in, G), 4), dtype=torch.uint8, device=dev)
     idx = torch.empty((G, c_out, nb), dtype=torch.uint8, device=dev)
@@ -382,16 +384,14 @@ def main():
     codes = torch.empty((G, c_out, nb), dtype=torch.uint8, device=dev)
     gscale = torch.empty(G, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    # HIP events bracket the dominant call (the sweep with its fake-quant) in
-    # every timed step; the other calls' GPU times come from graph replays
-    # (launch_ms), so the timed steps carry no further event records.
+    # HIP events bracket the dominant launch (the sweep with its fake-quant,
+    # one kernel) in every timed step; the other calls' GPU times come from
+    # graph replays (launch_ms), so the timed steps carry no further records.
     def step(ev=None):
-        lh.lh_absmax(w, out=amax)
-        lh.lh_accumulate_hessian(x, h=h, workspace=ws if ws_bytes else None)
+        lh.lh_calibrate_prologue(w, x, amax, h, cws)
         if ev is not None:
             ev[0].record(stream)
-        lh.lh_scale_sweep_fake_quant(w, h, amax, best_idx=idx, best_err=err, best_amax=bam, w_q=wq, packed=packed,
-                                     scale_e4m3=codes, global_scale=gscale, workspace=sws)
+        lh.lh_calibrate_sweep(w, h, amax, cws, idx, err, bam, wq, packed, codes, gscale)
         if ev is not None:
             ev[1].record(stream)
 
@@ -405,10 +405,13 @@ def main():
         step(events[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_kernel_ms = {"sweep_fake_quant": sum(e[0].elapsed_time(e[1]) for e in events) / args.steps}
-    # per-launch GPU time of each call, free of host launch overhead
-    # (the sweep and the fake-quant also as two separate calls, for comparison)
+    per_kernel_ms = {"calibrate_sweep": sum(e[0].elapsed_time(e[1]) for e in events) / args.steps}
+    # per-call GPU time, free of host launch overhead: the step's two calls,
+    # and for comparison the separate calls that compute the same
     launch_ms = {
+        "calibrate_prologue": graph_time(lambda: lh.lh_calibrate_prologue(w, x, amax, h, cws)),
+        "calibrate_sweep": graph_time(lambda: lh.lh_calibrate_sweep(w, h, amax, cws, idx, err, bam, wq, packed,
+                                                                    codes, gscale), reps=5),
         "absmax": graph_time(lambda: lh.lh_absmax(w, out=amax)),
         "hessian": graph_time(lambda: lh.lh_accumulate_hessian(x, h=h, workspace=ws if ws_bytes else None)),
         "sweep_fake_quant": graph_time(lambda: lh.lh_scale_sweep_fake_quant(
@@ -420,8 +423,10 @@ def main():
                                                                 scale_e4m3=codes, global_scale=gscale)),
     }
     ms_per_step = wall * 1e3 / args.steps
-    sweep_s = per_kernel_ms["sweep_fake_quant"] / 1e3
+    sweep_s = per_kernel_ms["calibrate_sweep"] / 1e3
     hess_gbps = work.x_bytes / (launch_ms["hessian"] / 1e3) / 1e9
+    w_bytes = work.w.numel() * work.w.element_size()
+    pro_gbps = (work.x_bytes + w_bytes) / (launch_ms["calibrate_prologue"] / 1e3) / 1e9
     achieved_tflops = SWEEP_FLOP_PER_BLOCK * blocks / sweep_s / 1e12
     src_hash = kernel_source_hash()
     traffic = traffic_from_profiles("sweep", wl.SHORT_NAMES[args.workload], src_hash)
@@ -456,6 +461,7 @@ def main():
         "copy_gbps": copy_bw,
         "hessian": {"gbps": hess_gbps, "frac_hbm": hess_gbps / HBM_PEAK_GBPS, "frac_copy": hess_gbps / copy_bw,
                     "x_bytes": work.x_bytes, "warm": True},
+        "prologue": {"gbps": pro_gbps, "frac_hbm": pro_gbps / HBM_PEAK_GBPS, "bytes": work.x_bytes + w_bytes},
         "source_hash": src_hash,
     }
     if not args.no_extras:

@@ -266,6 +266,77 @@ lh_status lh_scale_sweep_fake_quant(const void *w, int w_dtype, int64_t c_out, i
                                     void *stream);
 
 /*
+ * Scratch bytes lh_calibrate_nvfp4 needs: the per-block skip certificates
+ * and the Hessian's per-slice partial sums (and partial amax values).
+ */
+size_t lh_calibrate_workspace_bytes(int64_t c_out, int64_t c_in, int64_t n_tokens, int64_t n_groups);
+
+/*
+ * The first half of lh_calibrate_nvfp4: amax and h (as lh_absmax and
+ * lh_accumulate_hessian with alpha = fl32(1/N), beta = 0), and the sweep's
+ * skip certificates, which stay in the workspace for lh_calibrate_sweep.
+ * Arguments as lh_calibrate_nvfp4.  With channel-major X and a contiguous W
+ * (ld_w == c_in), both 16-byte aligned, this is two launches (amax and the
+ * Hessian's token slices in one, the Hessian's finalisation with the
+ * certificates in the other).
+ * Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_LAYOUT,
+ * LH_ERR_WORKSPACE, LH_ERR_ARG, LH_ERR_HIP.
+ */
+lh_status lh_calibrate_prologue(const void *w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
+                                int64_t n_groups, int64_t group_stride_w, const void *x, int x_dtype,
+                                int x_layout, int64_t n_tokens, int64_t ld_x, int64_t group_stride_x,
+                                float *amax, float *h, int64_t group_stride_h, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/*
+ * The second half of lh_calibrate_nvfp4: lh_scale_sweep_fake_quant with the
+ * certificates that lh_calibrate_prologue left in the workspace (same
+ * workspace, same h and w, in stream order; no other call may write the
+ * workspace in between).  Arguments as lh_scale_sweep_fake_quant; the
+ * workspace is required.
+ * Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_WORKSPACE,
+ * LH_ERR_ARG, LH_ERR_HIP.
+ */
+lh_status lh_calibrate_sweep(const void *w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
+                             int64_t n_groups, int64_t group_stride_w, const float *h,
+                             int64_t group_stride_h, const float *amax, uint8_t *best_idx,
+                             float *best_err, float *best_amax, float *w_q, uint8_t *packed_e2m1,
+                             uint8_t *scale_e4m3, float *global_scale, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * The whole calibration path for a layer in one call: the global amax of W
+ * ("Algorithm principle": the kernel receives the global FP32 amax), the
+ * normalised local Hessians H_b = X_b X_b^T / N ("Entry API and calibration
+ * flow", phase 3), the 126-candidate sweep and the fake-quant of its result
+ * (as lh_scale_sweep_fake_quant).  Every output equals what lh_absmax,
+ * lh_accumulate_hessian (alpha = fl32(1/N), beta = 0), lh_scale_sweep and
+ * lh_fake_quant_nvfp4 write, bit for bit.
+ *   w, w_dtype, c_out, c_in, ld_w, n_groups, group_stride_w: as lh_scale_sweep.
+ *   x, x_dtype, x_layout, n_tokens, ld_x, group_stride_x: as
+ *             lh_accumulate_hessian (N = n_tokens; N = 0 gives H = 0).
+ *   amax      fp32 [n_groups] output.
+ *   h         fp32 [n_groups][c_in/16][16][16] output, 16-byte aligned,
+ *             group stride group_stride_h (multiple of 4).
+ *   best_idx (required), best_err, best_amax, w_q, packed_e2m1, scale_e4m3,
+ *   global_scale: as lh_scale_sweep_fake_quant.
+ *   workspace: at least lh_calibrate_workspace_bytes(c_out, c_in, n_tokens,
+ *             n_groups) bytes, 256-byte aligned, required.
+ * It is lh_calibrate_prologue followed by lh_calibrate_sweep: three
+ * launches with channel-major X and a contiguous W, both 16-byte aligned;
+ * other layouts run the separate calls' kernels in turn.
+ * Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_LAYOUT,
+ * LH_ERR_WORKSPACE, LH_ERR_ARG, LH_ERR_HIP.
+ */
+lh_status lh_calibrate_nvfp4(const void *w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
+                             int64_t n_groups, int64_t group_stride_w, const void *x, int x_dtype,
+                             int x_layout, int64_t n_tokens, int64_t ld_x, int64_t group_stride_x,
+                             float *amax, float *h, int64_t group_stride_h, uint8_t *best_idx,
+                             float *best_err, float *best_amax, float *w_q, uint8_t *packed_e2m1,
+                             uint8_t *scale_e4m3, float *global_scale, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
  * Block-scale selection by rule: the scale rules the Local-Hessian guide
  * compares against ("What is Local-Hessian": max scaling takes the block
  * scale from the block's largest |w|; Four-Over-Six picks one of two

@@ -65,6 +65,15 @@ def _load() -> ctypes.CDLL:
     lib.lh_scale_sweep_fake_quant.argtypes = [P, I, I64, I64, I64, I64, I64, P, I64, P, P, P, P, P, P, P, P, P,
                                               SZ, P]
     lib.lh_scale_sweep_fake_quant.restype = I
+    lib.lh_calibrate_workspace_bytes.argtypes = [I64, I64, I64, I64]
+    lib.lh_calibrate_workspace_bytes.restype = SZ
+    lib.lh_calibrate_nvfp4.argtypes = [P, I, I64, I64, I64, I64, I64, P, I, I, I64, I64, I64, P, P, I64, P, P, P, P, P,
+                                       P, P, P, SZ, P]
+    lib.lh_calibrate_nvfp4.restype = I
+    lib.lh_calibrate_prologue.argtypes = [P, I, I64, I64, I64, I64, I64, P, I, I, I64, I64, I64, P, P, I64, P, SZ, P]
+    lib.lh_calibrate_prologue.restype = I
+    lib.lh_calibrate_sweep.argtypes = [P, I, I64, I64, I64, I64, I64, P, I64, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.lh_calibrate_sweep.restype = I
     lib.lh_full_hessian.argtypes = [P, I, I64, I64, I64, I64, I64, F, P, I64, I64, P]
     lib.lh_full_hessian.restype = I
     lib.lh_output_error_workspace_bytes.argtypes = [I64, I64, I64]
@@ -88,7 +97,8 @@ lib = _load()
 EXPORTS = ("lh_abi_version", "lh_status_string", "lh_last_error_message", "lh_absmax",
            "lh_hessian_workspace_bytes", "lh_accumulate_hessian", "lh_hessian_ragged_workspace_bytes",
            "lh_accumulate_hessian_ragged", "lh_sweep_workspace_bytes", "lh_scale_sweep",
-           "lh_scale_sweep_fake_quant", "lh_select_scales", "lh_fake_quant_nvfp4", "lh_full_hessian", "lh_output_error_workspace_bytes",
+           "lh_scale_sweep_fake_quant", "lh_calibrate_workspace_bytes", "lh_calibrate_nvfp4",
+           "lh_calibrate_prologue", "lh_calibrate_sweep", "lh_select_scales", "lh_fake_quant_nvfp4", "lh_full_hessian", "lh_output_error_workspace_bytes",
            "lh_output_error", "lh_scaled_histogram", "lh_gptq_workspace_bytes", "lh_gptq_prepare",
            "lh_gptq_quantize")
 
@@ -327,6 +337,114 @@ def lh_scale_sweep_fake_quant(w: torch.Tensor, h: torch.Tensor, amax: torch.Tens
     res = dict(idx=idx, err=err, amax=bam)
     res.update({k: v for k, v in quant.items() if v is not None})
     return res
+
+
+def lh_calibrate_workspace_bytes(c_out: int, c_in: int, n_tokens: int, n_groups: int = 1) -> int:
+    return int(lib.lh_calibrate_workspace_bytes(c_out, c_in, n_tokens, n_groups))
+
+
+def _calibrate_outputs(w3, x3, layout, out, best_err, best_amax, w_q, packed, scale_e4m3, global_scale):
+    g, c_out, c_in = w3.shape
+    if layout == "channel":
+        lay, n_tok = LH_LAYOUT_CHANNEL_MAJOR, x3.shape[2]
+    elif layout == "token":
+        lay, n_tok = LH_LAYOUT_TOKEN_MAJOR, x3.shape[1]
+    else:
+        raise ValueError("layout must be 'channel' or 'token'")
+    if n_tok > 0 and x3.stride(-1) != 1:
+        raise ValueError("last dim of x must be contiguous")
+    nb = c_in // BLOCK
+    dev = w3.device
+    out = dict(out or {})
+
+    def get(name, req, shape, dtype):
+        if name in out:
+            return out[name]
+        return torch.empty(shape, dtype=dtype, device=dev) if req else None
+
+    res = dict(amax=get("amax", True, (g,), torch.float32),
+               h=get("h", True, (g, nb, 16, 16), torch.float32),
+               idx=get("idx", True, (g, c_out, nb), torch.uint8),
+               err=get("err", best_err, (g, c_out, nb), torch.float32),
+               amax_blk=get("amax_blk", best_amax, (g, c_out, nb), torch.float32),
+               w_q=get("w_q", w_q, (g, c_out, c_in), torch.float32),
+               packed=get("packed", packed, (g, c_out, c_in // 2), torch.uint8),
+               scale_e4m3=get("scale_e4m3", scale_e4m3, (g, c_out, nb), torch.uint8),
+               global_scale=get("global_scale", global_scale, (g,), torch.float32))
+    if n_tok > 0:
+        ld_x = _ld(x3)
+    else:  # nothing is read; any row stride the boundary accepts
+        ld_x = 1 if lay == LH_LAYOUT_CHANNEL_MAJOR else max(c_in, 1)
+    return res, lay, n_tok, ld_x
+
+
+def lh_calibrate_nvfp4(w: torch.Tensor, x: torch.Tensor, layout: str = "channel", out: dict | None = None,
+                       best_err: bool = True, best_amax: bool = True, w_q: bool = True, packed: bool = False,
+                       scale_e4m3: bool = False, global_scale: bool = False,
+                       workspace: torch.Tensor | None = None, split: bool = False) -> dict:
+    """The whole path: global amax, normalised local Hessians (x
+    [.., c_in, N] channel-major or [.., N, c_in] token-major), the
+    126-candidate sweep and the fake-quant of its result.  Returns a dict
+    with amax, h, idx and the requested outputs (err, amax_blk, w_q, packed,
+    scale_e4m3, global_scale); tensors given in `out` under those names are
+    written in place.  split=True makes the same computation as the two calls
+    lh_calibrate_prologue and lh_calibrate_sweep."""
+    _require_device(w, x)
+    w3, x3 = _as3(w), _as3(x)
+    if w3.stride(-1) != 1:
+        raise ValueError("last dim of w must be contiguous")
+    g, c_out, c_in = w3.shape
+    res, lay, n_tok, ld_x = _calibrate_outputs(w3, x3, layout, out, best_err, best_amax, w_q, packed, scale_e4m3,
+                                               global_scale)
+    if workspace is None:
+        workspace = torch.empty(max(lh_calibrate_workspace_bytes(c_out, c_in, n_tok, g), 1), dtype=torch.uint8,
+                                device=w.device)
+    wsb = workspace.numel() * workspace.element_size()
+    h = res["h"]
+    h_gstride = h.stride(0) if h.dim() == 4 and h.shape[0] > 1 else 0
+    wargs = (_ptr(w3), _dtype(w3), c_out, c_in, _ld(w3), g, _group_stride(w3))
+    fq = (_ptr(res["w_q"]), _ptr(res["packed"]), _ptr(res["scale_e4m3"]), _ptr(res["global_scale"]))
+    if split:
+        _check(lib.lh_calibrate_prologue(*wargs, _ptr(x3), _dtype(x3), lay, n_tok, ld_x, _group_stride(x3),
+                                         _ptr(res["amax"]), _ptr(h), h_gstride, _ptr(workspace), wsb, _stream(w)))
+        _check(lib.lh_calibrate_sweep(*wargs, _ptr(h), h_gstride, _ptr(res["amax"]), _ptr(res["idx"]),
+                                      _ptr(res["err"]), _ptr(res["amax_blk"]), *fq, _ptr(workspace), wsb,
+                                      _stream(w)))
+    else:
+        _check(lib.lh_calibrate_nvfp4(*wargs, _ptr(x3), _dtype(x3), lay, n_tok, ld_x, _group_stride(x3),
+                                      _ptr(res["amax"]), _ptr(h), h_gstride, _ptr(res["idx"]), _ptr(res["err"]),
+                                      _ptr(res["amax_blk"]), *fq, _ptr(workspace), wsb, _stream(w)))
+    return {k: v for k, v in res.items() if v is not None}
+
+
+def lh_calibrate_prologue(w: torch.Tensor, x: torch.Tensor, amax: torch.Tensor, h: torch.Tensor,
+                          workspace: torch.Tensor, layout: str = "channel") -> None:
+    """amax, h and the sweep's certificates (left in workspace) for
+    lh_calibrate_sweep; output tensors given."""
+    _require_device(w, x, amax, h, workspace)
+    w3, x3 = _as3(w), _as3(x)
+    g, c_out, c_in = w3.shape
+    _, lay, n_tok, ld_x = _calibrate_outputs(w3, x3, layout, dict(amax=amax, h=h, idx=None), False, False, False,
+                                             False, False, False)
+    h_gstride = h.stride(0) if h.dim() == 4 and h.shape[0] > 1 else 0
+    _check(lib.lh_calibrate_prologue(_ptr(w3), _dtype(w3), c_out, c_in, _ld(w3), g, _group_stride(w3), _ptr(x3),
+                                     _dtype(x3), lay, n_tok, ld_x, _group_stride(x3), _ptr(amax), _ptr(h), h_gstride,
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(w)))
+
+
+def lh_calibrate_sweep(w: torch.Tensor, h: torch.Tensor, amax: torch.Tensor, workspace: torch.Tensor,
+                       best_idx: torch.Tensor, best_err=None, best_amax=None, w_q=None, packed=None, scale_e4m3=None,
+                       global_scale=None) -> None:
+    """The sweep and fake-quant with the certificates lh_calibrate_prologue
+    left in workspace; output tensors given (None to skip)."""
+    _require_device(w, h, amax, workspace, best_idx)
+    w3 = _as3(w)
+    g, c_out, c_in = w3.shape
+    h_gstride = h.stride(0) if h.dim() == 4 and h.shape[0] > 1 else 0
+    _check(lib.lh_calibrate_sweep(_ptr(w3), _dtype(w3), c_out, c_in, _ld(w3), g, _group_stride(w3), _ptr(h),
+                                  h_gstride, _ptr(amax), _ptr(best_idx), _ptr(best_err), _ptr(best_amax), _ptr(w_q),
+                                  _ptr(packed), _ptr(scale_e4m3), _ptr(global_scale), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(w)))
 
 
 def lh_select_scales(rule: int, w: torch.Tensor, h: torch.Tensor | None, amax: torch.Tensor,

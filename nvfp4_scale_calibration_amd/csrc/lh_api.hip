@@ -168,7 +168,8 @@ lh_status select_common(const char* fn, int rule, bool h_required, const void* w
                         int64_t c_in, int64_t ld_w, int64_t n_groups, int64_t group_stride_w, const float* h,
                         int64_t group_stride_h, const float* amax, uint8_t* best_idx, float* best_err,
                         float* best_amax, void* workspace, size_t workspace_bytes, void* stream,
-                        QuantPtrs qp = QuantPtrs{nullptr, nullptr, nullptr, nullptr}) {
+                        QuantPtrs qp = QuantPtrs{nullptr, nullptr, nullptr, nullptr}, bool cert_ready = false,
+                        bool launch = true) {
   g_msg[0] = '\0';
   if (rule < 0 || rule > 3) return fail(LH_ERR_ARG, "%s: rule must be 0..3", fn);
   if (!valid_dtype(w_dtype)) return fail(LH_ERR_DTYPE, "%s: w_dtype must be 0 (f32) or 1 (bf16)", fn);
@@ -191,6 +192,7 @@ lh_status select_common(const char* fn, int rule, bool h_required, const void* w
   if (!aligned(qp.w_q, 16) || !aligned(qp.packed, 8) || !aligned(qp.gscale, 4))
     return fail(LH_ERR_ARG, "%s: misaligned pointer (w_q needs 16 bytes, packed_e2m1 8, global_scale 4)", fn);
   if (qp.gscale != nullptr && n_groups > 0 && amax == nullptr) return fail(LH_ERR_NULL, "%s: amax is NULL", fn);
+  if (!launch) return LH_OK;   // arguments checked only
   if (!work) {
     if (qp.gscale == nullptr || n_groups == 0) return LH_OK;
     // no block, but S_g is still asked for
@@ -201,9 +203,39 @@ lh_status select_common(const char* fn, int rule, bool h_required, const void* w
   }
   lh::SweepArgs a{w, w_dtype, c_out, c_in, ld_w, n_groups, group_stride_w, h, group_stride_h, amax,
                   best_idx, best_err, best_amax, workspace, workspace_bytes, rule,
-                  qp.w_q, qp.packed, qp.codes, qp.gscale};
+                  qp.w_q, qp.packed, qp.codes, qp.gscale, cert_ready};
   hipError_t e = lh::launch_sweep(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LH_OK : hip_fail(e, fn);
+}
+
+// Workspace of lh_calibrate_nvfp4: the per-block certificates, then the
+// Hessian partial sums (of the fused prologue or of lh_accumulate_hessian),
+// then the prologue's partial maxima.
+size_t calibrate_cert_bytes(int64_t c_in, int64_t n_groups) {
+  return ((size_t)n_groups * (size_t)(c_in / 16) * sizeof(float) + 255) & ~(size_t)255;
+}
+
+size_t calibrate_ws_bytes(int64_t c_out, int64_t c_in, int64_t n_tokens, int64_t n_groups) {
+  const size_t fused = lh::prologue_ws_bytes(c_in, n_tokens, n_groups, c_out * c_in);
+  const size_t plain = lh::hessian_ws_bytes(c_in, n_tokens, n_groups);
+  return calibrate_cert_bytes(c_in, n_groups) + (fused > plain ? fused : plain);
+}
+
+// lh_calibrate_sweep; with launch == false only its arguments are checked
+// (lh_calibrate_nvfp4 checks both halves before it enqueues anything).
+lh_status calibrate_sweep(const char* fn, bool launch, const void* w, int w_dtype, int64_t c_out, int64_t c_in,
+                          int64_t ld_w, int64_t n_groups, int64_t group_stride_w, const float* h,
+                          int64_t group_stride_h, const float* amax, uint8_t* best_idx, float* best_err,
+                          float* best_amax, QuantPtrs qp, void* workspace, size_t workspace_bytes, void* stream) {
+  g_msg[0] = '\0';
+  if (workspace == nullptr && n_groups > 0 && c_out > 0 && c_in > 0)
+    return fail(LH_ERR_NULL, "%s: workspace (from lh_calibrate_prologue) is required", fn);
+  if (!aligned(workspace, 256)) return fail(LH_ERR_ARG, "%s: workspace not 256-byte aligned", fn);
+  if (workspace != nullptr && c_in >= 0 && n_groups >= 0 && workspace_bytes < calibrate_cert_bytes(c_in, n_groups))
+    return fail(LH_ERR_WORKSPACE, "%s: workspace smaller than lh_calibrate_workspace_bytes()", fn);
+  const size_t cert_bytes = c_in >= 0 && n_groups >= 0 ? calibrate_cert_bytes(c_in, n_groups) : 0;
+  return select_common(fn, 0, true, w, w_dtype, c_out, c_in, ld_w, n_groups, group_stride_w, h, group_stride_h,
+                       amax, best_idx, best_err, best_amax, workspace, cert_bytes, stream, qp, true, launch);
 }
 
 }  // namespace
@@ -228,6 +260,112 @@ lh_status lh_scale_sweep_fake_quant(const void* w, int w_dtype, int64_t c_out, i
   return select_common("lh_scale_sweep_fake_quant", 0, true, w, w_dtype, c_out, c_in, ld_w, n_groups,
                        group_stride_w, h, group_stride_h, amax, best_idx, best_err, best_amax, workspace,
                        workspace_bytes, stream, QuantPtrs{w_q, packed_e2m1, scale_e4m3, global_scale});
+}
+
+size_t lh_calibrate_workspace_bytes(int64_t c_out, int64_t c_in, int64_t n_tokens, int64_t n_groups) {
+  if (c_out <= 0 || c_in <= 0 || n_groups <= 0 || n_tokens < 0 || c_in % 16 != 0) return 0;
+  return calibrate_ws_bytes(c_out, c_in, n_tokens, n_groups);
+}
+
+lh_status lh_calibrate_prologue(const void* w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
+                                int64_t n_groups, int64_t group_stride_w, const void* x, int x_dtype, int x_layout,
+                                int64_t n_tokens, int64_t ld_x, int64_t group_stride_x, float* amax, float* h,
+                                int64_t group_stride_h, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "lh_calibrate_prologue";
+  g_msg[0] = '\0';
+  if (!valid_dtype(w_dtype) || !valid_dtype(x_dtype))
+    return fail(LH_ERR_DTYPE, "%s: w_dtype and x_dtype must be 0 (f32) or 1 (bf16)", fn);
+  if (x_layout != LH_LAYOUT_CHANNEL_MAJOR && x_layout != LH_LAYOUT_TOKEN_MAJOR)
+    return fail(LH_ERR_LAYOUT, "%s: x_layout must be 0 (channel-major) or 1 (token-major)", fn);
+  if (c_out < 0 || c_in < 0 || n_groups < 0 || n_tokens < 0 || group_stride_w < 0 || group_stride_x < 0 ||
+      group_stride_h < 0)
+    return fail(LH_ERR_SHAPE, "%s: negative size or stride", fn);
+  if (c_in % 16 != 0) return fail(LH_ERR_SHAPE, "%s: c_in must be a multiple of 16", fn);
+  if (ld_w < c_in) return fail(LH_ERR_SHAPE, "%s: ld_w < c_in", fn);
+  const int64_t min_ld = x_layout == LH_LAYOUT_CHANNEL_MAJOR ? n_tokens : c_in;
+  if (ld_x < min_ld || ld_x < 1) return fail(LH_ERR_SHAPE, "%s: ld_x smaller than the contiguous extent", fn);
+  const int64_t nb = c_in / 16;
+  if (n_groups > 1 && group_stride_h < nb * 256)
+    return fail(LH_ERR_SHAPE, "%s: group_stride_h < (c_in/16)*256 would overlap outputs", fn);
+  const bool work = n_groups > 0 && c_out > 0 && c_in > 0;
+  if (work && (w == nullptr || amax == nullptr || h == nullptr || workspace == nullptr ||
+               (n_tokens > 0 && x == nullptr)))
+    return fail(LH_ERR_NULL, "%s: w, x, amax, h and workspace are required", fn);
+  if (!aligned(w, elem_size(w_dtype)) || !aligned(x, elem_size(x_dtype)) || !aligned(amax, 4) ||
+      !aligned(workspace, 256))
+    return fail(LH_ERR_ARG, "%s: misaligned pointer (workspace: 256 bytes)", fn);
+  if (h != nullptr && (!aligned(h, 16) || group_stride_h % 4 != 0))
+    return fail(LH_ERR_ARG, "%s: h must be 16-byte aligned and group_stride_h a multiple of 4", fn);
+  if (!work) return LH_OK;
+  if (workspace_bytes < calibrate_ws_bytes(c_out, c_in, n_tokens, n_groups))
+    return fail(LH_ERR_WORKSPACE, "%s: workspace smaller than lh_calibrate_workspace_bytes()", fn);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* cert = reinterpret_cast<float*>(ws);
+  char* rest = ws + calibrate_cert_bytes(c_in, n_groups);
+  const size_t rest_bytes = workspace_bytes - calibrate_cert_bytes(c_in, n_groups);
+  const float alpha = n_tokens > 0 ? (float)(1.0 / (double)n_tokens) : 0.0f;
+  const int64_t epx = 16 / elem_size(x_dtype), epw = 16 / elem_size(w_dtype);
+  const bool fused = x_layout == LH_LAYOUT_CHANNEL_MAJOR && n_tokens > 0 && aligned(x, 16) && ld_x % epx == 0 &&
+                     group_stride_x % epx == 0 && aligned(w, 16) && ld_w == c_in && group_stride_w % epw == 0;
+  hipError_t e;
+  bool certified = false;
+  if (fused) {
+    const lh::ProloguePlan q = lh::prologue_plan(c_in, n_tokens, n_groups, c_out * c_in);
+    float* part = reinterpret_cast<float*>(rest);
+    uint32_t* abs_part = reinterpret_cast<uint32_t*>(part + q.hess.nsplit * n_groups * nb * 256);
+    lh::PrologueArgs pa{x, x_dtype, c_in, n_tokens, ld_x, group_stride_x, n_groups, w, w_dtype, c_out,
+                        group_stride_w, part, abs_part};
+    e = lh::launch_prologue(pa, q, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    lh::FinalizeCertifyArgs fa{part, q.hess.nsplit, n_groups, c_in, alpha, h, group_stride_h, cert, abs_part,
+                               q.abs_per_group, amax};
+    e = lh::launch_finalize_certify(fa, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    certified = lh::finalize_certifies(n_groups * nb);
+  } else {
+    lh::AbsmaxArgs aa{w, w_dtype, c_out, c_in, ld_w, n_groups, group_stride_w, amax};
+    e = lh::launch_absmax(aa, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    lh::HessianArgs ha{x, x_dtype, x_layout, c_in, n_tokens, ld_x, group_stride_x, n_groups, alpha, 0.0f,
+                       h, group_stride_h, rest, rest_bytes};
+    e = lh::launch_hessian(ha, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+  }
+  if (!certified) {
+    e = lh::launch_certificate(h, group_stride_h, c_in, n_groups, cert, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+  }
+  return LH_OK;
+}
+
+lh_status lh_calibrate_sweep(const void* w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
+                             int64_t n_groups, int64_t group_stride_w, const float* h, int64_t group_stride_h,
+                             const float* amax, uint8_t* best_idx, float* best_err, float* best_amax, float* w_q,
+                             uint8_t* packed_e2m1, uint8_t* scale_e4m3, float* global_scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return calibrate_sweep("lh_calibrate_sweep", true, w, w_dtype, c_out, c_in, ld_w, n_groups, group_stride_w, h,
+                         group_stride_h, amax, best_idx, best_err, best_amax,
+                         QuantPtrs{w_q, packed_e2m1, scale_e4m3, global_scale}, workspace, workspace_bytes, stream);
+}
+
+lh_status lh_calibrate_nvfp4(const void* w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w, int64_t n_groups,
+                             int64_t group_stride_w, const void* x, int x_dtype, int x_layout, int64_t n_tokens,
+                             int64_t ld_x, int64_t group_stride_x, float* amax, float* h, int64_t group_stride_h,
+                             uint8_t* best_idx, float* best_err, float* best_amax, float* w_q, uint8_t* packed_e2m1,
+                             uint8_t* scale_e4m3, float* global_scale, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  const QuantPtrs qp{w_q, packed_e2m1, scale_e4m3, global_scale};
+  lh_status st = calibrate_sweep("lh_calibrate_nvfp4", false, w, w_dtype, c_out, c_in, ld_w, n_groups,
+                                 group_stride_w, h, group_stride_h, amax, best_idx, best_err, best_amax, qp, workspace,
+                                 workspace_bytes, stream);
+  if (st != LH_OK) return st;
+  st = lh_calibrate_prologue(w, w_dtype, c_out, c_in, ld_w, n_groups, group_stride_w, x, x_dtype, x_layout,
+                                       n_tokens, ld_x, group_stride_x, amax, h, group_stride_h, workspace,
+                                       workspace_bytes, stream);
+  if (st != LH_OK) return st;
+  return calibrate_sweep("lh_calibrate_nvfp4", true, w, w_dtype, c_out, c_in, ld_w, n_groups, group_stride_w, h,
+                         group_stride_h, amax, best_idx, best_err, best_amax, qp, workspace, workspace_bytes, stream);
 }
 
 lh_status lh_select_scales(int rule, const void* w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,

@@ -61,6 +61,64 @@ __device__ __forceinline__ float e2m1_round_mag(float x) {
   return (xc + magic) - magic;
 }
 
+// p[0] + p[stride] + ... + p[(n-1) stride], added in slice order; eight
+// loads are issued ahead of their adds.
+__device__ __forceinline__ float sum_slices(const float* __restrict__ p, int64_t stride, int64_t n) {
+  float v = p[0];
+  int64_t s = 1;
+  for (; s + 8 <= n; s += 8) {
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = p[(s + i) * stride];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v += t[i];
+  }
+  for (; s < n; ++s) v += p[s * stride];
+  return v;
+}
+
+// Largest |w| bit pattern among the 16 bytes u (eight bf16 or four fp32):
+// |w| as fp32 bits is monotone in |w|, so the maximum is an unsigned max.
+__device__ __forceinline__ uint32_t absbits_max(uint32_t m, const uint4 u, bool bf16) {
+  const uint32_t v[4] = {u.x, u.y, u.z, u.w};
+  if (bf16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, max((v[i] << 16) & 0x7FFF0000u, v[i] & 0x7FFF0000u));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, v[i] & 0x7FFFFFFFu);
+  }
+  return m;
+}
+
+// Workgroup share `chunk` of `per_group` of a flat array of n16 16-byte
+// vectors: the largest |w| bits it holds (grid-stride, four loads in
+// flight per thread), reduced over the workgroup; valid in thread 0.
+template <bool kBf16>
+__device__ __forceinline__ uint32_t absmax_flat_share(const uint4* __restrict__ v, int64_t n16, int64_t chunk,
+                                                      int64_t per_group) {
+  __shared__ uint32_t part[kThreads / 64];
+  uint32_t m = 0;
+  const int64_t stride = per_group * kThreads;
+  int64_t i = chunk * kThreads + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = v[i], b = v[i + stride], c = v[i + 2 * stride], d = v[i + 3 * stride];
+    m = absbits_max(m, a, kBf16);
+    m = absbits_max(m, b, kBf16);
+    m = absbits_max(m, c, kBf16);
+    m = absbits_max(m, d, kBf16);
+  }
+  for (; i < n16; i += stride) m = absbits_max(m, v[i], kBf16);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  uint32_t t = part[0];
+#pragma unroll
+  for (int k = 1; k < kThreads / 64; ++k) t = max(t, part[k]);
+  return t;
+}
+
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // NVFP4 cast of one 16-weight block with block scale s ("Algorithm

@@ -99,17 +99,17 @@ __device__ __forceinline__ void load_cm(const float* row, int64_t tb, int64_t t1
 // ---------------------------------------------------------------------------
 // Channel-major kernel: x[(16b + c) * ld + t].
 // ---------------------------------------------------------------------------
+// Workgroup `id` = (group, block, token slice): the slice's X_b X_b^T,
+// written as h = beta h + alpha S without a workspace, else as the slice's
+// partial sum in ws[slice][group][block].
 template <typename T, bool kVec>
-__global__ __launch_bounds__(kThreads) void hessian_cm_kernel(const T* __restrict__ x, int64_t n_tok,
-                                                              int64_t ld, int64_t gstride, int64_t nb,
-                                                              int64_t n_groups, int64_t nsplit,
-                                                              int64_t chunk, float alpha, float beta,
-                                                              float* __restrict__ h, int64_t h_gstride,
-                                                              float* __restrict__ ws) {
+__device__ __forceinline__ void hessian_cm_block(int64_t id, const T* __restrict__ x, int64_t n_tok, int64_t ld,
+                                                 int64_t gstride, int64_t nb, int64_t n_groups, int64_t nsplit,
+                                                 int64_t chunk, float alpha, float beta, float* __restrict__ h,
+                                                 int64_t h_gstride, float* __restrict__ ws) {
   __shared__ float red[4][256];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ch = lane & 15, kg = lane >> 4;
-  int64_t id = blockIdx.x;
   const int64_t s = id % nsplit;
   id /= nsplit;
   const int64_t b = id % nb, grp = id / nb;
@@ -142,12 +142,49 @@ __global__ __launch_bounds__(kThreads) void hessian_cm_kernel(const T* __restric
   __syncthreads();
   const int e = threadIdx.x;
   const float v = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
-  if (nsplit == 1) {
+  if (ws == nullptr) {
     float* hp = h + grp * h_gstride + b * 256 + e;
     *hp = (beta == 0.0f) ? alpha * v : beta * (*hp) + alpha * v;
   } else {
     ws[((s * n_groups + grp) * nb + b) * 256 + e] = v;
   }
+}
+
+template <typename T, bool kVec>
+__global__ __launch_bounds__(kThreads) void hessian_cm_kernel(const T* __restrict__ x, int64_t n_tok,
+                                                              int64_t ld, int64_t gstride, int64_t nb,
+                                                              int64_t n_groups, int64_t nsplit,
+                                                              int64_t chunk, float alpha, float beta,
+                                                              float* __restrict__ h, int64_t h_gstride,
+                                                              float* __restrict__ ws) {
+  hessian_cm_block<T, kVec>(blockIdx.x, x, n_tok, ld, gstride, nb, n_groups, nsplit, chunk, alpha, beta, h,
+                            h_gstride, ws);
+}
+
+// The calibration prologue in one launch: the first workgroups fold W's
+// |w| bits into one partial maximum each (W flat, 16-byte aligned), the
+// others compute the token-slice partial sums of the channel-major Hessian
+// (X 16-byte aligned); no atomics, so no output has to be zeroed first.  The
+// finalize kernel completes both.
+template <typename T, typename TW>
+__global__ __launch_bounds__(kThreads) void prologue_cm_kernel(const T* __restrict__ x, int64_t n_tok, int64_t ld,
+                                                               int64_t gstride, int64_t nb, int64_t n_groups,
+                                                               int64_t nsplit, int64_t chunk, float* __restrict__ ws,
+                                                               const TW* __restrict__ w,
+                                                               int64_t w_n16, int64_t w_gstride, int64_t per_group,
+                                                               uint32_t* __restrict__ abs_part) {
+  // the amax shares (long, few) come first in the grid, the Hessian slices fill in behind them
+  const int64_t n_abs = n_groups * per_group;
+  if ((int64_t)blockIdx.x >= n_abs) {
+    hessian_cm_block<T, true>((int64_t)blockIdx.x - n_abs, x, n_tok, ld, gstride, nb, n_groups, nsplit, chunk, 1.0f,
+                              0.0f, nullptr, 0, ws);
+    return;
+  }
+  const int64_t id = blockIdx.x;
+  const int64_t grp = id / per_group, share = id - grp * per_group;
+  const uint32_t m = absmax_flat_share<sizeof(TW) == 2>(reinterpret_cast<const uint4*>(w + grp * w_gstride), w_n16,
+                                                        share, per_group);
+  if (threadIdx.x == 0) abs_part[id] = m;
 }
 
 // ---------------------------------------------------------------------------
@@ -355,22 +392,6 @@ __global__ __launch_bounds__(kThreads) void hessian_tm_kernel(const T* __restric
   }
 }
 
-// p[0] + p[stride] + ... + p[(n-1) stride], added in slice order; eight
-// loads are issued ahead of their adds.
-__device__ __forceinline__ float sum_slices(const float* __restrict__ p, int64_t stride, int64_t n) {
-  float v = p[0];
-  int64_t s = 1;
-  for (; s + 8 <= n; s += 8) {
-    float t[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) t[i] = p[(s + i) * stride];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v += t[i];
-  }
-  for (; s < n; ++s) v += p[s * stride];
-  return v;
-}
-
 __global__ __launch_bounds__(kThreads) void hessian_ragged_finalize_kernel(
     const float* __restrict__ ws, int64_t nsplit, int64_t slice_rows, int64_t n_groups, int64_t nb, int64_t n_rows,
     const int64_t* __restrict__ offsets, const int64_t* __restrict__ counts, float* __restrict__ h,
@@ -561,6 +582,43 @@ size_t hessian_ws_bytes(int64_t c_in, int64_t n_tok, int64_t n_groups) {
   }
   if (ns <= 1) return 0;
   return (size_t)ns * (size_t)n_groups * (size_t)(c_in / 16) * 256u * sizeof(float);
+}
+
+ProloguePlan prologue_plan(int64_t c_in, int64_t n_tok, int64_t n_groups, int64_t w_elems) {
+  ProloguePlan q;
+  q.hess = hessian_plan(c_in, n_tok, n_groups, 0, true);
+  const int64_t n16 = w_elems / 8;  // at least this many 16-byte vectors (bf16); fp32 has twice as many
+  int64_t per = (1024 + n_groups - 1) / n_groups;
+  const int64_t need = (n16 + 4 * kThreads - 1) / (4 * kThreads);
+  if (per > need) per = need;
+  q.abs_per_group = per < 1 ? 1 : per;
+  return q;
+}
+
+size_t prologue_ws_bytes(int64_t c_in, int64_t n_tok, int64_t n_groups, int64_t w_elems) {
+  const ProloguePlan q = prologue_plan(c_in, n_tok, n_groups, w_elems);
+  return (size_t)q.hess.nsplit * n_groups * (c_in / 16) * 256 * sizeof(float) +
+         (size_t)n_groups * q.abs_per_group * sizeof(uint32_t);
+}
+
+template <typename T, typename TW>
+hipError_t launch_prologue_typed(const PrologueArgs& a, const ProloguePlan& q, hipStream_t stream) {
+  const int64_t nb = a.c_in / 16;
+  const int64_t n_hess = a.n_groups * nb * q.hess.nsplit;
+  const int64_t w_n16 = a.c_out * a.c_in * (int64_t)sizeof(TW) / 16;
+  const int64_t grid = n_hess + a.n_groups * q.abs_per_group;
+  prologue_cm_kernel<T, TW><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+      static_cast<const T*>(a.x), a.n_tok, a.ld_x, a.gstride_x, nb, a.n_groups, q.hess.nsplit, q.hess.chunk, a.h_part,
+      static_cast<const TW*>(a.w), w_n16, a.gstride_w, q.abs_per_group, a.abs_part);
+  return hipGetLastError();
+}
+
+hipError_t launch_prologue(const PrologueArgs& a, const ProloguePlan& q, hipStream_t stream) {
+  if (a.x_dtype == 1)
+    return a.w_dtype == 1 ? launch_prologue_typed<uint16_t, uint16_t>(a, q, stream)
+                          : launch_prologue_typed<uint16_t, float>(a, q, stream);
+  return a.w_dtype == 1 ? launch_prologue_typed<float, uint16_t>(a, q, stream)
+                        : launch_prologue_typed<float, float>(a, q, stream);
 }
 
 hipError_t launch_hessian(const HessianArgs& a, hipStream_t stream) {

@@ -30,6 +30,27 @@ HessianPlan hessian_plan(int64_t c_in, int64_t n_tok, int64_t n_groups, int layo
 size_t hessian_ws_bytes(int64_t c_in, int64_t n_tok, int64_t n_groups);
 hipError_t launch_hessian(const HessianArgs& a, hipStream_t stream);
 
+// The fused calibration prologue (channel-major X, flat W): partial Hessian
+// sums for every token slice and partial |w| maxima, completed by
+// launch_finalize_certify.
+struct ProloguePlan {
+  HessianPlan hess;       // always through the workspace (nsplit >= 1)
+  int64_t abs_per_group;  // partial maxima per group
+};
+struct PrologueArgs {
+  const void* x;
+  int x_dtype;
+  int64_t c_in, n_tok, ld_x, gstride_x, n_groups;
+  const void* w;          // [n_groups][c_out][c_in], contiguous
+  int w_dtype;
+  int64_t c_out, gstride_w;
+  float* h_part;          // [nsplit][n_groups][c_in/16][256]
+  uint32_t* abs_part;     // [n_groups][abs_per_group]
+};
+ProloguePlan prologue_plan(int64_t c_in, int64_t n_tok, int64_t n_groups, int64_t w_elems);
+size_t prologue_ws_bytes(int64_t c_in, int64_t n_tok, int64_t n_groups, int64_t w_elems);
+hipError_t launch_prologue(const PrologueArgs& a, const ProloguePlan& q, hipStream_t stream);
+
 struct HessianRaggedArgs {
   const void* x;          // token-major [n_rows][ld]
   int dtype;              // 0 fp32, 1 bf16
@@ -70,7 +91,27 @@ struct SweepArgs {
   uint8_t* packed = nullptr;
   uint8_t* codes = nullptr;
   float* gscale = nullptr;
+  bool cert_ready = false;  // ws already holds the per-block certificates
 };
+
+struct FinalizeCertifyArgs {
+  const float* h_part;    // the prologue's partial sums
+  int64_t nsplit, n_groups, c_in;
+  float alpha;
+  float* h;
+  int64_t h_gstride;
+  float* cert;            // [n_groups][c_in/16]
+  const uint32_t* abs_part;
+  int64_t abs_per_group;
+  float* amax;            // [n_groups]
+};
+// Whether launch_finalize_certify also writes the certificates for this many
+// blocks (else the sweep computes them in its own pre-pass).
+bool finalize_certifies(int64_t blocks);
+// The sweep's certificate pre-pass alone: cert[g][b] for every block.
+hipError_t launch_certificate(const float* h, int64_t gstride_h, int64_t c_in, int64_t n_groups, float* cert,
+                              hipStream_t stream);
+hipError_t launch_finalize_certify(const FinalizeCertifyArgs& a, hipStream_t stream);
 size_t sweep_ws_bytes(int64_t c_in, int64_t n_groups);
 hipError_t launch_sweep(const SweepArgs& a, hipStream_t stream);
 

@@ -113,18 +113,6 @@ __global__ void absmax_init_kernel(float* __restrict__ out, int64_t n) {
   if (i < n) out[i] = 0.0f;
 }
 
-__device__ __forceinline__ uint32_t absbits_max(uint32_t m, const uint4 u, bool bf16) {
-  const uint32_t v[4] = {u.x, u.y, u.z, u.w};
-  if (bf16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) m = max(m, max((v[i] << 16) & 0x7FFF0000u, v[i] & 0x7FFF0000u));
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) m = max(m, v[i] & 0x7FFFFFFFu);
-  }
-  return m;
-}
-
 // Contiguous groups (ld == cols): the group is one flat array of n16 16-byte
 // vectors; grid-stride loop with four loads in flight per thread.
 // Otherwise rows are walked one by one (kFlat == false), vectorised when the
@@ -133,26 +121,17 @@ template <typename T, bool kVec, bool kFlat>
 __global__ __launch_bounds__(kThreads) void absmax_kernel(const T* __restrict__ w, int64_t rows, int64_t cols,
                                                           int64_t ld, int64_t gstride, int64_t per_group,
                                                           float* __restrict__ out) {
-  __shared__ uint32_t part[kThreads / 64];
   const int64_t grp = (int64_t)blockIdx.x / per_group;
   const int64_t chunk = (int64_t)blockIdx.x - grp * per_group;
   const T* base = w + grp * gstride;
   constexpr bool kBf16 = sizeof(T) == 2;
-  uint32_t m = 0;
+  uint32_t t;
   if (kFlat) {
-    const uint4* v = reinterpret_cast<const uint4*>(base);
-    const int64_t n16 = rows * cols * (int64_t)sizeof(T) / 16;
-    const int64_t stride = per_group * kThreads;
-    int64_t i = chunk * kThreads + threadIdx.x;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-      const uint4 a = v[i], b = v[i + stride], c = v[i + 2 * stride], d = v[i + 3 * stride];
-      m = absbits_max(m, a, kBf16);
-      m = absbits_max(m, b, kBf16);
-      m = absbits_max(m, c, kBf16);
-      m = absbits_max(m, d, kBf16);
-    }
-    for (; i < n16; i += stride) m = absbits_max(m, v[i], kBf16);
+    t = absmax_flat_share<kBf16>(reinterpret_cast<const uint4*>(base), rows * cols * (int64_t)sizeof(T) / 16, chunk,
+                                 per_group);
   } else {
+    __shared__ uint32_t part[kThreads / 64];
+    uint32_t m = 0;
     constexpr int kV = 16 / sizeof(T);
     for (int64_t r = chunk; r < rows; r += per_group) {
       const T* rp = base + r * ld;
@@ -168,15 +147,15 @@ __global__ __launch_bounds__(kThreads) void absmax_kernel(const T* __restrict__ 
         }
       }
     }
-  }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t t = part[0];
+    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    t = part[0];
 #pragma unroll
     for (int i = 1; i < kThreads / 64; ++i) t = max(t, part[i]);
+  }
+  if (threadIdx.x == 0) {
     // Atomics on one address serialise in L2; the stored value only grows, so
     // a workgroup whose maximum does not exceed what it reads (possibly a
     // stale, smaller value) has nothing to add.

@@ -69,6 +69,8 @@
 #include "lh_internal.h"
 
 namespace lh {
+hipError_t launch_certificate(const float* h, int64_t gstride_h, int64_t c_in, int64_t n_groups, float* cert,
+                              hipStream_t stream);
 namespace {
 
 // Index of (i, j), i < j, in the packed strict upper triangle (row-major).
@@ -525,15 +527,11 @@ __device__ __forceinline__ void team_cholesky(float (&a)[16], bool& ok) {
 // it column by column (right-looking: the pivot and then each entry of the
 // new column are broadcast within the team), so each lane does 16 steps of
 // a few operations instead of a whole factorisation.
-__global__ __launch_bounds__(kThreads) void sweep_certificate_team_kernel(const float* __restrict__ h, int64_t gstride_h,
-                                                                     int64_t nb, float* __restrict__ cert) {
-  __shared__ float hs[16][17];
-  __shared__ float taus[16];
-  const int64_t t = blockIdx.x;
+// The certificate of one block whose H sits in hs (row q, column i), by the
+// 256 threads of the workgroup (team q = threadIdx.x / 16); the result is
+// valid in thread 0.
+__device__ float certify_team(const float (*hs)[17], float* taus) {
   const int q = threadIdx.x >> 4, i = threadIdx.x & 15;
-  const int64_t grp = t / nb, b = t - grp * nb;
-  hs[q][i] = h[grp * gstride_h + b * 256 + threadIdx.x];  // row q, column i
-  __syncthreads();
   bool pos = true;
   float rs[16];
 #pragma unroll
@@ -569,13 +567,62 @@ __global__ __launch_bounds__(kThreads) void sweep_certificate_team_kernel(const 
   }
   if (i == 0) taus[q] = tau;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float best = taus[0];
+  float best = taus[0];
 #pragma unroll
-    for (int k = 1; k < 16; ++k) best = fmaxf(best, taus[k]);
-    const float err = 35.0f * 0x1p-24f * (1.0f + rho) / best;
-    if (!pos || !(best >= 0.02f) || !(err <= 0x1p-11f)) best = 0.0f;
-    cert[t] = best;
+  for (int k = 1; k < 16; ++k) best = fmaxf(best, taus[k]);
+  const float err = 35.0f * 0x1p-24f * (1.0f + rho) / best;
+  if (!pos || !(best >= 0.02f) || !(err <= 0x1p-11f)) best = 0.0f;
+  return best;
+}
+
+__global__ __launch_bounds__(kThreads) void sweep_certificate_team_kernel(const float* __restrict__ h, int64_t gstride_h,
+                                                                     int64_t nb, float* __restrict__ cert) {
+  __shared__ float hs[16][17];
+  __shared__ float taus[16];
+  const int64_t t = blockIdx.x;
+  const int64_t grp = t / nb, b = t - grp * nb;
+  hs[threadIdx.x >> 4][threadIdx.x & 15] = h[grp * gstride_h + b * 256 + threadIdx.x];  // row q, column i
+  __syncthreads();
+  const float c = certify_team(hs, taus);
+  if (threadIdx.x == 0) cert[t] = c;
+}
+
+// The calibration prologue's second launch, one workgroup per block: H_b =
+// alpha * (sum of the token slices, in slice order), its skip certificate
+// from the same registers (when cert is given), and for the first n_groups
+// workgroups the global amax of group blockIdx.x from its partial maxima.
+__global__ __launch_bounds__(kThreads) void finalize_certify_kernel(const float* __restrict__ part, int64_t nsplit,
+                                                                    int64_t n_groups, int64_t nb, float alpha,
+                                                                    float* __restrict__ h, int64_t h_gstride,
+                                                                    float* __restrict__ cert,
+                                                                    const uint32_t* __restrict__ abs_part,
+                                                                    int64_t abs_per_group, float* __restrict__ amax) {
+  __shared__ float hs[16][17];
+  __shared__ float taus[16];
+  __shared__ uint32_t wmax[kThreads / 64];
+  const int64_t blk = blockIdx.x;
+  const int64_t grp = blk / nb, b = blk - grp * nb;
+  const int e = threadIdx.x;
+  if (blk < n_groups) {  // the whole workgroup folds group blk's partial maxima
+    uint32_t m = 0;
+    for (int64_t k = e; k < abs_per_group; k += kThreads) m = max(m, abs_part[blk * abs_per_group + k]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    if ((e & 63) == 0) wmax[e >> 6] = m;
+  }
+  const float v = alpha * sum_slices(part + blk * 256 + e, n_groups * nb * 256, nsplit);
+  h[grp * h_gstride + b * 256 + e] = v;
+  hs[e >> 4][e & 15] = v;
+  __syncthreads();
+  const float c = cert ? certify_team(hs, taus) : 0.0f;  // cert is uniform across the launch
+  if (e == 0) {
+    if (cert) cert[blk] = c;
+    if (blk < n_groups) {
+      uint32_t m = wmax[0];
+#pragma unroll
+      for (int k = 1; k < kThreads / 64; ++k) m = max(m, wmax[k]);
+      amax[blk] = __uint_as_float(m);
+    }
   }
 }
 
@@ -1019,14 +1066,11 @@ hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   float* cert = nullptr;
-  if (a.ws != nullptr && a.ws_bytes >= sweep_ws_bytes(a.c_in, a.n_groups)) {
+  if (a.cert_ready) {
+    cert = static_cast<float*>(a.ws);  // certificates already written (finalize_certify_kernel)
+  } else if (a.ws != nullptr && a.ws_bytes >= sweep_ws_bytes(a.c_in, a.n_groups)) {
     cert = static_cast<float*>(a.ws);
-    if (per_k <= kCertTeamMaxBlocks)
-      sweep_certificate_team_kernel<<<dim3((unsigned)per_k), dim3(kThreads), 0, stream>>>(a.h, a.gstride_h, nb, cert);
-    else
-      sweep_certificate_lane_kernel<<<dim3((unsigned)((per_k + kThreads / 16 - 1) / (kThreads / 16))), dim3(kThreads), 0,
-                                      stream>>>(a.h, a.gstride_h, nb, per_k, cert);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_certificate(a.h, a.gstride_h, a.c_in, a.n_groups, cert, stream);
     if (e != hipSuccess) return e;
   }
   if (quant)
@@ -1044,6 +1088,30 @@ hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
 
 size_t sweep_ws_bytes(int64_t c_in, int64_t n_groups) {
   return (size_t)n_groups * (size_t)(c_in / 16) * sizeof(float);
+}
+
+bool finalize_certifies(int64_t blocks) { return blocks <= kCertTeamMaxBlocks; }
+
+hipError_t launch_certificate(const float* h, int64_t gstride_h, int64_t c_in, int64_t n_groups, float* cert,
+                              hipStream_t stream) {
+  const int64_t nb = c_in / 16, per_k = n_groups * nb;
+  if (per_k == 0) return hipSuccess;
+  if (per_k <= kCertTeamMaxBlocks)
+    sweep_certificate_team_kernel<<<dim3((unsigned)per_k), dim3(kThreads), 0, stream>>>(h, gstride_h, nb, cert);
+  else
+    sweep_certificate_lane_kernel<<<dim3((unsigned)((per_k + kThreads / 16 - 1) / (kThreads / 16))), dim3(kThreads), 0,
+                                    stream>>>(h, gstride_h, nb, per_k, cert);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize_certify(const FinalizeCertifyArgs& a, hipStream_t stream) {
+  const int64_t nb = a.c_in / 16;
+  const int64_t blocks = a.n_groups * nb;
+  // beyond kCertTeamMaxBlocks the sweep's own lane pre-pass is the faster certificate
+  float* cert = finalize_certifies(blocks) ? a.cert : nullptr;
+  finalize_certify_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(
+      a.h_part, a.nsplit, a.n_groups, nb, a.alpha, a.h, a.h_gstride, cert, a.abs_part, a.abs_per_group, a.amax);
+  return hipGetLastError();
 }
 
 hipError_t launch_sweep(const SweepArgs& a, hipStream_t stream) {

@@ -196,6 +196,75 @@ def test_sweep_fake_quant_validation(lib):
     assert call(g=0, gsc=P(FAKE), amax=None) == OK
 
 
+def test_calibrate_validation(lib):
+    P = ctypes.c_void_p
+    ok = dict(w=P(FAKE), wdt=1, c_out=4, c_in=32, ldw=32, g=1, gsw=0, x=P(FAKE), xdt=1, lay=0, n=64, ldx=64, gsx=0,
+              amax=P(FAKE), h=P(FAKE), gsh=0, idx=P(FAKE), err=None, am=None, wq=None, pk=None, codes=None, gsc=None,
+              ws=P(FAKE), wsb=1 << 20, st=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.lh_calibrate_nvfp4(a["w"], a["wdt"], a["c_out"], a["c_in"], a["ldw"], a["g"], a["gsw"], a["x"],
+                                      a["xdt"], a["lay"], a["n"], a["ldx"], a["gsx"], a["amax"], a["h"], a["gsh"],
+                                      a["idx"], a["err"], a["am"], a["wq"], a["pk"], a["codes"], a["gsc"], a["ws"],
+                                      a["wsb"], a["st"])
+
+    assert call(wdt=2) == DTYPE
+    assert call(xdt=7) == DTYPE
+    assert call(lay=2) == LAYOUT
+    assert call(c_in=40) == SHAPE
+    assert call(ldw=16) == SHAPE
+    assert call(ldx=10) == SHAPE                      # channel-major: ld_x >= n_tokens
+    assert call(lay=1, ldx=16) == SHAPE                # token-major: ld_x >= c_in
+    assert call(g=2, gsh=100) == SHAPE                 # Hessian groups would overlap
+    for k in ("w", "x", "amax", "h", "idx", "ws"):
+        assert call(**{k: None}) == NULL, k
+    assert call(wq=P(FAKE + 4)) == ARG
+    assert call(ws=P(FAKE + 16)) == ARG                # workspace: 256-byte aligned
+    assert call(h=P(FAKE + 4)) == ARG
+    assert call(wsb=16) == WORKSPACE
+    assert lib.lh_calibrate_workspace_bytes(4, 32, 64, 1) > 0
+    assert call(c_out=0, w=None, idx=None) == OK       # empty problem: nothing to do
+    assert call(pk=P(FAKE + 2)) == ARG                 # a sweep argument: rejected before the prologue launches
+
+
+def test_calibrate_halves_validation(lib):
+    P = ctypes.c_void_p
+    ok = dict(w=P(FAKE), wdt=1, c_out=4, c_in=32, ldw=32, g=1, gsw=0, x=P(FAKE), xdt=1, lay=0, n=64, ldx=64, gsx=0,
+              amax=P(FAKE), h=P(FAKE), gsh=0, idx=P(FAKE), err=None, am=None, wq=None, pk=None, codes=None, gsc=None,
+              ws=P(FAKE), wsb=1 << 20, st=None)
+
+    def pro(**kw):
+        a = dict(ok, **kw)
+        return lib.lh_calibrate_prologue(a["w"], a["wdt"], a["c_out"], a["c_in"], a["ldw"], a["g"], a["gsw"], a["x"],
+                                         a["xdt"], a["lay"], a["n"], a["ldx"], a["gsx"], a["amax"], a["h"], a["gsh"],
+                                         a["ws"], a["wsb"], a["st"])
+
+    def swp(**kw):
+        a = dict(ok, **kw)
+        return lib.lh_calibrate_sweep(a["w"], a["wdt"], a["c_out"], a["c_in"], a["ldw"], a["g"], a["gsw"], a["h"],
+                                      a["gsh"], a["amax"], a["idx"], a["err"], a["am"], a["wq"], a["pk"], a["codes"],
+                                      a["gsc"], a["ws"], a["wsb"], a["st"])
+
+    assert pro(xdt=5) == DTYPE
+    assert pro(lay=3) == LAYOUT
+    assert pro(c_in=20) == SHAPE
+    assert pro(ldx=8) == SHAPE
+    for k in ("w", "x", "amax", "h", "ws"):
+        assert pro(**{k: None}) == NULL, k
+    assert pro(ws=P(FAKE + 64)) == ARG
+    assert pro(wsb=16) == WORKSPACE
+    assert pro(c_out=0) == OK
+    assert swp(wdt=4) == DTYPE
+    assert swp(c_in=8) == SHAPE
+    for k in ("w", "h", "amax", "idx", "ws"):
+        assert swp(**{k: None}) == NULL, k
+    assert swp(ws=P(FAKE + 16)) == ARG
+    assert swp(wq=P(FAKE + 8)) == ARG
+    assert swp(wsb=4) == WORKSPACE                     # smaller than the certificates
+    assert swp(c_out=0, w=None, idx=None) == OK
+
+
 def test_ragged_hessian_validation(lib):
     P = ctypes.c_void_p
     ok = dict(x=P(FAKE), dt=1, c_in=32, ld=32, rows=100, off=P(FAKE), g=3, mx=0, h=P(FAKE), hs=512, cnt=None,

@@ -1,5 +1,6 @@
-"""The whole path (and the fused sweep + fake-quant call) captured in one HIP
-graph: every replay, with eager work and synchronisations between replays,
+"""The whole path (the separate calls, the fused sweep + fake-quant call and
+the two halves lh_calibrate_prologue and lh_calibrate_sweep) captured in one
+HIP graph: every replay, with eager work and synchronisations between replays,
 reproduces the eager results bit for bit (the library records only kernel
 launches: no memset, copy, sync or allocation)."""
 import pytest
@@ -35,10 +36,14 @@ def test_path_in_hip_graph_replays_match_eager(lh):
                wq=torch.empty((G, c_out, c_in), **f32), packed=torch.empty((G, c_out, c_in // 2), **u8),
                codes=torch.empty((G, c_out, nb), **u8), gs=torch.empty(G, **f32),
                f_idx=torch.empty((G, c_out, nb), **u8), f_wq=torch.empty((G, c_out, c_in), **f32),
-               f_packed=torch.empty((G, c_out, c_in // 2), **u8), f_codes=torch.empty((G, c_out, nb), **u8))
+               f_packed=torch.empty((G, c_out, c_in // 2), **u8), f_codes=torch.empty((G, c_out, nb), **u8),
+               c_amax=torch.empty(G, **f32), c_h=torch.empty((G, nb, 16, 16), **f32),
+               c_idx=torch.empty((G, c_out, nb), **u8), c_wq=torch.empty((G, c_out, c_in), **f32),
+               c_packed=torch.empty((G, c_out, c_in // 2), **u8), c_codes=torch.empty((G, c_out, nb), **u8))
     hws = torch.empty(max(lh.lh_hessian_workspace_bytes(c_in, n, G), 4), **u8)
     rws = torch.empty(max(lh.lh_hessian_ragged_workspace_bytes(c_in, 2 * n, 3), 4), **u8)
     sws = torch.empty(max(lh.lh_sweep_workspace_bytes(c_in, G), 4), **u8)
+    cws = torch.empty(lh.lh_calibrate_workspace_bytes(c_out, c_in, n, G), **u8)
     assert hws.numel() > 4  # the split-token path with its finalize kernel is part of the graph
 
     def step():
@@ -54,12 +59,17 @@ def test_path_in_hip_graph_replays_match_eager(lh):
         lh.lh_scale_sweep_fake_quant(w, out["h"], out["amax"], best_idx=out["f_idx"], best_err=False,
                                      best_amax=False, w_q=out["f_wq"], packed=out["f_packed"],
                                      scale_e4m3=out["f_codes"], workspace=sws)
+        lh.lh_calibrate_prologue(w, x, out["c_amax"], out["c_h"], cws)
+        lh.lh_calibrate_sweep(w, out["c_h"], out["c_amax"], cws, out["c_idx"], w_q=out["c_wq"],
+                              packed=out["c_packed"], scale_e4m3=out["c_codes"])
 
     step()
     torch.cuda.synchronize()
     eager = {k: v.clone() for k, v in out.items()}
     for k in ("idx", "wq", "packed", "codes"):     # the fused call writes what the two separate calls write
         assert torch.equal(eager["f_" + k], eager[k]), k
+    for k in ("amax", "h", "idx", "wq", "packed", "codes"):   # and so do the two halves of the whole path
+        assert torch.equal(eager["c_" + k], eager[k]), k
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()
