@@ -65,15 +65,16 @@ def copy_probe() -> None:
     print(json.dumps({"copy_probe_bytes_per_launch": n}), flush=True)
 
 
-SWEEP_SOURCES = ("lh_device.h", "lh_sweep.hip")   # the sources the sweep kernel is built from
+# the sources the step's kernels (prologue and sweep) are built from
+KERNEL_SOURCES = ("lh_device.h", "lh_sweep.hip", "lh_hessian.hip")
 
 
 def kernel_source_hash() -> str:
-    """Hash of the sweep kernel's sources: counter readings taken on other
-    sources no longer describe the kernel and are not reported."""
+    """Hash of the step kernels' sources: counter readings taken on other
+    sources no longer describe the kernels and are not reported."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nvfp4_scale_calibration_amd", "csrc")
-    for name in SWEEP_SOURCES:
+    for name in KERNEL_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -461,7 +462,8 @@ def main():
         "copy_gbps": copy_bw,
         "hessian": {"gbps": hess_gbps, "frac_hbm": hess_gbps / HBM_PEAK_GBPS, "frac_copy": hess_gbps / copy_bw,
                     "x_bytes": work.x_bytes, "warm": True},
-        "prologue": {"gbps": pro_gbps, "frac_hbm": pro_gbps / HBM_PEAK_GBPS, "bytes": work.x_bytes + w_bytes},
+        "prologue": {"gbps": pro_gbps, "frac_hbm": pro_gbps / HBM_PEAK_GBPS, "bytes": work.x_bytes + w_bytes,
+                     "traffic": traffic_from_profiles("prologue", wl.SHORT_NAMES[args.workload], src_hash)},
         "source_hash": src_hash,
     }
     if not args.no_extras:
