@@ -736,6 +736,20 @@ __global__ __launch_bounds__(kThreads) void sweep_certificate_lane_kernel(const 
 }
 
 // Fake-quant outputs written by the fused sweep (each optional).
+// Rows of a sweep launch split over lanes in two phases.  Lanes below
+// lanes_a walk rows [0, rows_a) with stride step_a (several rows each); the
+// rest walk rows [rows_a, c_out) with stride step_b.  The dispatcher starts
+// workgroups roughly in index order, so the second phase's short lanes fill
+// the end of the launch, where long ones would leave SIMDs idle while the
+// last waves finish.
+struct LanePlan {
+  int64_t lanes;
+  int64_t lanes_a;
+  int64_t rows_a;
+  int64_t step_a;
+  int64_t step_b;
+};
+
 struct QuantOut {
   float* wq;
   uint8_t* packed;
@@ -754,7 +768,7 @@ struct QuantOut {
 template <typename T, bool kVec, bool kMse, bool kQuant>
 __global__ __launch_bounds__(kSweepThreads, 2) void sweep_kernel(const T* __restrict__ wt, int64_t c_out,
                                                          int64_t ld_w, int64_t gstride_w, int64_t nb,
-                                                         int64_t rows_step, int64_t lanes,
+                                                         LanePlan lp,
                                                          const float* __restrict__ h, int64_t gstride_h,
                                                          const float* __restrict__ amax,
                                                          uint8_t* __restrict__ idx_out,
@@ -762,12 +776,17 @@ __global__ __launch_bounds__(kSweepThreads, 2) void sweep_kernel(const T* __rest
                                                          float* __restrict__ amax_out,
                                                          const float* __restrict__ cert, QuantOut qo) {
   const int64_t L = (int64_t)blockIdx.x * kSweepThreads + threadIdx.x;
-  if (L >= lanes) return;
+  if (L >= lp.lanes) return;
+  const bool tail = L >= lp.lanes_a;
+  const int64_t Lp = tail ? L - lp.lanes_a : L;
+  const int64_t rows_step = tail ? lp.step_b : lp.step_a;
+  const int64_t row_end = tail ? c_out : lp.rows_a;
   const int64_t per_group = nb * rows_step;
-  const int64_t grp = L / per_group;
-  const int64_t rem = L - grp * per_group;
-  const int64_t row0 = rem / nb;
-  const int64_t b = rem - row0 * nb;
+  const int64_t grp = Lp / per_group;
+  const int64_t rem = Lp - grp * per_group;
+  const int64_t r0 = rem / nb;
+  const int64_t b = rem - r0 * nb;
+  const int64_t row0 = (tail ? lp.rows_a : 0) + r0;
 
   float diag[16], sym[120];
   if constexpr (kMse) {
@@ -823,7 +842,7 @@ __global__ __launch_bounds__(kSweepThreads, 2) void sweep_kernel(const T* __rest
   const bool fast = (Sg >= 0x1p-117f) && (Sg <= 0x1p127f);
   const int e_g = (Sg > 0.0f && Sg <= 0x1p127f) ? ilogbf(Sg) : 0;
 
-  for (int64_t row = row0; row < c_out; row += rows_step) {
+  for (int64_t row = row0; row < row_end; row += rows_step) {
     float w[16];
     load_block<T, kVec>(wt + grp * gstride_w + row * ld_w + 16 * b, w);
     const int e = row_exponent(e_g, w);
@@ -1016,6 +1035,29 @@ __global__ __launch_bounds__(kThreads) void select_kernel(int rule, const T* __r
   }
 }
 
+// The 126-value sweep's lanes: about sixteen rounds of lanes at two waves per
+// SIMD on 256 CUs, so that waves of unequal work pack well, with at least
+// three rows per lane (its Hessian load and certificate are paid once per
+// walk); the last rows, up to four rounds' worth and at most a quarter of
+// them, go to lanes of one row each (measured: 1-3% faster on the larger
+// layers, no change on 4096 x 4096).
+LanePlan sweep_lane_plan(int64_t c_out, int64_t per_k) {
+  const int64_t round = 256LL * 4 * 2 * 64;
+  int64_t p = (c_out * per_k + 16 * round - 1) / (16 * round);
+  p = (p < 2 ? 2 : p) + 1;
+  int64_t rows_b = 4 * round / per_k;
+  if (rows_b > c_out / 4) rows_b = c_out / 4;
+  const int64_t rows_a = c_out - rows_b;  // >= 1 when c_out >= 1
+  if (p > rows_a) p = rows_a > 0 ? rows_a : 1;
+  LanePlan lp;
+  lp.rows_a = rows_a;
+  lp.step_a = rows_a > 0 ? (rows_a + p - 1) / p : 1;
+  lp.lanes_a = rows_a > 0 ? per_k * lp.step_a : 0;
+  lp.step_b = rows_b > 0 ? rows_b : 1;
+  lp.lanes = lp.lanes_a + (rows_b > 0 ? per_k * rows_b : 0);
+  return lp;
+}
+
 template <typename T, bool kVec>
 hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
   const int64_t nb = a.c_in / 16;
@@ -1041,27 +1083,18 @@ hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
           a.amax, a.idx, a.err, a.best_amax);
     return hipGetLastError();
   }
-  // The 126-value sweep: about sixteen rounds of lanes at two waves per SIMD
-  // on 256 CUs, so that waves of unequal work pack well, but at least two
-  // rows per lane (its Hessian load and certificate are paid once per walk);
-  // rows split evenly.
-  const int64_t target = 256LL * 4 * 2 * 64 * 16;
-  int64_t rows_per_lane = (a.c_out * per_k + target - 1) / target;
-  if (rows_per_lane < 2) rows_per_lane = 2;
-  if (rows_per_lane > a.c_out) rows_per_lane = a.c_out;
-  const int64_t k = (a.c_out + rows_per_lane - 1) / rows_per_lane;
-  const int64_t lanes = per_k * k;
-  const int64_t sgrid = (lanes + kSweepThreads - 1) / kSweepThreads;
+  const LanePlan lp = sweep_lane_plan(a.c_out, per_k);
+  const int64_t sgrid = (lp.lanes + kSweepThreads - 1) / kSweepThreads;
   const QuantOut qo{a.wq, a.packed, a.codes, a.gscale, a.n_groups};
   const bool quant = a.wq || a.packed || a.codes || a.gscale;
   if (mse) {
     if (quant)
       sweep_kernel<T, kVec, true, true><<<dim3((unsigned)sgrid), dim3(kSweepThreads), 0, stream>>>(
-          static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, k, lanes, nullptr, 0, a.amax, a.idx,
+          static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, lp, nullptr, 0, a.amax, a.idx,
           a.err, a.best_amax, nullptr, qo);
     else
       sweep_kernel<T, kVec, true, false><<<dim3((unsigned)sgrid), dim3(kSweepThreads), 0, stream>>>(
-          static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, k, lanes, nullptr, 0, a.amax, a.idx,
+          static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, lp, nullptr, 0, a.amax, a.idx,
           a.err, a.best_amax, nullptr, qo);
     return hipGetLastError();
   }
@@ -1075,11 +1108,11 @@ hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
   }
   if (quant)
     sweep_kernel<T, kVec, false, true><<<dim3((unsigned)sgrid), dim3(kSweepThreads), 0, stream>>>(
-        static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, k, lanes, a.h, a.gstride_h, a.amax,
+        static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, lp, a.h, a.gstride_h, a.amax,
         a.idx, a.err, a.best_amax, cert, qo);
   else
     sweep_kernel<T, kVec, false, false><<<dim3((unsigned)sgrid), dim3(kSweepThreads), 0, stream>>>(
-        static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, k, lanes, a.h, a.gstride_h, a.amax,
+        static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, lp, a.h, a.gstride_h, a.amax,
         a.idx, a.err, a.best_amax, cert, qo);
   return hipGetLastError();
 }
