@@ -158,21 +158,30 @@ __device__ __forceinline__ void nvfp4_decode_block(const uint32_t (&pk)[2], floa
   }
 }
 
-// The per-block outputs of the fake-quant for block (row rg, input block b)
-// of a dense [rows][nb] layout from its nibbles, each optional: 16 fp32
-// Q = fl32(r * s) values, 8 bytes of nibbles, the E4M3 code k + 1.
+// The per-block outputs of the fake-quant for the block with index o in a
+// dense [rows][nb] layout (o = row * nb + b) from its nibbles, each optional:
+// 16 fp32 Q = fl32(r * s) values, 8 bytes of nibbles, the E4M3 code k + 1.
+// kAll: every output pointer is known to be non-null.
+template <bool kAll = false>
+__device__ __forceinline__ void nvfp4_emit_at(const uint32_t (&pk)[2], float s, int k, int64_t o,
+                                              float* __restrict__ wq, uint8_t* __restrict__ packed,
+                                              uint8_t* __restrict__ codes) {
+  if (kAll || wq) {
+    float q[16];
+    nvfp4_decode_block(pk, s, q);
+    float4* d = reinterpret_cast<float4*>(wq + 16 * o);
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) d[qd] = make_float4(q[4 * qd], q[4 * qd + 1], q[4 * qd + 2], q[4 * qd + 3]);
+  }
+  if (kAll || packed) *reinterpret_cast<uint2*>(packed + 8 * o) = make_uint2(pk[0], pk[1]);
+  if (kAll || codes) codes[o] = (uint8_t)(k + 1);
+}
+
+// Same, for block (row rg, input block b).
 __device__ __forceinline__ void nvfp4_emit_block(const uint32_t (&pk)[2], float s, int k, int64_t rg, int64_t b,
                                                  int64_t nb, float* __restrict__ wq, uint8_t* __restrict__ packed,
                                                  uint8_t* __restrict__ codes) {
-  if (wq) {
-    float q[16];
-    nvfp4_decode_block(pk, s, q);
-    float4* o = reinterpret_cast<float4*>(wq + rg * (nb * 16) + 16 * b);
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd) o[qd] = make_float4(q[4 * qd], q[4 * qd + 1], q[4 * qd + 2], q[4 * qd + 3]);
-  }
-  if (packed) *reinterpret_cast<uint2*>(packed + rg * (nb * 8) + 8 * b) = make_uint2(pk[0], pk[1]);
-  if (codes) codes[rg * nb + b] = (uint8_t)(k + 1);
+  nvfp4_emit_at(pk, s, k, rg * nb + b, wq, packed, codes);
 }
 
 }  // namespace lh

@@ -435,6 +435,60 @@ __device__ __forceinline__ void load_hessian(const float* hb, float (&diag)[16],
   }
 }
 
+// Makes the compiler treat the 16 words as used at this point.
+__device__ __forceinline__ void wait_raw(uint32_t (&r)[16]) {
+  asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]),
+               "+v"(r[7]), "+v"(r[8]), "+v"(r[9]), "+v"(r[10]), "+v"(r[11]), "+v"(r[12]), "+v"(r[13]),
+               "+v"(r[14]), "+v"(r[15]));
+}
+
+// A weight row's 16 values as loaded (bf16 pairs or fp32 bits), and their
+// fp32 values: split so that a load can be issued long before its use.
+template <typename T, bool kVec>
+__device__ __forceinline__ void load_raw(const T* p, uint32_t (&r)[16]) {
+  if constexpr (sizeof(T) == 2) {
+    if (kVec) {
+      const uint4 u0 = reinterpret_cast<const uint4*>(p)[0];
+      const uint4 u1 = reinterpret_cast<const uint4*>(p)[1];
+      r[0] = u0.x; r[1] = u0.y; r[2] = u0.z; r[3] = u0.w;
+      r[4] = u1.x; r[5] = u1.y; r[6] = u1.z; r[7] = u1.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) r[i] = p[i];
+    }
+  } else {
+    if (kVec) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 u = reinterpret_cast<const uint4*>(p)[q];
+        r[4 * q] = u.x; r[4 * q + 1] = u.y; r[4 * q + 2] = u.z; r[4 * q + 3] = u.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) r[i] = __float_as_uint(p[i]);
+    }
+  }
+}
+
+template <typename T, bool kVec>
+__device__ __forceinline__ void raw_to_float(const uint32_t (&r)[16], float (&w)[16]) {
+  if constexpr (sizeof(T) == 2) {
+    if (kVec) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        w[2 * i] = __uint_as_float(r[i] << 16);
+        w[2 * i + 1] = __uint_as_float(r[i] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w[i] = bf16_bits_to_f32(r[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = __uint_as_float(r[i]);
+  }
+}
+
 template <typename T, bool kVec>
 __device__ __forceinline__ void load_block(const T* p, float (&w)[16]) {
   if constexpr (sizeof(T) == 2) {
@@ -736,15 +790,19 @@ __global__ __launch_bounds__(kThreads) void sweep_certificate_lane_kernel(const 
 }
 
 // Fake-quant outputs written by the fused sweep (each optional).
-// Rows of a sweep launch split over lanes in two phases.  Lanes below
-// lanes_a walk rows [0, rows_a) with stride step_a (several rows each); the
-// rest walk rows [rows_a, c_out) with stride step_b.  The dispatcher starts
+// Rows of a sweep launch split over lanes in two phases.  The first waves_a
+// waves hold lanes_a lanes that walk rows [0, rows_a) with stride step_a
+// (several rows each); the waves after them hold lanes_b lanes that walk rows
+// [rows_a, c_out) with stride step_b.  Phases start on a wave boundary, so
+// each wave's walk (stride, end) is uniform.  The dispatcher starts
 // workgroups roughly in index order, so the second phase's short lanes fill
 // the end of the launch, where long ones would leave SIMDs idle while the
 // last waves finish.
 struct LanePlan {
-  int64_t lanes;
+  int64_t waves;
+  int64_t waves_a;
   int64_t lanes_a;
+  int64_t lanes_b;
   int64_t rows_a;
   int64_t step_a;
   int64_t step_b;
@@ -758,14 +816,15 @@ struct QuantOut {
   int64_t n_groups;
 };
 
-// Two waves per SIMD: the allocator then spills ~14 row-setup values to
+// Two waves per SIMD: the allocator then spills ~15 row-setup values to
 // scratch (none inside the candidate loop), which costs far less than the
 // latency a single wave per SIMD leaves exposed.  With kQuant each row also
 // writes the fake-quant of its block with the index just chosen: the
 // nibbles come from candidate_nibbles on the row's working values (or
 // nvfp4_cast_block on the raw weights for the rare rows that need them),
-// the stores from nvfp4_emit_block, the standalone fake-quant's code.
-template <typename T, bool kVec, bool kMse, bool kQuant>
+// the stores from nvfp4_emit_at, the standalone fake-quant's code.  kAll:
+// every optional per-block output pointer is non-null.
+template <typename T, bool kVec, bool kMse, bool kQuant, bool kAll = false>
 __global__ __launch_bounds__(kSweepThreads, 2) void sweep_kernel(const T* __restrict__ wt, int64_t c_out,
                                                          int64_t ld_w, int64_t gstride_w, int64_t nb,
                                                          LanePlan lp,
@@ -776,9 +835,9 @@ __global__ __launch_bounds__(kSweepThreads, 2) void sweep_kernel(const T* __rest
                                                          float* __restrict__ amax_out,
                                                          const float* __restrict__ cert, QuantOut qo) {
   const int64_t L = (int64_t)blockIdx.x * kSweepThreads + threadIdx.x;
-  if (L >= lp.lanes) return;
-  const bool tail = L >= lp.lanes_a;
-  const int64_t Lp = tail ? L - lp.lanes_a : L;
+  const bool tail = (int64_t)blockIdx.x >= lp.waves_a;  // uniform over the wave
+  const int64_t Lp = tail ? L - lp.waves_a * kSweepThreads : L;
+  if (Lp >= (tail ? lp.lanes_b : lp.lanes_a)) return;
   const int64_t rows_step = tail ? lp.step_b : lp.step_a;
   const int64_t row_end = tail ? c_out : lp.rows_a;
   const int64_t per_group = nb * rows_step;
@@ -842,9 +901,28 @@ __global__ __launch_bounds__(kSweepThreads, 2) void sweep_kernel(const T* __rest
   const bool fast = (Sg >= 0x1p-117f) && (Sg <= 0x1p127f);
   const int e_g = (Sg > 0.0f && Sg <= 0x1p127f) ? ilogbf(Sg) : 0;
 
-  for (int64_t row = row0; row < row_end; row += rows_step) {
-    float w[16];
-    load_block<T, kVec>(wt + grp * gstride_w + row * ld_w + 16 * b, w);
+  // Vector-memory loads and stores share one completion counter that
+  // retires in issue order, so a wait for a load also waits for every store
+  // issued before it.  Hence the next row's weights are loaded before this
+  // row's stores and awaited after them (wait_raw: with the same stores on
+  // every path in between, the wait leaves them in flight), and the row's
+  // position and output base live in LDS rather than in registers, where
+  // they would be spilled across the candidate loops and reloaded from
+  // scratch (a load) after the stores.  The empty asm with a memory clobber
+  // at each row start makes the compiler read them back from LDS.
+  uint32_t raw[16];
+  __shared__ int64_t lds_row[kSweepThreads];
+  __shared__ int64_t lds_obase[kSweepThreads];  // output index of the lane's block in row 0
+  __shared__ int64_t lds_wofs[kSweepThreads];   // element offset of the lane's block in row 0
+  lds_row[tid] = row0;
+  lds_obase[tid] = grp * c_out * nb + b;
+  lds_wofs[tid] = grp * gstride_w + 16 * b;
+  load_raw<T, kVec>(wt + (grp * gstride_w + 16 * b) + row0 * ld_w, raw);
+  wait_raw(raw);
+  float w[16];
+  raw_to_float<T, kVec>(raw, w);
+  for (;;) {  // row0 < row_end: every lane has a first row
+    asm volatile("" ::: "memory");
     const int e = row_exponent(e_g, w);
     const float Su = ldexpf(Sg, -e);  // S_g in units of 2^e: [1, 2) unless the weights moved e
     Best best{INFINITY, kCandidates};
@@ -903,22 +981,33 @@ __global__ __launch_bounds__(kSweepThreads, 2) void sweep_kernel(const T* __rest
     } else {
       for (int k = 0; k < kCandidates; ++k) eval_direct<kMse>(best, k, Sg, e, w, diag, sym);
     }
+    const int64_t row = lds_row[tid];
+    const T* const wrow = wt + lds_wofs[tid] + row * ld_w;
+    // (the last row loads itself again: the load count per row stays fixed)
+    load_raw<T, kVec>(row + rows_step < row_end ? wrow + rows_step * ld_w : wrow, raw);
     const int k = best.k < kCandidates ? best.k : 0;  // NaN errors only
-    const int64_t o = (grp * c_out + row) * nb + b;
+    const int64_t o = lds_obase[tid] + row * nb;
     idx_out[o] = (uint8_t)k;
-    if (err_out) err_out[o] = ldexpf(best.err, 2 * e);
-    if (amax_out) amax_out[o] = 6.0f * (e4m3_candidate(k) * Sg);
+    if (kAll || err_out) err_out[o] = ldexpf(best.err, 2 * e);
+    if (kAll || amax_out) amax_out[o] = 6.0f * (e4m3_candidate(k) * Sg);
     if constexpr (kQuant) {
       const float s = e4m3_candidate(k) * Sg;
       uint32_t pk[2];
       if (fast && e == e_g) {
         candidate_nibbles(k, Su, w, pk);
       } else {
-        if (fast) reload_block(wt + grp * gstride_w + row * ld_w + 16 * b, w);  // w was prescaled
+        if (fast) reload_block(wrow, w);  // w was prescaled
         nvfp4_cast_block(w, s, pk);
       }
-      nvfp4_emit_block(pk, s, k, grp * c_out + row, b, nb, qo.wq, qo.packed, qo.codes);
+      nvfp4_emit_at<kAll>(pk, s, k, o, qo.wq, qo.packed, qo.codes);
     }
+    lds_row[tid] = row + rows_step;
+    if (row + rows_step >= row_end) break;
+    // The next row's weights are awaited here, after this row's stores (an
+    // empty asm that takes them as operands): on every path to this point
+    // the same stores follow the loads, so the wait need not cover them.
+    wait_raw(raw);
+    raw_to_float<T, kVec>(raw, w);
   }
   if constexpr (kQuant) {
     if (qo.gscale && L < qo.n_groups) qo.gscale[L] = amax[L] / kAmaxDivisor;  // S_g, once per group
@@ -1053,8 +1142,10 @@ LanePlan sweep_lane_plan(int64_t c_out, int64_t per_k) {
   lp.rows_a = rows_a;
   lp.step_a = rows_a > 0 ? (rows_a + p - 1) / p : 1;
   lp.lanes_a = rows_a > 0 ? per_k * lp.step_a : 0;
+  lp.waves_a = (lp.lanes_a + kSweepThreads - 1) / kSweepThreads;
   lp.step_b = rows_b > 0 ? rows_b : 1;
-  lp.lanes = lp.lanes_a + (rows_b > 0 ? per_k * rows_b : 0);
+  lp.lanes_b = rows_b > 0 ? per_k * rows_b : 0;
+  lp.waves = lp.waves_a + (lp.lanes_b + kSweepThreads - 1) / kSweepThreads;
   return lp;
 }
 
@@ -1084,7 +1175,7 @@ hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const LanePlan lp = sweep_lane_plan(a.c_out, per_k);
-  const int64_t sgrid = (lp.lanes + kSweepThreads - 1) / kSweepThreads;
+  const int64_t sgrid = lp.waves;
   const QuantOut qo{a.wq, a.packed, a.codes, a.gscale, a.n_groups};
   const bool quant = a.wq || a.packed || a.codes || a.gscale;
   if (mse) {
@@ -1106,8 +1197,20 @@ hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
     hipError_t e = launch_certificate(a.h, a.gstride_h, a.c_in, a.n_groups, cert, stream);
     if (e != hipSuccess) return e;
   }
-  if (quant)
+  // kAll: every per-block output requested (the fake-quant's too, with
+  // them), so the stores are unconditional and the wait for the next row's
+  // weights need not wait for them
+  const bool all = a.err && a.best_amax && a.wq && a.packed && a.codes;
+  if (quant && all)
+    sweep_kernel<T, kVec, false, true, true><<<dim3((unsigned)sgrid), dim3(kSweepThreads), 0, stream>>>(
+        static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, lp, a.h, a.gstride_h, a.amax,
+        a.idx, a.err, a.best_amax, cert, qo);
+  else if (quant)
     sweep_kernel<T, kVec, false, true><<<dim3((unsigned)sgrid), dim3(kSweepThreads), 0, stream>>>(
+        static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, lp, a.h, a.gstride_h, a.amax,
+        a.idx, a.err, a.best_amax, cert, qo);
+  else if (a.err && a.best_amax)
+    sweep_kernel<T, kVec, false, false, true><<<dim3((unsigned)sgrid), dim3(kSweepThreads), 0, stream>>>(
         static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, lp, a.h, a.gstride_h, a.amax,
         a.idx, a.err, a.best_amax, cert, qo);
   else
