@@ -326,11 +326,13 @@ __device__ __forceinline__ void candidate_class(int k, int& m, int& j) {
     j = (code >> 3) - 7;
     return;
   }
-  // subnormal codes c * 2^-9, c = 1..7
-  const int cm[8] = {0, 0, 0, 4, 0, 2, 4, 6};
-  const int cj[8] = {0, -9, -8, -8, -7, -7, -7, -7};
-  m = cm[code];
-  j = cj[code];
+  // subnormal codes c * 2^-9, c = 1..7: with f = floor(log2 c),
+  // c = (c 2^(3-f) / 8) 2^f, so m = c 2^(3-f) - 8 and j = f - 9 (computed,
+  // not looked up: a table in memory would be a load, and waiting for it
+  // would also wait for the stores issued before it)
+  const int f = 31 - __builtin_clz((unsigned)code);
+  m = (code << (3 - f)) - 8;
+  j = f - 9;
 }
 
 // The lane's max-scaling candidate: smallest c_k >= max|w| / (6 S_g), i.e. the
