@@ -95,6 +95,11 @@ __device__ __forceinline__ void keep_best(Best& b, float e, int k) {
 
 constexpr float kSkipMargin = 1.0f + 0x1p-10f;
 
+// True when p holds on some active lane of the wave (the lane mask of a
+// comparison goes straight to the ballot, without a round trip through a
+// 0/1 register).
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
 // Per-row state of the skip test: the four bound elements (prescaled weights,
 // gamma * H_ee) and their packed FP4 codes.
 struct SkipSet {
@@ -103,7 +108,9 @@ struct SkipSet {
   float p[4];      // w[e] / sigma of the current mantissa class (same bits as p[idx])
   uint32_t pk;
   float gamma;     // certificate (0 when off)
-  bool on;         // this lane's gamma allows skipping
+  float margin;    // kSkipMargin, or NaN when the lane has no certificate
+                   // (then best * margin is NaN, no bound exceeds it and
+                   // nothing is skipped, whatever the sign of best)
 };
 
 // E = dw^T H dw = sum_i dw_i (H_ii dw_i + sum_{j>i} (H_ij + H_ji) dw_j), or
@@ -229,8 +236,7 @@ __device__ __forceinline__ void eval_scaled_skip(Best& best, const SkipSet& t, i
   float d2 = yd[0] * dw[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) d2 = __builtin_fmaf(yd[i], dw[i], d2);
-  const bool need = !(t.on && t.gamma * d2 > best.err * kSkipMargin);
-  if (__ballot(need) == 0) return;
+  if (!wave_any(!(t.gamma * d2 > best.err * t.margin))) return;
   keep_best(best, quad_form_from(yd, sym, dw), k);
 }
 
@@ -259,22 +265,20 @@ __device__ __forceinline__ void eval_direct(Best& best, int k, float Sg, int e, 
 // test alone.
 __device__ __forceinline__ bool needs_eval(SkipSet& t, const Best& best, int j, float s) {
   const float pow2j = __uint_as_float((uint32_t)(127 + j) << 23);
-  const float thr = best.err * kSkipMargin;
+  const float thr = best.err * t.margin;
   t.pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t.pk, t.p[0], t.p[1], pow2j, 0);
   const f32x2_t r01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.pk, 1.0f, 0);
   const float d0 = r01.x * s - t.w[0], d1 = r01.y * s - t.w[1];
   float lb = (t.dg[0] * d0) * d0;
   lb = __builtin_fmaf(t.dg[1] * d1, d1, lb);
-  bool need = !(t.on && lb > thr);
-  if (__ballot(need) != 0) {
+  if (wave_any(!(lb > thr))) {
     t.pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t.pk, t.p[2], t.p[3], pow2j, 1);
     const f32x2_t r23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.pk, 1.0f, 1);
     const float d2 = r23.x * s - t.w[2], d3 = r23.y * s - t.w[3];
     lb = __builtin_fmaf(t.dg[2] * d2, d2, lb);
     lb = __builtin_fmaf(t.dg[3] * d3, d3, lb);
-    need = need && !(t.on && lb > thr);
   }
-  return need;
+  return !(lb > thr);
 }
 
 // E4M3 code of mantissa class m at power j (value (1 + m/8) 2^j): normal
@@ -309,7 +313,7 @@ __device__ __forceinline__ void sweep_mantissa(Best& best, SkipSet& t, float Sg,
 #pragma unroll
   for (int c = 0; c <= jmax - jmin; ++c)
     if (needs_eval(t, best, jmin + c, ldexpf(sigma, jmin + c))) need |= 1u << c;
-  while (__ballot(need != 0) != 0) {
+  while (wave_any(need != 0)) {
     if (need != 0) {
       const int j = jmin + __builtin_ctz(need);
       need &= need - 1;
@@ -958,7 +962,7 @@ __global__ __launch_bounds__(kSweepThreads, 2) void sweep_kernel(const T* __rest
         }
         t.pk = 0u;
         t.gamma = gamma;
-        t.on = gamma > 0.0f;
+        t.margin = gamma > 0.0f ? kSkipMargin : __int_as_float(0x7FC00000);
       }
       // incumbent: the max-scaling candidate, evaluated exactly as in the loop
       {
