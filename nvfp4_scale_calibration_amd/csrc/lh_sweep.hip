@@ -86,9 +86,10 @@ struct Best {
   int k;
 };
 
-__device__ __forceinline__ void keep_best(Best& b, float e, int k) {
-  // lowest index on equal errors (bitwise ops: no branches)
-  const bool take = (e < b.err) | ((e == b.err) & (k < b.k));
+__device__ __forceinline__ void keep_best(Best& b, float e, int k, bool has = true) {
+  // lowest index on equal errors (bitwise ops: no branches); has == false:
+  // the lane evaluated no candidate of its own and keeps its best
+  const bool take = has & ((e < b.err) | ((e == b.err) & (k < b.k)));
   b.err = take ? e : b.err;
   b.k = take ? k : b.k;
 }
@@ -169,7 +170,7 @@ __device__ __forceinline__ float div_rn(float a, float b, float rb) {
 template <bool kMse>
 __device__ __forceinline__ void eval_scaled(Best& best, int k, int j, float sigma, const float (&p)[16],
                                             const float (&w)[16], const float (&diag)[16],
-                                            const float (&sym)[120], uint32_t (&pk)[2]) {
+                                            const float (&sym)[120], uint32_t (&pk)[2], bool has = true) {
   const float s = ldexpf(sigma, j);
   const float pow2j = __uint_as_float((uint32_t)(127 + j) << 23);
 #pragma unroll
@@ -192,38 +193,43 @@ __device__ __forceinline__ void eval_scaled(Best& best, int k, int j, float sigm
   float dw[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) dw[i] = r[i] * s - w[i];  // Q = fl32(r * s), then Q - w
-  keep_best(best, quad_form<kMse>(diag, sym, dw), k);
+  keep_best(best, quad_form<kMse>(diag, sym, dw), k, has);
 }
 
 // eval_scaled with a second skip test after the cast: E >= gamma *
 // sum_i H_ii dw_i^2 over all 16 weights, which reuses the products H_ii dw_i
 // that start the rows of the quadratic form; the rest of the form runs only
-// if some lane of the wave still needs it.  Bit-identical E when it runs.
+// if some lane of the wave with a candidate (has) still needs it.
+// Bit-identical E when it runs.  Every lane executes it, so that the wave
+// runs no divergent branch; lanes without a candidate compute on a dummy
+// power and change nothing.
 template <bool kMse>
-__device__ __forceinline__ void eval_scaled_skip(Best& best, const SkipSet& t, int k, int j, float sigma,
-                                                 const float (&p)[16], const float (&w)[16],
+__device__ __forceinline__ void eval_scaled_skip(Best& best, const SkipSet& t, bool has, int k, int j,
+                                                 float sigma, const float (&p)[16], const float (&w)[16],
                                                  const float (&diag)[16], const float (&sym)[120],
                                                  uint32_t (&pk)[2]) {
   if constexpr (kMse) {  // the diagonal bound is the whole error here
-    eval_scaled<true>(best, k, j, sigma, p, w, diag, sym, pk);
+    eval_scaled<true>(best, k, j, sigma, p, w, diag, sym, pk, has);
     return;
   }
   const float s = ldexpf(sigma, j);
   const float pow2j = __uint_as_float((uint32_t)(127 + j) << 23);
+  (void)pk;
+  uint32_t pkl[2] = {0u, 0u};  // every byte is written below
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 0], p[8 * h + 1], pow2j, 0);
-    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 2], p[8 * h + 3], pow2j, 1);
-    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 4], p[8 * h + 5], pow2j, 2);
-    pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 6], p[8 * h + 7], pow2j, 3);
+    pkl[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pkl[h], p[8 * h + 0], p[8 * h + 1], pow2j, 0);
+    pkl[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pkl[h], p[8 * h + 2], p[8 * h + 3], pow2j, 1);
+    pkl[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pkl[h], p[8 * h + 4], p[8 * h + 5], pow2j, 2);
+    pkl[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pkl[h], p[8 * h + 6], p[8 * h + 7], pow2j, 3);
   }
   float r[16];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const f32x2_t r0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 0);
-    const f32x2_t r1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 1);
-    const f32x2_t r2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 2);
-    const f32x2_t r3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 3);
+    const f32x2_t r0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pkl[h], 1.0f, 0);
+    const f32x2_t r1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pkl[h], 1.0f, 1);
+    const f32x2_t r2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pkl[h], 1.0f, 2);
+    const f32x2_t r3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pkl[h], 1.0f, 3);
     r[8 * h + 0] = r0.x; r[8 * h + 1] = r0.y; r[8 * h + 2] = r1.x; r[8 * h + 3] = r1.y;
     r[8 * h + 4] = r2.x; r[8 * h + 5] = r2.y; r[8 * h + 6] = r3.x; r[8 * h + 7] = r3.y;
   }
@@ -236,8 +242,8 @@ __device__ __forceinline__ void eval_scaled_skip(Best& best, const SkipSet& t, i
   float d2 = yd[0] * dw[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) d2 = __builtin_fmaf(yd[i], dw[i], d2);
-  if (!wave_any(!(t.gamma * d2 > best.err * t.margin))) return;
-  keep_best(best, quad_form_from(yd, sym, dw), k);
+  if (!wave_any(has && !(t.gamma * d2 > best.err * t.margin))) return;
+  keep_best(best, quad_form_from(yd, sym, dw), k, has);
 }
 
 // Candidate k straight from the definition: x = fl32(|w| / s), software
@@ -314,11 +320,10 @@ __device__ __forceinline__ void sweep_mantissa(Best& best, SkipSet& t, float Sg,
   for (int c = 0; c <= jmax - jmin; ++c)
     if (needs_eval(t, best, jmin + c, ldexpf(sigma, jmin + c))) need |= 1u << c;
   while (wave_any(need != 0)) {
-    if (need != 0) {
-      const int j = jmin + __builtin_ctz(need);
-      need &= need - 1;
-      eval_scaled_skip<kMse>(best, t, class_code(m, j) - 1, j, sigma, p, w, diag, sym, pk);
-    }
+    const bool has = need != 0;
+    const int j = jmin + __builtin_ctz(need | 0x80000000u);  // a dummy power when !has
+    need &= need - 1;
+    eval_scaled_skip<kMse>(best, t, has, class_code(m, j) - 1, j, sigma, p, w, diag, sym, pk);
   }
 }
 
