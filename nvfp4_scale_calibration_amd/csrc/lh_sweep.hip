@@ -29,8 +29,9 @@
 // v_cvt_scalef32_pk_fp4_f32 divides two fp32 values by the power-of-two part
 // of its scale operand and rounds them to E2M1 (round to nearest, ties to
 // even, saturating at +-6), which with scale 2^j is exactly the cast of
-// 2^-j * p = fl32(w / s); v_cvt_scalef32_pk_f32_fp4 with scale 1 returns the
-// signed grid values.  Then Q = fl32(r * s) and dw = Q - w.  Three VALU
+// 2^-j * p = fl32(w / s); v_cvt_scalef32_pk_f32_fp4 with the same scale
+// returns the signed grid values times 2^j, exactly.  Then
+// Q = fl32((r 2^j) sigma) = fl32(r s) and dw = Q - w.  Three VALU
 // instructions per weight and candidate.
 //
 // Skipping (exact): for a symmetric H with positive diagonal and
@@ -171,7 +172,6 @@ template <bool kMse>
 __device__ __forceinline__ void eval_scaled(Best& best, int k, int j, float sigma, const float (&p)[16],
                                             const float (&w)[16], const float (&diag)[16],
                                             const float (&sym)[120], uint32_t (&pk)[2], bool has = true) {
-  const float s = ldexpf(sigma, j);
   const float pow2j = __uint_as_float((uint32_t)(127 + j) << 23);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -183,16 +183,16 @@ __device__ __forceinline__ void eval_scaled(Best& best, int k, int j, float sigm
   float r[16];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const f32x2_t r0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 0);
-    const f32x2_t r1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 1);
-    const f32x2_t r2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 2);
-    const f32x2_t r3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], 1.0f, 3);
+    const f32x2_t r0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], pow2j, 0);
+    const f32x2_t r1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], pow2j, 1);
+    const f32x2_t r2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], pow2j, 2);
+    const f32x2_t r3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], pow2j, 3);
     r[8 * h + 0] = r0.x; r[8 * h + 1] = r0.y; r[8 * h + 2] = r1.x; r[8 * h + 3] = r1.y;
     r[8 * h + 4] = r2.x; r[8 * h + 5] = r2.y; r[8 * h + 6] = r3.x; r[8 * h + 7] = r3.y;
   }
   float dw[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) dw[i] = r[i] * s - w[i];  // Q = fl32(r * s), then Q - w
+  for (int i = 0; i < 16; ++i) dw[i] = r[i] * sigma - w[i];  // Q = fl32(r 2^j sigma) = fl32(r s), then Q - w
   keep_best(best, quad_form<kMse>(diag, sym, dw), k, has);
 }
 
@@ -212,7 +212,6 @@ __device__ __forceinline__ void eval_scaled_skip(Best& best, const SkipSet& t, b
     eval_scaled<true>(best, k, j, sigma, p, w, diag, sym, pk, has);
     return;
   }
-  const float s = ldexpf(sigma, j);
   const float pow2j = __uint_as_float((uint32_t)(127 + j) << 23);
   (void)pk;
   uint32_t pkl[2] = {0u, 0u};  // every byte is written below
@@ -226,17 +225,17 @@ __device__ __forceinline__ void eval_scaled_skip(Best& best, const SkipSet& t, b
   float r[16];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const f32x2_t r0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pkl[h], 1.0f, 0);
-    const f32x2_t r1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pkl[h], 1.0f, 1);
-    const f32x2_t r2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pkl[h], 1.0f, 2);
-    const f32x2_t r3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pkl[h], 1.0f, 3);
+    const f32x2_t r0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pkl[h], pow2j, 0);
+    const f32x2_t r1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pkl[h], pow2j, 1);
+    const f32x2_t r2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pkl[h], pow2j, 2);
+    const f32x2_t r3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pkl[h], pow2j, 3);
     r[8 * h + 0] = r0.x; r[8 * h + 1] = r0.y; r[8 * h + 2] = r1.x; r[8 * h + 3] = r1.y;
     r[8 * h + 4] = r2.x; r[8 * h + 5] = r2.y; r[8 * h + 6] = r3.x; r[8 * h + 7] = r3.y;
   }
   float dw[16], yd[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    dw[i] = r[i] * s - w[i];  // Q = fl32(r * s), then Q - w
+    dw[i] = r[i] * sigma - w[i];  // Q = fl32(r 2^j sigma) = fl32(r s), then Q - w
     yd[i] = diag[i] * dw[i];
   }
   float d2 = yd[0] * dw[0];
@@ -269,18 +268,18 @@ __device__ __forceinline__ void eval_direct(Best& best, int k, float Sg, int e, 
 // rounded sum, so a lane stopped by the two-element bound would also be
 // stopped by the four-element one: the outcome is that of the four-element
 // test alone.
-__device__ __forceinline__ bool needs_eval(SkipSet& t, const Best& best, int j, float s) {
+__device__ __forceinline__ bool needs_eval(SkipSet& t, const Best& best, int j, float sigma) {
   const float pow2j = __uint_as_float((uint32_t)(127 + j) << 23);
   const float thr = best.err * t.margin;
   t.pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t.pk, t.p[0], t.p[1], pow2j, 0);
-  const f32x2_t r01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.pk, 1.0f, 0);
-  const float d0 = r01.x * s - t.w[0], d1 = r01.y * s - t.w[1];
+  const f32x2_t r01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.pk, pow2j, 0);
+  const float d0 = r01.x * sigma - t.w[0], d1 = r01.y * sigma - t.w[1];
   float lb = (t.dg[0] * d0) * d0;
   lb = __builtin_fmaf(t.dg[1] * d1, d1, lb);
   if (wave_any(!(lb > thr))) {
     t.pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t.pk, t.p[2], t.p[3], pow2j, 1);
-    const f32x2_t r23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.pk, 1.0f, 1);
-    const float d2 = r23.x * s - t.w[2], d3 = r23.y * s - t.w[3];
+    const f32x2_t r23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.pk, pow2j, 1);
+    const float d2 = r23.x * sigma - t.w[2], d3 = r23.y * sigma - t.w[3];
     lb = __builtin_fmaf(t.dg[2] * d2, d2, lb);
     lb = __builtin_fmaf(t.dg[3] * d3, d3, lb);
   }
@@ -318,7 +317,7 @@ __device__ __forceinline__ void sweep_mantissa(Best& best, SkipSet& t, float Sg,
   uint32_t need = 0;
 #pragma unroll
   for (int c = 0; c <= jmax - jmin; ++c)
-    if (needs_eval(t, best, jmin + c, ldexpf(sigma, jmin + c))) need |= 1u << c;
+    if (needs_eval(t, best, jmin + c, sigma)) need |= 1u << c;
   while (wave_any(need != 0)) {
     const bool has = need != 0;
     const int j = jmin + __builtin_ctz(need | 0x80000000u);  // a dummy power when !has
