@@ -499,6 +499,34 @@ __device__ __forceinline__ void raw_to_float(const uint32_t (&r)[16], float (&w)
   }
 }
 
+// Scaled Gershgorin certificate gamma = 1 - max_i sum_{j != i} |S_ij| /
+// (2 sqrt(H_ii H_jj)), less 1e-3 for the rounding of this estimate, used
+// only when >= 0.1 (then the fp32 error of E is below 35u * 19); 0 when the
+// diagonal is not positive and finite.
+__device__ __forceinline__ float gershgorin_gamma(const float (&diag)[16], const float (&sym)[120]) {
+  bool pos = true;
+  float rs[16], rho[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    pos = pos && (diag[i] > 0.0f) && (diag[i] < INFINITY);
+    rs[i] = diag[i] > 0.0f ? 1.0f / sqrtf(diag[i]) : 0.0f;
+    rho[i] = 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+#pragma unroll
+    for (int j = i + 1; j < 16; ++j) {
+      const float c = fabsf(sym[tri(i, j)]) * 0.5f * rs[i] * rs[j];
+      rho[i] += c;
+      rho[j] += c;
+    }
+  float mx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mx = fmaxf(mx, rho[i]);
+  const float gamma = 1.0f - mx - 1e-3f;
+  return (!pos || !(gamma >= 0.1f)) ? 0.0f : gamma;
+}
+
 template <typename T, bool kVec>
 __device__ __forceinline__ void load_block(const T* p, float (&w)[16]) {
   if constexpr (sizeof(T) == 2) {
@@ -872,31 +900,7 @@ __global__ __launch_bounds__(kSweepThreads, 2) void sweep_kernel(const T* __rest
   // H = I: C = I and tau = 1 exactly; E = sum dw^2 is accurate to 16u.
   float gamma = 1.0f;
   if constexpr (!kMse) {
-    if (cert) {
-      gamma = cert[grp * nb + b];
-    } else {
-      bool pos = true;
-      float rs[16], rho[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        pos = pos && (diag[i] > 0.0f) && (diag[i] < INFINITY);
-        rs[i] = diag[i] > 0.0f ? 1.0f / sqrtf(diag[i]) : 0.0f;
-        rho[i] = 0.0f;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-#pragma unroll
-        for (int j = i + 1; j < 16; ++j) {
-          const float c = fabsf(sym[tri(i, j)]) * 0.5f * rs[i] * rs[j];
-          rho[i] += c;
-          rho[j] += c;
-        }
-      float mx = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, rho[i]);
-      gamma = 1.0f - mx - 1e-3f;
-      if (!pos || !(gamma >= 0.1f)) gamma = 0.0f;
-    }
+    gamma = cert ? cert[grp * nb + b] : gershgorin_gamma(diag, sym);
   }
   // Per-lane scratch in LDS, element-major so that 64 lanes hit 64 consecutive
   // words: the diagonal (fixed) and the current row's prescaled weights.
@@ -1024,6 +1028,153 @@ __global__ __launch_bounds__(kSweepThreads, 2) void sweep_kernel(const T* __rest
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// The sweep with one input block per wave: lane i of a wave takes row
+// chunk * 64 + i of the wave's (group, block b), and the wave walks chunks
+// c0, c0 + cstep, ...  H_b, its certificate and gamma are then the same on
+// every lane, and so are most of the skip decisions: rows of one block
+// under one Hessian need similar candidates, so a wave pays less for its
+// busiest lane than when its lanes hold 64 different blocks.  The H_b load
+// is a broadcast (every lane reads the same 1 KiB).  Each lane does the work
+// of sweep_kernel on its row with the same arithmetic, so the results are
+// the same bits.  Lanes past the last row work on the last row and store
+// nothing.
+// ---------------------------------------------------------------------------
+struct RowPlan {
+  int64_t n_chunks;  // chunks of 64 rows
+  int64_t cstep;     // waves per (group, block); cstep == n_chunks: one chunk per wave
+};
+
+// Orders this wave's LDS accesses at this point: a workgroup here is one
+// wave, whose LDS instructions execute in issue order, so only the compiler
+// has to be kept from moving accesses across.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <typename T, bool kVec, bool kQuant, bool kAll>
+__global__ __launch_bounds__(kSweepThreads, 2) void sweep_rows_kernel(const T* __restrict__ wt, int64_t c_out,
+                                                              int64_t ld_w, int64_t gstride_w, int64_t nb,
+                                                              RowPlan rp, const float* __restrict__ h,
+                                                              int64_t gstride_h, const float* __restrict__ amax,
+                                                              uint8_t* __restrict__ idx_out,
+                                                              float* __restrict__ err_out,
+                                                              float* __restrict__ amax_out,
+                                                              const float* __restrict__ cert, QuantOut qo) {
+  const int tid = threadIdx.x;
+  // consecutive waves on consecutive chunks of one block (measured: ordering
+  // them by chunk instead, neighbouring blocks of the same rows next to
+  // each other, is 7% slower)
+  const int64_t gb = (int64_t)blockIdx.x / rp.cstep;
+  const int64_t c0 = (int64_t)blockIdx.x - gb * rp.cstep;
+  const int64_t grp = gb / nb;
+  const int64_t b = gb - grp * nb;
+  __shared__ float lds_w[16][kSweepThreads];  // the lanes' working weights (bound-set gather)
+  __shared__ float lds_diag[16];
+  float diag[16], sym[120];
+  // The same address on every lane; a zero the compiler cannot see as
+  // uniform keeps the 136 values in vector registers (scalar registers
+  // cannot hold them, and spilled ones would cost a read-lane per use).
+  int zero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+  load_hessian(h + grp * gstride_h + b * 256 + zero, diag, sym);
+  if (tid < 16) lds_diag[tid] = h[grp * gstride_h + b * 256 + tid * 17];
+  const float gamma = cert ? cert[gb] : gershgorin_gamma(diag, sym);
+  const float g = amax[grp];
+  const float Sg = g / kAmaxDivisor;
+  const bool fast = (Sg >= 0x1p-117f) && (Sg <= 0x1p127f);
+  const int e_g = (Sg > 0.0f && Sg <= 0x1p127f) ? ilogbf(Sg) : 0;
+  wave_sync();
+  for (int64_t chunk = c0; chunk < rp.n_chunks; chunk += rp.cstep) {
+    const int64_t row = chunk * kSweepThreads + tid;
+    const bool valid = row < c_out;
+    const int64_t rr = valid ? row : c_out - 1;
+    const T* const wrow = wt + grp * gstride_w + rr * ld_w + 16 * b;
+    float w[16];
+    load_block<T, kVec>(wrow, w);
+    const int e = row_exponent(e_g, w);
+    const float Su = ldexpf(Sg, -e);
+    Best best{INFINITY, kCandidates};
+    uint32_t pk[2] = {0u, 0u};
+    if (fast) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w[i] = ldexpf(w[i], -e);
+      SkipSet t;
+      {
+        float kv[4] = {-1.0f, -1.0f, -1.0f, -1.0f};
+        int ki[4] = {0, 1, 2, 3};
+        wave_sync();  // the previous chunk's readers of lds_w are done
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          lds_w[i][tid] = w[i];
+          const float key = diag[i] * w[i] * w[i];
+          const bool q0 = key > kv[0], q1 = key > kv[1], q2 = key > kv[2], q3 = key > kv[3];
+          kv[3] = q2 ? kv[2] : (q3 ? key : kv[3]);
+          ki[3] = q2 ? ki[2] : (q3 ? i : ki[3]);
+          kv[2] = q1 ? kv[1] : (q2 ? key : kv[2]);
+          ki[2] = q1 ? ki[1] : (q2 ? i : ki[2]);
+          kv[1] = q0 ? kv[0] : (q1 ? key : kv[1]);
+          ki[1] = q0 ? ki[0] : (q1 ? i : ki[1]);
+          kv[0] = q0 ? key : kv[0];
+          ki[0] = q0 ? i : ki[0];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          t.w[q] = lds_w[ki[q]][tid];
+          t.dg[q] = gamma * lds_diag[ki[q]];
+        }
+        t.pk = 0u;
+        t.gamma = gamma;
+        t.margin = gamma > 0.0f ? kSkipMargin : __int_as_float(0x7FC00000);
+      }
+      {
+        const int k0 = max_scaling_candidate(w, Su);
+        int m0, j0;
+        candidate_class(k0, m0, j0);
+        const float sigma0 = (1.0f + 0.125f * (float)m0) * Su;
+        const float rs0 = 1.0f / sigma0;
+        float p0[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p0[i] = div_rn(w[i], sigma0, rs0);
+        eval_scaled<false>(best, k0, j0, sigma0, p0, w, diag, sym, pk);
+      }
+      sweep_mantissa<0, false>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<1, false>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<2, false>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<3, false>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<4, false>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<5, false>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<6, false>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<7, false>(best, t, Su, w, diag, sym, pk);
+    } else {
+      for (int k = 0; k < kCandidates; ++k) eval_direct<false>(best, k, Sg, e, w, diag, sym);
+    }
+    if (valid) {
+      const int k = best.k < kCandidates ? best.k : 0;  // NaN errors only
+      const int64_t o = (grp * c_out + row) * nb + b;
+      idx_out[o] = (uint8_t)k;
+      if (kAll || err_out) err_out[o] = ldexpf(best.err, 2 * e);
+      if (kAll || amax_out) amax_out[o] = 6.0f * (e4m3_candidate(k) * Sg);
+      if constexpr (kQuant) {
+        const float s = e4m3_candidate(k) * Sg;
+        uint32_t qk[2];
+        if (fast && e == e_g) {
+          candidate_nibbles(k, Su, w, qk);
+        } else {
+          if (fast) reload_block(wrow, w);  // w was prescaled
+          nvfp4_cast_block(w, s, qk);
+        }
+        nvfp4_emit_at<kAll>(qk, s, k, o, qo.wq, qo.packed, qo.codes);
+      }
+    }
+  }
+  if constexpr (kQuant) {
+    const int64_t gl = (int64_t)blockIdx.x * kSweepThreads + tid;
+    if (qo.gscale && gl < qo.n_groups) qo.gscale[gl] = amax[gl] / kAmaxDivisor;  // S_g, once per group
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Scale rules other than the 126-value sweep ("Local-Hessian weight-scale
@@ -1159,6 +1310,21 @@ LanePlan sweep_lane_plan(int64_t c_out, int64_t per_k) {
   return lp;
 }
 
+// The row-per-lane sweep's waves.  With at least 32 chunks of rows per
+// block, one chunk per wave (measured best on 4096 and 5120 rows); with
+// fewer, about sixteen rounds of waves at two waves per SIMD on 256 CUs,
+// each walking every cstep-th chunk of its block, so that its Hessian load
+// serves several chunks (measured best on 1024 rows).
+RowPlan row_plan(int64_t c_out, int64_t per_k) {
+  RowPlan rp;
+  rp.n_chunks = (c_out + kSweepThreads - 1) / kSweepThreads;
+  const int64_t target = 256LL * 4 * 2 * 16;
+  int64_t cs = (target + per_k - 1) / per_k;
+  if (cs > rp.n_chunks || rp.n_chunks >= 32) cs = rp.n_chunks;
+  rp.cstep = cs < 1 ? 1 : cs;
+  return rp;
+}
+
 template <typename T, bool kVec>
 hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
   const int64_t nb = a.c_in / 16;
@@ -1207,26 +1373,24 @@ hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
     hipError_t e = launch_certificate(a.h, a.gstride_h, a.c_in, a.n_groups, cert, stream);
     if (e != hipSuccess) return e;
   }
-  // kAll: every per-block output requested (the fake-quant's too, with
-  // them), so the stores are unconditional and the wait for the next row's
-  // weights need not wait for them
+  // With a Hessian, the row-per-lane kernel; kAll: every optional per-block
+  // output requested (the fake-quant's too, with them), no null checks.
   const bool all = a.err && a.best_amax && a.wq && a.packed && a.codes;
+  const RowPlan rp = row_plan(a.c_out, per_k);
+  const dim3 rgrid((unsigned)(per_k * rp.cstep));
+  const T* wp = static_cast<const T*>(a.w);
   if (quant && all)
-    sweep_kernel<T, kVec, false, true, true><<<dim3((unsigned)sgrid), dim3(kSweepThreads), 0, stream>>>(
-        static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, lp, a.h, a.gstride_h, a.amax,
-        a.idx, a.err, a.best_amax, cert, qo);
+    sweep_rows_kernel<T, kVec, true, true><<<rgrid, dim3(kSweepThreads), 0, stream>>>(
+        wp, a.c_out, a.ld_w, a.gstride_w, nb, rp, a.h, a.gstride_h, a.amax, a.idx, a.err, a.best_amax, cert, qo);
   else if (quant)
-    sweep_kernel<T, kVec, false, true><<<dim3((unsigned)sgrid), dim3(kSweepThreads), 0, stream>>>(
-        static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, lp, a.h, a.gstride_h, a.amax,
-        a.idx, a.err, a.best_amax, cert, qo);
+    sweep_rows_kernel<T, kVec, true, false><<<rgrid, dim3(kSweepThreads), 0, stream>>>(
+        wp, a.c_out, a.ld_w, a.gstride_w, nb, rp, a.h, a.gstride_h, a.amax, a.idx, a.err, a.best_amax, cert, qo);
   else if (a.err && a.best_amax)
-    sweep_kernel<T, kVec, false, false, true><<<dim3((unsigned)sgrid), dim3(kSweepThreads), 0, stream>>>(
-        static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, lp, a.h, a.gstride_h, a.amax,
-        a.idx, a.err, a.best_amax, cert, qo);
+    sweep_rows_kernel<T, kVec, false, true><<<rgrid, dim3(kSweepThreads), 0, stream>>>(
+        wp, a.c_out, a.ld_w, a.gstride_w, nb, rp, a.h, a.gstride_h, a.amax, a.idx, a.err, a.best_amax, cert, qo);
   else
-    sweep_kernel<T, kVec, false, false><<<dim3((unsigned)sgrid), dim3(kSweepThreads), 0, stream>>>(
-        static_cast<const T*>(a.w), a.c_out, a.ld_w, a.gstride_w, nb, lp, a.h, a.gstride_h, a.amax,
-        a.idx, a.err, a.best_amax, cert, qo);
+    sweep_rows_kernel<T, kVec, false, false><<<rgrid, dim3(kSweepThreads), 0, stream>>>(
+        wp, a.c_out, a.ld_w, a.gstride_w, nb, rp, a.h, a.gstride_h, a.amax, a.idx, a.err, a.best_amax, cert, qo);
   return hipGetLastError();
 }
 
