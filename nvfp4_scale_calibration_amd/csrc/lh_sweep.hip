@@ -1087,13 +1087,17 @@ __global__ __launch_bounds__(kSweepThreads, 2) void sweep_rows_kernel(const T* _
   const bool fast = (Sg >= 0x1p-117f) && (Sg <= 0x1p127f);
   const int e_g = (Sg > 0.0f && Sg <= 0x1p127f) ? ilogbf(Sg) : 0;
   wave_sync();
-  for (int64_t chunk = c0; chunk < rp.n_chunks; chunk += rp.cstep) {
+  const T* const wblk = wt + grp * gstride_w + 16 * b;
+  uint32_t raw[16];
+  load_raw<T, kVec>(wblk + (c0 * kSweepThreads + tid < c_out ? c0 * kSweepThreads + tid : c_out - 1) * ld_w, raw);
+  wait_raw(raw);
+  float w[16];
+  raw_to_float<T, kVec>(raw, w);
+  for (int64_t chunk = c0;;) {
     const int64_t row = chunk * kSweepThreads + tid;
     const bool valid = row < c_out;
     const int64_t rr = valid ? row : c_out - 1;
-    const T* const wrow = wt + grp * gstride_w + rr * ld_w + 16 * b;
-    float w[16];
-    load_block<T, kVec>(wrow, w);
+    const T* const wrow = wblk + rr * ld_w;
     const int e = row_exponent(e_g, w);
     const float Su = ldexpf(Sg, -e);
     Best best{INFINITY, kCandidates};
@@ -1151,9 +1155,18 @@ __global__ __launch_bounds__(kSweepThreads, 2) void sweep_rows_kernel(const T* _
     } else {
       for (int k = 0; k < kCandidates; ++k) eval_direct<false>(best, k, Sg, e, w, diag, sym);
     }
-    if (valid) {
+    // Past the last chunk: stores for the valid lanes, done.  Otherwise the
+    // next chunk's weights are loaded before this chunk's stores and awaited
+    // after them (wait_raw): a wait for a load also waits for every store
+    // issued before it, and with the same stores on every path in between
+    // the compiler's wait leaves them in flight.  Only the last chunk of a
+    // block can hold lanes past the last row, so the stores of the other
+    // chunks are unconditional.
+    const int64_t next = chunk + rp.cstep;
+    const bool last = next >= rp.n_chunks;  // uniform over the wave
+    auto emit = [&]() {
       const int k = best.k < kCandidates ? best.k : 0;  // NaN errors only
-      const int64_t o = (grp * c_out + row) * nb + b;
+      const int64_t o = (grp * c_out + rr) * nb + b;
       idx_out[o] = (uint8_t)k;
       if (kAll || err_out) err_out[o] = ldexpf(best.err, 2 * e);
       if (kAll || amax_out) amax_out[o] = 6.0f * (e4m3_candidate(k) * Sg);
@@ -1168,7 +1181,17 @@ __global__ __launch_bounds__(kSweepThreads, 2) void sweep_rows_kernel(const T* _
         }
         nvfp4_emit_at<kAll>(qk, s, k, o, qo.wq, qo.packed, qo.codes);
       }
+    };
+    if (last) {
+      if (valid) emit();
+      break;
     }
+    const int64_t nrow = next * kSweepThreads + tid;
+    load_raw<T, kVec>(wblk + (nrow < c_out ? nrow : c_out - 1) * ld_w, raw);
+    emit();
+    chunk = next;
+    wait_raw(raw);
+    raw_to_float<T, kVec>(raw, w);
   }
   if constexpr (kQuant) {
     const int64_t gl = (int64_t)blockIdx.x * kSweepThreads + tid;
