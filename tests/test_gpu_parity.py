@@ -274,6 +274,35 @@ def test_full_size_workloads_sampled(lh, n):
     check_all(lh, work, n_hess_sel=24, n_sweep_sel=3000, seed=n)
 
 
+def test_sweep_waves_walking_several_chunks_with_a_partial_last_chunk(lh):
+    """Enough input blocks that each wave of the sweep walks several chunks
+    of 64 rows of its block (3 x 1024 blocks: waves take every 11th of the
+    16 chunks), and 1000 rows, so the last chunk holds 40 rows and 24 idle
+    lanes.  The whole path (certificates from the prologue) is sampled
+    against the oracle, every output of the fused sweep on the sample, and
+    the certificate-free sweep of the same H must give the same bits."""
+    work = wl.make_custom(1000, 16384, 64, n_groups=3, dtype="bf16", seed=77, w_dist="t3", x_dist="lognormal")
+    G, c_out, c_in = work.n_groups, work.c_out, work.c_in
+    nb = c_in // 16
+    print("case multi-chunk G=%d c_out=%d c_in=%d" % (G, c_out, c_in), flush=True)
+    wd, xd = work.w.to(DEV), work.x.to(DEV)
+    res = lh.lh_calibrate_nvfp4(wd, xd, packed=True, scale_e4m3=True, global_scale=True, split=True)
+    # the same H through the certificate-free path (in-kernel Gershgorin): same results
+    idx2, err2, bam2 = lh.lh_scale_sweep(wd, res["h"], res["amax"])
+    torch.cuda.synchronize()
+    for a, b in ((res["idx"], idx2), (res["err"], err2), (res["amax_blk"], bam2)):
+        assert torch.equal(a, b)
+    w_np = wl.np_bits(work.w)
+    amax_np, h_np = res["amax"].cpu().numpy(), res["h"].cpu().numpy()
+    sel = np.sort(np.random.default_rng(77).choice(G * c_out * nb, 4000, replace=False))
+    idx_np = res["idx"].cpu().numpy()
+    stats = parity.sweep_against_oracle(w_np, h_np, amax_np, c_out, c_in, G, sel, idx_np, res["err"].cpu().numpy(),
+                                        res["amax_blk"].cpu().numpy(), "multi-chunk")
+    parity.fake_quant_against_oracle(w_np, idx_np, amax_np, c_out, c_in, G, sel,
+                                     {k: res[k].cpu().numpy() for k in ("w_q", "packed", "scale_e4m3")}, "multi-chunk")
+    print("  ok: %s" % stats, flush=True)
+
+
 def test_skipping_never_changes_results(lh):
     """The sweep with the certificate pre-pass, with the on-the-fly
     certificate, and on Hessians that admit no certificate (rank-deficient,
