@@ -268,7 +268,7 @@ __device__ __forceinline__ void eval_direct(Best& best, int k, float Sg, int e, 
 // rounded sum, so a lane stopped by the two-element bound would also be
 // stopped by the four-element one: the outcome is that of the four-element
 // test alone.
-__device__ __forceinline__ bool needs_eval(SkipSet& t, const Best& best, int j, float sigma) {
+__device__ __forceinline__ bool needs_eval(SkipSet& t, const Best& best, int j, float sigma, uint64_t& live2) {
   const float pow2j = __uint_as_float((uint32_t)(127 + j) << 23);
   const float thr = best.err * t.margin;
   t.pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t.pk, t.p[0], t.p[1], pow2j, 0);
@@ -276,7 +276,8 @@ __device__ __forceinline__ bool needs_eval(SkipSet& t, const Best& best, int j, 
   const float d0 = r01.x * sigma - t.w[0], d1 = r01.y * sigma - t.w[1];
   float lb = (t.dg[0] * d0) * d0;
   lb = __builtin_fmaf(t.dg[1] * d1, d1, lb);
-  if (wave_any(!(lb > thr))) {
+  live2 = __builtin_amdgcn_ballot_w64(!(lb > thr));  // lanes the two-element bound leaves in
+  if (live2 != 0) {
     t.pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t.pk, t.p[2], t.p[3], pow2j, 1);
     const f32x2_t r23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.pk, pow2j, 1);
     const float d2 = r23.x * sigma - t.w[2], d3 = r23.y * sigma - t.w[3];
@@ -284,6 +285,10 @@ __device__ __forceinline__ bool needs_eval(SkipSet& t, const Best& best, int j, 
     lb = __builtin_fmaf(t.dg[3] * d3, d3, lb);
   }
   return !(lb > thr);
+}
+__device__ __forceinline__ bool needs_eval(SkipSet& t, const Best& best, int j, float sigma) {
+  uint64_t live2;
+  return needs_eval(t, best, j, sigma, live2);
 }
 
 // E4M3 code of mantissa class m at power j (value (1 + m/8) 2^j): normal
@@ -300,8 +305,12 @@ __device__ __forceinline__ int class_code(int m, int j) {
 // each lane evaluates its own candidates in increasing index while any lane
 // of the wave has one left.  A wave therefore costs the largest per-lane
 // count rather than the union over its lanes, and every candidate a lane
-// skips is still certified worse than that lane's incumbent.
-template <int m, bool kMse>
+// skips is still certified worse than that lane's incumbent.  With kScan
+// the level-1 tests run from the highest power down and stop where the
+// saturation argument below rules out all the lower ones at once (the
+// masks come out the same; the row-per-lane kernel, whose lanes share a
+// block and so reach that point together, uses it).
+template <int m, bool kMse, bool kScan = false>
 __device__ __forceinline__ void sweep_mantissa(Best& best, SkipSet& t, float Sg, const float (&w)[16],
                                                const float (&diag)[16], const float (&sym)[120],
                                                uint32_t (&pk)[2]) {
@@ -315,9 +324,29 @@ __device__ __forceinline__ void sweep_mantissa(Best& best, SkipSet& t, float Sg,
   constexpr int jmin = (m == 0) ? -9 : (m == 4) ? -8 : (m == 2 || m == 6) ? -7 : -6;
   constexpr int jmax = (m == 7) ? 7 : 8;
   uint32_t need = 0;
+  if constexpr (kScan) {
+    // Powers from the top down.  Below js2 the two leading bound elements
+    // both saturate (|p| >= 6 * 2^j: E2M1 gives 6, Q = 6 * 2^j * sigma), so
+    // their |dw| only grows as j falls and so does the two-element bound
+    // (rounded products and sums of non-negative terms are monotone): once
+    // every lane of the wave is at or below its js2 and the two-element
+    // bound rules the candidate out on every lane, it rules out every lower
+    // power too, and the scan stops.
+    const uint32_t a0 = __float_as_uint(t.p[0]) & 0x7FFFFFFFu, a1 = __float_as_uint(t.p[1]) & 0x7FFFFFFFu;
+    const uint32_t amin2 = min(a0, a1);  // a NaN (above every finite value) only counts when both are
+    const int js2 = (int)(amin2 >> 23) - 130 + (int)((amin2 & 0x7FFFFFu) >= 0x400000u);
 #pragma unroll
-  for (int c = 0; c <= jmax - jmin; ++c)
-    if (needs_eval(t, best, jmin + c, sigma)) need |= 1u << c;
+    for (int c = jmax - jmin; c >= 0; --c) {
+      const int j = jmin + c;
+      uint64_t live2;
+      if (needs_eval(t, best, j, sigma, live2)) need |= 1u << c;
+      if ((__builtin_amdgcn_ballot_w64(j > js2) | live2) == 0) break;
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c <= jmax - jmin; ++c)
+      if (needs_eval(t, best, jmin + c, sigma)) need |= 1u << c;
+  }
   while (wave_any(need != 0)) {
     const bool has = need != 0;
     const int j = jmin + __builtin_ctz(need | 0x80000000u);  // a dummy power when !has
@@ -1144,14 +1173,14 @@ __global__ __launch_bounds__(kSweepThreads, 2) void sweep_rows_kernel(const T* _
         for (int i = 0; i < 16; ++i) p0[i] = div_rn(w[i], sigma0, rs0);
         eval_scaled<false>(best, k0, j0, sigma0, p0, w, diag, sym, pk);
       }
-      sweep_mantissa<0, false>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<1, false>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<2, false>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<3, false>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<4, false>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<5, false>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<6, false>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<7, false>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<0, false, true>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<1, false, true>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<2, false, true>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<3, false, true>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<4, false, true>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<5, false, true>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<6, false, true>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<7, false, true>(best, t, Su, w, diag, sym, pk);
     } else {
       for (int k = 0; k < kCandidates; ++k) eval_direct<false>(best, k, Sg, e, w, diag, sym);
     }

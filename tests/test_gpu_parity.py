@@ -177,6 +177,40 @@ def test_degenerate_amax_and_zero_blocks(lh):
         _sweep_case(lh, ws, hs, gs, "scaled %g" % scale, check_err=(2.0 ** -40 <= scale <= 2.0 ** 100))  # tiny weights: E underflows fp32
 
 
+def test_level1_scan_stop_on_saturating_blocks(lh):
+    """Blocks built around the stop of the top-down level-1 scan: leading
+    elements that saturate together or far apart, one dominant weight,
+    equal magnitudes, weights on exact multiples of 6 x a candidate scale,
+    log-uniform magnitudes over twenty octaves, and channel scales that make
+    the bound elements (largest H_ee w^2) differ from the largest |w|; two
+    global amax values (the weights' own, and a third of it so that whole
+    blocks sit in the saturation region)."""
+    rng = np.random.default_rng(26)
+    c_out, nb = 192, 8
+    w = (rng.standard_normal((c_out, nb, 16)) * 0.01).astype(np.float32)
+    sign = np.where(rng.random((c_out, 16)) < 0.5, -1.0, 1.0).astype(np.float32)
+    big = np.exp(rng.uniform(-3, 0, c_out)).astype(np.float32)
+    w[:, 0, :2] = big[:, None] * sign[:, :2]                                  # two equal leaders
+    w[:, 1, 0] = big * sign[:, 0]
+    w[:, 1, 1] = big / np.float32(37.0) * sign[:, 1]                          # leaders far apart
+    w[:, 2, 5] = big * np.float32(4.0) * sign[:, 5]                           # one dominant weight
+    w[:, 3, :] = big[:, None] * sign                                          # sixteen equal magnitudes
+    w[:, 5, :] = (np.exp2(rng.uniform(-20, 0, (c_out, 16))) * sign).astype(np.float32)
+    w[:, 6, :] = w[:, 6, :] * np.float32(1e-3)                                # far below the amax
+    w[:, 7, :] = (rng.standard_t(2, (c_out, 16)) * 0.02).astype(np.float32)
+    g = float(np.abs(w).max())
+    s = oracle.candidate_scales(np.float32(g))                                # 6 * s[125] is g (to an ulp)
+    k = rng.integers(0, 126, c_out)
+    w[:, 4, :4] = (np.float32(6.0) * s[k])[:, None] * sign[:, :4]             # exactly 6 x a candidate
+    w = w.reshape(c_out, nb * 16)
+    x = rng.standard_normal((nb * 16, 96)).astype(np.float32)
+    x *= np.exp(rng.standard_normal((nb * 16, 1))).astype(np.float32)         # channel scales
+    _, h = oracle.hessian(x, nb * 16, 96)
+    _sweep_case(lh, w, h, g, "scan-stop")
+    _sweep_case(lh, w, h, g / 3.0, "scan-stop amax/3")
+    _sweep_case(lh, w, _spd(rng, nb), g, "scan-stop white H")
+
+
 def test_planted_solutions(lh):
     rng = np.random.default_rng(22)
     c_out, c_in = 64, 128
