@@ -286,10 +286,6 @@ __device__ __forceinline__ bool needs_eval(SkipSet& t, const Best& best, int j, 
   }
   return !(lb > thr);
 }
-__device__ __forceinline__ bool needs_eval(SkipSet& t, const Best& best, int j, float sigma) {
-  uint64_t live2;
-  return needs_eval(t, best, j, sigma, live2);
-}
 
 // E4M3 code of mantissa class m at power j (value (1 + m/8) 2^j): normal
 // codes 8 (j + 7) + m for j >= -6, subnormal codes (8 + m) 2^(j + 9) / 8
@@ -300,17 +296,16 @@ __device__ __forceinline__ int class_code(int m, int j) {
 
 // All candidates of mantissa class m (mu = 1 + m/8): powers j in
 // [jmin, jmax] (codes 1..126 only; 0x7F is NaN).  First every lane runs the
-// level-1 test on every candidate of the class against its incumbent at the
-// class start and keeps a mask of the candidates it cannot rule out; then
+// level-1 test on the class's candidates against its incumbent at the class
+// start and keeps a mask of the candidates it cannot rule out; then
 // each lane evaluates its own candidates in increasing index while any lane
 // of the wave has one left.  A wave therefore costs the largest per-lane
 // count rather than the union over its lanes, and every candidate a lane
-// skips is still certified worse than that lane's incumbent.  With kScan
-// the level-1 tests run from the highest power down and stop where the
-// saturation argument below rules out all the lower ones at once (the
-// masks come out the same; the row-per-lane kernel, whose lanes share a
-// block and so reach that point together, uses it).
-template <int m, bool kMse, bool kScan = false>
+// skips is still certified worse than that lane's incumbent.  The level-1
+// tests run from the highest power down and stop where the saturation
+// argument below rules out all the lower ones at once, so the masks are
+// those of testing every power.
+template <int m, bool kMse>
 __device__ __forceinline__ void sweep_mantissa(Best& best, SkipSet& t, float Sg, const float (&w)[16],
                                                const float (&diag)[16], const float (&sym)[120],
                                                uint32_t (&pk)[2]) {
@@ -324,7 +319,7 @@ __device__ __forceinline__ void sweep_mantissa(Best& best, SkipSet& t, float Sg,
   constexpr int jmin = (m == 0) ? -9 : (m == 4) ? -8 : (m == 2 || m == 6) ? -7 : -6;
   constexpr int jmax = (m == 7) ? 7 : 8;
   uint32_t need = 0;
-  if constexpr (kScan) {
+  {
     // Powers from the top down.  Below js2 the two leading bound elements
     // both saturate (|p| >= 6 * 2^j: E2M1 gives 6, Q = 6 * 2^j * sigma), so
     // their |dw| only grows as j falls and so does the two-element bound
@@ -342,10 +337,6 @@ __device__ __forceinline__ void sweep_mantissa(Best& best, SkipSet& t, float Sg,
       if (needs_eval(t, best, j, sigma, live2)) need |= 1u << c;
       if ((__builtin_amdgcn_ballot_w64(j > js2) | live2) == 0) break;
     }
-  } else {
-#pragma unroll
-    for (int c = 0; c <= jmax - jmin; ++c)
-      if (needs_eval(t, best, jmin + c, sigma)) need |= 1u << c;
   }
   while (wave_any(need != 0)) {
     const bool has = need != 0;
@@ -1173,14 +1164,14 @@ __global__ __launch_bounds__(kSweepThreads, 2) void sweep_rows_kernel(const T* _
         for (int i = 0; i < 16; ++i) p0[i] = div_rn(w[i], sigma0, rs0);
         eval_scaled<false>(best, k0, j0, sigma0, p0, w, diag, sym, pk);
       }
-      sweep_mantissa<0, false, true>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<1, false, true>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<2, false, true>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<3, false, true>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<4, false, true>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<5, false, true>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<6, false, true>(best, t, Su, w, diag, sym, pk);
-      sweep_mantissa<7, false, true>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<0, false>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<1, false>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<2, false>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<3, false>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<4, false>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<5, false>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<6, false>(best, t, Su, w, diag, sym, pk);
+      sweep_mantissa<7, false>(best, t, Su, w, diag, sym, pk);
     } else {
       for (int k = 0; k < kCandidates; ++k) eval_direct<false>(best, k, Sg, e, w, diag, sym);
     }
