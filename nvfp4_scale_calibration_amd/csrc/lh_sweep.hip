@@ -600,11 +600,12 @@ __device__ __forceinline__ void load_block(const T* p, float (&w)[16]) {
 // factorisation per lane, 16x fewer instructions in total) is.
 constexpr int64_t kCertTeamMaxBlocks = 2048;
 
-// Value of lane k of this lane's 16-lane team (ds_swizzle bit mode within
-// 32-lane halves: new lane = (lane & 16) | k).
+// Value of lane k of this lane's 16-lane team.  A team is one DPP row, and
+// row_newbcast copies the row's lane k to all sixteen (a VALU move, no LDS
+// round trip; every lane of the team is active here).
 template <int k>
 __device__ __forceinline__ float team_lane(float v) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x10 | (k << 5)));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + k, 0xF, 0xF, false));
 }
 
 // A_ik -= l_ij l_kj for k = k0..15, l_kj from lane k of the team.
