@@ -66,7 +66,7 @@ def _load():
     lib.oracle_block_errors.argtypes = [P, P, F, P]
     lib.oracle_absmax.argtypes = [P, I32, I64, I64, I64, I64, I64, P]
     lib.oracle_hessian.argtypes = [P, I32, I32, I64, I64, I64, I64, D, D, P, I64, P, P]
-    lib.oracle_sweep.argtypes = [P, I32, I64, I64, I64, I64, P, I64, P, P, I64, P, P, P, P, P]
+    lib.oracle_sweep.argtypes = [P, I32, I64, I64, I64, I64, P, I64, P, P, I64, P, P, P, P, P, P, P, P, P]
     lib.oracle_fake_quant.argtypes = [P, I32, I64, I64, I64, I64, P, P, P, I64, P, P, P]
     lib.oracle_e4m3_round_code.argtypes = [F]
     lib.oracle_e4m3_round_code.restype = I32
@@ -74,7 +74,7 @@ def _load():
     lib.oracle_amax_multiplier.restype = F
     lib.oracle_rule_candidates.argtypes = [I32, P, F, P]
     lib.oracle_rule_candidates.restype = I32
-    lib.oracle_select.argtypes = [I32, P, I32, I64, I64, I64, I64, P, I64, P, P, I64, P, P, P, P, P]
+    lib.oracle_select.argtypes = [I32, P, I32, I64, I64, I64, I64, P, I64, P, P, I64, P, P, P, P, P, P, P, P, P]
     lib.oracle_hessian_ragged.argtypes = [P, I32, I64, I64, P, I64, P, P, I64, P, P, P]
     lib.oracle_full_hessian.argtypes = [P, I32, I64, I64, I64, D, P]
     lib.oracle_output_error.argtypes = [P, I32, P, I64, I64, I64, P, P, I64, P]
@@ -172,13 +172,29 @@ def hessian(x: np.ndarray, c_in: int, n_tok: int, layout: int = CHANNEL_MAJOR,
     return h64, h32
 
 
+def _probe_outputs(n: int, probe, forms: bool) -> dict:
+    out = {}
+    if probe is not None:
+        out["e_probe"] = np.empty(n, np.float64)
+    if forms:
+        out["s_best"] = np.empty(n, np.float64)
+        if probe is not None:
+            out["s_probe"] = np.empty(n, np.float64)
+    return out
+
+
 def sweep(w: np.ndarray, H: np.ndarray, amax: np.ndarray, c_out: int, c_in: int,
           ld_w: int | None = None, n_groups: int = 1, group_stride_w: int | None = None,
-          group_stride_h: int | None = None, sel: np.ndarray | None = None) -> dict:
+          group_stride_h: int | None = None, sel: np.ndarray | None = None, probe: np.ndarray | None = None,
+          forms: bool = False) -> dict:
     """Exhaustive 126-candidate sweep for the selected flat block indices
     ((group * c_out + row) * c_in/16 + b).  H is the fp32 Hessian tensor the
     sweep consumes ([n_groups][c_in/16][16][16]).  Returns a dict of compact
-    arrays: idx, e1 (best error), e2 (second best), err (fl32(e1)), amax."""
+    arrays: idx, e1 (best error), e2 (second best), err (fl32(e1)), amax.
+    With ``probe`` (one candidate index per selected block, e.g. another
+    implementation's pick) also e_probe = the error at that candidate; with
+    ``forms`` also s_best (and s_probe) = sum_ij |H_ij| |dw_i| |dw_j| at the
+    best (and the probed) candidate, which sizes fp32 rounding in checks."""
     w = np.ascontiguousarray(w)
     H = np.ascontiguousarray(H, np.float32)
     amax = np.ascontiguousarray(amax, np.float32).reshape(-1)
@@ -190,9 +206,12 @@ def sweep(w: np.ndarray, H: np.ndarray, amax: np.ndarray, c_out: int, c_in: int,
     n = len(sel)
     out = dict(idx=np.empty(n, np.int32), e1=np.empty(n, np.float64), e2=np.empty(n, np.float64),
                err=np.empty(n, np.float32), amax=np.empty(n, np.float32))
+    pr = None if probe is None else np.ascontiguousarray(probe, np.int32).reshape(n)
+    out.update(_probe_outputs(n, pr, forms))
     _load().oracle_sweep(_ptr(w), _dtype_code(w), c_out, c_in, ld_w, gsw, _ptr(H), gsh, _ptr(amax),
                          _ptr(sel), n, _ptr(out["idx"]), _ptr(out["e1"]), _ptr(out["e2"]),
-                         _ptr(out["err"]), _ptr(out["amax"]))
+                         _ptr(out["err"]), _ptr(out["amax"]), _ptr(pr), _ptr(out.get("e_probe")),
+                         _ptr(out.get("s_probe")), _ptr(out.get("s_best")))
     return out
 
 
@@ -239,11 +258,13 @@ def rule_candidates(rule: int, w16, g: float) -> np.ndarray:
 
 def select(rule: int, w: np.ndarray, H, amax: np.ndarray, c_out: int, c_in: int,
            ld_w: int | None = None, n_groups: int = 1, group_stride_w: int | None = None,
-           group_stride_h: int | None = None, sel: np.ndarray | None = None) -> dict:
+           group_stride_h: int | None = None, sel: np.ndarray | None = None, probe: np.ndarray | None = None,
+           forms: bool = False) -> dict:
     """Scale selection by rule (RULE_SWEEP: all 126 candidates, RULE_MAX,
     RULE_FOUR_OVER_SIX, RULE_AMAX_SEARCH) for the selected flat block
     indices.  H is the fp32 Hessian tensor, or None for the plain weight
-    error (H = I).  Returns idx, e1, e2, err, amax like ``sweep``."""
+    error (H = I).  Returns idx, e1, e2, err, amax like ``sweep``, and the
+    same optional probe / form outputs (under the rule's objective)."""
     w = np.ascontiguousarray(w)
     Hc = None if H is None else np.ascontiguousarray(H, np.float32)
     amax = np.ascontiguousarray(amax, np.float32).reshape(-1)
@@ -255,10 +276,13 @@ def select(rule: int, w: np.ndarray, H, amax: np.ndarray, c_out: int, c_in: int,
     n = len(sel)
     out = dict(idx=np.empty(n, np.int32), e1=np.empty(n, np.float64), e2=np.empty(n, np.float64),
                err=np.empty(n, np.float32), amax=np.empty(n, np.float32))
+    pr = None if probe is None else np.ascontiguousarray(probe, np.int32).reshape(n)
+    out.update(_probe_outputs(n, pr, forms))
     _load().oracle_select(int(rule), _ptr(w), _dtype_code(w), c_out, c_in, ld_w, gsw,
                           None if Hc is None else _ptr(Hc), gsh, _ptr(amax), _ptr(sel), n,
                           _ptr(out["idx"]), _ptr(out["e1"]), _ptr(out["e2"]), _ptr(out["err"]),
-                          _ptr(out["amax"]))
+                          _ptr(out["amax"]), _ptr(pr), _ptr(out.get("e_probe")), _ptr(out.get("s_probe")),
+                          _ptr(out.get("s_best")))
     return out
 
 

@@ -178,6 +178,43 @@ void oracle_block_errors(const float *w, const float *H, float g, double *E /* [
     }
 }
 
+/* S = sum_ij |H_ij| |dw_i| |dw_j| of one block at candidate k (H NULL: the
+ * identity).  Not part of the method: the parity tests use it to size the
+ * rounding error that an fp32 evaluation of dw^T H dw may carry. */
+static double abs_form_at(const float *w, const float *H, float g, int k)
+{
+    float s[126];
+    oracle_candidate_scales(g, s);
+    double dw[16];
+    for (int i = 0; i < 16; ++i)
+        dw[i] = fabs((double)oracle_quantize(w[i], s[k], 0) - (double)w[i]);
+    double acc = 0.0;
+    for (int i = 0; i < 16; ++i)
+        for (int j = 0; j < 16; ++j) {
+            double hij = H ? fabs((double)H[i * 16 + j]) : (i == j ? 1.0 : 0.0);
+            acc += dw[i] * hij * dw[j];
+        }
+    return acc;
+}
+
+/* Optional per-block outputs for checking another implementation's pick:
+ * the error at a probed candidate (e.g. the one the GPU chose), and the
+ * absolute forms S at the probed and at the best candidate. */
+static void probe_block(const float *w, const float *H, float g, const double *E, int kb,
+                        const int32_t *probe, int64_t n, double *e_probe, double *s_probe,
+                        double *s_best)
+{
+    int kp = probe ? probe[n] : kb;
+    if (kp < 0 || kp > 125)
+        kp = kb;
+    if (e_probe)
+        e_probe[n] = E[kp];
+    if (s_probe)
+        s_probe[n] = abs_form_at(w, H, g, kp);
+    if (s_best)
+        s_best[n] = abs_form_at(w, H, g, kb);
+}
+
 /* Argmin with the lowest index on ties (R5); e2 = best error among k != k*. */
 static void argmin126(const double *E, int *k_out, double *e1, double *e2)
 {
@@ -262,7 +299,8 @@ void oracle_hessian(const void *x, int dtype, int layout, int64_t c_in, int64_t 
 void oracle_sweep(const void *w, int dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
                   int64_t gstride_w, const float *H, int64_t gstride_h, const float *amax,
                   const int64_t *sel, int64_t n_sel, int32_t *idx_out, double *e1_out,
-                  double *e2_out, float *err_out, float *amax_out)
+                  double *e2_out, float *err_out, float *amax_out, const int32_t *probe,
+                  double *e_probe, double *s_probe, double *s_best)
 {
     const int64_t nb = c_in / 16;
 #pragma omp parallel for schedule(dynamic, 16)
@@ -275,10 +313,12 @@ void oracle_sweep(const void *w, int dtype, int64_t c_out, int64_t c_in, int64_t
         for (int i = 0; i < 16; ++i)
             wb[i] = widen_f32(w, dtype, g * gstride_w + row * ld_w + 16 * b + i);
         double E[126];
-        oracle_block_errors(wb, H + g * gstride_h + b * 256, amax[g], E);
+        const float *Hb = H + g * gstride_h + b * 256;
+        oracle_block_errors(wb, Hb, amax[g], E);
         int k;
         double e1, e2;
         argmin126(E, &k, &e1, &e2);
+        probe_block(wb, Hb, amax[g], E, k, probe, n, e_probe, s_probe, s_best);
         if (idx_out)
             idx_out[n] = k;
         if (e1_out)
@@ -453,7 +493,8 @@ static void block_errors_objective(const float *w, const float *H, float g, doub
 void oracle_select(int rule, const void *w, int dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
                    int64_t gstride_w, const float *H, int64_t gstride_h, const float *amax,
                    const int64_t *sel, int64_t n_sel, int32_t *idx_out, double *e1_out,
-                   double *e2_out, float *err_out, float *amax_out)
+                   double *e2_out, float *err_out, float *amax_out, const int32_t *probe,
+                   double *e_probe, double *s_probe, double *s_best)
 {
     const int64_t nb = c_in / 16;
 #pragma omp parallel for schedule(dynamic, 16)
@@ -466,7 +507,8 @@ void oracle_select(int rule, const void *w, int dtype, int64_t c_out, int64_t c_
         for (int i = 0; i < 16; ++i)
             wb[i] = widen_f32(w, dtype, g * gstride_w + row * ld_w + 16 * b + i);
         double E[126];
-        block_errors_objective(wb, H ? H + g * gstride_h + b * 256 : 0, amax[g], E);
+        const float *Hb = H ? H + g * gstride_h + b * 256 : 0;
+        block_errors_objective(wb, Hb, amax[g], E);
         int ks[126];
         int nk = oracle_rule_candidates(rule, wb, amax[g], ks);
         int kb = ks[0];
@@ -477,6 +519,7 @@ void oracle_select(int rule, const void *w, int dtype, int64_t c_out, int64_t c_
         for (int i = 0; i < nk; ++i)
             if (ks[i] != kb && E[ks[i]] < second)
                 second = E[ks[i]];
+        probe_block(wb, Hb, amax[g], E, kb, probe, n, e_probe, s_probe, s_best);
         if (idx_out)
             idx_out[n] = kb;
         if (e1_out)
@@ -509,7 +552,8 @@ void oracle_select(int rule, const void *w, int dtype, int64_t c_out, int64_t c_
 /*       H_g = (n_old H_g + S_g) / (n_old + n_g), counts[g] = n_old + n_g; */
 /*       unchanged while n_old + n_g = 0.                                  */
 /* Outputs are compact per selected flat block g * (c_in/16) + b; h_old    */
-/* (compact, fp32) is the previous H of those blocks.                      */
+/* (compact, fp32) is the previous H of those blocks.  offsets must be     */
+/* nondecreasing and within x's rows (callers clamp them first).           */
 /* ====================================================================== */
 void oracle_hessian_ragged(const void *x, int dtype, int64_t c_in, int64_t ld_x,
                            const int64_t *offsets, int64_t n_groups, const int64_t *counts,

@@ -48,7 +48,7 @@ def run_path(lh, w, x, layout="channel", workspace=True):
                 bam=bam.cpu().numpy(), fq={k: v.cpu().numpy() for k, v in fq.items()})
 
 
-def check_all(lh, work: wl.Workload, layout="channel", n_hess_sel=None, n_sweep_sel=None, seed=0):
+def check_all(lh, work: wl.Workload, layout="channel", n_hess_sel=None, n_sweep_sel=None, seed=0, strict=False):
     G, c_out, c_in, n = work.n_groups, work.c_out, work.c_in, work.n_tok
     nb = c_in // 16
     print("case %s G=%d c_out=%d c_in=%d N=%d %s %s" % (work.name, G, c_out, c_in, n, work.dtype, layout), flush=True)
@@ -65,7 +65,7 @@ def check_all(lh, work: wl.Workload, layout="channel", n_hess_sel=None, n_sweep_
     total = G * c_out * nb
     ssel = np.arange(total) if n_sweep_sel is None else np.sort(rng.choice(total, min(n_sweep_sel, total), replace=False))
     stats = parity.sweep_against_oracle(w_np, got["h"], got["amax"], c_out, c_in, G, ssel, got["idx"], got["err"],
-                                        got["bam"], work.name)
+                                        got["bam"], work.name, strict=strict)
     # fake-quant with the GPU's indices: bit-exact
     parity.fake_quant_against_oracle(w_np, got["idx"], got["amax"], c_out, c_in, G, ssel, got["fq"], work.name)
     np.testing.assert_array_equal(got["fq"]["global_scale"], got["amax"] / np.float32(2688.0))
@@ -75,7 +75,7 @@ def check_all(lh, work: wl.Workload, layout="channel", n_hess_sel=None, n_sweep_
 
 def test_linear_256_end_to_end(lh):
     work = wl.make(1)
-    got, stats = check_all(lh, work)
+    got, stats = check_all(lh, work, strict=True)
     assert stats["n"] == 4096
     # end to end, each side with its own H: report the index agreement
     _, h32 = oracle.hessian(wl.np_bits(work.x), 256, 128)
@@ -132,6 +132,26 @@ def test_hessian_alpha_beta_chunks_and_empty(lh):
     lh.lh_accumulate_hessian(x[:, :, :0], alpha=1.0, beta=0.5, h=h0)
     torch.cuda.synchronize()
     assert torch.equal(h0, h * 0.5)
+
+
+def test_hessian_alpha_nan_is_the_normalised_factor(lh):
+    """alpha = NaN (the binding's default) makes the library apply
+    fl32(1/N) itself: bit-identical to passing that factor explicitly, for
+    the local and the full Hessian, and equal to the oracle's 1/N Hessian."""
+    work = wl.make_custom(4, 64, 777, dtype="bf16", seed=19)
+    x = work.x.to(DEV)
+    a = float(np.float32(1.0 / 777))
+    h_nan = lh.lh_accumulate_hessian(x, alpha=float("nan"))
+    h_exp = lh.lh_accumulate_hessian(x, alpha=a)
+    h_def = lh.lh_accumulate_hessian(x)
+    f_nan = lh.lh_full_hessian(x, alpha=float("nan"))
+    f_exp = lh.lh_full_hessian(x, alpha=a)
+    torch.cuda.synchronize()
+    assert torch.equal(h_nan.view(torch.int32), h_exp.view(torch.int32))
+    assert torch.equal(h_def.view(torch.int32), h_exp.view(torch.int32))
+    assert torch.equal(f_nan.view(torch.int32), f_exp.view(torch.int32))
+    h64, _ = oracle.hessian(wl.np_bits(work.x), 64, 777)
+    parity.check_hessian(h_nan.cpu().numpy(), h64, "alpha NaN")
 
 
 def _sweep_case(lh, w_np32, h_np, amax_val, what, check_err=True):
@@ -300,12 +320,64 @@ def test_empty_problems(lh):
     assert idx.numel() == 0
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("n", [2, 3, 4, 5])
-def test_full_size_workloads_sampled(lh, n):
-    """The named workloads at full size, in the launch configuration the
-    benchmark times; outputs sampled for the oracle."""
+def test_full_size_benchmarked_pair_every_block(lh, n):
+    """The named workloads at full size through the two calls the benchmark
+    times (lh_calibrate_prologue, then lh_calibrate_sweep, with the
+    benchmark's buffers), every output of every block against the oracle:
+    global amax bit-exact, every Hessian block, every block's index, error
+    and amax under the near-tie rules with no block passing only through the
+    fp32 allowance, and Q, nibbles and E4M3 codes bit-exact.  The separate
+    calls (lh_absmax, lh_accumulate_hessian, lh_fake_quant_nvfp4) and the
+    sweep without certificates (lh_scale_sweep without a workspace, which
+    evaluates without the prologue's skip bounds) must give the same bits."""
     work = wl.make(n)
-    check_all(lh, work, n_hess_sel=24, n_sweep_sel=3000, seed=n)
+    G, c_out, c_in, N = work.n_groups, work.c_out, work.c_in, work.n_tok
+    nb = c_in // 16
+    print("case full-size %s G=%d c_out=%d c_in=%d N=%d" % (work.name, G, c_out, c_in, N), flush=True)
+    w, x = work.w.to(DEV), work.x.to(DEV)
+    amax = torch.empty(G, dtype=torch.float32, device=DEV)
+    h = torch.empty((G, nb, 16, 16), dtype=torch.float32, device=DEV)
+    cws = torch.empty(lh.lh_calibrate_workspace_bytes(c_out, c_in, N, G), dtype=torch.uint8, device=DEV)
+    idx = torch.empty((G, c_out, nb), dtype=torch.uint8, device=DEV)
+    err = torch.empty((G, c_out, nb), dtype=torch.float32, device=DEV)
+    bam = torch.empty((G, c_out, nb), dtype=torch.float32, device=DEV)
+    wq = torch.empty((G, c_out, c_in), dtype=torch.float32, device=DEV)
+    packed = torch.empty((G, c_out, c_in // 2), dtype=torch.uint8, device=DEV)
+    codes = torch.empty((G, c_out, nb), dtype=torch.uint8, device=DEV)
+    gscale = torch.empty(G, dtype=torch.float32, device=DEV)
+    lh.lh_calibrate_prologue(w, x, amax, h, cws)
+    lh.lh_calibrate_sweep(w, h, amax, cws, idx, err, bam, wq, packed, codes, gscale)
+    # the separate calls and the certificate-free sweep: the same bits
+    amax2 = lh.lh_absmax(w)
+    h2 = lh.lh_accumulate_hessian(x)
+    i2, e2, b2 = lh.lh_scale_sweep(w, h, amax, workspace=False)
+    fq2 = lh.lh_fake_quant_nvfp4(w, idx, amax, w_q=True, packed=True, scale_e4m3=True, global_scale=True)
+    torch.cuda.synchronize()
+    for name, a, b in (("amax", amax, amax2), ("h", h, h2), ("idx", idx, i2), ("err", err, e2), ("amax_blk", bam, b2),
+                       ("w_q", wq, fq2["w_q"]), ("packed", packed, fq2["packed"]),
+                       ("scale_e4m3", codes, fq2["scale_e4m3"]), ("global_scale", gscale, fq2["global_scale"])):
+        if a.dtype == torch.float32:
+            a, b = a.view(torch.int32), b.view(torch.int32)
+        assert torch.equal(a, b), "%s: %s differs between the benchmarked pair and the separate calls" % (work.name,
+                                                                                                          name)
+    del amax2, h2, i2, e2, b2, fq2, x
+    got = dict(amax=amax.cpu().numpy(), h=h.cpu().numpy(), idx=idx.cpu().numpy(), err=err.cpu().numpy(),
+               bam=bam.cpu().numpy(), fq=dict(w_q=wq.cpu().numpy(), packed=packed.cpu().numpy(),
+                                              scale_e4m3=codes.cpu().numpy()))
+    gs = gscale.cpu().numpy()
+    w_np, x_np = wl.np_bits(work.w), wl.np_bits(work.x)
+    np.testing.assert_array_equal(got["amax"], oracle.absmax(w_np, c_out, c_in, n_groups=G))
+    np.testing.assert_array_equal(gs, got["amax"] / np.float32(2688.0))
+    h64, _ = oracle.hessian(x_np, c_in, N, n_groups=G)
+    hdev = parity.check_hessian(got["h"], h64, work.name)
+    del h64, x_np
+    sel = np.arange(G * c_out * nb, dtype=np.int64)
+    stats = parity.sweep_against_oracle(w_np, got["h"], got["amax"], c_out, c_in, G, sel, got["idx"], got["err"],
+                                        got["bam"], work.name, strict=True)
+    parity.fake_quant_against_oracle(w_np, got["idx"], got["amax"], c_out, c_in, G, sel, got["fq"], work.name)
+    print("  ok %s: every block; Hessian worst normalised deviation %.3g; %s" % (work.name, hdev, stats), flush=True)
 
 
 def test_sweep_waves_walking_several_chunks_with_a_partial_last_chunk(lh):
