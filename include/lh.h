@@ -111,6 +111,15 @@ lh_status lh_absmax(const void *w, int w_dtype, int64_t rows, int64_t cols, int6
                     int64_t n_groups, int64_t group_stride_w, float *amax, void *stream);
 
 /*
+ * The normalisation factor that lh_accumulate_hessian and lh_full_hessian
+ * apply for a given alpha: alpha itself, or for alpha = NaN the normalised
+ * Hessian's factor 1/N of "Entry API and calibration flow", phase 3 (the
+ * per-block Hessian normalised by the token count), as fl32(1/n_tokens), and 0
+ * for n_tokens <= 0.  Pure host function; lh_calibrate_* use the same factor.
+ */
+float lh_hessian_alpha(float alpha, int64_t n_tokens);
+
+/*
  * Scratch bytes that let lh_accumulate_hessian split the token dimension of
  * each block over several workgroups and reduce the partial sums in a fixed
  * order (deterministic).  0 bytes is always accepted (one workgroup per
@@ -127,8 +136,10 @@ size_t lh_hessian_workspace_bytes(int64_t c_in, int64_t n_tokens, int64_t n_grou
  *                 + alpha * sum_{t < n_tokens} X[g][16b+i][t] * X[g][16b+j][t]
  *
  * for every group g < n_groups, input block b < c_in / 16, 0 <= i, j < 16.
- * alpha = 1/n_tokens, beta = 0 gives the normalised one-shot Hessian;
- * alpha = 1, beta = 1 streams further token chunks into h.  beta == 0 never
+ * alpha = NaN asks for the normalised Hessian's factor: the library uses
+ * lh_hessian_alpha(NaN, n_tokens) = fl32(1/n_tokens) (0 when n_tokens = 0).
+ * alpha = 1/n_tokens (or NaN), beta = 0 gives the normalised one-shot
+ * Hessian; alpha = 1, beta = 1 streams further token chunks into h.  beta == 0 never
  * reads h (so h may be uninitialised).  Products are exact (bf16 x bf16 or
  * fp32 x fp32 on matrix cores), sums are fp32.
  *   x        activations, x_dtype, `layout` (see lh_layout), leading
@@ -408,8 +419,9 @@ lh_status lh_fake_quant_nvfp4(const void *w, int w_dtype, int64_t c_out, int64_t
  * Full Hessian h_full[g] = alpha * X_g X_g^T (C_in x C_in, fp32 accumulation
  * on matrix cores), X channel-major x[g][c * ld_x + t] (fp32 or bf16),
  * h_full[g][i * ld_h + j], ld_h >= c_in, group strides >= 0 (h groups must not
- * overlap).  With alpha = 1/N its diagonal 16 x 16 blocks are the local
- * Hessians.  n_tokens = 0 writes zeros.
+ * overlap).  With alpha = 1/N (or NaN, which the library replaces by
+ * lh_hessian_alpha(NaN, n_tokens) = fl32(1/N)) its diagonal 16 x 16 blocks are
+ * the local Hessians.  n_tokens = 0 writes zeros.
  * Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_ARG, LH_ERR_HIP.
  */
 lh_status lh_full_hessian(const void *x, int x_dtype, int64_t c_in, int64_t n_tokens, int64_t ld_x,

@@ -48,6 +48,8 @@ def _load() -> ctypes.CDLL:
     lib.lh_last_error_message.restype = ctypes.c_char_p
     lib.lh_absmax.argtypes = [P, I, I64, I64, I64, I64, I64, P, P]
     lib.lh_absmax.restype = I
+    lib.lh_hessian_alpha.argtypes = [F, I64]
+    lib.lh_hessian_alpha.restype = F
     lib.lh_hessian_workspace_bytes.argtypes = [I64, I64, I64]
     lib.lh_hessian_workspace_bytes.restype = SZ
     lib.lh_accumulate_hessian.argtypes = [P, I, I, I64, I64, I64, I64, I64, F, F, P, I64, P, SZ, P]
@@ -94,7 +96,7 @@ def _load() -> ctypes.CDLL:
 
 
 lib = _load()
-EXPORTS = ("lh_abi_version", "lh_status_string", "lh_last_error_message", "lh_absmax",
+EXPORTS = ("lh_abi_version", "lh_status_string", "lh_last_error_message", "lh_absmax", "lh_hessian_alpha",
            "lh_hessian_workspace_bytes", "lh_accumulate_hessian", "lh_hessian_ragged_workspace_bytes",
            "lh_accumulate_hessian_ragged", "lh_sweep_workspace_bytes", "lh_scale_sweep",
            "lh_scale_sweep_fake_quant", "lh_calibrate_workspace_bytes", "lh_calibrate_nvfp4",
@@ -167,6 +169,11 @@ def lh_absmax(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     return out
 
 
+def lh_hessian_alpha(alpha: float, n_tokens: int) -> float:
+    """The factor the Hessian calls apply for `alpha` (NaN: fl32(1/N))."""
+    return float(lib.lh_hessian_alpha(float(alpha), int(n_tokens)))
+
+
 def lh_hessian_workspace_bytes(c_in: int, n_tokens: int, n_groups: int = 1) -> int:
     return int(lib.lh_hessian_workspace_bytes(c_in, n_tokens, n_groups))
 
@@ -190,7 +197,7 @@ def lh_accumulate_hessian(x: torch.Tensor, layout: str = "channel", alpha: float
     c_in, n_tok = (x3.shape[1], x3.shape[2]) if lay == LH_LAYOUT_CHANNEL_MAJOR else (x3.shape[2], x3.shape[1])
     nb = c_in // BLOCK
     if alpha is None:
-        alpha = 1.0 / n_tok if n_tok > 0 else 0.0
+        alpha = float("nan")   # the library applies the normalised Hessian's 1/N
     if h is None:
         h = torch.empty((g, nb, BLOCK, BLOCK), dtype=torch.float32, device=x.device)
         if beta != 0.0:
@@ -486,7 +493,7 @@ def lh_full_hessian(x: torch.Tensor, alpha: float | None = None, h: torch.Tensor
     if n > 0 and x3.stride(-1) != 1:
         raise ValueError("last dim of x must be contiguous")
     if alpha is None:
-        alpha = 1.0 / n if n > 0 else 0.0
+        alpha = float("nan")   # the library applies 1/N
     if h is None:
         h = torch.empty((g, c_in, c_in), dtype=torch.float32, device=x.device)
     h3 = _as3(h)

@@ -27,6 +27,14 @@ bool valid_dtype(int d) { return d == LH_DTYPE_F32 || d == LH_DTYPE_BF16; }
 size_t elem_size(int d) { return d == LH_DTYPE_BF16 ? 2 : 4; }
 bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
+// The normalisation factor of a Hessian: the caller's alpha, or for NaN the
+// normalised Hessian's fl32(1/N) (0 for N = 0), computed here once for every
+// entry point so that callers do none of the method's arithmetic.
+float hessian_alpha(float alpha, int64_t n_tokens) {
+  if (!isnan(alpha)) return alpha;
+  return n_tokens > 0 ? (float)(1.0 / (double)n_tokens) : 0.0f;
+}
+
 }  // namespace
 
 extern "C" {
@@ -48,6 +56,8 @@ const char* lh_status_string(int status) {
 }
 
 const char* lh_last_error_message(void) { return g_msg; }
+
+float lh_hessian_alpha(float alpha, int64_t n_tokens) { return hessian_alpha(alpha, n_tokens); }
 
 lh_status lh_absmax(const void* w, int w_dtype, int64_t rows, int64_t cols, int64_t ld_w,
                     int64_t n_groups, int64_t group_stride_w, float* amax, void* stream) {
@@ -100,8 +110,8 @@ lh_status lh_accumulate_hessian(const void* x, int x_dtype, int layout, int64_t 
     if (workspace_bytes < need) return fail(LH_ERR_WORKSPACE, "%s: workspace smaller than lh_hessian_workspace_bytes()", fn);
   }
   if (!work) return LH_OK;
-  lh::HessianArgs a{x, x_dtype, layout, c_in, n_tokens, ld_x, group_stride_x, n_groups, alpha, beta,
-                    h, group_stride_h, workspace, workspace_bytes};
+  lh::HessianArgs a{x, x_dtype, layout, c_in, n_tokens, ld_x, group_stride_x, n_groups,
+                    hessian_alpha(alpha, n_tokens), beta, h, group_stride_h, workspace, workspace_bytes};
   hipError_t e = lh::launch_hessian(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LH_OK : hip_fail(e, fn);
 }
@@ -304,7 +314,7 @@ lh_status lh_calibrate_prologue(const void* w, int w_dtype, int64_t c_out, int64
   float* cert = reinterpret_cast<float*>(ws);
   char* rest = ws + calibrate_cert_bytes(c_in, n_groups);
   const size_t rest_bytes = workspace_bytes - calibrate_cert_bytes(c_in, n_groups);
-  const float alpha = n_tokens > 0 ? (float)(1.0 / (double)n_tokens) : 0.0f;
+  const float alpha = hessian_alpha(NAN, n_tokens);
   const int64_t epx = 16 / elem_size(x_dtype), epw = 16 / elem_size(w_dtype);
   const bool fused = x_layout == LH_LAYOUT_CHANNEL_MAJOR && n_tokens > 0 && aligned(x, 16) && ld_x % epx == 0 &&
                      group_stride_x % epx == 0 && aligned(w, 16) && ld_w == c_in && group_stride_w % epw == 0;
@@ -427,8 +437,8 @@ lh_status lh_full_hessian(const void* x, int x_dtype, int64_t c_in, int64_t n_to
   if (!aligned(x, elem_size(x_dtype)) || !aligned(h_full, 4))
     return fail(LH_ERR_ARG, "%s: pointer not aligned to its element size", fn);
   if (!work) return LH_OK;
-  lh::FullHessianArgs a{x, x_dtype, c_in, n_tokens, ld_x, group_stride_x, n_groups, alpha, h_full, ld_h,
-                        group_stride_h};
+  lh::FullHessianArgs a{x, x_dtype, c_in, n_tokens, ld_x, group_stride_x, n_groups, hessian_alpha(alpha, n_tokens),
+                        h_full, ld_h, group_stride_h};
   hipError_t e = lh::launch_full_hessian(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LH_OK : hip_fail(e, fn);
 }

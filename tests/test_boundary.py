@@ -295,3 +295,23 @@ def test_ragged_hessian_validation(lib):
     assert lib.lh_hessian_ragged_workspace_bytes(2048, 32768, 64, 4230) == 5 * 64 * 128 * 256 * 4
     assert lib.lh_hessian_ragged_workspace_bytes(2048, 32768, 64, 1000) == 0
     assert call(g=0) == OK and call(c_in=0) == OK
+
+
+def test_hessian_alpha_sentinel(lib):
+    """alpha = NaN asks the library for the normalised Hessian's factor
+    fl32(1/N) ("Entry API and calibration flow", phase 3); any other alpha is
+    used as given; N = 0 gives 0.  The binding passes NaN by default and so
+    computes no part of the method itself."""
+    import numpy as np
+    for n in (1, 3, 7, 128, 4096, 16384, 17408, 123457, 2 ** 31 - 1):
+        got = np.float32(lib.lh_hessian_alpha(float("nan"), n))
+        assert got == np.float32(np.float64(1.0) / np.float64(n)), n
+        assert got == np.float32(1.0) / np.float32(n) or n >= 2 ** 24, n
+    assert lib.lh_hessian_alpha(float("nan"), 0) == 0.0
+    assert lib.lh_hessian_alpha(0.25, 12) == 0.25
+    assert lib.lh_hessian_alpha(1.0, 0) == 1.0
+    import nvfp4_scale_calibration_amd as m
+    assert m.lh_hessian_alpha(float("nan"), 3) == float(np.float32(1 / 3))
+    # validation still runs before anything else with the sentinel
+    st = lib.lh_accumulate_hessian(None, 1, 0, 32, 10, 10, 1, 0, float("nan"), 0.0, None, 0, None, 0, None)
+    assert st == NULL
