@@ -5,15 +5,20 @@ One step = the whole path over one layer's synthetic inputs, inputs resident
 in HBM: global amax and local Hessians (lh_calibrate_prologue), then the
 126-candidate scale sweep and the NVFP4 fake-quant of its result
 (dequantised fp32 weights + packed E2M1 nibbles + E4M3 scale codes + S_g,
-lh_calibrate_sweep).  W warm-up steps, then K timed steps between device
-synchronisations; the sweep's launch is also timed with HIP events recorded
-on the stream it is launched on (the current torch stream, which the binding
-passes to the library).
+lh_calibrate_sweep).  The default layer is the largest named workload, the
+MLP down projection W[5120 x 17408] with X[17408 x 16384 tokens] (5,570,560
+blocks; the only one whose activations exceed the 256 MB last-level cache).
+W warm-up steps, then K timed steps between device synchronisations; the
+sweep's launch is also timed with HIP events recorded on the stream it is
+launched on (the current torch stream, which the binding passes to the
+library).
 
 Prints ONE JSON line.  value = NVFP4 blocks scale-swept per second over the
-whole step; the line also carries the Hessian pass in GB/s, the sweep in
-blocks/s and TFLOP/s, the roofline of the dominant kernel (the sweep) and
-the CPU oracle's rate on a bounded sample of the same workload.
+whole step.  The line also carries the Hessian pass in GB/s measured after
+a last-level-cache flush (per named workload), the roofline of the dominant
+kernel (the sweep: VALU issue, from the rocprofv3 counters of one dispatch
+committed under profiles/ for these kernel sources) and the CPU oracle's
+rate on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -29,10 +34,14 @@ sys.path.insert(0, ROOT)
 
 METRIC = "NVFP4 blocks/s scale-swept (126 cand) + Hessian-accum GB/s, % roofline"
 HBM_PEAK_GBPS = 8000.0
-FP32_VECTOR_PEAK_TFLOPS = 157.3       # MI355X published fp32 vector peak (packed)
-FP32_NONPACKED_TFLOPS = 78.6          # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
-SWEEP_FLOP_PER_BLOCK = 126 * (16 * 16 + 16) * 2   # 68,544: dense dw^T H dw per candidate
+FP32_NONPACKED_TFLOPS = 78.6          # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz (packed FP32 is off)
+N_SIMD = 256 * 4                      # MI355X: 256 CUs x 4 SIMDs
+N_XCD = 8                             # GRBM_GUI_ACTIVE reads summed over the 8 XCDs
+CLOCK_GHZ = 2.4                       # published peak engine clock
+VALU_QUAD_PEAK_G = N_SIMD * CLOCK_GHZ / 4   # G quad-cycles/s: one wave64 VALU issue per SIMD per 4 clocks
+SWEEP_FLOP_PER_BLOCK = 126 * (16 * 16 + 16) * 2   # 68,544: dense dw^T H dw of every candidate
 PROFILES = os.path.join(ROOT, "profiles")
+COUNTERS = os.path.join(PROFILES, "counters.json")
 
 
 def parse():
@@ -40,11 +49,14 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", type=int, default=2, help="named workload 1..5 (default: dense-4096)")
+    p.add_argument("--workload", type=int, default=5, help="named workload 1..5 (default: mlp-down-5120x17408)")
+    p.add_argument("--extras-workload", type=int, default=2,
+                   help="named workload of the adjacent parts (rules, ragged, diagnostics, GPTQ)")
+    p.add_argument("--cold", default="2,3,4,5", help="named workloads whose Hessian is timed cache-cold")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true",
-                   help="skip the cold-cache Hessian timing and the scale-rule variants")
+                   help="skip the cold-cache Hessian timings and the adjacent parts")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 256 MiB device copy 5 times (HBM counter calibration)")
     return p.parse_args()
@@ -80,32 +92,54 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel: str, workload: str, src_hash: str):
-    """HBM bytes per launch from committed rocprofv3 counter summaries
-    (FETCH_SIZE + WRITE_SIZE, copy-kernel calibrated); None when absent or
-    taken on other kernel sources."""
-    path = os.path.join(PROFILES, "traffic.json")
-    if not os.path.exists(path):
+def profile_entry(kernel: str, workload: str, src_hash: str):
+    """The committed rocprofv3 counter summary of one kernel on one workload
+    (profiles/counters.json), or None when absent or taken on other kernel
+    sources."""
+    if not os.path.exists(COUNTERS):
         return None
-    with open(path) as f:
+    with open(COUNTERS) as f:
         data = json.load(f)
-    ent = data.get("%s/%s" % (kernel, workload))
+    ent = data.get("kernels", {}).get("%s/%s" % (kernel, workload))
     if not ent or ent.get("source_hash") != src_hash:
         return None
-    return ent.get("bytes_per_launch")
+    return ent
 
 
-def valu_from_profiles(workload: str, src_hash: str):
-    """The sweep kernel's executed VALU issue fraction from the committed
-    rocprofv3 counter summary (SQ_INSTS_VALU), if taken on these sources."""
-    path = os.path.join(PROFILES, "traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        data = json.load(f)
-    if data.get("sweep/%s" % workload, {}).get("source_hash") != src_hash:
-        return None
-    return data.get("valu", {}).get(workload)
+def sweep_roofline(ent, live_ms: float, blocks: int) -> dict:
+    """Roofline of the sweep kernel, bound by VALU issue.
+
+    From one dispatch's counters (deterministic instruction counts; the
+    issue counters of the same dispatch): busy = SQ_ACTIVE_INST_VALU -
+    SQ_ACTIVE_INST_VALU2, the SIMD quad-cycles in which the VALU issued at
+    least one wave64 instruction (gfx950 can issue two VALU instructions in
+    one quad-cycle; ACTIVE_INST_VALU counts both, VALU2 counts such
+    quad-cycles once).  achieved = busy quad-cycles per launch / the live
+    HIP-event launch time; peak = 1024 SIMDs x 2.4 GHz / 4; frac = their
+    ratio.  frac_dispatch uses the dispatch's own cycle count
+    (GRBM_GUI_ACTIVE / 8 XCDs) instead of the published clock."""
+    if ent is None or "valu" not in ent:
+        return {"bound": "alu", "achieved": None, "peak": VALU_QUAD_PEAK_G, "unit": "Gquad/s", "frac": None,
+                "traffic": None, "note": "no counter summary for these kernel sources"}
+    v = ent["valu"]
+    busy = v["SQ_ACTIVE_INST_VALU"] - v["SQ_ACTIVE_INST_VALU2"]
+    cycles = v["GRBM_GUI_ACTIVE"] / N_XCD
+    achieved = busy / (live_ms / 1e3) / 1e9
+    out = {"bound": "alu", "achieved": achieved, "peak": VALU_QUAD_PEAK_G, "unit": "Gquad/s",
+           "frac": achieved / VALU_QUAD_PEAK_G,
+           "traffic": ent.get("bytes_per_launch"),
+           "frac_dispatch": busy / (N_SIMD * cycles / 4),
+           "dispatch_clock_ghz": cycles / v["dispatch_ns"],
+           "valu_instr_per_block": v["SQ_INSTS_VALU"] * 64 / blocks,
+           "instr_per_busy_quad": v["SQ_INSTS_VALU"] / busy,
+           "lanes_active": v["SQ_THREAD_CYCLES_VALU"] / (64.0 * v["SQ_ACTIVE_INST_VALU"]),
+           "source": "rocprofv3 --pmc, one dispatch (profiles/counters.json, hash %s)" % ent["source_hash"]}
+    ops = ent.get("ops")
+    if ops:
+        flop = 64.0 * (2 * ops["SQ_INSTS_VALU_FMA_F32"] + ops["SQ_INSTS_VALU_MUL_F32"] + ops["SQ_INSTS_VALU_ADD_F32"])
+        out["fp32_executed_tflops"] = flop / (live_ms / 1e3) / 1e12
+        out["fp32_executed_frac_78_6"] = out["fp32_executed_tflops"] / FP32_NONPACKED_TFLOPS
+    return out
 
 
 def copy_gbps(device) -> float:
@@ -174,16 +208,63 @@ def pct(v, q):
     return float(np.percentile(np.asarray(v), q))
 
 
-def extras(lh, work, w, x, h, amax, idx, err, bam, ws, ws_bytes, stream) -> dict:
-    """Outside the timed steps: (1) the Hessian pass with the last-level
-    cache flushed before every rep (a 512 MiB scratch write), median and
-    p10/p90; (2) every scale rule of lh_select_scales on the same layer,
-    with the local Hessian and with the plain weight error."""
+def read_flush(device):
+    """A 1 GiB buffer whose read (a sum) evicts the 256 MB last-level cache
+    and the L2s before a cold rep; reading leaves no dirty lines whose
+    write-back could overlap the timed launch."""
     import torch
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=w.device)
-    cold = timed(lambda: lh.lh_accumulate_hessian(x, h=h, workspace=ws if ws_bytes else None), stream, 15,
-                 before=lambda: scratch.fill_(1))
-    del scratch
+    buf = torch.ones(1 << 28, dtype=torch.float32, device=device)
+    out = torch.empty((), dtype=torch.float32, device=device)
+    return lambda: torch.sum(buf, dim=0, out=out)   # fp32 in, fp32 out: a pure read of 1 GiB
+
+
+def cold_prologue_and_hessian(lh, work, stream, reps: int = 9, w=None, x=None) -> dict:
+    """The Hessian pass (lh_accumulate_hessian with its split-token
+    workspace) and the step's prologue (lh_calibrate_prologue: amax, H and
+    the skip certificates) timed with HIP events right after a read flush of
+    the last-level cache; median and p10/p90 over `reps`.  GB/s counts the
+    algorithmic bytes: X read once (Hessian), W + X (prologue)."""
+    import torch
+    dev = torch.device("cuda:0")
+    G, c_out, c_in, n = work.n_groups, work.c_out, work.c_in, work.n_tok
+    nb = c_in // 16
+    w = work.w.to(dev) if w is None else w
+    x = work.x.to(dev) if x is None else x
+    h = torch.empty((G, nb, 16, 16), dtype=torch.float32, device=dev)
+    amax = torch.empty(G, dtype=torch.float32, device=dev)
+    ws_bytes = lh.lh_hessian_workspace_bytes(c_in, n, G)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    cws = torch.empty(lh.lh_calibrate_workspace_bytes(c_out, c_in, n, G), dtype=torch.uint8, device=dev)
+    flush = read_flush(dev)
+    hess = timed(lambda: lh.lh_accumulate_hessian(x, h=h, workspace=ws if ws_bytes else None), stream, reps,
+                 before=flush)
+    pro = timed(lambda: lh.lh_calibrate_prologue(w, x, amax, h, cws), stream, reps, before=flush)
+    xb = work.x_bytes
+    wb = work.w.numel() * work.w.element_size()
+    med_h, med_p = pct(hess, 50), pct(pro, 50)
+    return {"workload": work.name, "x_bytes": xb, "w_bytes": wb,
+            "hessian_ms": med_h, "hessian_p10_ms": pct(hess, 10), "hessian_p90_ms": pct(hess, 90),
+            "hessian_gbps": xb / (med_h / 1e3) / 1e9, "hessian_frac_hbm": xb / (med_h / 1e3) / 1e9 / HBM_PEAK_GBPS,
+            "prologue_ms": med_p, "prologue_p10_ms": pct(pro, 10), "prologue_p90_ms": pct(pro, 90),
+            "prologue_gbps": (xb + wb) / (med_p / 1e3) / 1e9,
+            "prologue_frac_hbm": (xb + wb) / (med_p / 1e3) / 1e9 / HBM_PEAK_GBPS}
+
+
+def extras(lh, work, stream) -> dict:
+    """Outside the timed steps, on workload `work` (a layer resident in
+    HBM): every scale rule of lh_select_scales with the local Hessian and
+    with the plain weight error (N2); the ragged MoE capture with a running
+    mean (N1); the approximation diagnostics and GPTQ (N3, N4)."""
+    import torch
+    dev = torch.device("cuda:0")
+    G, c_out, c_in, n = work.n_groups, work.c_out, work.c_in, work.n_tok
+    nb = c_in // 16
+    w, x = work.w.to(dev), work.x.to(dev)
+    amax = lh.lh_absmax(w)
+    h = lh.lh_accumulate_hessian(x)
+    idx = torch.empty((G, c_out, nb), dtype=torch.uint8, device=dev)
+    err = torch.empty((G, c_out, nb), dtype=torch.float32, device=dev)
+    bam = torch.empty((G, c_out, nb), dtype=torch.float32, device=dev)
     blocks = work.n_blocks
     rules = {}
     names = {0: "sweep126", 1: "max", 2: "four_over_six", 3: "amax_search"}
@@ -200,27 +281,22 @@ def extras(lh, work, w, x, h, amax, idx, err, bam, ws, ws_bytes, stream) -> dict
     # ragged / streaming Hessian on the MoE layer's capture (skewed routing)
     import lh_workloads as wl
     cap = wl.make_ragged_moe()
-    xr = cap.x.to(w.device)
-    off = torch.from_numpy(cap.offsets).to(w.device)
-    hr = torch.zeros((cap.n_groups, cap.c_in // 16, 16, 16), dtype=torch.float32, device=w.device)
-    cnt = torch.zeros(cap.n_groups, dtype=torch.int64, device=w.device)
+    xr = cap.x.to(dev)
+    off = torch.from_numpy(cap.offsets).to(dev)
+    hr = torch.zeros((cap.n_groups, cap.c_in // 16, 16, 16), dtype=torch.float32, device=dev)
+    cnt = torch.zeros(cap.n_groups, dtype=torch.int64, device=dev)
     largest = int((cap.offsets[1:] - cap.offsets[:-1]).max())   # known where the tokens were routed
     rb = lh.lh_hessian_ragged_workspace_bytes(cap.c_in, xr.shape[0], cap.n_groups, largest)
-    rws = torch.empty(max(rb, 1), dtype=torch.uint8, device=w.device)
+    rws = torch.empty(max(rb, 1), dtype=torch.uint8, device=dev)
     fn = (lambda: lh.lh_accumulate_hessian_ragged(xr, off, h=hr, counts=cnt, workspace=rws if rb else None,
                                                   max_group_rows=largest))
     fn()
     warm = timed(fn, stream, 15)
     launch_ms = graph_time(fn)
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=w.device)
-    rcold = timed(fn, stream, 15, before=lambda: scratch.fill_(1))
-    del scratch
+    rcold = timed(fn, stream, 15, before=read_flush(dev))
     counts = cap.offsets[1:] - cap.offsets[:-1]
     diag = diagnostics(lh, work, w, x, h, amax, idx, err, bam)
-    xb = work.x_bytes
-    return {"hessian_cold": {"median_ms": pct(cold, 50), "p10_ms": pct(cold, 10), "p90_ms": pct(cold, 90),
-                             "gbps_median": xb / (pct(cold, 50) / 1e3) / 1e9,
-                             "flush": "512 MiB device write before every rep"},
+    return {"workload": work.name,
             "hessian_ragged": {"workload": cap.description, "x_bytes": cap.x_bytes,
                                "max_group_rows": int(counts.max()), "empty_groups": int((counts == 0).sum()),
                                "running_mean": True,
@@ -228,7 +304,8 @@ def extras(lh, work, w, x, h, amax, idx, err, bam, ws, ws_bytes, stream) -> dict
                                "warm_median_ms": pct(warm, 50), "warm_gbps": cap.x_bytes / (pct(warm, 50) / 1e3) / 1e9,
                                "cold_median_ms": pct(rcold, 50), "cold_p10_ms": pct(rcold, 10),
                                "cold_p90_ms": pct(rcold, 90),
-                               "cold_gbps": cap.x_bytes / (pct(rcold, 50) / 1e3) / 1e9},
+                               "cold_gbps": cap.x_bytes / (pct(rcold, 50) / 1e3) / 1e9,
+                               "flush": "1 GiB device read before every cold rep"},
             "scale_rules": rules,
             "diagnostics": diag}
 
@@ -424,17 +501,18 @@ def main():
                                                                 scale_e4m3=codes, global_scale=gscale)),
     }
     ms_per_step = wall * 1e3 / args.steps
-    sweep_s = per_kernel_ms["calibrate_sweep"] / 1e3
-    hess_gbps = work.x_bytes / (launch_ms["hessian"] / 1e3) / 1e9
+    sweep_ms = per_kernel_ms["calibrate_sweep"]
     w_bytes = work.w.numel() * work.w.element_size()
-    pro_gbps = (work.x_bytes + w_bytes) / (launch_ms["calibrate_prologue"] / 1e3) / 1e9
-    achieved_tflops = SWEEP_FLOP_PER_BLOCK * blocks / sweep_s / 1e12
     src_hash = kernel_source_hash()
-    traffic = traffic_from_profiles("sweep", wl.SHORT_NAMES[args.workload], src_hash)
-    valu = valu_from_profiles(wl.SHORT_NAMES[args.workload], src_hash)
+    name = wl.SHORT_NAMES[args.workload]
+    sweep_ent = profile_entry("sweep", name, src_hash)
+    pro_ent = profile_entry("prologue", name, src_hash)
     copy_bw = copy_gbps(dev)
+    # the headline Hessian figure: this layer, after a read flush of the last-level cache
+    cold = cold_prologue_and_hessian(lh, work, stream, w=w, x=x)
     # fake-quant: W + indices read, Q + nibbles + codes written (algorithmic bytes)
-    fq_bytes = work.w.numel() * work.w.element_size() + blocks + blocks * 16 * 4 + blocks * 8 + blocks
+    fq_bytes = w_bytes + blocks + blocks * 16 * 4 + blocks * 8 + blocks
+    dense_tflops = SWEEP_FLOP_PER_BLOCK * blocks / (sweep_ms / 1e3) / 1e12
     out = {
         "metric": METRIC,
         "value": blocks / (ms_per_step / 1e3),
@@ -448,26 +526,42 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": work.description, "name": wl.SHORT_NAMES[args.workload], "n_groups": G,
+        "config": {"workload": work.description, "name": name, "n_groups": G,
                    "c_out": c_out, "c_in": c_in, "n_tokens": n, "blocks": blocks, "storage": work.dtype},
-        "roofline": {"bound": "alu", "achieved": achieved_tflops, "peak": FP32_VECTOR_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": traffic},
+        "roofline": sweep_roofline(sweep_ent, sweep_ms, blocks),
         "kernels_ms": per_kernel_ms,
         "launch_ms": launch_ms,
-        "sweep": {"blocks_per_s": blocks / sweep_s, "tflops": achieved_tflops,
-                  "frac_nonpacked_fp32": achieved_tflops / FP32_NONPACKED_TFLOPS,
-                  "valu_issue_frac": None if valu is None else valu["issue_frac"],
-                  "valu_instr_per_block": None if valu is None else valu["valu_instr_per_block"]},
+        "sweep": {"blocks_per_s": blocks / (sweep_ms / 1e3),
+                  "dense_equivalent_tflops": dense_tflops,
+                  "dense_equivalent_note": "68,544 flop per block (every candidate's dense dw^T H dw); the kernel "
+                                           "skips candidates it proves cannot win, so this is not executed work"},
         "fake_quant": {"gbps": fq_bytes / (launch_ms["fake_quant"] / 1e3) / 1e9, "bytes": fq_bytes},
         "copy_gbps": copy_bw,
-        "hessian": {"gbps": hess_gbps, "frac_hbm": hess_gbps / HBM_PEAK_GBPS, "frac_copy": hess_gbps / copy_bw,
-                    "x_bytes": work.x_bytes, "warm": True},
-        "prologue": {"gbps": pro_gbps, "frac_hbm": pro_gbps / HBM_PEAK_GBPS, "bytes": work.x_bytes + w_bytes,
-                     "traffic": traffic_from_profiles("prologue", wl.SHORT_NAMES[args.workload], src_hash)},
+        "hessian": {"gbps": cold["hessian_gbps"], "frac_hbm": cold["hessian_frac_hbm"],
+                    "frac_copy": cold["hessian_gbps"] / copy_bw, "median_ms": cold["hessian_ms"],
+                    "p10_ms": cold["hessian_p10_ms"], "p90_ms": cold["hessian_p90_ms"], "x_bytes": work.x_bytes,
+                    "cold": "1 GiB device read before every rep (last-level cache flushed, nothing dirty)",
+                    "warm_graph_gbps": work.x_bytes / (launch_ms["hessian"] / 1e3) / 1e9,
+                    "traffic": None if profile_entry("hessian", name, src_hash) is None
+                    else profile_entry("hessian", name, src_hash).get("bytes_per_launch")},
+        "prologue": {"gbps": cold["prologue_gbps"], "frac_hbm": cold["prologue_frac_hbm"],
+                     "median_ms": cold["prologue_ms"], "bytes": work.x_bytes + w_bytes, "cold": True,
+                     "traffic": None if pro_ent is None else pro_ent.get("bytes_per_launch")},
         "source_hash": src_hash,
     }
     if not args.no_extras:
-        out["extras"] = extras(lh, work, w, x, h, amax, idx, err, bam, ws, ws_bytes, stream)
+        per = {}
+        for k in [int(v) for v in args.cold.split(",") if v.strip()]:
+            if k == args.workload:
+                per[wl.SHORT_NAMES[k]] = cold
+            else:
+                other = wl.make(k)
+                per[wl.SHORT_NAMES[k]] = cold_prologue_and_hessian(lh, other, stream)
+                del other
+                torch.cuda.empty_cache()
+        out["hessian_cold"] = per
+        ework = work if args.extras_workload == args.workload else wl.make(args.extras_workload)
+        out["extras"] = extras(lh, ework, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(work, args.cpu_seconds)
     print(json.dumps(out), flush=True)
