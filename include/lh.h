@@ -348,6 +348,30 @@ lh_status lh_calibrate_nvfp4(const void *w, int w_dtype, int64_t c_out, int64_t 
                              size_t workspace_bytes, void *stream);
 
 /*
+ * lh_calibrate_nvfp4 for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments without the workspace, the same outputs
+ * bit for bit.  Its scratch is a device array inside the library, 32 MiB on
+ * each GPU the library runs on, held until the process ends; the call
+ * allocates nothing.  Layers whose lh_calibrate_workspace_bytes(c_out, c_in,
+ * n_tokens, n_groups) exceeds 32 MiB are rejected with LH_ERR_WORKSPACE
+ * before anything is enqueued (mlp-down 5120 x 17408 with 16384 tokens needs
+ * 17 MiB).  The stream must belong to the current device.  Every call on a
+ * GPU uses that GPU's one array: calls that overlap on one GPU (other
+ * streams, other host threads) race and must be ordered by the caller.  No
+ * part of the array needs to start at zero: each call writes the scratch it
+ * reads before reading it.
+ * Errors: as lh_calibrate_nvfp4 (LH_ERR_WORKSPACE: layer too large for the
+ * array; LH_ERR_ARG: stream of another device).
+ */
+lh_status lh_calibrate_nvfp4_noalloc(const void *w, int w_dtype, int64_t c_out, int64_t c_in, int64_t ld_w,
+                                     int64_t n_groups, int64_t group_stride_w, const void *x, int x_dtype,
+                                     int x_layout, int64_t n_tokens, int64_t ld_x, int64_t group_stride_x,
+                                     float *amax, float *h, int64_t group_stride_h, uint8_t *best_idx,
+                                     float *best_err, float *best_amax, float *w_q, uint8_t *packed_e2m1,
+                                     uint8_t *scale_e4m3, float *global_scale, void *stream);
+
+/*
  * Block-scale selection by rule: the scale rules the Local-Hessian guide
  * compares against ("What is Local-Hessian": max scaling takes the block
  * scale from the block's largest |w|; Four-Over-Six picks one of two

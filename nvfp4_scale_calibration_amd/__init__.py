@@ -72,6 +72,9 @@ def _load() -> ctypes.CDLL:
     lib.lh_calibrate_nvfp4.argtypes = [P, I, I64, I64, I64, I64, I64, P, I, I, I64, I64, I64, P, P, I64, P, P, P, P, P,
                                        P, P, P, SZ, P]
     lib.lh_calibrate_nvfp4.restype = I
+    lib.lh_calibrate_nvfp4_noalloc.argtypes = [P, I, I64, I64, I64, I64, I64, P, I, I, I64, I64, I64, P, P, I64, P, P,
+                                               P, P, P, P, P, P]
+    lib.lh_calibrate_nvfp4_noalloc.restype = I
     lib.lh_calibrate_prologue.argtypes = [P, I, I64, I64, I64, I64, I64, P, I, I, I64, I64, I64, P, P, I64, P, SZ, P]
     lib.lh_calibrate_prologue.restype = I
     lib.lh_calibrate_sweep.argtypes = [P, I, I64, I64, I64, I64, I64, P, I64, P, P, P, P, P, P, P, P, P, SZ, P]
@@ -100,7 +103,7 @@ EXPORTS = ("lh_abi_version", "lh_status_string", "lh_last_error_message", "lh_ab
            "lh_hessian_workspace_bytes", "lh_accumulate_hessian", "lh_hessian_ragged_workspace_bytes",
            "lh_accumulate_hessian_ragged", "lh_sweep_workspace_bytes", "lh_scale_sweep",
            "lh_scale_sweep_fake_quant", "lh_calibrate_workspace_bytes", "lh_calibrate_nvfp4",
-           "lh_calibrate_prologue", "lh_calibrate_sweep", "lh_select_scales", "lh_fake_quant_nvfp4", "lh_full_hessian", "lh_output_error_workspace_bytes",
+           "lh_calibrate_prologue", "lh_calibrate_sweep", "lh_calibrate_nvfp4_noalloc", "lh_select_scales", "lh_fake_quant_nvfp4", "lh_full_hessian", "lh_output_error_workspace_bytes",
            "lh_output_error", "lh_scaled_histogram", "lh_gptq_workspace_bytes", "lh_gptq_prepare",
            "lh_gptq_quantize")
 
@@ -421,6 +424,30 @@ def lh_calibrate_nvfp4(w: torch.Tensor, x: torch.Tensor, layout: str = "channel"
         _check(lib.lh_calibrate_nvfp4(*wargs, _ptr(x3), _dtype(x3), lay, n_tok, ld_x, _group_stride(x3),
                                       _ptr(res["amax"]), _ptr(h), h_gstride, _ptr(res["idx"]), _ptr(res["err"]),
                                       _ptr(res["amax_blk"]), *fq, _ptr(workspace), wsb, _stream(w)))
+    return {k: v for k, v in res.items() if v is not None}
+
+
+def lh_calibrate_nvfp4_noalloc(w: torch.Tensor, x: torch.Tensor, layout: str = "channel", out: dict | None = None,
+                               best_err: bool = True, best_amax: bool = True, w_q: bool = True, packed: bool = False,
+                               scale_e4m3: bool = False, global_scale: bool = False) -> dict:
+    """lh_calibrate_nvfp4 through the entry point that takes no workspace
+    (its scratch is a fixed device array in the library, 32 MiB per GPU).
+    Outputs given in `out` are written in place; missing ones are created
+    here (the C call itself allocates nothing)."""
+    _require_device(w, x)
+    w3, x3 = _as3(w), _as3(x)
+    if w3.stride(-1) != 1:
+        raise ValueError("last dim of w must be contiguous")
+    g, c_out, c_in = w3.shape
+    res, lay, n_tok, ld_x = _calibrate_outputs(w3, x3, layout, out, best_err, best_amax, w_q, packed, scale_e4m3,
+                                               global_scale)
+    h = res["h"]
+    h_gstride = h.stride(0) if h.dim() == 4 and h.shape[0] > 1 else 0
+    _check(lib.lh_calibrate_nvfp4_noalloc(_ptr(w3), _dtype(w3), c_out, c_in, _ld(w3), g, _group_stride(w3), _ptr(x3),
+                                          _dtype(x3), lay, n_tok, ld_x, _group_stride(x3), _ptr(res["amax"]), _ptr(h),
+                                          h_gstride, _ptr(res["idx"]), _ptr(res["err"]), _ptr(res["amax_blk"]),
+                                          _ptr(res["w_q"]), _ptr(res["packed"]), _ptr(res["scale_e4m3"]),
+                                          _ptr(res["global_scale"]), _stream(w)))
     return {k: v for k, v in res.items() if v is not None}
 
 

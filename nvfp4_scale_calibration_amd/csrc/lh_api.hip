@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "lh.h"
 #include "lh_internal.h"
 #include <math.h>
@@ -546,3 +548,75 @@ lh_status lh_gptq_quantize(const void* w, int w_dtype, int64_t c_out, int64_t c_
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The whole path for callers that cannot allocate (code under graph capture,
+// tight serving loops, harnesses that forbid allocation).  The scratch that
+// lh_calibrate_nvfp4 takes as its workspace (skip certificates, the
+// Hessian's token-slice partial sums, the amax shares) lives in the
+// file-scope device array `scratch` instead: each GPU the library runs on
+// holds its own copy, kNoAllocScratchBytes, until the process ends.  In host
+// code the array's name is only a stand-in, never a device address: the
+// address on a device comes from hipGetSymbolAddress, looked up once per
+// device (the first call with that device current) and kept.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+constexpr int kNoAllocMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kNoAllocMaxDevices];
+
+// The address of this device's `scratch`, for the current device, which must
+// also be the stream's.
+lh_status noalloc_scratch(const char* fn, void* stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  if (dev < 0 || dev >= kNoAllocMaxDevices) return fail(LH_ERR_ARG, "%s: device index out of range", fn);
+  hipDevice_t sdev = -1;
+  e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  if (sdev != dev) return fail(LH_ERR_ARG, "%s: the stream belongs to another device than the current one", fn);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LH_OK;
+}
+
+}  // namespace
+
+extern "C" lh_status lh_calibrate_nvfp4_noalloc(const void* w, int w_dtype, int64_t c_out, int64_t c_in,
+                                                int64_t ld_w, int64_t n_groups, int64_t group_stride_w,
+                                                const void* x, int x_dtype, int x_layout, int64_t n_tokens,
+                                                int64_t ld_x, int64_t group_stride_x, float* amax, float* h,
+                                                int64_t group_stride_h, uint8_t* best_idx, float* best_err,
+                                                float* best_amax, float* w_q, uint8_t* packed_e2m1,
+                                                uint8_t* scale_e4m3, float* global_scale, void* stream) {
+  const char* fn = "lh_calibrate_nvfp4_noalloc";
+  g_msg[0] = '\0';
+  if (c_out > 0 && c_in > 0 && n_groups > 0 && n_tokens >= 0 && c_in % 16 == 0) {
+    const size_t need = calibrate_ws_bytes(c_out, c_in, n_tokens, n_groups);
+    if (need > kNoAllocScratchBytes) {
+      snprintf(g_msg, sizeof g_msg,
+               "%s: this layer needs %zu bytes of scratch, more than the %zu bytes the entry point holds on each "
+               "device; call lh_calibrate_nvfp4 with a workspace instead",
+               fn, need, kNoAllocScratchBytes);
+      return LH_ERR_WORKSPACE;
+    }
+  }
+  void* ws = nullptr;
+  const lh_status st = noalloc_scratch(fn, stream, &ws);
+  if (st != LH_OK) return st;
+  return lh_calibrate_nvfp4(w, w_dtype, c_out, c_in, ld_w, n_groups, group_stride_w, x, x_dtype, x_layout, n_tokens,
+                            ld_x, group_stride_x, amax, h, group_stride_h, best_idx, best_err, best_amax, w_q,
+                            packed_e2m1, scale_e4m3, global_scale, ws, kNoAllocScratchBytes, stream);
+}

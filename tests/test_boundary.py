@@ -315,3 +315,20 @@ def test_hessian_alpha_sentinel(lib):
     # validation still runs before anything else with the sentinel
     st = lib.lh_accumulate_hessian(None, 1, 0, 32, 10, 10, 1, 0, float("nan"), 0.0, None, 0, None, 0, None)
     assert st == NULL
+
+
+def test_noalloc_calibrate_refuses_layers_beyond_its_array(lib):
+    """lh_calibrate_nvfp4_noalloc holds 32 MiB of scratch per device; a layer
+    that needs more is refused with LH_ERR_WORKSPACE and a message naming
+    both sizes, before any HIP call (so this runs without a GPU)."""
+    import nvfp4_scale_calibration_amd as m
+    c_out, c_in, n_tok, g = 5120, 17408, 16384, 4
+    need = m.lh_calibrate_workspace_bytes(c_out, c_in, n_tok, g)
+    assert need > 32 << 20
+    P = ctypes.c_void_p
+    st = lib.lh_calibrate_nvfp4_noalloc(P(FAKE), 1, c_out, c_in, c_in, g, c_out * c_in, P(FAKE), 1, 0, n_tok, n_tok,
+                                        c_in * n_tok, P(FAKE), P(FAKE), c_in * 16, P(FAKE), None, None, None, None,
+                                        None, None, None)
+    assert st == WORKSPACE
+    msg = _msg(lib)
+    assert "lh_calibrate_nvfp4_noalloc" in msg and str(need) in msg and str(32 << 20) in msg, msg
