@@ -305,6 +305,50 @@ __device__ __forceinline__ int class_code(int m, int j) {
 // tests run from the highest power down and stop where the saturation
 // argument below rules out all the lower ones at once, so the masks are
 // those of testing every power.
+// Powers of two of mantissa class m that are E4M3 candidates (codes 1..126;
+// 0x7F is NaN): j in [jmin, jmax].
+template <int m>
+struct ClassRange {
+  static constexpr int jmin = (m == 0) ? -9 : (m == 4) ? -8 : (m == 2 || m == 6) ? -7 : -6;
+  static constexpr int jmax = (m == 7) ? 7 : 8;
+};
+
+// Level-1 tests of class m (quotients t.p of the bound elements already
+// formed) against the lane's incumbent: returns the mask of the powers
+// (bit c = power jmin + c) this lane cannot rule out.  The tests run from the
+// highest power down and stop where the saturation argument below rules out
+// all the lower ones at once, so the mask is that of testing every power.
+template <int m>
+__device__ __forceinline__ uint32_t level1_scan(const Best& best, SkipSet& t, float sigma) {
+  constexpr int jmin = ClassRange<m>::jmin, jmax = ClassRange<m>::jmax;
+  uint32_t need = 0;
+  // Powers from the top down.  Below js2 the two leading bound elements
+  // both saturate (|p| >= 6 * 2^j: E2M1 gives 6, Q = 6 * 2^j * sigma), so
+  // their |dw| only grows as j falls and so does the two-element bound
+  // (rounded products and sums of non-negative terms are monotone): once
+  // every lane of the wave is at or below its js2 and the two-element
+  // bound rules the candidate out on every lane, it rules out every lower
+  // power too, and the scan stops.
+  const uint32_t a0 = __float_as_uint(t.p[0]) & 0x7FFFFFFFu, a1 = __float_as_uint(t.p[1]) & 0x7FFFFFFFu;
+  const uint32_t amin2 = min(a0, a1);  // a NaN (above every finite value) only counts when both are
+  const int js2 = (int)(amin2 >> 23) - 130 + (int)((amin2 & 0x7FFFFFu) >= 0x400000u);
+#pragma unroll
+  for (int c = jmax - jmin; c >= 0; --c) {
+    const int j = jmin + c;
+    uint64_t live2;
+    if (needs_eval(t, best, j, sigma, live2)) need |= 1u << c;
+    if ((__builtin_amdgcn_ballot_w64(j > js2) | live2) == 0) break;
+  }
+  return need;
+}
+
+// All candidates of mantissa class m (mu = 1 + m/8) for the lanes-on-blocks
+// sweep: first the level-1 scan gives each lane a mask of the candidates it
+// cannot rule out; then each lane evaluates its own candidates in increasing
+// index while any lane of the wave has one left.  A wave therefore costs the
+// largest per-lane count rather than the union over its lanes, and every
+// candidate a lane skips is still certified worse than that lane's
+// incumbent.
 template <int m, bool kMse>
 __device__ __forceinline__ void sweep_mantissa(Best& best, SkipSet& t, float Sg, const float (&w)[16],
                                                const float (&diag)[16], const float (&sym)[120],
@@ -316,31 +360,10 @@ __device__ __forceinline__ void sweep_mantissa(Best& best, SkipSet& t, float Sg,
   for (int i = 0; i < 16; ++i) p[i] = div_rn(w[i], sigma, rs);  // = fl32(w / sigma)
 #pragma unroll
   for (int e = 0; e < 4; ++e) t.p[e] = div_rn(t.w[e], sigma, rs);  // same operation on the same bits as p[idx]
-  constexpr int jmin = (m == 0) ? -9 : (m == 4) ? -8 : (m == 2 || m == 6) ? -7 : -6;
-  constexpr int jmax = (m == 7) ? 7 : 8;
-  uint32_t need = 0;
-  {
-    // Powers from the top down.  Below js2 the two leading bound elements
-    // both saturate (|p| >= 6 * 2^j: E2M1 gives 6, Q = 6 * 2^j * sigma), so
-    // their |dw| only grows as j falls and so does the two-element bound
-    // (rounded products and sums of non-negative terms are monotone): once
-    // every lane of the wave is at or below its js2 and the two-element
-    // bound rules the candidate out on every lane, it rules out every lower
-    // power too, and the scan stops.
-    const uint32_t a0 = __float_as_uint(t.p[0]) & 0x7FFFFFFFu, a1 = __float_as_uint(t.p[1]) & 0x7FFFFFFFu;
-    const uint32_t amin2 = min(a0, a1);  // a NaN (above every finite value) only counts when both are
-    const int js2 = (int)(amin2 >> 23) - 130 + (int)((amin2 & 0x7FFFFFu) >= 0x400000u);
-#pragma unroll
-    for (int c = jmax - jmin; c >= 0; --c) {
-      const int j = jmin + c;
-      uint64_t live2;
-      if (needs_eval(t, best, j, sigma, live2)) need |= 1u << c;
-      if ((__builtin_amdgcn_ballot_w64(j > js2) | live2) == 0) break;
-    }
-  }
+  uint32_t need = level1_scan<m>(best, t, sigma);
   while (wave_any(need != 0)) {
     const bool has = need != 0;
-    const int j = jmin + __builtin_ctz(need | 0x80000000u);  // a dummy power when !has
+    const int j = ClassRange<m>::jmin + __builtin_ctz(need | 0x80000000u);  // a dummy power when !has
     need &= need - 1;
     eval_scaled_skip<kMse>(best, t, has, class_code(m, j) - 1, j, sigma, p, w, diag, sym, pk);
   }
@@ -1075,8 +1098,403 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// ---------------------------------------------------------------------------
+// Pooled candidate rounds.  After a class's level-1 scan each lane holds the
+// mask of candidates its row still needs, and the counts differ a lot between
+// the rows of a wave (the busiest row needs about three times the mean).  So
+// rather than each lane working through its own list, the wave lists every
+// pending (row, power) item in LDS and evaluates them 64 at a time, each lane
+// on any row: the rows of a wave share H_b and the skip certificate, and
+// what else an item needs (the row's quotients for the class, its working
+// weights, sigma and incumbent) is in LDS.  Items are listed by rank (every
+// row's first pending power, then every row's second, ...), so a row's
+// candidates still go in increasing index and later ones see the errors
+// found before them.  Each row's best (error, index) is a 64-bit key in LDS
+// that orders by the error's value, then by the index, and is lowered with an
+// atomic min, so ties keep the lowest index.  Which candidates get evaluated
+// depends on the incumbents at the time, but a candidate is only skipped when
+// certified worse than an evaluated one, so the result is the exact minimum,
+// the same bits as evaluating every candidate.
+// ---------------------------------------------------------------------------
+constexpr int kRowStride = 20;                   // floats per row in LDS (16 + 4 spreads rows over the banks)
+constexpr int kMaxItems = kSweepThreads * 18;    // a class has at most 18 powers
+
+struct __align__(16) PoolLds {
+  float w[kSweepThreads * kRowStride];    // each lane's working weights
+  float p[kSweepThreads * kRowStride];    // each row's quotients fl32(w / sigma) for the current class
+  float sig[kSweepThreads];               // each row's sigma for the class (rows differ in working exponent)
+  unsigned long long key[kSweepThreads];  // each row's best, as best_key()
+  uint16_t items[kMaxItems];              // pending items: (row << 5) | power index
+};
+
+// An fp32 error's bits mapped to an unsigned order (negative values below
+// positive ones), above the candidate index.
+__device__ __forceinline__ unsigned long long best_key(float e, int k) {
+  const uint32_t u = __float_as_uint(e);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)o << 32) | (uint32_t)k;
+}
+
+__device__ __forceinline__ Best key_best(unsigned long long key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  return Best{__uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o), (int)(uint32_t)key};
+}
+
+__device__ __forceinline__ void store_row(float* dst, const float (&v)[16]) {
+  float4* d = reinterpret_cast<float4*>(dst);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) d[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+}
+
+__device__ __forceinline__ void load_row(const float* src, float (&v)[16]) {
+  const float4* s = reinterpret_cast<const float4*>(src);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 f = s[q];
+    v[4 * q] = f.x;
+    v[4 * q + 1] = f.y;
+    v[4 * q + 2] = f.z;
+    v[4 * q + 3] = f.w;
+  }
+}
+
+// The symmetrised strict upper triangle of H_b in LDS (shared by every lane
+// of the wave, read as broadcasts), in the order of tri(): 30 float4.
+// Same sum as quad_form_from, term for term: y_i starts at yd_i and takes
+// S_ij dw_j for j = i+1 .. 15 in order, then E = sum_i dw_i y_i in order of
+// i, so the result has the same bits.
+__device__ __forceinline__ float quad_form_lds(const float (&yd)[16], const float4* __restrict__ S,
+                                               const float (&dw)[16]) {
+  float y[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] = yd[i];
+#pragma unroll
+  for (int q = 0; q < 30; ++q) {
+    const float4 f = S[q];
+    const float v[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int k = 4 * q + c;
+      // (i, j) of packed index k, resolved at compile time
+      int i = 0;
+      while (tri(i, 15) < k) ++i;
+      const int j = k - tri(i, i + 1) + i + 1;
+      y[i] = __builtin_fmaf(v[c], dw[j], y[i]);
+    }
+  }
+  float e = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) e = __builtin_fmaf(dw[i], y[i], e);
+  return e;
+}
+
+// Class m of the lane's row (working weights w, bound set t, units Su; its
+// best in `best` and in L.key[tid] on entry and on return).  `live` is false
+// for lanes past the last row: they list nothing.
+template <int m>
+__device__ __forceinline__ void sweep_class_pooled(PoolLds& L, int tid, bool live, Best& best, SkipSet& t,
+                                                   float Su, const float (&w)[16], const float (&diag)[16],
+                                                   const float4* __restrict__ S) {
+  constexpr int jmin = ClassRange<m>::jmin;
+  const float sigma = (1.0f + 0.125f * (float)m) * Su;  // fl32(mu * S_g) in the row's units
+  const float rs = 1.0f / sigma;                        // IEEE division, once per class
+  {
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = div_rn(w[i], sigma, rs);  // = fl32(w / sigma)
+    store_row(&L.p[tid * kRowStride], p);
+  }
+  L.sig[tid] = sigma;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) t.p[e] = div_rn(t.w[e], sigma, rs);  // same operation on the same bits as p[idx]
+  uint32_t need = level1_scan<m>(best, t, sigma);
+  if (!live) need = 0;
+  // List the pending items by rank.
+  int total = 0;
+  for (uint32_t rem = need;;) {
+    const uint64_t mask = __builtin_amdgcn_ballot_w64(rem != 0);
+    if (mask == 0) break;
+    if (rem != 0) {
+      const int pos = total + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+      L.items[pos] = (uint16_t)((tid << 5) | __builtin_ctz(rem));
+      rem &= rem - 1;
+    }
+    total += (int)__builtin_popcountll(mask);
+  }
+  // Rounds of 64 items; lanes past the end redo the last item and change
+  // nothing.  Each round's row data is loaded during the round before (the
+  // registers of the quotients and weights are free once the residual is
+  // formed), so the LDS latency hides behind the quadratic form; the
+  // incumbent is read at the top of its own round, after every earlier
+  // round's atomic (a wave's LDS accesses complete in issue order).
+  if (total == 0) return;
+  wave_sync();  // the list and the rows are in place
+  const int last = total - 1;
+  uint32_t item = L.items[tid < total ? tid : last];
+  uint32_t next = L.items[kSweepThreads + tid < total ? kSweepThreads + tid : last];
+  float p[16], wo[16];
+  load_row(&L.p[(item >> 5) * kRowStride], p);
+  load_row(&L.w[(item >> 5) * kRowStride], wo);
+  float sg = L.sig[item >> 5];
+  for (int base = 0; base < total; base += kSweepThreads) {
+    const bool has = base + tid < total;
+    const int owner = (int)(item >> 5);
+    const int j = jmin + (int)(item & 31u);
+    // issued first: the incumbent (after every earlier round's atomic) and
+    // the item two rounds ahead
+    const unsigned long long okey = L.key[owner];
+    const int nn = base + 2 * kSweepThreads + tid;
+    const uint32_t after = L.items[nn < total ? nn : last];
+    __builtin_amdgcn_sched_barrier(0);
+    const float pow2j = __uint_as_float((uint32_t)(127 + j) << 23);
+    uint32_t pk[2] = {0u, 0u};  // every byte is written below
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 0], p[8 * h + 1], pow2j, 0);
+      pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 2], p[8 * h + 3], pow2j, 1);
+      pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 4], p[8 * h + 5], pow2j, 2);
+      pk[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[h], p[8 * h + 6], p[8 * h + 7], pow2j, 3);
+    }
+    float dw[16];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x2_t r0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], pow2j, 0);
+      const f32x2_t r1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], pow2j, 1);
+      const f32x2_t r2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], pow2j, 2);
+      const f32x2_t r3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[h], pow2j, 3);
+      const float r[8] = {r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dw[8 * h + i] = r[i] * sg - wo[8 * h + i];  // Q = fl32(r s), then Q - w
+    }
+    // the next round's rows, into the registers just freed
+    item = next;
+    next = after;
+    load_row(&L.p[(item >> 5) * kRowStride], p);
+    load_row(&L.w[(item >> 5) * kRowStride], wo);
+    sg = L.sig[item >> 5];
+    float yd[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) yd[i] = diag[i] * dw[i];
+    float d2 = yd[0] * dw[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) d2 = __builtin_fmaf(yd[i], dw[i], d2);
+    // level 2: the rest of the form only if some lane's item survives (a lane
+    // without an item compares against -inf and never asks for it)
+    const float thr = has ? key_best(okey).err * t.margin : -INFINITY;
+    if (!wave_any(!(t.gamma * d2 > thr))) continue;
+    const float e = quad_form_lds(yd, S, dw);
+    // only a key below the one read at the top can lower the row's minimum
+    const unsigned long long key = best_key(e, class_code(m, j) - 1);
+    if (!(t.gamma * d2 > thr) && !isnan(e) && key < okey) atomicMin(&L.key[owner], key);
+  }
+  wave_sync();
+  best = key_best(L.key[tid]);
+}
+
 template <typename T, bool kVec, bool kQuant, bool kAll>
-__global__ __launch_bounds__(kSweepThreads, 2) void sweep_rows_kernel(const T* __restrict__ wt, int64_t c_out,
+__global__ __launch_bounds__(kSweepThreads, 3) void sweep_rows_kernel(const T* __restrict__ wt, int64_t c_out,
+                                                              int64_t ld_w, int64_t gstride_w, int64_t nb,
+                                                              RowPlan rp, const float* __restrict__ h,
+                                                              int64_t gstride_h, const float* __restrict__ amax,
+                                                              uint8_t* __restrict__ idx_out,
+                                                              float* __restrict__ err_out,
+                                                              float* __restrict__ amax_out,
+                                                              const float* __restrict__ cert, QuantOut qo) {
+  const int tid = threadIdx.x;
+  // consecutive waves on consecutive chunks of one block (measured: ordering
+  // them by chunk instead, neighbouring blocks of the same rows next to
+  // each other, is 7% slower)
+  const int64_t gb = (int64_t)blockIdx.x / rp.cstep;
+  const int64_t c0 = (int64_t)blockIdx.x - gb * rp.cstep;
+  const int64_t grp = gb / nb;
+  const int64_t b = gb - grp * nb;
+  __shared__ PoolLds lds;  // rows, quotients, keys and items of the pooled rounds
+  __shared__ float lds_diag[16];
+  __shared__ float4 lds_sym[30];  // H_ij + H_ji, i < j, in the order of tri()
+  const float* const hb = h + grp * gstride_h + b * 256;
+  float diag[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) diag[i] = hb[17 * i];
+  if (tid < 16) lds_diag[tid] = hb[17 * tid];
+  for (int k = tid; k < 120; k += kSweepThreads) {
+    int i = 0;
+    while (tri(i, 15) < k) ++i;
+    const int j = k - tri(i, i + 1) + i + 1;
+    reinterpret_cast<float*>(lds_sym)[k] = hb[16 * i + j] + hb[16 * j + i];
+  }
+  wave_sync();
+  float gamma;
+  if (cert) {
+    gamma = cert[gb];
+  } else {
+    float sym[120];
+#pragma unroll
+    for (int k = 0; k < 120; ++k) sym[k] = reinterpret_cast<const float*>(lds_sym)[k];
+    gamma = gershgorin_gamma(diag, sym);
+  }
+  const float g = amax[grp];
+  const float Sg = g / kAmaxDivisor;
+  const bool fast = (Sg >= 0x1p-117f) && (Sg <= 0x1p127f);
+  const int e_g = (Sg > 0.0f && Sg <= 0x1p127f) ? ilogbf(Sg) : 0;
+  wave_sync();
+  const T* const wblk = wt + grp * gstride_w + 16 * b;
+  uint32_t raw[16];
+  load_raw<T, kVec>(wblk + (c0 * kSweepThreads + tid < c_out ? c0 * kSweepThreads + tid : c_out - 1) * ld_w, raw);
+  wait_raw(raw);
+  float w[16];
+  raw_to_float<T, kVec>(raw, w);
+  for (int64_t chunk = c0;;) {
+    const int64_t row = chunk * kSweepThreads + tid;
+    const bool valid = row < c_out;
+    const int64_t rr = valid ? row : c_out - 1;
+    const T* const wrow = wblk + rr * ld_w;
+    const int e = row_exponent(e_g, w);
+    const float Su = ldexpf(Sg, -e);
+    Best best{INFINITY, kCandidates};
+    uint32_t pk[2] = {0u, 0u};
+    if (fast) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w[i] = ldexpf(w[i], -e);
+      SkipSet t;
+      {
+        float kv[4] = {-1.0f, -1.0f, -1.0f, -1.0f};
+        int ki[4] = {0, 1, 2, 3};
+        wave_sync();  // the previous chunk's readers of the rows are done
+        store_row(&lds.w[tid * kRowStride], w);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float key = diag[i] * w[i] * w[i];
+          const bool q0 = key > kv[0], q1 = key > kv[1], q2 = key > kv[2], q3 = key > kv[3];
+          kv[3] = q2 ? kv[2] : (q3 ? key : kv[3]);
+          ki[3] = q2 ? ki[2] : (q3 ? i : ki[3]);
+          kv[2] = q1 ? kv[1] : (q2 ? key : kv[2]);
+          ki[2] = q1 ? ki[1] : (q2 ? i : ki[2]);
+          kv[1] = q0 ? kv[0] : (q1 ? key : kv[1]);
+          ki[1] = q0 ? ki[0] : (q1 ? i : ki[1]);
+          kv[0] = q0 ? key : kv[0];
+          ki[0] = q0 ? i : ki[0];
+        }
+        wave_sync();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          t.w[q] = lds.w[tid * kRowStride + ki[q]];
+          t.dg[q] = gamma * lds_diag[ki[q]];
+        }
+        t.pk = 0u;
+        t.gamma = gamma;
+        t.margin = gamma > 0.0f ? kSkipMargin : __int_as_float(0x7FC00000);
+      }
+      {
+        const int k0 = max_scaling_candidate(w, Su);
+        int m0, j0;
+        candidate_class(k0, m0, j0);
+        const float sigma0 = (1.0f + 0.125f * (float)m0) * Su;
+        const float rs0 = 1.0f / sigma0;
+        float p0[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p0[i] = div_rn(w[i], sigma0, rs0);
+        // the incumbent: the max-scaling candidate, with the arithmetic of the rounds
+        const float pow2j = __uint_as_float((uint32_t)(127 + j0) << 23);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          pk[hh] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[hh], p0[8 * hh + 0], p0[8 * hh + 1], pow2j, 0);
+          pk[hh] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[hh], p0[8 * hh + 2], p0[8 * hh + 3], pow2j, 1);
+          pk[hh] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[hh], p0[8 * hh + 4], p0[8 * hh + 5], pow2j, 2);
+          pk[hh] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[hh], p0[8 * hh + 6], p0[8 * hh + 7], pow2j, 3);
+        }
+        float dw0[16], yd0[16];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const f32x2_t r0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[hh], pow2j, 0);
+          const f32x2_t r1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[hh], pow2j, 1);
+          const f32x2_t r2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[hh], pow2j, 2);
+          const f32x2_t r3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[hh], pow2j, 3);
+          const float r[8] = {r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dw0[8 * hh + i] = r[i] * sigma0 - w[8 * hh + i];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) yd0[i] = diag[i] * dw0[i];
+        keep_best(best, quad_form_lds(yd0, lds_sym, dw0), k0);
+      }
+      lds.key[tid] = best_key(best.err, best.k);
+      sweep_class_pooled<0>(lds, tid, valid, best, t, Su, w, diag, lds_sym);
+      sweep_class_pooled<1>(lds, tid, valid, best, t, Su, w, diag, lds_sym);
+      sweep_class_pooled<2>(lds, tid, valid, best, t, Su, w, diag, lds_sym);
+      sweep_class_pooled<3>(lds, tid, valid, best, t, Su, w, diag, lds_sym);
+      sweep_class_pooled<4>(lds, tid, valid, best, t, Su, w, diag, lds_sym);
+      sweep_class_pooled<5>(lds, tid, valid, best, t, Su, w, diag, lds_sym);
+      sweep_class_pooled<6>(lds, tid, valid, best, t, Su, w, diag, lds_sym);
+      sweep_class_pooled<7>(lds, tid, valid, best, t, Su, w, diag, lds_sym);
+    } else {
+      // subnormal candidate scales: the definition, per candidate (see eval_direct)
+      for (int k = 0; k < kCandidates; ++k) {
+        const float sk = e4m3_candidate(k) * Sg;
+        float dw[16], yd[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float x = (sk == 0.0f) ? 0.0f : fabsf(w[i]) / sk;
+          const float q = copysignf(e2m1_round_mag(x) * sk, w[i]);
+          dw[i] = ldexpf(q - w[i], -e);
+          yd[i] = diag[i] * dw[i];
+        }
+        keep_best(best, quad_form_lds(yd, lds_sym, dw), k);
+      }
+    }
+    // Past the last chunk: stores for the valid lanes, done.  Otherwise the
+    // next chunk's weights are loaded before this chunk's stores and awaited
+    // after them (wait_raw): a wait for a load also waits for every store
+    // issued before it, and with the same stores on every path in between
+    // the compiler's wait leaves them in flight.  Only the last chunk of a
+    // block can hold lanes past the last row, so the stores of the other
+    // chunks are unconditional.
+    const int64_t next = chunk + rp.cstep;
+    const bool last = next >= rp.n_chunks;  // uniform over the wave
+    auto emit = [&]() {
+      const int k = best.k < kCandidates ? best.k : 0;  // NaN errors only
+      const int64_t o = (grp * c_out + rr) * nb + b;
+      idx_out[o] = (uint8_t)k;
+      if (kAll || err_out) err_out[o] = ldexpf(best.err, 2 * e);
+      if (kAll || amax_out) amax_out[o] = 6.0f * (e4m3_candidate(k) * Sg);
+      if constexpr (kQuant) {
+        const float s = e4m3_candidate(k) * Sg;
+        uint32_t qk[2];
+        if (fast && e == e_g) {
+          candidate_nibbles(k, Su, w, qk);
+        } else {
+          if (fast) reload_block(wrow, w);  // w was prescaled
+          nvfp4_cast_block(w, s, qk);
+        }
+        nvfp4_emit_at<kAll>(qk, s, k, o, qo.wq, qo.packed, qo.codes);
+      }
+    };
+    if (last) {
+      if (valid) emit();
+      break;
+    }
+    const int64_t nrow = next * kSweepThreads + tid;
+    load_raw<T, kVec>(wblk + (nrow < c_out ? nrow : c_out - 1) * ld_w, raw);
+    emit();
+    chunk = next;
+    wait_raw(raw);
+    raw_to_float<T, kVec>(raw, w);
+  }
+  if constexpr (kQuant) {
+    const int64_t gl = (int64_t)blockIdx.x * kSweepThreads + tid;
+    if (qo.gscale && gl < qo.n_groups) qo.gscale[gl] = amax[gl] / kAmaxDivisor;  // S_g, once per group
+  }
+}
+
+// The same sweep with each lane working through its own row's candidates
+// (sweep_mantissa) and H_b in registers, two waves per SIMD: for layers
+// whose waves walk several chunks of rows (fewer than 32 chunks per input
+// block), where the rows of a wave need similar numbers of candidates and
+// most evaluations run the full form, it measured faster than the pooled
+// rounds (which read H_b from LDS in every full form).  Same results, bit
+// for bit.
+template <typename T, bool kVec, bool kQuant, bool kAll>
+__global__ __launch_bounds__(kSweepThreads, 2) void sweep_rows_own_kernel(const T* __restrict__ wt, int64_t c_out,
                                                               int64_t ld_w, int64_t gstride_w, int64_t nb,
                                                               RowPlan rp, const float* __restrict__ h,
                                                               int64_t gstride_h, const float* __restrict__ amax,
@@ -1369,6 +1787,17 @@ RowPlan row_plan(int64_t c_out, int64_t per_k) {
   return rp;
 }
 
+template <typename T, bool kVec, bool kQuant, bool kAll>
+void launch_rows(bool pooled, dim3 grid, hipStream_t stream, const T* wp, const SweepArgs& a, int64_t nb,
+                 const RowPlan& rp, const float* cert, const QuantOut& qo) {
+  if (pooled)
+    sweep_rows_kernel<T, kVec, kQuant, kAll><<<grid, dim3(kSweepThreads), 0, stream>>>(
+        wp, a.c_out, a.ld_w, a.gstride_w, nb, rp, a.h, a.gstride_h, a.amax, a.idx, a.err, a.best_amax, cert, qo);
+  else
+    sweep_rows_own_kernel<T, kVec, kQuant, kAll><<<grid, dim3(kSweepThreads), 0, stream>>>(
+        wp, a.c_out, a.ld_w, a.gstride_w, nb, rp, a.h, a.gstride_h, a.amax, a.idx, a.err, a.best_amax, cert, qo);
+}
+
 template <typename T, bool kVec>
 hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
   const int64_t nb = a.c_in / 16;
@@ -1423,18 +1852,17 @@ hipError_t launch_sweep_typed(const SweepArgs& a, hipStream_t stream) {
   const RowPlan rp = row_plan(a.c_out, per_k);
   const dim3 rgrid((unsigned)(per_k * rp.cstep));
   const T* wp = static_cast<const T*>(a.w);
+  // One chunk of rows per wave: the pooled rounds; several (small c_out):
+  // each lane through its own candidates (measured faster there).
+  const bool pooled = rp.cstep == rp.n_chunks;
   if (quant && all)
-    sweep_rows_kernel<T, kVec, true, true><<<rgrid, dim3(kSweepThreads), 0, stream>>>(
-        wp, a.c_out, a.ld_w, a.gstride_w, nb, rp, a.h, a.gstride_h, a.amax, a.idx, a.err, a.best_amax, cert, qo);
+    launch_rows<T, kVec, true, true>(pooled, rgrid, stream, wp, a, nb, rp, cert, qo);
   else if (quant)
-    sweep_rows_kernel<T, kVec, true, false><<<rgrid, dim3(kSweepThreads), 0, stream>>>(
-        wp, a.c_out, a.ld_w, a.gstride_w, nb, rp, a.h, a.gstride_h, a.amax, a.idx, a.err, a.best_amax, cert, qo);
+    launch_rows<T, kVec, true, false>(pooled, rgrid, stream, wp, a, nb, rp, cert, qo);
   else if (a.err && a.best_amax)
-    sweep_rows_kernel<T, kVec, false, true><<<rgrid, dim3(kSweepThreads), 0, stream>>>(
-        wp, a.c_out, a.ld_w, a.gstride_w, nb, rp, a.h, a.gstride_h, a.amax, a.idx, a.err, a.best_amax, cert, qo);
+    launch_rows<T, kVec, false, true>(pooled, rgrid, stream, wp, a, nb, rp, cert, qo);
   else
-    sweep_rows_kernel<T, kVec, false, false><<<rgrid, dim3(kSweepThreads), 0, stream>>>(
-        wp, a.c_out, a.ld_w, a.gstride_w, nb, rp, a.h, a.gstride_h, a.amax, a.idx, a.err, a.best_amax, cert, qo);
+    launch_rows<T, kVec, false, false>(pooled, rgrid, stream, wp, a, nb, rp, cert, qo);
   return hipGetLastError();
 }
 
