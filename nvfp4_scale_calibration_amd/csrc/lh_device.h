@@ -93,14 +93,14 @@ __device__ __forceinline__ uint32_t absbits_max(uint32_t m, const uint4 u, bool 
 
 // Workgroup share `chunk` of `per_group` of a flat array of n16 16-byte
 // vectors: the largest |w| bits it holds (grid-stride, four loads in
-// flight per thread), reduced over the workgroup; valid in thread 0.
-template <bool kBf16>
+// flight per thread), reduced over the kT-thread workgroup; valid in thread 0.
+template <bool kBf16, int kT = kThreads>
 __device__ __forceinline__ uint32_t absmax_flat_share(const uint4* __restrict__ v, int64_t n16, int64_t chunk,
                                                       int64_t per_group) {
-  __shared__ uint32_t part[kThreads / 64];
+  __shared__ uint32_t part[kT / 64];
   uint32_t m = 0;
-  const int64_t stride = per_group * kThreads;
-  int64_t i = chunk * kThreads + threadIdx.x;
+  const int64_t stride = per_group * kT;
+  int64_t i = chunk * kT + threadIdx.x;
   for (; i + 3 * stride < n16; i += 4 * stride) {
     const uint4 a = v[i], b = v[i + stride], c = v[i + 2 * stride], d = v[i + 3 * stride];
     m = absbits_max(m, a, kBf16);
@@ -115,7 +115,7 @@ __device__ __forceinline__ uint32_t absmax_flat_share(const uint4* __restrict__ 
   __syncthreads();
   uint32_t t = part[0];
 #pragma unroll
-  for (int k = 1; k < kThreads / 64; ++k) t = max(t, part[k]);
+  for (int k = 1; k < kT / 64; ++k) t = max(t, part[k]);
   return t;
 }
 

@@ -8,15 +8,16 @@
 //
 //   h[g][b] = beta * h[g][b] + alpha * X_b X_b^T
 //
-// Design: one 256-thread workgroup (4 wave64s) per (group, block, token
-// slice).  The contraction over tokens runs on MFMA with fp32 accumulation:
+// Design: one workgroup per (group, block, token slice): 4, 8 or 16 wave64s
+// channel-major (the plan's choice), 4 token-major.  The contraction over
+// tokens runs on MFMA with fp32 accumulation:
 // v_mfma_f32_16x16x32_bf16 for bf16 X, v_mfma_f32_16x16x4_f32 for fp32 X.
 // For H = X_b X_b^T the A operand (16 channels x K tokens) and the B operand
 // (its transpose) hold the same values in each lane (lane l: channel l%16,
 // K-slot group l/16), so one register set feeds both.  The token order inside
 // a K step is free (a sum), which lets each lane read 16 contiguous tokens
 // (channel-major) or a bank-conflict-free LDS column (token-major).
-// The four waves of a workgroup reduce in LDS in a fixed order; token slices
+// The waves of a workgroup reduce in LDS in a fixed order; token slices
 // of one block reduce in a second kernel in a fixed order: results do not
 // depend on timing.
 #include "lh_device.h"
@@ -30,7 +31,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 namespace {
 
 constexpr int kSlab = 64;                 // tokens per wave per step
-constexpr int kRound = kSlab * 4;         // tokens per workgroup per step
+constexpr int kRound = kSlab * 4;         // tokens per 4-wave workgroup per step
 constexpr int64_t kRaggedSlice = 1024;    // rows per ragged slice when the largest group is known
 
 // Sixteen token values of one channel, in the lane's register layout.
@@ -102,12 +103,16 @@ __device__ __forceinline__ void load_cm(const float* row, int64_t tb, int64_t t1
 // Workgroup `id` = (group, block, token slice): the slice's X_b X_b^T,
 // written as h = beta h + alpha S without a workspace, else as the slice's
 // partial sum in ws[slice][group][block].
-template <typename T, bool kVec>
+// kNW waves: wave w takes the slabs at tokens t0 + 64 w + 64 kNW k, so
+// together the waves read 128 kNW contiguous bytes of each bf16 row at a
+// time.
+template <typename T, bool kVec, int kNW>
 __device__ __forceinline__ void hessian_cm_block(int64_t id, const T* __restrict__ x, int64_t n_tok, int64_t ld,
                                                  int64_t gstride, int64_t nb, int64_t n_groups, int64_t nsplit,
                                                  int64_t chunk, float alpha, float beta, float* __restrict__ h,
                                                  int64_t h_gstride, float* __restrict__ ws) {
-  __shared__ float red[4][256];
+  constexpr int kR = kSlab * kNW;  // tokens per workgroup per step
+  __shared__ float red[kNW][256];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ch = lane & 15, kg = lane >> 4;
   const int64_t s = id % nsplit;
@@ -122,15 +127,15 @@ __device__ __forceinline__ void hessian_cm_block(int64_t id, const T* __restrict
   // Two slabs per trip keep four 16-byte loads per lane in flight; while both
   // slabs lie inside the slice no load needs a bounds check.
   if (kVec) {
-    for (; t + kRound + kSlab <= t1; t += 2 * kRound) {
+    for (; t + kR + kSlab <= t1; t += 2 * kR) {
       Vals16<T> v0, v1;
       load_cm<true, true>(row, t + 16 * kg, t1, v0);
-      load_cm<true, true>(row, t + kRound + 16 * kg, t1, v1);
+      load_cm<true, true>(row, t + kR + 16 * kg, t1, v1);
       acc = mfma_accumulate(v0, acc);
       acc = mfma_accumulate(v1, acc);
     }
   }
-  for (; t < t1; t += kRound) {
+  for (; t < t1; t += kR) {
     Vals16<T> v0;
     load_cm<kVec>(row, t + 16 * kg, t1, v0);
     acc = mfma_accumulate(v0, acc);
@@ -141,7 +146,10 @@ __device__ __forceinline__ void hessian_cm_block(int64_t id, const T* __restrict
   for (int i = 0; i < 4; ++i) red[wave][(4 * kg + i) * 16 + ch] = acc[i];
   __syncthreads();
   const int e = threadIdx.x;
-  const float v = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+  if (e >= 256) return;
+  float v = red[0][e];
+#pragma unroll
+  for (int k = 1; k < kNW; ++k) v += red[k][e];  // waves in order
   if (ws == nullptr) {
     float* hp = h + grp * h_gstride + b * 256 + e;
     *hp = (beta == 0.0f) ? alpha * v : beta * (*hp) + alpha * v;
@@ -150,14 +158,14 @@ __device__ __forceinline__ void hessian_cm_block(int64_t id, const T* __restrict
   }
 }
 
-template <typename T, bool kVec>
-__global__ __launch_bounds__(kThreads) void hessian_cm_kernel(const T* __restrict__ x, int64_t n_tok,
+template <typename T, bool kVec, int kNW>
+__global__ __launch_bounds__(64 * kNW) void hessian_cm_kernel(const T* __restrict__ x, int64_t n_tok,
                                                               int64_t ld, int64_t gstride, int64_t nb,
                                                               int64_t n_groups, int64_t nsplit,
                                                               int64_t chunk, float alpha, float beta,
                                                               float* __restrict__ h, int64_t h_gstride,
                                                               float* __restrict__ ws) {
-  hessian_cm_block<T, kVec>(blockIdx.x, x, n_tok, ld, gstride, nb, n_groups, nsplit, chunk, alpha, beta, h,
+  hessian_cm_block<T, kVec, kNW>(blockIdx.x, x, n_tok, ld, gstride, nb, n_groups, nsplit, chunk, alpha, beta, h,
                             h_gstride, ws);
 }
 
@@ -166,8 +174,8 @@ __global__ __launch_bounds__(kThreads) void hessian_cm_kernel(const T* __restric
 // others compute the token-slice partial sums of the channel-major Hessian
 // (X 16-byte aligned); no atomics, so no output has to be zeroed first.  The
 // finalize kernel completes both.
-template <typename T, typename TW>
-__global__ __launch_bounds__(kThreads) void prologue_cm_kernel(const T* __restrict__ x, int64_t n_tok, int64_t ld,
+template <typename T, typename TW, int kNW>
+__global__ __launch_bounds__(64 * kNW) void prologue_cm_kernel(const T* __restrict__ x, int64_t n_tok, int64_t ld,
                                                                int64_t gstride, int64_t nb, int64_t n_groups,
                                                                int64_t nsplit, int64_t chunk, float* __restrict__ ws,
                                                                const TW* __restrict__ w,
@@ -176,14 +184,14 @@ __global__ __launch_bounds__(kThreads) void prologue_cm_kernel(const T* __restri
   // the amax shares (long, few) come first in the grid, the Hessian slices fill in behind them
   const int64_t n_abs = n_groups * per_group;
   if ((int64_t)blockIdx.x >= n_abs) {
-    hessian_cm_block<T, true>((int64_t)blockIdx.x - n_abs, x, n_tok, ld, gstride, nb, n_groups, nsplit, chunk, 1.0f,
+    hessian_cm_block<T, true, kNW>((int64_t)blockIdx.x - n_abs, x, n_tok, ld, gstride, nb, n_groups, nsplit, chunk, 1.0f,
                               0.0f, nullptr, 0, ws);
     return;
   }
   const int64_t id = blockIdx.x;
   const int64_t grp = id / per_group, share = id - grp * per_group;
-  const uint32_t m = absmax_flat_share<sizeof(TW) == 2>(reinterpret_cast<const uint4*>(w + grp * w_gstride), w_n16,
-                                                        share, per_group);
+  const uint32_t m = absmax_flat_share<sizeof(TW) == 2, 64 * kNW>(reinterpret_cast<const uint4*>(w + grp * w_gstride),
+                                                                  w_n16, share, per_group);
   if (threadIdx.x == 0) abs_part[id] = m;
 }
 
@@ -448,10 +456,16 @@ hipError_t launch_typed(const HessianArgs& a, const HessianPlan& p, hipStream_t 
   float* ws = p.nsplit > 1 ? static_cast<float*>(a.ws) : nullptr;
   const T* x = static_cast<const T*>(a.x);
   if (a.layout == 0) {
-    const int64_t grid = a.n_groups * nb * p.nsplit;
-    hessian_cm_kernel<T, kVec><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
-        x, a.n_tok, a.ld, a.gstride, nb, a.n_groups, p.nsplit, p.chunk, a.alpha, a.beta, a.h,
-        a.h_gstride, ws);
+    const dim3 grid((unsigned)(a.n_groups * nb * p.nsplit));
+    if (p.nw == 16)
+      hessian_cm_kernel<T, kVec, 16><<<grid, dim3(64 * 16), 0, stream>>>(
+          x, a.n_tok, a.ld, a.gstride, nb, a.n_groups, p.nsplit, p.chunk, a.alpha, a.beta, a.h, a.h_gstride, ws);
+    else if (p.nw == 8)
+      hessian_cm_kernel<T, kVec, 8><<<grid, dim3(64 * 8), 0, stream>>>(
+          x, a.n_tok, a.ld, a.gstride, nb, a.n_groups, p.nsplit, p.chunk, a.alpha, a.beta, a.h, a.h_gstride, ws);
+    else
+      hessian_cm_kernel<T, kVec, 4><<<grid, dim3(64 * 4), 0, stream>>>(
+          x, a.n_tok, a.ld, a.gstride, nb, a.n_groups, p.nsplit, p.chunk, a.alpha, a.beta, a.h, a.h_gstride, ws);
   } else {
     const int64_t grid = a.n_groups * ((nb + 3) / 4) * p.nsplit;
     hessian_tm_kernel<T, kVec, false><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
@@ -546,21 +560,33 @@ hipError_t launch_hessian_ragged(const HessianRaggedArgs& a, hipStream_t stream)
   return aligned ? launch_ragged_typed<float, true>(a, p, stream) : launch_ragged_typed<float, false>(a, p, stream);
 }
 
-// Token slices per block.  Channel-major, measured on MI355X (17408 x 16384
-// bf16 X): the pass streams best with ~1024-token slices (16 slices:
-// 5.7 TB/s, vs 4.7 TB/s for 2 slices, whose 2176 workgroups leave a nearly
-// empty second wave of workgroups), so slices are ~1024 tokens, at most 16
-// of them.  Token-major workgroups cover four blocks: see tm_nsplit.
-// Chunks are whole multiples of 256 tokens (both kernels' rounds divide it).
+// Channel-major plan: waves per workgroup and token slices per block,
+// measured on MI355X with the caches flushed by a 1 GiB read (bf16, kernel
+// plus the slice sum):
+//   X 17408 x 16384: 16 waves, 4 slices 102 us; 4 waves, 8 slices 112 us;
+//   16 waves, 1 slice 141 us (1088 workgroups of 16 waves: two rounds and
+//   a thin third);
+//   X 4096 x 4096: 16 waves, 1 slice 10.6 us; 4 waves, 4 slices 12.4 us;
+//   64 x 2048 x 512: 8 waves 26.0 us, 4 waves 26.5 us, 16 waves 34.8 us
+//   (half of them without a slab).
+// So: the most waves (up to 16) that each still get a 64-token slab; one
+// slice while the chip holds every workgroup at once (no sum kernel) or
+// there are 8 rounds of them anyway; in between, slices until there are
+// 8 rounds (at most 16 slices, each at least one step of the workgroup).
+// Token-major workgroups cover four blocks: see tm_nsplit.  Chunks are whole
+// multiples of 256 tokens.
 HessianPlan hessian_plan(int64_t c_in, int64_t n_tok, int64_t n_groups, int layout, bool have_ws) {
-  HessianPlan p{1, ((n_tok + kRound - 1) / kRound) * kRound};
+  HessianPlan p{1, ((n_tok + kRound - 1) / kRound) * kRound, 4};
+  if (layout == 0)
+    while (p.nw < 16 && (int64_t)kSlab * 2 * p.nw <= n_tok) p.nw *= 2;
   const int64_t blocks = n_groups * (c_in / 16);
   if (!have_ws || blocks <= 0) return p;
-  int64_t ns;
+  int64_t ns = 1;
   if (layout == 0) {
-    if (n_tok < 2048) return p;
-    ns = n_tok / 1024;
-    if (ns > 16) ns = 16;
+    const int64_t resident = 256 * 32 / p.nw;  // 256 CUs x 32 waves
+    const int64_t cap = n_tok / ((int64_t)kSlab * p.nw);
+    if (blocks > resident)
+      while (ns < 16 && 2 * ns <= cap && blocks * ns < 8 * resident) ns *= 2;
   } else {
     ns = tm_nsplit(c_in, n_tok, n_groups);
   }
@@ -569,7 +595,10 @@ HessianPlan hessian_plan(int64_t c_in, int64_t n_tok, int64_t n_groups, int layo
   chunk = ((chunk + kRound - 1) / kRound) * kRound;
   p.chunk = chunk;
   p.nsplit = (n_tok + chunk - 1) / chunk;
-  if (p.nsplit <= 1) p = HessianPlan{1, ((n_tok + kRound - 1) / kRound) * kRound};
+  if (p.nsplit <= 1) {
+    p.nsplit = 1;
+    p.chunk = ((n_tok + kRound - 1) / kRound) * kRound;
+  }
   return p;
 }
 
@@ -587,9 +616,10 @@ size_t hessian_ws_bytes(int64_t c_in, int64_t n_tok, int64_t n_groups) {
 ProloguePlan prologue_plan(int64_t c_in, int64_t n_tok, int64_t n_groups, int64_t w_elems) {
   ProloguePlan q;
   q.hess = hessian_plan(c_in, n_tok, n_groups, 0, true);
+  const int64_t threads = 64 * q.hess.nw;  // the launch's workgroup size
   const int64_t n16 = w_elems / 8;  // at least this many 16-byte vectors (bf16); fp32 has twice as many
-  int64_t per = (1024 + n_groups - 1) / n_groups;
-  const int64_t need = (n16 + 4 * kThreads - 1) / (4 * kThreads);
+  int64_t per = (4096 / q.hess.nw + n_groups - 1) / n_groups;  // ~256 K threads over W
+  const int64_t need = (n16 + 4 * threads - 1) / (4 * threads);
   if (per > need) per = need;
   q.abs_per_group = per < 1 ? 1 : per;
   return q;
@@ -601,15 +631,25 @@ size_t prologue_ws_bytes(int64_t c_in, int64_t n_tok, int64_t n_groups, int64_t 
          (size_t)n_groups * q.abs_per_group * sizeof(uint32_t);
 }
 
-template <typename T, typename TW>
-hipError_t launch_prologue_typed(const PrologueArgs& a, const ProloguePlan& q, hipStream_t stream) {
+template <typename T, typename TW, int kNW>
+void launch_prologue_nw(const PrologueArgs& a, const ProloguePlan& q, hipStream_t stream) {
   const int64_t nb = a.c_in / 16;
   const int64_t n_hess = a.n_groups * nb * q.hess.nsplit;
   const int64_t w_n16 = a.c_out * a.c_in * (int64_t)sizeof(TW) / 16;
   const int64_t grid = n_hess + a.n_groups * q.abs_per_group;
-  prologue_cm_kernel<T, TW><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+  prologue_cm_kernel<T, TW, kNW><<<dim3((unsigned)grid), dim3(64 * kNW), 0, stream>>>(
       static_cast<const T*>(a.x), a.n_tok, a.ld_x, a.gstride_x, nb, a.n_groups, q.hess.nsplit, q.hess.chunk, a.h_part,
       static_cast<const TW*>(a.w), w_n16, a.gstride_w, q.abs_per_group, a.abs_part);
+}
+
+template <typename T, typename TW>
+hipError_t launch_prologue_typed(const PrologueArgs& a, const ProloguePlan& q, hipStream_t stream) {
+  if (q.hess.nw == 16)
+    launch_prologue_nw<T, TW, 16>(a, q, stream);
+  else if (q.hess.nw == 8)
+    launch_prologue_nw<T, TW, 8>(a, q, stream);
+  else
+    launch_prologue_nw<T, TW, 4>(a, q, stream);
   return hipGetLastError();
 }
 

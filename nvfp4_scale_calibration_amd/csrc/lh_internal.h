@@ -25,6 +25,7 @@ struct HessianArgs {
 struct HessianPlan {
   int64_t nsplit;
   int64_t chunk;
+  int nw;  // channel-major: waves per workgroup (4, 8 or 16)
 };
 HessianPlan hessian_plan(int64_t c_in, int64_t n_tok, int64_t n_groups, int layout, bool have_ws);
 size_t hessian_ws_bytes(int64_t c_in, int64_t n_tok, int64_t n_groups);

@@ -322,7 +322,7 @@ def test_noalloc_calibrate_refuses_layers_beyond_its_array(lib):
     that needs more is refused with LH_ERR_WORKSPACE and a message naming
     both sizes, before any HIP call (so this runs without a GPU)."""
     import nvfp4_scale_calibration_amd as m
-    c_out, c_in, n_tok, g = 5120, 17408, 16384, 4
+    c_out, c_in, n_tok, g = 1024, 16384, 4096, 64  # 64 experts: 65,536 input blocks
     need = m.lh_calibrate_workspace_bytes(c_out, c_in, n_tok, g)
     assert need > 32 << 20
     P = ctypes.c_void_p
