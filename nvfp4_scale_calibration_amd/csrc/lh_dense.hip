@@ -17,7 +17,9 @@
 // K advances in 128-byte chunks staged through LDS (rows padded by 16 bytes)
 // with the next chunk's global loads in flight during the MFMAs.  Operand
 // loaders are plug-ins (plain, or q - w formed on the fly); epilogues are a
-// scaled store or a fixed-order row dot with D (for the output error).
+// scaled store or a fixed-order row dot with D (for the output error).  The
+// full Hessian of a wide bf16 layer (at least 128 tiles of 256 x 256) runs
+// on xxt_big_kernel below instead.
 #include "lh_device.h"
 #include "lh_internal.h"
 
@@ -25,6 +27,7 @@ namespace lh {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 namespace {
 
@@ -230,6 +233,207 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(LA la, LB lb, GemmArg
       if (m < g.M) g.part[(grp * g.M + m) * gridDim.x + blockIdx.x] = rowsum[0][tid] + rowsum[1][tid];
     }
   }
+}
+
+// Large-tile X X^T for bf16 X (the full Hessian of a wide layer), rows of
+// X 16-byte aligned.  A 256-thread workgroup owns a 256 x 256 tile of C and
+// its four waves 128 x 128 quadrants, each a 4 x 4 grid of 32 x 32 MFMA
+// tiles (v_mfma_f32_32x32x16_bf16: measured on MI355X at 2.2 PFLOP/s with
+// independent accumulators, against 1.4 for the 16 x 16 x 32 form; 256 fp32
+// accumulators per lane in the accumulation registers, one wave per SIMD).
+// Per 32-token step a wave reads 16 KiB of operands from LDS for 32 MFMAs,
+// 64 flop per LDS byte (the 64 x 64 tile above gets 16).
+//
+// LDS holds four buffers of 2 x 256 rows of 64 bytes; the 16-byte chunk c
+// of row r sits at slot c ^ f(r), f(r) = ((r >> 1) ^ (r >> 2)) & 3, so the
+// 8 (or 16) lanes that LDS serves together read 8 (16) rows' chunk c from
+// distinct banks and write whole rows.  Step j's global loads go out at the
+// top of step j - 3 and are stored to LDS at the top of step j - 2, its
+// fragments are read during step j - 1 (while that step's MFMAs run), and
+// step j runs its MFMAs: no wait in a step is for work issued in the same
+// step.  One barrier per step.  The steps run over whole 32-token slices;
+// tokens past the last one go through one more step with checked loads.
+// Rows past c_in read row c_in - 1 (those outputs are not stored).
+constexpr int kBigTile = 256;
+constexpr int kBigKc = 32;                  // tokens per step (64 bytes of a bf16 row)
+constexpr int kBigLoads = kBigTile * (kBigKc / 8) / kThreads;  // 16-byte loads per operand per thread (4)
+
+__device__ __forceinline__ int big_slot(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row >> 2)) & 3); }
+
+// 16 bytes of a row at token kk (past k_len: zeros; the chunk that straddles
+// k_len is read whole, which stays inside the 16-byte aligned row, and its
+// elements past k_len are cleared).
+__device__ __forceinline__ uint4 big_tail_chunk(const uint16_t* p, int64_t kk, int64_t k_len) {
+  if (kk >= k_len) return make_uint4(0u, 0u, 0u, 0u);
+  uint4 v = *reinterpret_cast<const uint4*>(p);
+  const int64_t n = k_len - kk;  // valid elements, 1..
+  if (n < 8) {
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t keep = (2 * e + 1 < n) ? 0xffffffffu : (2 * e < n ? 0x0000ffffu : 0u);
+      w[e] &= keep;
+    }
+    v = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __restrict__ x, int64_t ld,
+                                                              int64_t gstride, int64_t c, int64_t k_len,
+                                                              float alpha, float* __restrict__ h, int64_t ldh,
+                                                              int64_t gstride_h) {
+  __shared__ __attribute__((aligned(16))) uint16_t as[4][kBigTile * kBigKc];
+  __shared__ __attribute__((aligned(16))) uint16_t bs[4][kBigTile * kBigKc];
+  const int64_t grp = blockIdx.z;
+  const int64_t m0 = (int64_t)blockIdx.y * kBigTile, n0 = (int64_t)blockIdx.x * kBigTile;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // thread t loads rows (t >> 2) + 64 i of both operand tiles, 16 bytes at
+  // token (t & 3) * 8 of the step: four threads cover a row's 64 bytes
+  const int lrow = tid >> 2, lcol = (tid & 3) * 8;
+  const uint16_t* xg = x + grp * gstride;
+  const uint16_t* pa[kBigLoads];
+  const uint16_t* pb[kBigLoads];
+#pragma unroll
+  for (int i = 0; i < kBigLoads; ++i) {
+    const int64_t ra = min(m0 + lrow + 64 * i, c - 1), rb = min(n0 + lrow + 64 * i, c - 1);
+    pa[i] = xg + ra * ld + lcol;
+    pb[i] = xg + rb * ld + lcol;
+  }
+
+  uint4 ra[kBigLoads], rb[kBigLoads];
+  auto gload = [&](int st) {
+    const int64_t k0 = (int64_t)st * kBigKc;
+#pragma unroll
+    for (int i = 0; i < kBigLoads; ++i) {
+      ra[i] = *reinterpret_cast<const uint4*>(pa[i] + k0);
+      rb[i] = *reinterpret_cast<const uint4*>(pb[i] + k0);
+    }
+  };
+  // rows lrow + 64 i share f(row) (64 i leaves bits 1-2 alone)
+  const int lslot = big_slot(lrow, tid & 3) * 8;
+  auto lstore = [&](int buf) {
+    uint16_t* A = as[buf] + lrow * kBigKc + lslot;
+    uint16_t* B = bs[buf] + lrow * kBigKc + lslot;
+#pragma unroll
+    for (int i = 0; i < kBigLoads; ++i) {
+      *reinterpret_cast<uint4*>(A + 64 * i * kBigKc) = ra[i];
+      *reinterpret_cast<uint4*>(B + 64 * i * kBigKc) = rb[i];
+    }
+  };
+  // fragment (tile t, half q of the step) of lane l: row 32 t + (l & 31)
+  // (+128 w), 16-byte chunk 2 q + (l >> 5); f(row) depends on l & 31 alone
+  const int l32 = lane & 31, lh = lane >> 5;
+  bf16x8_t fa[2][2][4], fb[2][2][4];
+  auto fread = [&](int p, int buf) {
+    const uint16_t* A = as[buf] + (128 * wm + l32) * kBigKc;
+    const uint16_t* B = bs[buf] + (128 * wn + l32) * kBigKc;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int slot = big_slot(l32, 2 * q + lh) * 8;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        fb[p][q][t] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(B + 32 * t * kBigKc + slot));
+        fa[p][q][t] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(A + 32 * t * kBigKc + slot));
+      }
+    }
+  };
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  auto mfmas = [&](int p) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[p][q][i], fb[p][q][j], acc[i][j], 0, 0, 0);
+  };
+
+  // Step st (fragments in set p = st % 2, read during step st - 1): the
+  // loads of step st + 2 (issued a step ago) go to LDS buffer (st + 2) % 4,
+  // last read during step st - 3; the loads of step st + 3 go out; the
+  // fragments of step st + 1 are read from buffer (st + 1) % 4 (stored a
+  // step ago); the MFMAs run; one barrier ends the step.  The last steps
+  // load and store the last slice again (never read): with no branch around
+  // the loads the compiler waits for exactly the loads each store needs.
+  auto step = [&](int st, int full, int p) {
+    lstore((st + 2) & 3);
+    gload(min(st + 3, full - 1));
+    fread(p ^ 1, (st + 1) & 3);
+    mfmas(p);
+    // Issue order: the global loads first, then one LDS access after each
+    // MFMA.  Issuing all 24 LDS accesses ahead of the MFMAs stalls the wave
+    // until the LDS has taken most of them, so the matrix core sat idle for
+    // a third of every step.
+    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);  // global loads
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // MFMA
+    __syncthreads();
+  };
+
+  // step counts in 32 bits (the launcher keeps K below 2^31)
+  const int full = (int)(k_len / kBigKc);
+  if (full > 0) {
+    gload(0);
+    lstore(0);
+    gload(min(1, full - 1));
+    lstore(1);
+    gload(min(2, full - 1));  // stored at the top of step 0
+    __syncthreads();
+    fread(0, 0);
+  }
+  int st = 0;
+  for (; st + 1 < full; st += 2) {
+    step(st, full, 0);
+    step(st + 1, full, 1);
+  }
+  if (st < full) step(st, full, 0);
+  if ((int64_t)full * kBigKc < k_len) {  // the partial last step
+    // every wave has passed the last step's barrier: every buffer is free
+    const int64_t k0 = (int64_t)full * kBigKc;
+#pragma unroll
+    for (int i = 0; i < kBigLoads; ++i) {
+      ra[i] = big_tail_chunk(pa[i] + k0, k0 + lcol, k_len);
+      rb[i] = big_tail_chunk(pb[i] + k0, k0 + lcol, k_len);
+    }
+    lstore(0);
+    __syncthreads();
+    fread(0, 0);
+    mfmas(0);
+  }
+
+  // lane holds C[m0 + 128 wm + 32 i + 8 (e / 4) + 4 (l >> 5) + e % 4][n0 + 128 wn + 32 j + (l & 31)]
+  float* C = h + grp * gstride_h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t m = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
+      if (m >= c) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t n = n0 + 128 * wn + 32 * j + l32;
+        if (n < c) C[m * ldh + n] = alpha * acc[i][j][e];
+      }
+    }
 }
 
 // e[g][m] = sum over n-tiles of part, in tile order.
@@ -668,6 +872,16 @@ __global__ __launch_bounds__(kThreads) void gptq_trailing_kernel(float* __restri
 
 template <typename T, bool kVec>
 hipError_t launch_full_hessian_typed(const FullHessianArgs& a, hipStream_t stream) {
+  if constexpr (sizeof(T) == 2 && kVec) {
+    // 256 x 256 tiles where they fill at least half of the 256 CUs
+    const int64_t bt = (a.c_in + kBigTile - 1) / kBigTile;
+    if (bt * bt * a.n_groups >= 128 && a.n_tok < ((int64_t)1 << 31)) {
+      const dim3 grid((unsigned)bt, (unsigned)bt, (unsigned)a.n_groups);
+      xxt_big_kernel<<<grid, dim3(kThreads), 0, stream>>>(static_cast<const uint16_t*>(a.x), a.ld_x, a.gstride_x,
+                                                          a.c_in, a.n_tok, a.alpha, a.h, a.ld_h, a.gstride_h);
+      return hipGetLastError();
+    }
+  }
   PlainLoader<T, kVec> L{static_cast<const T*>(a.x), a.ld_x, a.gstride_x};
   GemmArgs g{a.c_in, a.c_in, a.n_tok, a.alpha, 0.0f, 0, a.h, a.ld_h, a.gstride_h, nullptr};
   const dim3 grid((unsigned)((a.c_in + kTile - 1) / kTile), (unsigned)((a.c_in + kTile - 1) / kTile),

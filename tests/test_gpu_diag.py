@@ -96,6 +96,20 @@ def test_diagnostics_ragged(lh, G, c_out, c_in, n, dtype):
         np.testing.assert_array_equal(got["counts"][g].astype(np.uint64), counts)
 
 
+@pytest.mark.parametrize("G,c_in,n", [(8, 1040, 304), (4, 784, 77), (1, 4096, 96)])
+def test_full_hessian_large_tiles(lh, G, c_in, n):
+    """Shapes whose full Hessian runs on the 256 x 256-tile kernel (at least
+    128 tiles): a ragged last tile row and column, a partial last K step
+    with 16-byte aligned rows, unaligned rows (N = 77), and a whole
+    4096-channel layer; every entry against the oracle."""
+    work = wl.make_custom(16, c_in, n, n_groups=G, dtype="bf16", seed=c_in + 7 * n, w_dist="t3", x_dist="lognormal")
+    print("case full Hessian G=%d c_in=%d N=%d" % (G, c_in, n), flush=True)
+    hf = lh.lh_full_hessian(work.x.to(DEV)).cpu().numpy()
+    x_np = wl.np_bits(work.x)
+    for g in range(G):
+        check_full_hessian(hf[g], x_np[g], c_in, n)
+
+
 def test_diagnostics_zero_weights_and_no_tokens(lh):
     work = wl.make_custom(16, 32, 0, dtype="f32", seed=1, w_dist="zeros")
     wd = work.w.to(DEV)
