@@ -66,8 +66,19 @@ struct PlainLoader {
   }
 };
 
-// fp32 operand D = q - w (q fp32, w of type TW), formed while loading.
-template <typename TW>
+// Four consecutive w as fp32 from one vector load (kVec: 16-byte aligned
+// fp32 or 8-byte aligned bf16).
+__device__ __forceinline__ float4 load4_as_f32(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4_as_f32(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
+
+// fp32 operand D = q - w (q fp32, w of type TW), formed while loading; kVec:
+// q rows 16-byte aligned and w rows aligned to four elements, so a whole
+// chunk is one vector load of each.
+template <typename TW, bool kVec>
 struct DiffLoader {
   const float* q;
   int64_t ldq;
@@ -83,8 +94,17 @@ struct DiffLoader {
   }
   __device__ __forceinline__ uint4 chunk(int64_t row, int64_t k, int64_t rows_end, int64_t k_end) const {
     float v[4];
+    if (kVec && row < rows_end && k + 4 <= k_end) {
+      const float4 a = *reinterpret_cast<const float4*>(q + row * ldq + k);
+      const float4 b = load4_as_f32(w + row * ldw + k);
+      v[0] = a.x - b.x;
+      v[1] = a.y - b.y;
+      v[2] = a.z - b.z;
+      v[3] = a.w - b.w;
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (row < rows_end && k + i < k_end) ? value(row, k + i) : 0.0f;
+      for (int i = 0; i < 4; ++i) v[i] = (row < rows_end && k + i < k_end) ? value(row, k + i) : 0.0f;
+    }
     return __builtin_bit_cast(uint4, v);
   }
 };
@@ -890,16 +910,16 @@ hipError_t launch_full_hessian_typed(const FullHessianArgs& a, hipStream_t strea
   return hipGetLastError();
 }
 
-template <typename TW, bool kVecH>
+template <typename TW, bool kVecH, bool kVecD>
 hipError_t launch_output_error_typed(const OutputErrorArgs& a, hipStream_t stream) {
-  DiffLoader<TW> D{a.q, a.ld_q, static_cast<const TW*>(a.w), a.ld_w, a.gstride_q, a.gstride_w};
+  DiffLoader<TW, kVecD> D{a.q, a.ld_q, static_cast<const TW*>(a.w), a.ld_w, a.gstride_q, a.gstride_w};
   PlainLoader<float, kVecH> H{a.h, a.ld_h, a.gstride_h};
   const int64_t tiles = (a.c_in + kTile - 1) / kTile;
   float* part = static_cast<float*>(a.ws);
   GemmArgs g{a.c_out, a.c_in, a.c_in, 1.0f, 0.0f, 0, nullptr, 0, 0, part};
   const dim3 grid((unsigned)tiles, (unsigned)((a.c_out + kTile - 1) / kTile), (unsigned)a.n_groups);
-  gemm_nt_kernel<float, DiffLoader<TW>, PlainLoader<float, kVecH>, kEpiRowDot><<<grid, dim3(kThreads), 0, stream>>>(
-      D, H, g);
+  gemm_nt_kernel<float, DiffLoader<TW, kVecD>, PlainLoader<float, kVecH>, kEpiRowDot>
+      <<<grid, dim3(kThreads), 0, stream>>>(D, H, g);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t rows = a.n_groups * a.c_out;
@@ -1046,9 +1066,19 @@ hipError_t launch_full_hessian(const FullHessianArgs& a, hipStream_t stream) {
 hipError_t launch_output_error(const OutputErrorArgs& a, hipStream_t stream) {
   if (a.n_groups == 0 || a.c_out == 0) return hipSuccess;
   const bool vh = reinterpret_cast<uintptr_t>(a.h) % 16 == 0 && a.ld_h % 4 == 0 && a.gstride_h % 4 == 0;
-  if (a.dtype == 1)
-    return vh ? launch_output_error_typed<uint16_t, true>(a, stream) : launch_output_error_typed<uint16_t, false>(a, stream);
-  return vh ? launch_output_error_typed<float, true>(a, stream) : launch_output_error_typed<float, false>(a, stream);
+  const size_t wsz = a.dtype == 1 ? 2 : 4;
+  const bool vd = reinterpret_cast<uintptr_t>(a.q) % 16 == 0 && a.ld_q % 4 == 0 && a.gstride_q % 4 == 0 &&
+                  reinterpret_cast<uintptr_t>(a.w) % (4 * wsz) == 0 && a.ld_w % 4 == 0 && a.gstride_w % 4 == 0;
+  if (a.dtype == 1) {
+    if (vd) return vh ? launch_output_error_typed<uint16_t, true, true>(a, stream)
+                      : launch_output_error_typed<uint16_t, false, true>(a, stream);
+    return vh ? launch_output_error_typed<uint16_t, true, false>(a, stream)
+              : launch_output_error_typed<uint16_t, false, false>(a, stream);
+  }
+  if (vd) return vh ? launch_output_error_typed<float, true, true>(a, stream)
+                    : launch_output_error_typed<float, false, true>(a, stream);
+  return vh ? launch_output_error_typed<float, true, false>(a, stream)
+            : launch_output_error_typed<float, false, false>(a, stream);
 }
 
 hipError_t launch_histogram(const HistogramArgs& a, hipStream_t stream) {
