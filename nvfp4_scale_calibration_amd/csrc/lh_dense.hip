@@ -264,16 +264,16 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(LA la, LB lb, GemmArg
 // Per 32-token step a wave reads 16 KiB of operands from LDS for 32 MFMAs,
 // 64 flop per LDS byte (the 64 x 64 tile above gets 16).
 //
-// LDS holds four buffers of 2 x 256 rows of 64 bytes; the 16-byte chunk c
-// of row r sits at slot c ^ f(r), f(r) = ((r >> 1) ^ (r >> 2)) & 3, so the
-// 8 (or 16) lanes that LDS serves together read 8 (16) rows' chunk c from
-// distinct banks and write whole rows.  Step j's global loads go out at the
-// top of step j - 3 and are stored to LDS at the top of step j - 2, its
-// fragments are read during step j - 1 (while that step's MFMAs run), and
-// step j runs its MFMAs: no wait in a step is for work issued in the same
-// step.  One barrier per step.  The steps run over whole 32-token slices;
-// tokens past the last one go through one more step with checked loads.
-// Rows past c_in read row c_in - 1 (those outputs are not stored).
+// LDS holds three buffers of 2 x 256 rows of 64 bytes, filled straight from
+// global memory (no staging registers); the 16-byte chunk c of row r sits
+// at slot c ^ f(r), f(r) = ((r >> 1) ^ (r >> 2)) & 3, so the 8 (or 16)
+// lanes that LDS serves together read 8 (16) rows' chunk c from distinct
+// banks.  Step j's loads go out at the top of step j - 3 and are waited for
+// at the end of step j - 2, its fragments are read during step j - 1 (while
+// that step's MFMAs run), and step j runs its MFMAs; one barrier per step.
+// The steps run over whole 32-token slices; tokens past the last one go
+// through one more step with checked register loads.  Rows past c_in read
+// row c_in - 1 (those outputs are not stored).
 constexpr int kBigTile = 256;
 constexpr int kBigKc = 32;                  // tokens per step (64 bytes of a bf16 row)
 constexpr int kBigLoads = kBigTile * (kBigKc / 8) / kThreads;  // 16-byte loads per operand per thread (4)
@@ -299,50 +299,62 @@ __device__ __forceinline__ uint4 big_tail_chunk(const uint16_t* p, int64_t kk, i
   return v;
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane l writes
+// LDS bytes lds + 16 l .. lds + 16 l + 15 (lds wave-uniform).  Written in
+// asm so that the compiler, which would otherwise wait for every such load
+// before any LDS read, leaves the waits to the kernel: the kernel waits with
+// s_waitcnt vmcnt before the barrier that publishes the data.  No register
+// is written; M0 carries the LDS address (nothing else in the kernel uses it).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __restrict__ x, int64_t ld,
                                                               int64_t gstride, int64_t c, int64_t k_len,
                                                               float alpha, float* __restrict__ h, int64_t ldh,
                                                               int64_t gstride_h) {
-  __shared__ __attribute__((aligned(16))) uint16_t as[4][kBigTile * kBigKc];
-  __shared__ __attribute__((aligned(16))) uint16_t bs[4][kBigTile * kBigKc];
+  __shared__ __attribute__((aligned(16))) uint16_t as[3][kBigTile * kBigKc];
+  __shared__ __attribute__((aligned(16))) uint16_t bs[3][kBigTile * kBigKc];
   const int64_t grp = blockIdx.z;
   const int64_t m0 = (int64_t)blockIdx.y * kBigTile, n0 = (int64_t)blockIdx.x * kBigTile;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-
-  // thread t loads rows (t >> 2) + 64 i of both operand tiles, 16 bytes at
-  // token (t & 3) * 8 of the step: four threads cover a row's 64 bytes
-  const int lrow = tid >> 2, lcol = (tid & 3) * 8;
   const uint16_t* xg = x + grp * gstride;
-  const uint16_t* pa[kBigLoads];
-  const uint16_t* pb[kBigLoads];
+
+  // Direct loads: one wave instruction fills a 1 KiB block of LDS (16 rows
+  // of 64 bytes), lane l writing bytes 16 l .. 16 l + 15, i.e. row l >> 2,
+  // slot l & 3.  So lane l fetches chunk (l & 3) ^ f(row) of its row.  Wave
+  // w fills row blocks w, w + 4, w + 8, w + 12 of both operand tiles.
+  const int drow = lane >> 2;
+  const int dcol = big_slot(drow, lane & 3) * 8;  // slot ^ f(row) = the chunk this slot holds
+  const uint16_t* ga[kBigLoads];
+  const uint16_t* gb[kBigLoads];
 #pragma unroll
   for (int i = 0; i < kBigLoads; ++i) {
-    const int64_t ra = min(m0 + lrow + 64 * i, c - 1), rb = min(n0 + lrow + 64 * i, c - 1);
-    pa[i] = xg + ra * ld + lcol;
-    pb[i] = xg + rb * ld + lcol;
+    const int64_t r = 16 * (wave + 4 * i) + drow;
+    ga[i] = xg + min(m0 + r, c - 1) * ld + dcol;
+    gb[i] = xg + min(n0 + r, c - 1) * ld + dcol;
   }
-
-  uint4 ra[kBigLoads], rb[kBigLoads];
-  auto gload = [&](int st) {
+  // LDS byte address of row block w + 4 i of buffer 0 (wave-uniform)
+  const uint32_t la0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(as[0] + 16 * wave * kBigKc));
+  const uint32_t lb0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(bs[0] + 16 * wave * kBigKc));
+  constexpr uint32_t kBufBytes = kBigTile * kBigKc * 2;
+  auto dload = [&](int st, int buf) {
     const int64_t k0 = (int64_t)st * kBigKc;
 #pragma unroll
     for (int i = 0; i < kBigLoads; ++i) {
-      ra[i] = *reinterpret_cast<const uint4*>(pa[i] + k0);
-      rb[i] = *reinterpret_cast<const uint4*>(pb[i] + k0);
+      lds_dma16(ga[i] + k0, la0 + buf * kBufBytes + i * (64 * kBigKc * 2));
+      lds_dma16(gb[i] + k0, lb0 + buf * kBufBytes + i * (64 * kBigKc * 2));
     }
   };
-  // rows lrow + 64 i share f(row) (64 i leaves bits 1-2 alone)
-  const int lslot = big_slot(lrow, tid & 3) * 8;
-  auto lstore = [&](int buf) {
-    uint16_t* A = as[buf] + lrow * kBigKc + lslot;
-    uint16_t* B = bs[buf] + lrow * kBigKc + lslot;
-#pragma unroll
-    for (int i = 0; i < kBigLoads; ++i) {
-      *reinterpret_cast<uint4*>(A + 64 * i * kBigKc) = ra[i];
-      *reinterpret_cast<uint4*>(B + 64 * i * kBigKc) = rb[i];
-    }
-  };
+
   // fragment (tile t, half q of the step) of lane l: row 32 t + (l & 31)
   // (+128 w), 16-byte chunk 2 q + (l >> 5); f(row) depends on l & 31 alone
   const int l32 = lane & 31, lh = lane >> 5;
@@ -379,46 +391,37 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
   };
 
   // Step st (fragments in set p = st % 2, read during step st - 1): the
-  // loads of step st + 2 (issued a step ago) go to LDS buffer (st + 2) % 4,
-  // last read during step st - 3; the loads of step st + 3 go out; the
-  // fragments of step st + 1 are read from buffer (st + 1) % 4 (stored a
-  // step ago); the MFMAs run; one barrier ends the step.  The last steps
-  // load and store the last slice again (never read): with no branch around
-  // the loads the compiler waits for exactly the loads each store needs.
+  // direct loads of step st + 3 go to LDS buffer st % 3 (its fragments were
+  // read during step st - 1, before that step's barrier); the fragments of
+  // step st + 1 are read from buffer (st + 1) % 3; the MFMAs run; the wave
+  // waits for its loads of step st + 2 (issued a step ago) and one barrier
+  // ends the step.  The last steps load the last slice again (never read):
+  // with no branch around the loads the compiler waits for exactly the
+  // loads each step needs.
   auto step = [&](int st, int full, int p) {
-    lstore((st + 2) & 3);
-    gload(min(st + 3, full - 1));
-    fread(p ^ 1, (st + 1) & 3);
+    dload(min(st + 3, full - 1), st % 3);
+    fread(p ^ 1, (st + 1) % 3);
     mfmas(p);
-    // Issue order: the global loads first, then one LDS access after each
-    // MFMA.  Issuing all 24 LDS accesses ahead of the MFMAs stalls the wave
-    // until the LDS has taken most of them, so the matrix core sat idle for
-    // a third of every step.
-    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);  // global loads
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
-    }
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMA
+    wait_vmcnt<8>();  // this wave's loads of step st + 2 have landed
     __syncthreads();
   };
 
   // step counts in 32 bits (the launcher keeps K below 2^31)
   const int full = (int)(k_len / kBigKc);
   if (full > 0) {
-    gload(0);
-    lstore(0);
-    gload(min(1, full - 1));
-    lstore(1);
-    gload(min(2, full - 1));  // stored at the top of step 0
+    dload(0, 0);
+    dload(min(1, full - 1), 1);
+    dload(min(2, full - 1), 2);
+    wait_vmcnt<8>();  // steps 0 and 1 have landed
     __syncthreads();
     fread(0, 0);
+    __syncthreads();  // every wave has read buffer 0 before step 0 refills it
   }
   int st = 0;
   for (; st + 1 < full; st += 2) {
@@ -426,15 +429,20 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
     step(st + 1, full, 1);
   }
   if (st < full) step(st, full, 0);
-  if ((int64_t)full * kBigKc < k_len) {  // the partial last step
-    // every wave has passed the last step's barrier: every buffer is free
+  if ((int64_t)full * kBigKc < k_len) {  // the partial last step, through registers
+    wait_vmcnt<0>();  // no direct load still lands
+    __syncthreads();
     const int64_t k0 = (int64_t)full * kBigKc;
+    const int lrow = tid >> 2, lcol = (tid & 3) * 8;
+    const int lslot = big_slot(lrow, tid & 3) * 8;
 #pragma unroll
     for (int i = 0; i < kBigLoads; ++i) {
-      ra[i] = big_tail_chunk(pa[i] + k0, k0 + lcol, k_len);
-      rb[i] = big_tail_chunk(pb[i] + k0, k0 + lcol, k_len);
+      const int64_t ra = min(m0 + lrow + 64 * i, c - 1), rb = min(n0 + lrow + 64 * i, c - 1);
+      const uint4 va = big_tail_chunk(xg + ra * ld + lcol + k0, k0 + lcol, k_len);
+      const uint4 vb = big_tail_chunk(xg + rb * ld + lcol + k0, k0 + lcol, k_len);
+      *reinterpret_cast<uint4*>(&as[0][(lrow + 64 * i) * kBigKc + lslot]) = va;
+      *reinterpret_cast<uint4*>(&bs[0][(lrow + 64 * i) * kBigKc + lslot]) = vb;
     }
-    lstore(0);
     __syncthreads();
     fread(0, 0);
     mfmas(0);
