@@ -99,16 +99,21 @@ def test_ragged_shapes(lh, G, c_out, c_in, n, dtype, layout):
     check_all(lh, work, layout=layout)
 
 
-def test_hessian_split_vs_one_pass_and_determinism(lh):
-    work = wl.make_custom(8, 256, 8192 + 77, dtype="bf16", seed=5, x_dist="lognormal")
+@pytest.mark.parametrize("c_in,n", [(256, 8192 + 77), (9600, 2048 + 77)])
+def test_hessian_split_vs_one_pass_and_determinism(lh, c_in, n):
+    """16 blocks over 8269 tokens: the channel-major plan keeps one slice
+    (16-wave workgroups, all resident at once), the token-major one splits;
+    600 blocks over 2125 tokens: the channel-major plan splits the tokens in
+    two slices of 16-wave workgroups, the second one ragged."""
+    work = wl.make_custom(8, c_in, n, dtype="bf16", seed=5, x_dist="lognormal")
     xd = work.x.to(DEV)
-    assert lh.lh_hessian_workspace_bytes(256, 8192 + 77, 1) > 0
+    assert lh.lh_hessian_workspace_bytes(c_in, n, 1) > 0
     h_split = lh.lh_accumulate_hessian(xd, workspace=True)
     h_split2 = lh.lh_accumulate_hessian(xd, workspace=True)
     h_one = lh.lh_accumulate_hessian(xd, workspace=False)
     torch.cuda.synchronize()
     assert torch.equal(h_split, h_split2)  # fixed reduction order
-    h64, _ = oracle.hessian(wl.np_bits(work.x), 256, 8192 + 77)
+    h64, _ = oracle.hessian(wl.np_bits(work.x), c_in, n)
     parity.check_hessian(h_split.cpu().numpy(), h64, "split")
     parity.check_hessian(h_one.cpu().numpy(), h64, "one-pass")
     # token-major gives the same matrix within tolerance
