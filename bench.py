@@ -432,7 +432,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (asked for %d)." % max(args.gpus, world),
+        print("bench.py measures one GPU only: the library has no multi-GPU path (asked for %d)." % max(args.gpus, world),
               file=sys.stderr)
         sys.exit(2)
 

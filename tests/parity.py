@@ -4,7 +4,7 @@ tests, the smoke check and the benchmark's self-check).
 Rules (the repository's design notes derive them):
   * Hessian: |H_gpu - H_oracle|_ij <= 1e-3 * sqrt(H_ii H_jj) (+1e-30): relative
     on the diagonal, Cauchy-Schwarz-scaled off it; the oracle sums in fp64.
-  * Sweep, judged on the same fp32 H fed to both sides.  For every block the
+  * Sweep, compared on the same fp32 H fed to both sides.  For every block the
     oracle also evaluates its error E_or[k_gpu] at the candidate the GPU
     chose (exact, fp64), so a different pick is accepted only when it is
     itself a near-tie of the best, and the GPU's reported error is compared
