@@ -310,6 +310,26 @@ def extras(lh, work, stream) -> dict:
             "diagnostics": diag}
 
 
+def full_hessian_wide(lh, work, x) -> dict:
+    """The full C_in x C_in Hessian of a wide layer's X (N3): at C_in = 17408
+    the kernel computes the lower triangle of 256 x 256 tiles (2346 of 4624)
+    and mirrors it.  Two rates: the full product's 2 C_in^2 N flop per
+    second (what a square GEMM would have to reach for the same result) and
+    the symmetric product's C_in (C_in + 1) N flop per second (work that no
+    C_in x C_in result can avoid); the MFMA peak applies to the second."""
+    import torch
+    c_in, n = work.c_in, work.n_tok
+    hf = torch.empty((1, c_in, c_in), dtype=torch.float32, device=x.device)
+    t = graph_time(lambda: lh.lh_full_hessian(x, h=hf), reps=3)
+    del hf
+    bt = (c_in + 255) // 256
+    sym = float(c_in) * (c_in + 1) * n / (t / 1e3) / 1e12
+    return {"workload": work.description, "c_in": c_in, "n_tokens": n, "ms": t,
+            "tiles": {"computed": bt * (bt + 1) // 2, "square": bt * bt},
+            "full_product_tflops": 2.0 * c_in * c_in * n / (t / 1e3) / 1e12,
+            "symmetric_tflops": sym, "symmetric_frac_bf16_peak": sym / 2500.0}
+
+
 def diagnostics(lh, work, w, x, h, amax, idx, err, bam) -> dict:
     """How much of the layer's output error the block-diagonal objective
     sees, per scale rule: the full error sum_r (q-w) H_full (q-w)^T (H_full =
@@ -560,6 +580,9 @@ def main():
                 del other
                 torch.cuda.empty_cache()
         out["hessian_cold"] = per
+        if G == 1:
+            out["full_hessian_wide"] = full_hessian_wide(lh, work, x)
+            torch.cuda.empty_cache()
         ework = work if args.extras_workload == args.workload else wl.make(args.extras_workload)
         out["extras"] = extras(lh, ework, stream)
     if not args.no_cpu_baseline:

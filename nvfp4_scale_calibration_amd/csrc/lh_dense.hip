@@ -316,14 +316,40 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Tile (ty, tx) of the lower triangle ty >= tx numbered row by row:
+// t = ty (ty + 1) / 2 + tx.
+__device__ __forceinline__ void tri_tile(int64_t t, int64_t& ty, int64_t& tx) {
+  int64_t y = (int64_t)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+  while ((y + 1) * (y + 2) / 2 <= t) ++y;
+  while (y * (y + 1) / 2 > t) --y;
+  ty = y;
+  tx = t - y * (y + 1) / 2;
+}
+
+// kSyrk: the grid walks the lower triangle of tiles (blockIdx.x = t above);
+// an off-diagonal tile also writes its transpose (H is symmetric), staged
+// through LDS so that the transposed rows go out as whole 128-byte lines.
+// vec_h: H rows are 16-byte aligned (ldh, gstride_h multiples of 4).
+template <bool kSyrk>
 __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __restrict__ x, int64_t ld,
                                                               int64_t gstride, int64_t c, int64_t k_len,
                                                               float alpha, float* __restrict__ h, int64_t ldh,
-                                                              int64_t gstride_h) {
+                                                              int64_t gstride_h, bool vec_h) {
   __shared__ __attribute__((aligned(16))) uint16_t as[3][kBigTile * kBigKc];
   __shared__ __attribute__((aligned(16))) uint16_t bs[3][kBigTile * kBigKc];
   const int64_t grp = blockIdx.z;
-  const int64_t m0 = (int64_t)blockIdx.y * kBigTile, n0 = (int64_t)blockIdx.x * kBigTile;
+  int64_t m0, n0;
+  bool mirror = false;
+  if constexpr (kSyrk) {
+    int64_t ty, tx;
+    tri_tile(blockIdx.x, ty, tx);
+    m0 = ty * kBigTile;
+    n0 = tx * kBigTile;
+    mirror = ty != tx;
+  } else {
+    m0 = (int64_t)blockIdx.y * kBigTile;
+    n0 = (int64_t)blockIdx.x * kBigTile;
+  }
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const uint16_t* xg = x + grp * gstride;
@@ -450,6 +476,45 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
 
   // lane holds C[m0 + 128 wm + 32 i + 8 (e / 4) + 4 (l >> 5) + e % 4][n0 + 128 wn + 32 j + (l & 31)]
   float* C = h + grp * gstride_h;
+  if (mirror) {
+    // C^T for the tile: n < c always holds here (tx < ty, so tx is not the
+    // last tile column); m may pass c in the last tile row.  Per 32-row
+    // slab i a wave writes its 128 x 32 block transposed into its own LDS
+    // region (waves 0, 1 in as, 2, 3 in bs; 128 rows of kMirPitch floats),
+    // then stores row n of it, 32 consecutive m, as 8 lanes x 16 bytes.
+    wait_vmcnt<0>();  // the last steps' direct loads have landed in LDS
+    __syncthreads();  // and every wave has finished reading its fragments
+    constexpr int kMirPitch = 36;
+    float* T = reinterpret_cast<float*>(wave < 2 ? as[0] : bs[0]) + (wave & 1) * (128 * kMirPitch);
+    const int rr = lane >> 3, cc = 4 * (lane & 7);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(&T[(32 * j + l32) * kMirPitch + 8 * q + 4 * lh]) =
+              make_float4(alpha * acc[i][j][4 * q], alpha * acc[i][j][4 * q + 1], alpha * acc[i][j][4 * q + 2],
+                          alpha * acc[i][j][4 * q + 3]);
+      __syncthreads();
+      const int64_t m = m0 + 128 * wm + 32 * i + cc;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const int r = 8 * s + rr;
+        const float4 v = *reinterpret_cast<const float4*>(&T[r * kMirPitch + cc]);
+        float* dst = C + (n0 + 128 * wn + r) * ldh + m;
+        if (vec_h && m + 3 < c) {
+          *reinterpret_cast<float4*>(dst) = v;
+        } else {
+          if (m < c) dst[0] = v.x;
+          if (m + 1 < c) dst[1] = v.y;
+          if (m + 2 < c) dst[2] = v.z;
+          if (m + 3 < c) dst[3] = v.w;
+        }
+      }
+      __syncthreads();  // the slab is read before the next one overwrites it
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -904,9 +969,18 @@ hipError_t launch_full_hessian_typed(const FullHessianArgs& a, hipStream_t strea
     // 256 x 256 tiles where they fill at least half of the 256 CUs
     const int64_t bt = (a.c_in + kBigTile - 1) / kBigTile;
     if (bt * bt * a.n_groups >= 128 && a.n_tok < ((int64_t)1 << 31)) {
-      const dim3 grid((unsigned)bt, (unsigned)bt, (unsigned)a.n_groups);
-      xxt_big_kernel<<<grid, dim3(kThreads), 0, stream>>>(static_cast<const uint16_t*>(a.x), a.ld_x, a.gstride_x,
-                                                          a.c_in, a.n_tok, a.alpha, a.h, a.ld_h, a.gstride_h);
+      // one triangle of tiles, mirrored, where it takes fewer rounds of the
+      // 256 CUs (one workgroup each) than the whole square
+      const int64_t tri = bt * (bt + 1) / 2;
+      const bool syrk = (tri * a.n_groups + 255) / 256 < (bt * bt * a.n_groups + 255) / 256 && tri < ((int64_t)1 << 31);
+      const bool vec_h = reinterpret_cast<uintptr_t>(a.h) % 16 == 0 && a.ld_h % 4 == 0 && a.gstride_h % 4 == 0;
+      const uint16_t* xx = static_cast<const uint16_t*>(a.x);
+      if (syrk)
+        xxt_big_kernel<true><<<dim3((unsigned)tri, 1, (unsigned)a.n_groups), dim3(kThreads), 0, stream>>>(
+            xx, a.ld_x, a.gstride_x, a.c_in, a.n_tok, a.alpha, a.h, a.ld_h, a.gstride_h, vec_h);
+      else
+        xxt_big_kernel<false><<<dim3((unsigned)bt, (unsigned)bt, (unsigned)a.n_groups), dim3(kThreads), 0, stream>>>(
+            xx, a.ld_x, a.gstride_x, a.c_in, a.n_tok, a.alpha, a.h, a.ld_h, a.gstride_h, vec_h);
       return hipGetLastError();
     }
   }

@@ -110,6 +110,31 @@ def test_full_hessian_large_tiles(lh, G, c_in, n):
         check_full_hessian(hf[g], x_np[g], c_in, n)
 
 
+@pytest.mark.parametrize("G,c_in,n,pad", [(1, 5120, 96, 0), (3, 2608, 200, 0), (3, 2608, 200, 1)])
+def test_full_hessian_syrk(lh, G, c_in, n, pad):
+    """Shapes whose lower triangle of 256 x 256 tiles fits in fewer rounds of
+    the CUs than the whole square, so the kernel computes one triangle and
+    mirrors it: a ragged last tile row (2608 = 10 x 256 + 48), several groups,
+    a partial last K step, and H rows that are not 16-byte aligned (pad = 1:
+    row stride c_in + 1, scalar mirrored stores).  Every entry against the
+    oracle; entries outside the diagonal tiles are exact mirrors."""
+    work = wl.make_custom(16, c_in, n, n_groups=G, dtype="bf16", seed=c_in + 3 * n, w_dist="t3", x_dist="lognormal")
+    print("case full Hessian syrk G=%d c_in=%d N=%d pad=%d" % (G, c_in, n, pad), flush=True)
+    hbuf = torch.full((G, c_in, c_in + pad), float("nan"), dtype=torch.float32, device=DEV)
+    hv = hbuf[:, :, :c_in]
+    lh.lh_full_hessian(work.x.to(DEV), h=hv)
+    hf = hv.cpu().numpy()
+    x_np = wl.np_bits(work.x)
+    tile = np.arange(c_in) // 256
+    off = tile[:, None] != tile[None, :]
+    for g in range(G):
+        assert np.isfinite(hf[g]).all()
+        np.testing.assert_array_equal(hf[g][off], hf[g].T[off])
+        check_full_hessian(hf[g], x_np[g], c_in, n)
+    if pad:
+        assert torch.isnan(hbuf[:, :, c_in:]).all()  # the padding column is never written
+
+
 def test_diagnostics_zero_weights_and_no_tokens(lh):
     work = wl.make_custom(16, 32, 0, dtype="f32", seed=1, w_dist="zeros")
     wd = work.w.to(DEV)
