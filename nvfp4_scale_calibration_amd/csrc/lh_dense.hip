@@ -261,24 +261,29 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(LA la, LB lb, GemmArg
 // tiles (v_mfma_f32_32x32x16_bf16: measured on MI355X at 2.2 PFLOP/s with
 // independent accumulators, against 1.4 for the 16 x 16 x 32 form; 256 fp32
 // accumulators per lane in the accumulation registers, one wave per SIMD).
-// Per 32-token step a wave reads 16 KiB of operands from LDS for 32 MFMAs,
-// 64 flop per LDS byte (the 64 x 64 tile above gets 16).
+// Per 32-token sub-step a wave reads 16 KiB of operands from LDS for 32
+// MFMAs, 64 flop per LDS byte (the 64 x 64 tile above gets 16).
 //
-// LDS holds three buffers of 2 x 256 rows of 64 bytes, filled straight from
+// The operands come in 64-token steps: per row one whole 128-byte line, so
+// each L2 request carries a full line (with 32-token steps every request
+// was half a line, and the L2 request rate held the kernel back).  LDS
+// holds two buffers of 2 x 256 rows of 128 bytes, filled straight from
 // global memory (no staging registers); the 16-byte chunk c of row r sits
-// at slot c ^ f(r), f(r) = ((r >> 1) ^ (r >> 2)) & 3, so the 8 (or 16)
-// lanes that LDS serves together read 8 (16) rows' chunk c from distinct
-// banks.  Step j's loads go out at the top of step j - 3 and are waited for
-// at the end of step j - 2, its fragments are read during step j - 1 (while
-// that step's MFMAs run), and step j runs its MFMAs; one barrier per step.
-// The steps run over whole 32-token slices; tokens past the last one go
-// through one more step with checked register loads.  Rows past c_in read
-// row c_in - 1 (those outputs are not stored).
+// at slot c ^ f(r), f(r) = ((r & 7) ^ (r >> 3)) & 7 over r mod 32, so the 8
+// (or 16) lanes that LDS serves together read 8 (16) rows' chunk c from
+// distinct banks.  Step S + 2's loads go out during the second sub-step of
+// step S (its buffer's last fragments were read before the barrier that
+// ends step S's first sub-step) and are waited for at the end of step
+// S + 1's first sub-step, where the one barrier per step publishes them.
+// Fragments are read one sub-step ahead, during the previous sub-step's
+// MFMAs.  Tokens past the last whole step go through one more step with
+// checked register loads.  Rows past c_in read row c_in - 1 (those outputs
+// are not stored).
 constexpr int kBigTile = 256;
-constexpr int kBigKc = 32;                  // tokens per step (64 bytes of a bf16 row)
-constexpr int kBigLoads = kBigTile * (kBigKc / 8) / kThreads;  // 16-byte loads per operand per thread (4)
+constexpr int kBigKc = 64;                  // tokens per step (one 128-byte line of a bf16 row)
+constexpr int kBigLoads = kBigTile * (kBigKc / 8) / kThreads;  // 16-byte loads per operand per thread (8)
 
-__device__ __forceinline__ int big_slot(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row >> 2)) & 3); }
+__device__ __forceinline__ int big_slot(int row, int chunk) { return chunk ^ (((row & 7) ^ (row >> 3)) & 7); }
 
 // 16 bytes of a row at token kk (past k_len: zeros; the chunk that straddles
 // k_len is read whole, which stays inside the 16-byte aligned row, and its
@@ -335,8 +340,8 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
                                                               int64_t gstride, int64_t c, int64_t k_len,
                                                               float alpha, float* __restrict__ h, int64_t ldh,
                                                               int64_t gstride_h, bool vec_h) {
-  __shared__ __attribute__((aligned(16))) uint16_t as[3][kBigTile * kBigKc];
-  __shared__ __attribute__((aligned(16))) uint16_t bs[3][kBigTile * kBigKc];
+  __shared__ __attribute__((aligned(16))) uint16_t as[2][kBigTile * kBigKc];
+  __shared__ __attribute__((aligned(16))) uint16_t bs[2][kBigTile * kBigKc];
   const int64_t grp = blockIdx.z;
   int64_t m0, n0;
   bool mirror = false;
@@ -354,49 +359,57 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
   const int wm = wave >> 1, wn = wave & 1;
   const uint16_t* xg = x + grp * gstride;
 
-  // Direct loads: one wave instruction fills a 1 KiB block of LDS (16 rows
-  // of 64 bytes), lane l writing bytes 16 l .. 16 l + 15, i.e. row l >> 2,
-  // slot l & 3.  So lane l fetches chunk (l & 3) ^ f(row) of its row.  Wave
-  // w fills row blocks w, w + 4, w + 8, w + 12 of both operand tiles.
-  const int drow = lane >> 2;
-  const int dcol = big_slot(drow, lane & 3) * 8;  // slot ^ f(row) = the chunk this slot holds
+  // Direct loads: one wave instruction fills a 1 KiB block of LDS (8 rows
+  // of 128 bytes), lane l writing bytes 16 l .. 16 l + 15, i.e. row l >> 3,
+  // slot l & 7.  So lane l fetches chunk (l & 7) ^ f(row) of its row, and
+  // the 8 lanes of a row together fetch its whole line.  Wave w fills row
+  // blocks w + 4 i (i < 8) of both operand tiles; f depends on the row mod
+  // 32 = 8 w + (l >> 3) alone.
+  const int drow = lane >> 3;
+  const int dcol = big_slot(8 * wave + drow, lane & 7) * 8;
   const uint16_t* ga[kBigLoads];
   const uint16_t* gb[kBigLoads];
 #pragma unroll
   for (int i = 0; i < kBigLoads; ++i) {
-    const int64_t r = 16 * (wave + 4 * i) + drow;
+    const int64_t r = 8 * (wave + 4 * i) + drow;
     ga[i] = xg + min(m0 + r, c - 1) * ld + dcol;
     gb[i] = xg + min(n0 + r, c - 1) * ld + dcol;
   }
-  // LDS byte address of row block w + 4 i of buffer 0 (wave-uniform)
-  const uint32_t la0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(as[0] + 16 * wave * kBigKc));
-  const uint32_t lb0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(bs[0] + 16 * wave * kBigKc));
+  // LDS byte address of row block w of buffer 0 (wave-uniform); block w + 4 i
+  // is i KiB x 4 further on
+  const uint32_t la0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(as[0] + 8 * wave * kBigKc));
+  const uint32_t lb0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(bs[0] + 8 * wave * kBigKc));
   constexpr uint32_t kBufBytes = kBigTile * kBigKc * 2;
+  constexpr uint32_t kBlkStride = 32 * kBigKc * 2;  // row blocks w and w + 4
   auto dload = [&](int st, int buf) {
     const int64_t k0 = (int64_t)st * kBigKc;
 #pragma unroll
     for (int i = 0; i < kBigLoads; ++i) {
-      lds_dma16(ga[i] + k0, la0 + buf * kBufBytes + i * (64 * kBigKc * 2));
-      lds_dma16(gb[i] + k0, lb0 + buf * kBufBytes + i * (64 * kBigKc * 2));
+      lds_dma16(ga[i] + k0, la0 + buf * kBufBytes + i * kBlkStride);
+      lds_dma16(gb[i] + k0, lb0 + buf * kBufBytes + i * kBlkStride);
     }
   };
 
-  // fragment (tile t, half q of the step) of lane l: row 32 t + (l & 31)
-  // (+128 w), 16-byte chunk 2 q + (l >> 5); f(row) depends on l & 31 alone
+  // fragment (tile t, half q of sub-step u) of lane l: row 32 t + (l & 31)
+  // (+128 w), 16-byte chunk 4 (u & 1) + 2 q + (l >> 5) of buffer (u >> 1) & 1;
+  // f(row) depends on l & 31 alone
   const int l32 = lane & 31, lh = lane >> 5;
   bf16x8_t fa[2][2][4], fb[2][2][4];
-  auto fread = [&](int p, int buf) {
-    const uint16_t* A = as[buf] + (128 * wm + l32) * kBigKc;
-    const uint16_t* B = bs[buf] + (128 * wn + l32) * kBigKc;
+  // read k (< 16) of sub-step u: half q = k >> 3, tile t = (k >> 1) & 3,
+  // operand B for even k, A for odd k
+  auto fread1 = [&](int p, int u, int k) {
+    const int buf = (u >> 1) & 1, q = k >> 3, t = (k >> 1) & 3;
+    const int slot = big_slot(l32, 4 * (u & 1) + 2 * q + lh) * 8;
+    if (k & 1)
+      fa[p][q][t] = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const uint4*>(as[buf] + (128 * wm + 32 * t + l32) * kBigKc + slot));
+    else
+      fb[p][q][t] = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const uint4*>(bs[buf] + (128 * wn + 32 * t + l32) * kBigKc + slot));
+  };
+  auto fread = [&](int p, int u) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int slot = big_slot(l32, 2 * q + lh) * 8;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        fb[p][q][t] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(B + 32 * t * kBigKc + slot));
-        fa[p][q][t] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(A + 32 * t * kBigKc + slot));
-      }
-    }
+    for (int k = 0; k < 16; ++k) fread1(p, u, k);
   };
 
   f32x16_t acc[4][4];
@@ -406,36 +419,60 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  auto mfma = [&](int p, int q, int i, int j) {
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[p][q][i], fb[p][q][j], acc[i][j], 0, 0, 0);
+  };
   auto mfmas = [&](int p) {
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[p][q][i], fb[p][q][j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) mfma(p, q, i, j);
   };
 
-  // Step st (fragments in set p = st % 2, read during step st - 1): the
-  // direct loads of step st + 3 go to LDS buffer st % 3 (its fragments were
-  // read during step st - 1, before that step's barrier); the fragments of
-  // step st + 1 are read from buffer (st + 1) % 3; the MFMAs run; the wave
-  // waits for its loads of step st + 2 (issued a step ago) and one barrier
-  // ends the step.  The last steps load the last slice again (never read):
-  // with no branch around the loads the compiler waits for exactly the
-  // loads each step needs.
-  auto step = [&](int st, int full, int p) {
-    dload(min(st + 3, full - 1), st % 3);
-    fread(p ^ 1, (st + 1) % 3);
-    mfmas(p);
+  // Step S in two sub-steps.  First (fragments in set 0): read the second
+  // sub-step's fragments, one LDS read per MFMA over the first 16 MFMAs,
+  // then 16 MFMAs with no LDS read so that the reads have landed when the
+  // wave waits for this wave's loads of step S + 1 and the barrier ends the
+  // sub-step.  Second (set 1): the loads of step S + 2 go into buffer S & 1
+  // (its last fragments were read before that barrier) and the next step's
+  // first fragments are read, one load and one read per MFMA over the first
+  // 16 MFMAs, so the reads land during the last 16; no barrier.  The last steps load the last slice
+  // again (never read): with no branch around the loads the compiler waits
+  // for exactly the loads each step needs.  sched_barrier keeps each group
+  // where it is written.
+  auto step = [&](int S, int full) {
+    fread(1, 2 * S + 1);
+    mfmas(0);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMA
-    wait_vmcnt<8>();  // this wave's loads of step st + 2 have landed
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<0>();  // this wave's loads of step S + 1 have landed
     __syncthreads();
+
+    const int64_t k0 = (int64_t)min(S + 2, full - 1) * kBigKc;
+    const uint32_t boff = (uint32_t)(S & 1) * kBufBytes;
+#pragma unroll
+    for (int i = 0; i < kBigLoads; ++i) {
+      lds_dma16(ga[i] + k0, la0 + boff + i * kBlkStride);
+      fread1(0, 2 * S + 2, 2 * i);
+      mfma(1, 0, i >> 1, 2 * (i & 1));
+      __builtin_amdgcn_sched_barrier(0);
+      lds_dma16(gb[i] + k0, lb0 + boff + i * kBlkStride);
+      fread1(0, 2 * S + 2, 2 * i + 1);
+      mfma(1, 0, i >> 1, 2 * (i & 1) + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mfma(1, 1, i, j);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // step counts in 32 bits (the launcher keeps K below 2^31)
@@ -443,35 +480,32 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
   if (full > 0) {
     dload(0, 0);
     dload(min(1, full - 1), 1);
-    dload(min(2, full - 1), 2);
-    wait_vmcnt<8>();  // steps 0 and 1 have landed
+    wait_vmcnt<2 * kBigLoads>();  // step 0 has landed
     __syncthreads();
     fread(0, 0);
-    __syncthreads();  // every wave has read buffer 0 before step 0 refills it
   }
-  int st = 0;
-  for (; st + 1 < full; st += 2) {
-    step(st, full, 0);
-    step(st + 1, full, 1);
-  }
-  if (st < full) step(st, full, 0);
+  for (int S = 0; S < full; ++S) step(S, full);
   if ((int64_t)full * kBigKc < k_len) {  // the partial last step, through registers
     wait_vmcnt<0>();  // no direct load still lands
     __syncthreads();
     const int64_t k0 = (int64_t)full * kBigKc;
-    const int lrow = tid >> 2, lcol = (tid & 3) * 8;
-    const int lslot = big_slot(lrow, tid & 3) * 8;
+    const int lrow = tid >> 3, lchunk = tid & 7;
+    const int lslot = big_slot(lrow, lchunk) * 8;
 #pragma unroll
     for (int i = 0; i < kBigLoads; ++i) {
-      const int64_t ra = min(m0 + lrow + 64 * i, c - 1), rb = min(n0 + lrow + 64 * i, c - 1);
-      const uint4 va = big_tail_chunk(xg + ra * ld + lcol + k0, k0 + lcol, k_len);
-      const uint4 vb = big_tail_chunk(xg + rb * ld + lcol + k0, k0 + lcol, k_len);
-      *reinterpret_cast<uint4*>(&as[0][(lrow + 64 * i) * kBigKc + lslot]) = va;
-      *reinterpret_cast<uint4*>(&bs[0][(lrow + 64 * i) * kBigKc + lslot]) = vb;
+      const int64_t ra = min(m0 + lrow + 32 * i, c - 1), rb = min(n0 + lrow + 32 * i, c - 1);
+      const uint4 va = big_tail_chunk(xg + ra * ld + 8 * lchunk + k0, k0 + 8 * lchunk, k_len);
+      const uint4 vb = big_tail_chunk(xg + rb * ld + 8 * lchunk + k0, k0 + 8 * lchunk, k_len);
+      *reinterpret_cast<uint4*>(&as[0][(lrow + 32 * i) * kBigKc + lslot]) = va;
+      *reinterpret_cast<uint4*>(&bs[0][(lrow + 32 * i) * kBigKc + lslot]) = vb;
     }
     __syncthreads();
     fread(0, 0);
     mfmas(0);
+    if (k_len - k0 > kBigKc / 2) {  // the second half holds tokens too
+      fread(0, 1);
+      mfmas(0);
+    }
   }
 
   // lane holds C[m0 + 128 wm + 32 i + 8 (e / 4) + 4 (l >> 5) + e % 4][n0 + 128 wn + 32 j + (l & 31)]
