@@ -267,18 +267,14 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(LA la, LB lb, GemmArg
 // The operands come in 64-token steps: per row one whole 128-byte line, so
 // each L2 request carries a full line (with 32-token steps every request
 // was half a line, and the L2 request rate held the kernel back).  LDS
-// holds two buffers of 2 x 256 rows of 128 bytes, filled straight from
-// global memory (no staging registers); the 16-byte chunk c of row r sits
-// at slot c ^ f(r), f(r) = ((r & 7) ^ (r >> 3)) & 7 over r mod 32, so the 8
-// (or 16) lanes that LDS serves together read 8 (16) rows' chunk c from
-// distinct banks.  Step S + 2's loads go out during the second sub-step of
-// step S (its buffer's last fragments were read before the barrier that
-// ends step S's first sub-step) and are waited for at the end of step
-// S + 1's first sub-step, where the one barrier per step publishes them.
-// Fragments are read one sub-step ahead, during the previous sub-step's
-// MFMAs.  Tokens past the last whole step go through one more step with
-// checked register loads.  Rows past c_in read row c_in - 1 (those outputs
-// are not stored).
+// holds three buffers of operand A and two of B, 256 rows of 128 bytes
+// each (160 KiB), filled straight from global memory (no staging
+// registers); the 16-byte chunk c of row r sits at slot c ^ f(r),
+// f(r) = ((r & 7) ^ (r >> 3)) & 7 over r mod 32, so the 8 (or 16) lanes
+// that LDS serves together read 8 (16) rows' chunk c from distinct banks.
+// The step loop below gives the schedule.  Tokens past the last whole step
+// go through one more step with checked register loads.  Rows past c_in
+// read row c_in - 1 (those outputs are not stored).
 constexpr int kBigTile = 256;
 constexpr int kBigKc = 64;                  // tokens per step (one 128-byte line of a bf16 row)
 constexpr int kBigLoads = kBigTile * (kBigKc / 8) / kThreads;  // 16-byte loads per operand per thread (8)
@@ -340,8 +336,8 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
                                                               int64_t gstride, int64_t c, int64_t k_len,
                                                               float alpha, float* __restrict__ h, int64_t ldh,
                                                               int64_t gstride_h, bool vec_h) {
-  __shared__ __attribute__((aligned(16))) uint16_t as[2][kBigTile * kBigKc];
-  __shared__ __attribute__((aligned(16))) uint16_t bs[2][kBigTile * kBigKc];
+  __shared__ __attribute__((aligned(16))) uint16_t as[3][kBigTile * kBigKc];  // 3 x 32 KiB
+  __shared__ __attribute__((aligned(16))) uint16_t bs[2][kBigTile * kBigKc];  // 2 x 32 KiB
   const int64_t grp = blockIdx.z;
   int64_t m0, n0;
   bool mirror = false;
@@ -381,13 +377,12 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
   const uint32_t lb0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(bs[0] + 8 * wave * kBigKc));
   constexpr uint32_t kBufBytes = kBigTile * kBigKc * 2;
   constexpr uint32_t kBlkStride = 32 * kBigKc * 2;  // row blocks w and w + 4
-  auto dload = [&](int st, int buf) {
-    const int64_t k0 = (int64_t)st * kBigKc;
-#pragma unroll
-    for (int i = 0; i < kBigLoads; ++i) {
-      lds_dma16(ga[i] + k0, la0 + buf * kBufBytes + i * kBlkStride);
-      lds_dma16(gb[i] + k0, lb0 + buf * kBufBytes + i * kBlkStride);
-    }
+  // the direct loads of operand A (B) for step st into A buffer abuf (B buffer bbuf)
+  auto dload_a = [&](int st, int abuf, int i) {
+    lds_dma16(ga[i] + (int64_t)st * kBigKc, la0 + abuf * kBufBytes + i * kBlkStride);
+  };
+  auto dload_b = [&](int st, int bbuf, int i) {
+    lds_dma16(gb[i] + (int64_t)st * kBigKc, lb0 + bbuf * kBufBytes + i * kBlkStride);
   };
 
   // fragment (tile t, half q of sub-step u) of lane l: row 32 t + (l & 31)
@@ -395,21 +390,22 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
   // f(row) depends on l & 31 alone
   const int l32 = lane & 31, lh = lane >> 5;
   bf16x8_t fa[2][2][4], fb[2][2][4];
-  // read k (< 16) of sub-step u: half q = k >> 3, tile t = (k >> 1) & 3,
-  // operand B for even k, A for odd k
-  auto fread1 = [&](int p, int u, int k) {
-    const int buf = (u >> 1) & 1, q = k >> 3, t = (k >> 1) & 3;
+  // read k (< 16) of sub-step u from A buffer abuf and B buffer bbuf (those of
+  // step u >> 1): half q = k >> 3, tile t = (k >> 1) & 3, operand B for even
+  // k, A for odd k
+  auto fread1 = [&](int p, int u, int abuf, int bbuf, int k) {
+    const int q = k >> 3, t = (k >> 1) & 3;
     const int slot = big_slot(l32, 4 * (u & 1) + 2 * q + lh) * 8;
     if (k & 1)
       fa[p][q][t] = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const uint4*>(as[buf] + (128 * wm + 32 * t + l32) * kBigKc + slot));
+          bf16x8_t, *reinterpret_cast<const uint4*>(as[abuf] + (128 * wm + 32 * t + l32) * kBigKc + slot));
     else
       fb[p][q][t] = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const uint4*>(bs[buf] + (128 * wn + 32 * t + l32) * kBigKc + slot));
+          bf16x8_t, *reinterpret_cast<const uint4*>(bs[bbuf] + (128 * wn + 32 * t + l32) * kBigKc + slot));
   };
-  auto fread = [&](int p, int u) {
+  auto fread = [&](int p, int u, int abuf, int bbuf) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) fread1(p, u, k);
+    for (int k = 0; k < 16; ++k) fread1(p, u, abuf, bbuf, k);
   };
 
   f32x16_t acc[4][4];
@@ -431,60 +427,66 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
         for (int j = 0; j < 4; ++j) mfma(p, q, i, j);
   };
 
-  // Step S in two sub-steps.  First (fragments in set 0): read the second
-  // sub-step's fragments, one LDS read per MFMA over the first 16 MFMAs,
-  // then 16 MFMAs with no LDS read so that the reads have landed when the
-  // wave waits for this wave's loads of step S + 1 and the barrier ends the
-  // sub-step.  Second (set 1): the loads of step S + 2 go into buffer S & 1
-  // (its last fragments were read before that barrier) and the next step's
-  // first fragments are read, one load and one read per MFMA over the first
-  // 16 MFMAs, so the reads land during the last 16; no barrier.  The last steps load the last slice
-  // again (never read): with no branch around the loads the compiler waits
-  // for exactly the loads each step needs.  sched_barrier keeps each group
-  // where it is written.
-  auto step = [&](int S, int full) {
-    fread(1, 2 * S + 1);
-    mfmas(0);
+  // Step S in two sub-steps of 32 MFMAs (fragments in set 0, then set 1);
+  // step S's operands are in A buffer S % 3 and B buffer S % 2.
+  // * First sub-step: A's loads of step S + 2 go into A buffer (S + 2) % 3
+  //   (step S - 1's, last read before the barrier that ended step S - 1's
+  //   first sub-step), one per four MFMAs; the second sub-step's fragments
+  //   are read, one per MFMA over the first 16.  Then the wave waits for all
+  //   but those eight loads (step S + 1's A and B have landed) and the
+  //   barrier publishes them.
+  // * Second sub-step: B's loads of step S + 2 go into B buffer S % 2 (its
+  //   last fragments were read before that barrier), one per four MFMAs; the
+  //   next step's first fragments are read, one per MFMA over the first 16.
+  //   No barrier.
+  // A step's 64 KiB of direct loads thus spread over both sub-steps: the
+  // load path takes 64 bytes per clock per CU, half of what the MFMAs leave
+  // it per sub-step.  The last steps load the last slice again (never
+  // read): with no branch around the loads the compiler waits for exactly
+  // the loads each step needs.  sched_barrier keeps every group where it is
+  // written.
+  auto sub_step = [&](int p, bool first, int ld_st, int ld_buf, int u, int abuf, int bbuf) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMA
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<0>();  // this wave's loads of step S + 1 have landed
-    __syncthreads();
-
-    const int64_t k0 = (int64_t)min(S + 2, full - 1) * kBigKc;
-    const uint32_t boff = (uint32_t)(S & 1) * kBufBytes;
-#pragma unroll
-    for (int i = 0; i < kBigLoads; ++i) {
-      lds_dma16(ga[i] + k0, la0 + boff + i * kBlkStride);
-      fread1(0, 2 * S + 2, 2 * i);
-      mfma(1, 0, i >> 1, 2 * (i & 1));
-      __builtin_amdgcn_sched_barrier(0);
-      lds_dma16(gb[i] + k0, lb0 + boff + i * kBlkStride);
-      fread1(0, 2 * S + 2, 2 * i + 1);
-      mfma(1, 0, i >> 1, 2 * (i & 1) + 1);
+    for (int n = 0; n < 32; ++n) {
+      if (n % 4 == 0) {
+        if (first)
+          dload_a(ld_st, ld_buf, n / 4);
+        else
+          dload_b(ld_st, ld_buf, n / 4);
+      }
+      if (n < 16) fread1(p ^ 1, u, abuf, bbuf, n);
+      mfma(p, n >> 4, (n >> 2) & 3, n & 3);
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mfma(1, 1, i, j);
-    __builtin_amdgcn_sched_barrier(0);
   };
 
   // step counts in 32 bits (the launcher keeps K below 2^31)
   const int full = (int)(k_len / kBigKc);
   if (full > 0) {
-    dload(0, 0);
-    dload(min(1, full - 1), 1);
+#pragma unroll
+    for (int i = 0; i < kBigLoads; ++i) dload_a(0, 0, i);
+#pragma unroll
+    for (int i = 0; i < kBigLoads; ++i) dload_b(0, 0, i);
+#pragma unroll
+    for (int i = 0; i < kBigLoads; ++i) dload_a(min(1, full - 1), 1, i);
+#pragma unroll
+    for (int i = 0; i < kBigLoads; ++i) dload_b(min(1, full - 1), 1, i);
     wait_vmcnt<2 * kBigLoads>();  // step 0 has landed
     __syncthreads();
-    fread(0, 0);
+    fread(0, 0, 0, 0);
   }
-  for (int S = 0; S < full; ++S) step(S, full);
+  int a_cur = 0, a_nxt = 1, a_ld = 2;  // S % 3, (S + 1) % 3, (S + 2) % 3
+  for (int S = 0; S < full; ++S) {
+    const int ld = min(S + 2, full - 1);
+    sub_step(0, true, ld, a_ld, 2 * S + 1, a_cur, S & 1);
+    wait_vmcnt<kBigLoads>();  // all but this sub-step's loads: step S + 1 has landed
+    __syncthreads();
+    sub_step(1, false, ld, S & 1, 2 * S + 2, a_nxt, (S + 1) & 1);
+    const int t3 = a_cur;
+    a_cur = a_nxt;
+    a_nxt = a_ld;
+    a_ld = t3;
+  }
   if ((int64_t)full * kBigKc < k_len) {  // the partial last step, through registers
     wait_vmcnt<0>();  // no direct load still lands
     __syncthreads();
@@ -500,10 +502,10 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
       *reinterpret_cast<uint4*>(&bs[0][(lrow + 32 * i) * kBigKc + lslot]) = vb;
     }
     __syncthreads();
-    fread(0, 0);
+    fread(0, 0, 0, 0);
     mfmas(0);
     if (k_len - k0 > kBigKc / 2) {  // the second half holds tokens too
-      fread(0, 1);
+      fread(0, 1, 0, 0);
       mfmas(0);
     }
   }
