@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void hessian_tm_kernel(const T* __restric
                                                               float beta,
                                                               float* __restrict__ h, int64_t h_gstride,
                                                               const int64_t* __restrict__ counts,
-                                                              float* __restrict__ ws) {
+                                                              float* __restrict__ ws, uint32_t* __restrict__ snap) {
   using S = TmShape<T>;
   __shared__ __attribute__((aligned(16))) T tile[2][S::kTok * kPitch];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -340,6 +340,13 @@ __global__ __launch_bounds__(kThreads) void hessian_tm_kernel(const T* __restric
   int64_t t0, t1, r0 = 0, r1 = 0;
   const T* seg;
   if constexpr (kRagged) {
+    // the group's token count before this call, for the slice-sum kernel
+    // (which also updates it); halves of the int64 at 4-byte alignment
+    if (snap != nullptr && s == 0 && q == 0 && threadIdx.x == 0) {
+      const uint64_t n_old = (uint64_t)counts[grp];
+      snap[2 * grp] = (uint32_t)n_old;
+      snap[2 * grp + 1] = (uint32_t)(n_old >> 32);
+    }
     ragged_range(offsets, grp, n_rows, r0, r1);
     const int64_t per = ragged_per(r1 - r0, nsplit, slice_rows);
     t0 = r0 + s * per;
@@ -400,20 +407,51 @@ __global__ __launch_bounds__(kThreads) void hessian_tm_kernel(const T* __restric
   }
 }
 
+// One workgroup per (group, kFinBlocks consecutive blocks): each thread sums
+// entry e of its blocks over the group's slices in slice order (the loads
+// of all its blocks for one slice in flight together), stores h, and the
+// group's first workgroup then sets the count from the snapshot the main
+// kernel took (every workgroup of the group reads the snapshot, never the
+// count it updates).
+constexpr int kFinBlocks = 8;
+
 __global__ __launch_bounds__(kThreads) void hessian_ragged_finalize_kernel(
     const float* __restrict__ ws, int64_t nsplit, int64_t slice_rows, int64_t n_groups, int64_t nb, int64_t n_rows,
-    const int64_t* __restrict__ offsets, const int64_t* __restrict__ counts, float* __restrict__ h,
-    int64_t h_gstride) {
-  const int64_t blk = blockIdx.x;  // grp * nb + b
-  const int64_t grp = blk / nb, b = blk % nb;
+    const int64_t* __restrict__ offsets, const uint32_t* __restrict__ snap, int64_t* __restrict__ counts,
+    float* __restrict__ h, int64_t h_gstride) {
+  const int64_t chunks = (nb + kFinBlocks - 1) / kFinBlocks;
+  const int64_t grp = blockIdx.x / chunks, c = blockIdx.x % chunks;
   const int e = threadIdx.x;
   int64_t r0, r1;
   ragged_range(offsets, grp, n_rows, r0, r1);
   const int64_t n_g = r1 - r0;
+  if (n_g == 0) return;  // h and the count stay as they are
   const int64_t per = ragged_per(n_g, nsplit, slice_rows);
-  const int64_t used = n_g > 0 ? (n_g + per - 1) / per : 0;  // slices the group wrote, in order
-  const float v = used > 0 ? sum_slices(ws + blk * 256 + e, n_groups * nb * 256, used) : 0.0f;
-  ragged_store(h + grp * h_gstride + b * 256 + e, v, n_g, counts, grp);
+  const int64_t used = (n_g + per - 1) / per;  // slices the group wrote, in order
+  const int64_t b0 = c * kFinBlocks;
+  const int nblk = (int)min((int64_t)kFinBlocks, nb - b0);
+  const int64_t sstride = n_groups * nb * 256;
+  const float* p = ws + (grp * nb + b0) * 256 + e;
+  float v[kFinBlocks];
+#pragma unroll
+  for (int i = 0; i < kFinBlocks; ++i) v[i] = i < nblk ? p[i * 256] : 0.0f;
+  for (int64_t sl = 1; sl < used; ++sl) {
+    float t[kFinBlocks];
+#pragma unroll
+    for (int i = 0; i < kFinBlocks; ++i) t[i] = i < nblk ? p[sl * sstride + i * 256] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < kFinBlocks; ++i) v[i] += t[i];
+  }
+  int64_t n_old = 0;
+  if (counts != nullptr) n_old = (int64_t)(((uint64_t)snap[2 * grp + 1] << 32) | snap[2 * grp]);
+  float* hp = h + grp * h_gstride + b0 * 256 + e;
+#pragma unroll
+  for (int i = 0; i < kFinBlocks; ++i) {
+    if (i >= nblk) break;
+    hp[i * 256] = counts != nullptr ? ((float)n_old * hp[i * 256] + v[i]) / (float)(n_old + n_g)
+                                    : v[i] / (float)n_g;
+  }
+  if (counts != nullptr && c == 0 && e == 0) counts[grp] = n_old + n_g;
 }
 
 // counts[g] += n_g, after every block of the group has read the old count.
@@ -470,7 +508,7 @@ hipError_t launch_typed(const HessianArgs& a, const HessianPlan& p, hipStream_t 
     const int64_t grid = a.n_groups * ((nb + 3) / 4) * p.nsplit;
     hessian_tm_kernel<T, kVec, false><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
         x, a.ld, a.gstride, a.n_tok, 0, nullptr, a.c_in, nb, a.n_groups, p.nsplit, p.chunk, 0, a.alpha, a.beta,
-        a.h, a.h_gstride, nullptr, ws);
+        a.h, a.h_gstride, nullptr, ws, nullptr);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.nsplit == 1) return err;
@@ -485,16 +523,20 @@ hipError_t launch_ragged_typed(const HessianRaggedArgs& a, const RaggedPlan& p, 
   const int64_t nsplit = p.nsplit;
   const int64_t grid = a.n_groups * ((nb + 3) / 4) * nsplit;
   float* ws = nsplit > 1 ? static_cast<float*>(a.ws) : nullptr;
+  // after the slice partials: the groups' counts before this call
+  uint32_t* snap = (ws != nullptr && a.counts != nullptr)
+                       ? reinterpret_cast<uint32_t*>(ws + nsplit * a.n_groups * nb * 256)
+                       : nullptr;
   hessian_tm_kernel<T, kVec, true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
       static_cast<const T*>(a.x), a.ld, 0, 0, a.n_rows, a.offsets, a.c_in, nb, a.n_groups, nsplit, 0, p.slice_rows,
-      1.0f, 0.0f, a.h, a.h_gstride, a.counts, ws);
+      1.0f, 0.0f, a.h, a.h_gstride, a.counts, ws, snap);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (nsplit > 1) {
-    hessian_ragged_finalize_kernel<<<dim3((unsigned)(a.n_groups * nb)), dim3(kThreads), 0, stream>>>(
-        ws, nsplit, p.slice_rows, a.n_groups, nb, a.n_rows, a.offsets, a.counts, a.h, a.h_gstride);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
+  if (nsplit > 1) {  // the slice sums also update the counts
+    const int64_t chunks = (nb + kFinBlocks - 1) / kFinBlocks;
+    hessian_ragged_finalize_kernel<<<dim3((unsigned)(a.n_groups * chunks)), dim3(kThreads), 0, stream>>>(
+        ws, nsplit, p.slice_rows, a.n_groups, nb, a.n_rows, a.offsets, snap, a.counts, a.h, a.h_gstride);
+    return hipGetLastError();
   }
   if (a.counts) {
     hessian_ragged_counts_kernel<<<dim3((unsigned)((a.n_groups + kThreads - 1) / kThreads)), dim3(kThreads), 0,
@@ -543,7 +585,10 @@ RaggedPlan hessian_ragged_plan(int64_t c_in, int64_t n_rows, int64_t n_groups, i
 size_t hessian_ragged_ws_bytes(int64_t c_in, int64_t n_rows, int64_t n_groups, int64_t max_group_rows) {
   const RaggedPlan p = hessian_ragged_plan(c_in, n_rows, n_groups, max_group_rows, true);
   if (p.nsplit <= 1) return 0;
-  return (size_t)p.nsplit * (size_t)n_groups * (size_t)(c_in / 16) * 256u * sizeof(float);
+  // slice partials, then each group's token count before the call (two
+  // 32-bit halves, for the running mean)
+  return (size_t)p.nsplit * (size_t)n_groups * (size_t)(c_in / 16) * 256u * sizeof(float) +
+         (size_t)n_groups * 2u * sizeof(uint32_t);
 }
 
 hipError_t launch_hessian_ragged(const HessianRaggedArgs& a, hipStream_t stream) {

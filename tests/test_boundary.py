@@ -288,11 +288,11 @@ def test_ragged_hessian_validation(lib):
     assert call(ws=None, wsb=8) == NULL
     assert call(mx=-1) == SHAPE
     big = lib.lh_hessian_ragged_workspace_bytes(4096, 1 << 16, 2, 0)
-    assert big > 0 and big % (256 * 4) == 0
+    assert big > 0 and (big - 2 * 8) % (256 * 4) == 0  # slice partials, then two groups' counts
     assert call(c_in=4096, ld=4096, rows=1 << 16, g=2, hs=256 * 256, ws=P(FAKE), wsb=big - 4) == WORKSPACE
     assert lib.lh_hessian_ragged_workspace_bytes(2048, 32768, 64, 0) == 0   # ~512 rows per group: one pass
     # a known largest group (4230 rows): five 1024-row slices per group
-    assert lib.lh_hessian_ragged_workspace_bytes(2048, 32768, 64, 4230) == 5 * 64 * 128 * 256 * 4
+    assert lib.lh_hessian_ragged_workspace_bytes(2048, 32768, 64, 4230) == 5 * 64 * 128 * 256 * 4 + 64 * 8
     assert lib.lh_hessian_ragged_workspace_bytes(2048, 32768, 64, 1000) == 0
     assert call(g=0) == OK and call(c_in=0) == OK
 
