@@ -386,8 +386,8 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
   };
 
   // fragment (tile t, half q of sub-step u) of lane l: row 32 t + (l & 31)
-  // (+128 w), 16-byte chunk 4 (u & 1) + 2 q + (l >> 5) of buffer (u >> 1) & 1;
-  // f(row) depends on l & 31 alone
+  // (+128 w), 16-byte chunk 4 (u & 1) + 2 q + (l >> 5) of the buffers that
+  // hold step u >> 1; f(row) depends on l & 31 alone
   const int l32 = lane & 31, lh = lane >> 5;
   bf16x8_t fa[2][2][4], fb[2][2][4];
   // read k (< 16) of sub-step u from A buffer abuf and B buffer bbuf (those of
@@ -516,12 +516,13 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
     // C^T for the tile: n < c always holds here (tx < ty, so tx is not the
     // last tile column); m may pass c in the last tile row.  Per 32-row
     // slab i a wave writes its 128 x 32 block transposed into its own LDS
-    // region (waves 0, 1 in as, 2, 3 in bs; 128 rows of kMirPitch floats),
-    // then stores row n of it, 32 consecutive m, as 8 lanes x 16 bytes.
+    // region (128 rows of kMirPitch floats, 18 KiB: waves 0, 1 at the start
+    // of as, waves 2, 3 at the start of bs), then stores row n of it, 32
+    // consecutive m, as 8 lanes x 16 bytes.
     wait_vmcnt<0>();  // the last steps' direct loads have landed in LDS
     __syncthreads();  // and every wave has finished reading its fragments
     constexpr int kMirPitch = 36;
-    float* T = reinterpret_cast<float*>(wave < 2 ? as[0] : bs[0]) + (wave & 1) * (128 * kMirPitch);
+    float* T = reinterpret_cast<float*>(wave < 2 ? &as[0][0] : &bs[0][0]) + (wave & 1) * (128 * kMirPitch);
     const int rr = lane >> 3, cc = 4 * (lane & 7);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
