@@ -322,10 +322,8 @@ def full_hessian_wide(lh, work, x) -> dict:
     hf = torch.empty((1, c_in, c_in), dtype=torch.float32, device=x.device)
     t = graph_time(lambda: lh.lh_full_hessian(x, h=hf), reps=3)
     del hf
-    bt = (c_in + 255) // 256
     sym = float(c_in) * (c_in + 1) * n / (t / 1e3) / 1e12
     return {"workload": work.description, "c_in": c_in, "n_tokens": n, "ms": t,
-            "tiles": {"computed": bt * (bt + 1) // 2, "square": bt * bt},
             "full_product_tflops": 2.0 * c_in * c_in * n / (t / 1e3) / 1e12,
             "symmetric_tflops": sym, "symmetric_frac_bf16_peak": sym / 2500.0}
 
@@ -350,7 +348,12 @@ def diagnostics(lh, work, w, x, h, amax, idx, err, bam) -> dict:
     grid = torch.tensor([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=torch.float64)
     centers = (torch.arange(160, dtype=torch.float64) + 0.5) / 20.0
     near_grid = (centers[:, None] - grid[None, :]).abs().min(1).values < 0.05
-    out = {"full_hessian_ms": t_hf, "full_hessian_tflops": 2.0 * c_in * c_in * n / (t_hf / 1e3) / 1e12}
+    sym = float(c_in) * (c_in + 1) * n / (t_hf / 1e3) / 1e12
+    out = {"full_hessian_ms": t_hf, "full_hessian_tflops": 2.0 * c_in * c_in * n / (t_hf / 1e3) / 1e12,
+           "full_hessian_symmetric_tflops": sym, "full_hessian_symmetric_frac_bf16_peak": sym / 2500.0,
+           "full_hessian_note": "full_hessian_tflops counts the full product (2 C_in^2 N flop); wide bf16 layers "
+                                "compute one triangle of tiles and mirror it, so the symmetric product's "
+                                "C_in (C_in + 1) N flop is the work no C_in x C_in result can avoid"}
     rules = {"local_hessian": (0, h), "mse": (0, None), "max": (1, h), "four_over_six": (2, None)}
     for name, (rule, hh) in rules.items():
         ri, re_, _ = lh.lh_select_scales(rule, w, hh, amax, best_idx=torch.empty_like(idx), best_err=True,

@@ -445,11 +445,12 @@ lh_status lh_fake_quant_nvfp4(const void *w, int w_dtype, int64_t c_out, int64_t
  * h_full[g][i * ld_h + j], ld_h >= c_in, group strides >= 0 (h groups must not
  * overlap).  With alpha = 1/N (or NaN, which the library replaces by
  * lh_hessian_alpha(NaN, n_tokens) = fl32(1/N)) its diagonal 16 x 16 blocks are
- * the local Hessians.  n_tokens = 0 writes zeros.  Where the lower triangle
- * of 256 x 256 output tiles takes fewer rounds of the GPU than the square
- * (wide or grouped bf16 layers), only that triangle is computed and each
- * off-diagonal tile is also written transposed, so those entries are exact
- * mirrors; otherwise h_full[i][j] and h_full[j][i] are computed separately.
+ * the local Hessians.  n_tokens = 0 writes zeros.  For bf16 layers with at
+ * least 128 output tiles of 256 x 256 (16-byte aligned rows), only the lower
+ * triangle of 256 x 256 or 192 x 192 tiles is computed and each off-diagonal
+ * tile is also written transposed, so entries outside the diagonal tiles are
+ * exact mirrors; otherwise h_full[i][j] and h_full[j][i] are computed
+ * separately.
  * Errors: LH_ERR_NULL, LH_ERR_SHAPE, LH_ERR_DTYPE, LH_ERR_ARG, LH_ERR_HIP.
  */
 lh_status lh_full_hessian(const void *x, int x_dtype, int64_t c_in, int64_t n_tokens, int64_t ld_x,

@@ -256,28 +256,27 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(LA la, LB lb, GemmArg
 }
 
 // Large-tile X X^T for bf16 X (the full Hessian of a wide layer), rows of
-// X 16-byte aligned.  A 256-thread workgroup owns a 256 x 256 tile of C and
-// its four waves 128 x 128 quadrants, each a 4 x 4 grid of 32 x 32 MFMA
-// tiles (v_mfma_f32_32x32x16_bf16: measured on MI355X at 2.2 PFLOP/s with
-// independent accumulators, against 1.4 for the 16 x 16 x 32 form; 256 fp32
-// accumulators per lane in the accumulation registers, one wave per SIMD).
-// Per 32-token sub-step a wave reads 16 KiB of operands from LDS for 32
-// MFMAs, 64 flop per LDS byte (the 64 x 64 tile above gets 16).
+// X 16-byte aligned.  A 256-thread workgroup owns a 256 x 256 (or 192 x 192)
+// tile of C and its four waves 128 x 128 (96 x 96) quadrants, each a 4 x 4
+// (3 x 3) grid of 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16: measured on
+// MI355X at 2.2 PFLOP/s with independent accumulators, against 1.4 for the
+// 16 x 16 x 32 form; up to 256 fp32 accumulators per lane in the
+// accumulation registers, one wave per SIMD).  Per 32-token sub-step a wave
+// of the 256 tile reads 16 KiB of operands from LDS for 32 MFMAs, 64 flop
+// per LDS byte (48 for the 192 tile; the 64 x 64 tile above gets 16).
 //
 // The operands come in 64-token steps: per row one whole 128-byte line, so
 // each L2 request carries a full line (with 32-token steps every request
 // was half a line, and the L2 request rate held the kernel back).  LDS
-// holds three buffers of operand A and two of B, 256 rows of 128 bytes
-// each (160 KiB), filled straight from global memory (no staging
-// registers); the 16-byte chunk c of row r sits at slot c ^ f(r),
+// holds three buffers of operand A and two of B, 256 (192) rows of 128
+// bytes each (160 KiB, or 120), filled straight from global memory (no
+// staging registers); the 16-byte chunk c of row r sits at slot c ^ f(r),
 // f(r) = ((r & 7) ^ (r >> 3)) & 7 over r mod 32, so the 8 (or 16) lanes
 // that LDS serves together read 8 (16) rows' chunk c from distinct banks.
 // The step loop below gives the schedule.  Tokens past the last whole step
 // go through one more step with checked register loads.  Rows past c_in
 // read row c_in - 1 (those outputs are not stored).
-constexpr int kBigTile = 256;
 constexpr int kBigKc = 64;                  // tokens per step (one 128-byte line of a bf16 row)
-constexpr int kBigLoads = kBigTile * (kBigKc / 8) / kThreads;  // 16-byte loads per operand per thread (8)
 
 __device__ __forceinline__ int big_slot(int row, int chunk) { return chunk ^ (((row & 7) ^ (row >> 3)) & 7); }
 
@@ -327,30 +326,27 @@ __device__ __forceinline__ void tri_tile(int64_t t, int64_t& ty, int64_t& tx) {
   tx = t - y * (y + 1) / 2;
 }
 
-// kSyrk: the grid walks the lower triangle of tiles (blockIdx.x = t above);
-// an off-diagonal tile also writes its transpose (H is symmetric), staged
-// through LDS so that the transposed rows go out as whole 128-byte lines.
-// vec_h: H rows are 16-byte aligned (ldh, gstride_h multiples of 4).
-template <bool kSyrk>
+// The grid walks the lower triangle of tiles (blockIdx.x = t above, one
+// group per blockIdx.z); an off-diagonal tile also writes its transpose (H is
+// symmetric), staged through LDS so that the transposed rows go out as whole
+// 128-byte lines.  kWT MFMA tiles per wave and side: 256 x 256 workgroup
+// tiles (kWT = 4) or 192 x 192 (kWT = 3).  vec_h: H rows are 16-byte aligned
+// (ldh, gstride_h multiples of 4).
+template <int kWT>
 __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __restrict__ x, int64_t ld,
                                                               int64_t gstride, int64_t c, int64_t k_len,
                                                               float alpha, float* __restrict__ h, int64_t ldh,
                                                               int64_t gstride_h, bool vec_h) {
-  __shared__ __attribute__((aligned(16))) uint16_t as[3][kBigTile * kBigKc];  // 3 x 32 KiB
-  __shared__ __attribute__((aligned(16))) uint16_t bs[2][kBigTile * kBigKc];  // 2 x 32 KiB
+  constexpr int kTile = 64 * kWT;    // workgroup tile (256 or 192)
+  constexpr int kWTile = 32 * kWT;   // wave tile
+  constexpr int kLoads = kTile * (kBigKc / 8) / kThreads;  // direct loads per operand per wave and step (2 kWT)
+  __shared__ __attribute__((aligned(16))) uint16_t as[3][kTile * kBigKc];  // 3 x 32 (24) KiB
+  __shared__ __attribute__((aligned(16))) uint16_t bs[2][kTile * kBigKc];  // 2 x 32 (24) KiB
   const int64_t grp = blockIdx.z;
-  int64_t m0, n0;
-  bool mirror = false;
-  if constexpr (kSyrk) {
-    int64_t ty, tx;
-    tri_tile(blockIdx.x, ty, tx);
-    m0 = ty * kBigTile;
-    n0 = tx * kBigTile;
-    mirror = ty != tx;
-  } else {
-    m0 = (int64_t)blockIdx.y * kBigTile;
-    n0 = (int64_t)blockIdx.x * kBigTile;
-  }
+  int64_t ty, tx;
+  tri_tile(blockIdx.x, ty, tx);
+  const int64_t m0 = ty * kTile, n0 = tx * kTile;
+  const bool mirror = ty != tx;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const uint16_t* xg = x + grp * gstride;
@@ -359,14 +355,14 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
   // of 128 bytes), lane l writing bytes 16 l .. 16 l + 15, i.e. row l >> 3,
   // slot l & 7.  So lane l fetches chunk (l & 7) ^ f(row) of its row, and
   // the 8 lanes of a row together fetch its whole line.  Wave w fills row
-  // blocks w + 4 i (i < 8) of both operand tiles; f depends on the row mod
+  // blocks w + 4 i (i < 2 kWT) of both operand tiles; f depends on the row mod
   // 32 = 8 w + (l >> 3) alone.
   const int drow = lane >> 3;
   const int dcol = big_slot(8 * wave + drow, lane & 7) * 8;
-  const uint16_t* ga[kBigLoads];
-  const uint16_t* gb[kBigLoads];
+  const uint16_t* ga[kLoads];
+  const uint16_t* gb[kLoads];
 #pragma unroll
-  for (int i = 0; i < kBigLoads; ++i) {
+  for (int i = 0; i < kLoads; ++i) {
     const int64_t r = 8 * (wave + 4 * i) + drow;
     ga[i] = xg + min(m0 + r, c - 1) * ld + dcol;
     gb[i] = xg + min(n0 + r, c - 1) * ld + dcol;
@@ -375,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
   // is i KiB x 4 further on
   const uint32_t la0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(as[0] + 8 * wave * kBigKc));
   const uint32_t lb0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(bs[0] + 8 * wave * kBigKc));
-  constexpr uint32_t kBufBytes = kBigTile * kBigKc * 2;
+  constexpr uint32_t kBufBytes = kTile * kBigKc * 2;
   constexpr uint32_t kBlkStride = 32 * kBigKc * 2;  // row blocks w and w + 4
   // the direct loads of operand A (B) for step st into A buffer abuf (B buffer bbuf)
   auto dload_a = [&](int st, int abuf, int i) {
@@ -386,33 +382,33 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
   };
 
   // fragment (tile t, half q of sub-step u) of lane l: row 32 t + (l & 31)
-  // (+128 w), 16-byte chunk 4 (u & 1) + 2 q + (l >> 5) of the buffers that
+  // (+ 32 kWT w), 16-byte chunk 4 (u & 1) + 2 q + (l >> 5) of the buffers that
   // hold step u >> 1; f(row) depends on l & 31 alone
   const int l32 = lane & 31, lh = lane >> 5;
-  bf16x8_t fa[2][2][4], fb[2][2][4];
-  // read k (< 16) of sub-step u from A buffer abuf and B buffer bbuf (those of
-  // step u >> 1): half q = k >> 3, tile t = (k >> 1) & 3, operand B for even
-  // k, A for odd k
+  bf16x8_t fa[2][2][kWT], fb[2][2][kWT];
+  // read k (< 4 kWT) of sub-step u from A buffer abuf and B buffer bbuf
+  // (those of step u >> 1): half q = k / (2 kWT), tile t = (k / 2) % kWT,
+  // operand B for even k, A for odd k
   auto fread1 = [&](int p, int u, int abuf, int bbuf, int k) {
-    const int q = k >> 3, t = (k >> 1) & 3;
+    const int q = k / (2 * kWT), t = (k >> 1) % kWT;
     const int slot = big_slot(l32, 4 * (u & 1) + 2 * q + lh) * 8;
     if (k & 1)
       fa[p][q][t] = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const uint4*>(as[abuf] + (128 * wm + 32 * t + l32) * kBigKc + slot));
+          bf16x8_t, *reinterpret_cast<const uint4*>(as[abuf] + (kWTile * wm + 32 * t + l32) * kBigKc + slot));
     else
       fb[p][q][t] = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const uint4*>(bs[bbuf] + (128 * wn + 32 * t + l32) * kBigKc + slot));
+          bf16x8_t, *reinterpret_cast<const uint4*>(bs[bbuf] + (kWTile * wn + 32 * t + l32) * kBigKc + slot));
   };
   auto fread = [&](int p, int u, int abuf, int bbuf) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) fread1(p, u, abuf, bbuf, k);
+    for (int k = 0; k < 4 * kWT; ++k) fread1(p, u, abuf, bbuf, k);
   };
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[kWT][kWT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kWT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kWT; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
   auto mfma = [&](int p, int q, int i, int j) {
@@ -422,22 +418,22 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kWT; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mfma(p, q, i, j);
+        for (int j = 0; j < kWT; ++j) mfma(p, q, i, j);
   };
 
-  // Step S in two sub-steps of 32 MFMAs (fragments in set 0, then set 1);
+  // Step S in two sub-steps of 2 kWT^2 MFMAs (fragments in set 0, then set 1);
   // step S's operands are in A buffer S % 3 and B buffer S % 2.
   // * First sub-step: A's loads of step S + 2 go into A buffer (S + 2) % 3
   //   (step S - 1's, last read before the barrier that ended step S - 1's
-  //   first sub-step), one per four MFMAs; the second sub-step's fragments
-  //   are read, one per MFMA over the first 16.  Then the wave waits for all
+  //   first sub-step), one per kWT MFMAs; the second sub-step's fragments
+  //   are read, one per MFMA over the first 4 kWT.  Then the wave waits for all
   //   but those eight loads (step S + 1's A and B have landed) and the
   //   barrier publishes them.
   // * Second sub-step: B's loads of step S + 2 go into B buffer S % 2 (its
-  //   last fragments were read before that barrier), one per four MFMAs; the
-  //   next step's first fragments are read, one per MFMA over the first 16.
+  //   last fragments were read before that barrier), one per kWT MFMAs; the
+  //   next step's first fragments are read, one per MFMA over the first 4 kWT.
   //   No barrier.
   // A step's 64 KiB of direct loads thus spread over both sub-steps: the
   // load path takes 64 bytes per clock per CU, half of what the MFMAs leave
@@ -447,15 +443,15 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
   // written.
   auto sub_step = [&](int p, bool first, int ld_st, int ld_buf, int u, int abuf, int bbuf) {
 #pragma unroll
-    for (int n = 0; n < 32; ++n) {
-      if (n % 4 == 0) {
+    for (int n = 0; n < 2 * kWT * kWT; ++n) {
+      if (n % kWT == 0) {
         if (first)
-          dload_a(ld_st, ld_buf, n / 4);
+          dload_a(ld_st, ld_buf, n / kWT);
         else
-          dload_b(ld_st, ld_buf, n / 4);
+          dload_b(ld_st, ld_buf, n / kWT);
       }
-      if (n < 16) fread1(p ^ 1, u, abuf, bbuf, n);
-      mfma(p, n >> 4, (n >> 2) & 3, n & 3);
+      if (n < 4 * kWT) fread1(p ^ 1, u, abuf, bbuf, n);
+      mfma(p, n / (kWT * kWT), (n % (kWT * kWT)) / kWT, n % kWT);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -464,14 +460,14 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
   const int full = (int)(k_len / kBigKc);
   if (full > 0) {
 #pragma unroll
-    for (int i = 0; i < kBigLoads; ++i) dload_a(0, 0, i);
+    for (int i = 0; i < kLoads; ++i) dload_a(0, 0, i);
 #pragma unroll
-    for (int i = 0; i < kBigLoads; ++i) dload_b(0, 0, i);
+    for (int i = 0; i < kLoads; ++i) dload_b(0, 0, i);
 #pragma unroll
-    for (int i = 0; i < kBigLoads; ++i) dload_a(min(1, full - 1), 1, i);
+    for (int i = 0; i < kLoads; ++i) dload_a(min(1, full - 1), 1, i);
 #pragma unroll
-    for (int i = 0; i < kBigLoads; ++i) dload_b(min(1, full - 1), 1, i);
-    wait_vmcnt<2 * kBigLoads>();  // step 0 has landed
+    for (int i = 0; i < kLoads; ++i) dload_b(min(1, full - 1), 1, i);
+    wait_vmcnt<2 * kLoads>();  // step 0 has landed
     __syncthreads();
     fread(0, 0, 0, 0);
   }
@@ -479,7 +475,7 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
   for (int S = 0; S < full; ++S) {
     const int ld = min(S + 2, full - 1);
     sub_step(0, true, ld, a_ld, 2 * S + 1, a_cur, S & 1);
-    wait_vmcnt<kBigLoads>();  // all but this sub-step's loads: step S + 1 has landed
+    wait_vmcnt<kLoads>();  // all but this sub-step's loads: step S + 1 has landed
     __syncthreads();
     sub_step(1, false, ld, S & 1, 2 * S + 2, a_nxt, (S + 1) & 1);
     const int t3 = a_cur;
@@ -494,7 +490,7 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
     const int lrow = tid >> 3, lchunk = tid & 7;
     const int lslot = big_slot(lrow, lchunk) * 8;
 #pragma unroll
-    for (int i = 0; i < kBigLoads; ++i) {
+    for (int i = 0; i < kLoads; ++i) {
       const int64_t ra = min(m0 + lrow + 32 * i, c - 1), rb = min(n0 + lrow + 32 * i, c - 1);
       const uint4 va = big_tail_chunk(xg + ra * ld + 8 * lchunk + k0, k0 + 8 * lchunk, k_len);
       const uint4 vb = big_tail_chunk(xg + rb * ld + 8 * lchunk + k0, k0 + 8 * lchunk, k_len);
@@ -510,36 +506,36 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
     }
   }
 
-  // lane holds C[m0 + 128 wm + 32 i + 8 (e / 4) + 4 (l >> 5) + e % 4][n0 + 128 wn + 32 j + (l & 31)]
+  // lane holds C[m0 + 32 kWT wm + 32 i + 8 (e / 4) + 4 (l >> 5) + e % 4][n0 + 32 kWT wn + 32 j + (l & 31)]
   float* C = h + grp * gstride_h;
   if (mirror) {
     // C^T for the tile: n < c always holds here (tx < ty, so tx is not the
     // last tile column); m may pass c in the last tile row.  Per 32-row
-    // slab i a wave writes its 128 x 32 block transposed into its own LDS
-    // region (128 rows of kMirPitch floats, 18 KiB: waves 0, 1 at the start
-    // of as, waves 2, 3 at the start of bs), then stores row n of it, 32
-    // consecutive m, as 8 lanes x 16 bytes.
+    // slab i a wave writes its 32 kWT x 32 block transposed into its own LDS
+    // region (32 kWT rows of kMirPitch floats, at most 18 KiB: waves 0, 1 at
+    // the start of as, waves 2, 3 at the start of bs), then stores row n of
+    // it, 32 consecutive m, as 8 lanes x 16 bytes.
     wait_vmcnt<0>();  // the last steps' direct loads have landed in LDS
     __syncthreads();  // and every wave has finished reading its fragments
     constexpr int kMirPitch = 36;
-    float* T = reinterpret_cast<float*>(wave < 2 ? &as[0][0] : &bs[0][0]) + (wave & 1) * (128 * kMirPitch);
+    float* T = reinterpret_cast<float*>(wave < 2 ? &as[0][0] : &bs[0][0]) + (wave & 1) * (kWTile * kMirPitch);
     const int rr = lane >> 3, cc = 4 * (lane & 7);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kWT; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < kWT; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           *reinterpret_cast<float4*>(&T[(32 * j + l32) * kMirPitch + 8 * q + 4 * lh]) =
               make_float4(alpha * acc[i][j][4 * q], alpha * acc[i][j][4 * q + 1], alpha * acc[i][j][4 * q + 2],
                           alpha * acc[i][j][4 * q + 3]);
       __syncthreads();
-      const int64_t m = m0 + 128 * wm + 32 * i + cc;
+      const int64_t m = m0 + kWTile * wm + 32 * i + cc;
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
+      for (int s = 0; s < 4 * kWT; ++s) {
         const int r = 8 * s + rr;
         const float4 v = *reinterpret_cast<const float4*>(&T[r * kMirPitch + cc]);
-        float* dst = C + (n0 + 128 * wn + r) * ldh + m;
+        float* dst = C + (n0 + kWTile * wn + r) * ldh + m;
         if (vec_h && m + 3 < c) {
           *reinterpret_cast<float4*>(dst) = v;
         } else {
@@ -553,14 +549,14 @@ __global__ __launch_bounds__(kThreads, 1) void xxt_big_kernel(const uint16_t* __
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kWT; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int64_t m = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
+      const int64_t m = m0 + kWTile * wm + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
       if (m >= c) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t n = n0 + 128 * wn + 32 * j + l32;
+      for (int j = 0; j < kWT; ++j) {
+        const int64_t n = n0 + kWTile * wn + 32 * j + l32;
         if (n < c) C[m * ldh + n] = alpha * acc[i][j][e];
       }
     }
@@ -1003,20 +999,22 @@ __global__ __launch_bounds__(kThreads) void gptq_trailing_kernel(float* __restri
 template <typename T, bool kVec>
 hipError_t launch_full_hessian_typed(const FullHessianArgs& a, hipStream_t stream) {
   if constexpr (sizeof(T) == 2 && kVec) {
-    // 256 x 256 tiles where they fill at least half of the 256 CUs
-    const int64_t bt = (a.c_in + kBigTile - 1) / kBigTile;
-    if (bt * bt * a.n_groups >= 128 && a.n_tok < ((int64_t)1 << 31)) {
-      // one triangle of tiles, mirrored, where it takes fewer rounds of the
-      // 256 CUs (one workgroup each) than the whole square
-      const int64_t tri = bt * (bt + 1) / 2;
-      const bool syrk = (tri * a.n_groups + 255) / 256 < (bt * bt * a.n_groups + 255) / 256 && tri < ((int64_t)1 << 31);
+    // Wide layers (at least 128 tiles of 256 x 256 in the square) on the
+    // large-tile kernel: the lower triangle of 256 x 256 tiles, or of
+    // 192 x 192 where its rounds of the 256 CUs (one workgroup each) cost
+    // less, a 192 tile's work counted at 0.5625 x 1.15 of a 256 tile's (its
+    // smaller MFMA grid reads more LDS per MFMA; measured 1.16-1.23).
+    const int64_t n4 = (a.c_in + 255) / 256, n3 = (a.c_in + 191) / 192;
+    if (n4 * n4 * a.n_groups >= 128 && a.n_tok < ((int64_t)1 << 31) && n3 * (n3 + 1) / 2 < ((int64_t)1 << 31)) {
       const bool vec_h = reinterpret_cast<uintptr_t>(a.h) % 16 == 0 && a.ld_h % 4 == 0 && a.gstride_h % 4 == 0;
       const uint16_t* xx = static_cast<const uint16_t*>(a.x);
-      if (syrk)
-        xxt_big_kernel<true><<<dim3((unsigned)tri, 1, (unsigned)a.n_groups), dim3(kThreads), 0, stream>>>(
+      const int64_t t4 = n4 * (n4 + 1) / 2, t3 = n3 * (n3 + 1) / 2;
+      const int64_t r4 = (t4 * a.n_groups + 255) / 256, r3 = (t3 * a.n_groups + 255) / 256;
+      if ((double)r3 * 0.5625 * 1.15 < (double)r4)
+        xxt_big_kernel<3><<<dim3((unsigned)t3, 1, (unsigned)a.n_groups), dim3(kThreads), 0, stream>>>(
             xx, a.ld_x, a.gstride_x, a.c_in, a.n_tok, a.alpha, a.h, a.ld_h, a.gstride_h, vec_h);
       else
-        xxt_big_kernel<false><<<dim3((unsigned)bt, (unsigned)bt, (unsigned)a.n_groups), dim3(kThreads), 0, stream>>>(
+        xxt_big_kernel<4><<<dim3((unsigned)t4, 1, (unsigned)a.n_groups), dim3(kThreads), 0, stream>>>(
             xx, a.ld_x, a.gstride_x, a.c_in, a.n_tok, a.alpha, a.h, a.ld_h, a.gstride_h, vec_h);
       return hipGetLastError();
     }

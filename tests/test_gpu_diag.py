@@ -98,8 +98,9 @@ def test_diagnostics_ragged(lh, G, c_out, c_in, n, dtype):
 
 @pytest.mark.parametrize("G,c_in,n", [(8, 1040, 304), (4, 784, 77), (1, 4096, 96), (2, 2048, 40), (1, 4096, 256)])
 def test_full_hessian_large_tiles(lh, G, c_in, n):
-    """Shapes whose full Hessian runs on the 256 x 256-tile kernel (at least
-    128 tiles): a ragged last tile row and column, a partial last 64-token
+    """Shapes whose full Hessian runs on the large-tile kernel (at least 128
+    tiles of 256 x 256 in the square): a ragged last tile row and column, a
+    partial last 64-token
     step with 16-byte aligned rows (304 = 4 x 64 + 48, 96 = 64 + 32),
     fewer tokens than one step (40), whole steps only (256), unaligned rows
     (N = 77), and a whole 4096-channel layer; every entry against the
@@ -112,15 +113,17 @@ def test_full_hessian_large_tiles(lh, G, c_in, n):
         check_full_hessian(hf[g], x_np[g], c_in, n)
 
 
-@pytest.mark.parametrize("G,c_in,n,pad", [(1, 5120, 96, 0), (3, 2608, 200, 0), (3, 2608, 200, 1), (3, 2608, 40, 0)])
+@pytest.mark.parametrize("G,c_in,n,pad", [(1, 5120, 96, 0), (3, 2608, 200, 0), (3, 2608, 200, 1), (3, 2608, 40, 0),
+                                          (1, 4096, 200, 0), (2, 2048, 72, 1)])
 def test_full_hessian_syrk(lh, G, c_in, n, pad):
-    """Shapes whose lower triangle of 256 x 256 tiles fits in fewer rounds of
-    the CUs than the whole square, so the kernel computes one triangle and
-    mirrors it: a ragged last tile row (2608 = 10 x 256 + 48), several groups,
-    a partial last K step (or only one, N = 40), and H rows that are not
-    16-byte aligned (pad = 1:
+    """The large-tile kernel computes the lower triangle of output tiles and
+    mirrors it: 256 x 256 tiles (5120; 2608 = 10 x 256 + 48, a ragged last
+    tile row, several groups) or 192 x 192 tiles where that takes cheaper
+    rounds (4096 = 21 x 192 + 64; 2048 in two groups); partial last K steps
+    (or only one, N = 40), and H rows that are not 16-byte aligned (pad = 1:
     row stride c_in + 1, scalar mirrored stores).  Every entry against the
-    oracle; entries outside the diagonal tiles are exact mirrors."""
+    oracle; entries outside the diagonal tiles (of either size) are exact
+    mirrors."""
     work = wl.make_custom(16, c_in, n, n_groups=G, dtype="bf16", seed=c_in + 3 * n, w_dist="t3", x_dist="lognormal")
     print("case full Hessian syrk G=%d c_in=%d N=%d pad=%d" % (G, c_in, n, pad), flush=True)
     hbuf = torch.full((G, c_in, c_in + pad), float("nan"), dtype=torch.float32, device=DEV)
@@ -128,8 +131,8 @@ def test_full_hessian_syrk(lh, G, c_in, n, pad):
     lh.lh_full_hessian(work.x.to(DEV), h=hv)
     hf = hv.cpu().numpy()
     x_np = wl.np_bits(work.x)
-    tile = np.arange(c_in) // 256
-    off = tile[:, None] != tile[None, :]
+    t256, t192 = np.arange(c_in) // 256, np.arange(c_in) // 192
+    off = (t256[:, None] != t256[None, :]) & (t192[:, None] != t192[None, :])
     for g in range(G):
         assert np.isfinite(hf[g]).all()
         np.testing.assert_array_equal(hf[g][off], hf[g].T[off])
