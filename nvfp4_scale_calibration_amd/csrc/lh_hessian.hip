@@ -686,6 +686,13 @@ ProloguePlan prologue_plan(int64_t c_in, int64_t n_tok, int64_t n_groups, int64_
   const int64_t threads = 64 * q.hess.nw;  // the launch's workgroup size
   const int64_t n16 = w_elems / 8;  // at least this many 16-byte vectors (bf16); fp32 has twice as many
   int64_t per = (4096 / q.hess.nw + n_groups - 1) / n_groups;  // ~256 K threads over W
+  // When the Hessian's workgroups take several rounds of the chip, half as
+  // many shares leave more room to them (cache-cold, W + X read once: MoE
+  // 64 x 1024 x 2048 85 -> 72 us, 5120 x 17408 with 16384 tokens 129 -> 124
+  // us); when both kinds fit in one round (256 Hessian workgroups), halving
+  // makes that round uneven (12288 x 4096: 32 -> 36 us).
+  const int64_t resident = 256 * 32 / q.hess.nw;  // 256 CUs x 32 waves
+  if (n_groups * (c_in / 16) * q.hess.nsplit > resident) per = (per + 1) / 2;
   const int64_t need = (n16 + 4 * threads - 1) / (4 * threads);
   if (per > need) per = need;
   q.abs_per_group = per < 1 ? 1 : per;
