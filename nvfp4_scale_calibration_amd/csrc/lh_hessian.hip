@@ -115,11 +115,12 @@ __device__ __forceinline__ void hessian_cm_block(int64_t id, const T* __restrict
   __shared__ float red[kNW][256];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ch = lane & 15, kg = lane >> 4;
-  const int64_t wg = id;
-  const int64_t s = id % nsplit;
-  id /= nsplit;
-  const int64_t b = id % nb, grp = id / nb;
-  const int64_t t0 = s * chunk;
+  // the grid's workgroup ids, slices and blocks fit 32 bits: 32-bit division
+  const uint32_t wg = (uint32_t)id;
+  const uint32_t s = wg % (uint32_t)nsplit;
+  const uint32_t gbk = wg / (uint32_t)nsplit;
+  const int64_t b = gbk % (uint32_t)nb, grp = gbk / (uint32_t)nb;
+  const int64_t t0 = (int64_t)s * chunk;
   const int64_t t1 = min(n_tok, t0 + chunk);
   const T* row = x + grp * gstride + (16 * b + ch) * ld;
 
@@ -134,7 +135,13 @@ __device__ __forceinline__ void hessian_cm_block(int64_t id, const T* __restrict
   const int64_t K = (t1 - t0) / kR;
   if (K > 0) {
     const int64_t S = K * kNW;
-    int64_t q = wave + (wg * 17) % S;
+    int64_t q = wave;
+    if (S < (1 << 27)) {  // 17 (wg mod S) fits 32 bits
+      const uint32_t S32 = (uint32_t)S;
+      q += ((wg % S32) * 17u) % S32;
+    } else {
+      q += (int64_t)(((uint64_t)wg * 17u) % (uint64_t)S);
+    }
     if (q >= S) q -= S;
     const T* base = row + t0 + 16 * kg;
     const int64_t rel = t1 - t0 - 16 * kg;  // the slice's end, relative to base
