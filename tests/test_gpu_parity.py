@@ -92,6 +92,7 @@ def test_linear_256_end_to_end(lh):
     (4, 64, 64, 1000, "f32", "channel"),
     (1, 3, 2064, 2500, "bf16", "channel"),
     (2, 70, 112, 513, "bf16", "token"),
+    (1, 5, 48, 3 * 1024 + 37, "f32", "channel"),
 ])
 def test_ragged_shapes(lh, G, c_out, c_in, n, dtype, layout):
     work = wl.make_custom(c_out, c_in, n, n_groups=G, dtype=dtype, seed=c_out + n, w_dist="t3",
@@ -99,12 +100,15 @@ def test_ragged_shapes(lh, G, c_out, c_in, n, dtype, layout):
     check_all(lh, work, layout=layout)
 
 
-@pytest.mark.parametrize("c_in,n", [(256, 8192 + 77), (9600, 2048 + 77)])
+@pytest.mark.parametrize("c_in,n", [(256, 8192 + 77), (9600, 2048 + 77), (48, 3 * 1024 + 50)])
 def test_hessian_split_vs_one_pass_and_determinism(lh, c_in, n):
     """16 blocks over 8269 tokens: the channel-major plan keeps one slice
     (16-wave workgroups, all resident at once), the token-major one splits;
     600 blocks over 2125 tokens: the channel-major plan splits the tokens in
-    two slices of 16-wave workgroups, the second one ragged."""
+    two slices of 16-wave workgroups, the second one ragged; 3 blocks over
+    3122 tokens: three full steps (an odd count, so the walk ends on one
+    slab) from starts 0, 17 and 34 of 48 slabs (the walk wraps), then a
+    ragged rest of 50 tokens."""
     work = wl.make_custom(8, c_in, n, dtype="bf16", seed=5, x_dist="lognormal")
     xd = work.x.to(DEV)
     assert lh.lh_hessian_workspace_bytes(c_in, n, 1) > 0
