@@ -637,10 +637,10 @@ hipError_t launch_hessian_ragged(const HessianRaggedArgs& a, hipStream_t stream)
 // Channel-major plan: waves per workgroup and token slices per block,
 // measured on MI355X with the caches flushed by a 1 GiB read (bf16, kernel
 // plus the slice sum):
-//   X 17408 x 16384: 16 waves, 4 slices 102 us; 4 waves, 8 slices 112 us;
-//   16 waves, 1 slice 141 us (1088 workgroups of 16 waves: two rounds and
-//   a thin third);
-//   X 4096 x 4096: 16 waves, 1 slice 10.6 us; 4 waves, 4 slices 12.4 us;
+//   X 17408 x 16384: 16 waves, 4 slices 100-102 us; 2, 3, 5, 6, 8 slices
+//   103-108 us; 1 slice 104 us (1088 workgroups of 16 waves: two rounds and
+//   a thin third); 4 waves, 8 slices 112 us;
+//   X 4096 x 4096: 16 waves, 1 slice 10.2 us; 4 waves, 4 slices 12.4 us;
 //   64 x 2048 x 512: 8 waves 26.0 us, 4 waves 26.5 us, 16 waves 34.8 us
 //   (half of them without a slab).
 // So: the most waves (up to 16) that each still get a 64-token slab; one
