@@ -17,3 +17,14 @@ def orc():
     import oracle
     oracle._load()
     return oracle
+
+
+def pytest_terminal_summary(terminalreporter):
+    """The parity cases' statistics (indices that differ from the oracle's,
+    near ties, blocks passing only through the fp32 allowance, worst
+    deviations), also when pytest captured the tests' output."""
+    import parity
+    if parity.SUMMARY:
+        terminalreporter.section("parity against the oracle")
+        for line in parity.SUMMARY:
+            terminalreporter.write_line(line)

@@ -32,6 +32,15 @@ import numpy as np
 
 import oracle
 
+# One line per parity case (what was compared and how it came out); the test
+# session prints them in its summary, so a quiet run's log carries them too.
+SUMMARY: list = []
+
+
+def note(line: str) -> None:
+    SUMMARY.append(line)
+
+
 H_RTOL = 1e-3
 TIE_RTOL = 1e-5
 ERR_RTOL = 1e-4

@@ -77,6 +77,7 @@ def test_linear_256_end_to_end(lh):
     work = wl.make(1)
     got, stats = check_all(lh, work, strict=True)
     assert stats["n"] == 4096
+    parity.note("%s (separate calls, every block): %s" % (work.name, stats))
     # end to end, each side with its own H: report the index agreement
     _, h32 = oracle.hessian(wl.np_bits(work.x), 256, 128)
     res = oracle.sweep(wl.np_bits(work.w), h32, got["amax"], 256, 256)
@@ -387,6 +388,8 @@ def test_full_size_benchmarked_pair_every_block(lh, n):
                                         got["bam"], work.name, strict=True)
     parity.fake_quant_against_oracle(w_np, got["idx"], got["amax"], c_out, c_in, G, sel, got["fq"], work.name)
     print("  ok %s: every block; Hessian worst normalised deviation %.3g; %s" % (work.name, hdev, stats), flush=True)
+    parity.note("%s (benchmarked pair, every block): Hessian worst |dH|/sqrt(Hii Hjj) %.3g; %s" % (work.name, hdev,
+                                                                                                 stats))
 
 
 def test_sweep_waves_walking_several_chunks_with_a_partial_last_chunk(lh):
