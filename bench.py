@@ -59,6 +59,9 @@ def parse():
                    help="skip the cold-cache Hessian timings and the adjacent parts")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 256 MiB device copy 5 times (HBM counter calibration)")
+    p.add_argument("--summarize-profiles", metavar="DIR",
+                   help="only turn the rocprofv3 runs under DIR into profiles/counters.json and the summaries")
+    p.add_argument("--profile-workloads", default="5,1,2,3,4", help="workloads to summarise from DIR")
     return p.parse_args()
 
 
@@ -448,10 +451,293 @@ def cpu_baseline(work, budget_s: float) -> dict:
     }
 
 
+# ---------------------------------------------------------------------------
+# Profile summaries: rocprofv3 CSVs -> profiles/counters.json and
+# profiles/pipeline_<workload>.md (python3 bench.py --summarize-profiles DIR).
+# DIR holds the runs named in the summaries' command lists: trace_w<n>,
+# valu_w<n>, ops_w<n>, fetch_w<n>, write_w<n> (each with the run's log
+# <run>.log beside it), copy_fetch, copy_write and, for the adjacent parts,
+# trace_extras_w2.
+# ---------------------------------------------------------------------------
+PROF_VALU = ("SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_VALU2 SQ_THREAD_CYCLES_VALU SQ_WAVES SQ_BUSY_CYCLES "
+             "GRBM_GUI_ACTIVE")
+PROF_OPS = ("SQ_INSTS_VALU_FMA_F32 SQ_INSTS_VALU_ADD_F32 SQ_INSTS_VALU_MUL_F32 SQ_INSTS_VALU_TRANS_F32 "
+            "SQ_INSTS_VALU_CVT SQ_INSTS_SALU SQ_INSTS_LDS GRBM_GUI_ACTIVE")
+
+
+def _short_kernel_name(name: str) -> str:
+    """A demangled kernel name without 'void ', the library's namespace and
+    the parameter list."""
+    s = name[5:] if name.startswith("void ") else name
+    s = s.replace("lh::(anonymous namespace)::", "")
+    if s.endswith(")"):
+        depth = 0
+        for i in range(len(s) - 1, -1, -1):
+            if s[i] == ")":
+                depth += 1
+            elif s[i] == "(":
+                depth -= 1
+                if depth == 0:
+                    return s[:i]
+    return s
+
+
+def _one_file(d: str, pattern: str) -> str:
+    import glob
+    fs = glob.glob(os.path.join(d, pattern), recursive=True)
+    if len(fs) != 1:
+        raise SystemExit("expected one %s under %s, found %d" % (pattern, d, len(fs)))
+    return fs[0]
+
+
+def _counter_dispatches(d: str, run: str) -> dict:
+    """Dispatch id -> {name, grid, ns, counters} of one --pmc run."""
+    import csv
+    out = {}
+    with open(_one_file(d, run + "/**/pmc_counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            e = out.setdefault(int(r["Dispatch_Id"]), {
+                "name": _short_kernel_name(r["Kernel_Name"]), "grid": int(r["Grid_Size"]),
+                "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), "c": {}})
+            e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def _trace_rows(d: str, run: str) -> list:
+    import csv
+    rows = []
+    with open(_one_file(d, run + "/**/trace_kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            rows.append({"name": _short_kernel_name(r["Kernel_Name"]),
+                         "grid": int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]),
+                         "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+    return rows
+
+
+def _trace_stats(d: str, run: str) -> list:
+    import csv
+    out = []
+    with open(_one_file(d, run + "/**/trace_kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            out.append((_short_kernel_name(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                        float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    return out
+
+
+def _copy_scales(d: str) -> dict:
+    """FETCH_SIZE / WRITE_SIZE of a plain 256 MiB device copy -> bytes per counter KiB."""
+    import statistics
+
+    def kib(run, cname):
+        v = [e["c"][cname] for e in _counter_dispatches(d, run).values() if e["name"] == "__amd_rocclr_copyBuffer"]
+        return statistics.median(v)
+    n = 256 << 20
+    fk, wk = kib("copy_fetch", "FETCH_SIZE"), kib("copy_write", "WRITE_SIZE")
+    return {"calibration": "plain 256 MiB device copy (python3 bench.py --copy-probe): FETCH_SIZE %d KiB, "
+                           "WRITE_SIZE %d KiB per launch" % (round(fk), round(wk)),
+            "fetch_scale": n / (fk * 1024), "write_scale": n / (wk * 1024)}
+
+
+def summarize_workload(d: str, w: int, data: dict, src_hash: str) -> None:
+    """counters.json entries (sweep, prologue, Hessian) and the pipeline
+    summary of named workload w.  The sweep's counters are those of the
+    median-duration dispatch of the workload's grid, leaving out the
+    kernel's first dispatch (its GRBM_GUI_ACTIVE spans more than the
+    dispatch); traffic is the mean over the workload's dispatches, scaled by
+    the copy calibration."""
+    import statistics
+    from collections import Counter
+    valu, ops = _counter_dispatches(d, "valu_w%d" % w), _counter_dispatches(d, "ops_w%d" % w)
+    fetch, write = _counter_dispatches(d, "fetch_w%d" % w), _counter_dispatches(d, "write_w%d" % w)
+    names = Counter(e["name"] for e in valu.values())
+    sweep = [n for n in names if n.startswith("sweep_rows") and n.endswith("true, true, true>")]
+    if len(sweep) != 1:
+        raise SystemExit("workload %d: expected one fused sweep kernel, found %r" % (w, sweep))
+    sweep = sweep[0]
+    grids = {}
+    for e in valu.values():
+        grids.setdefault(e["name"], Counter())[e["grid"]] += 1
+
+    def sel(dd, name):
+        g = grids[name].most_common(1)[0][0]
+        return [e for e in dd.values() if e["name"] == name and e["grid"] == g]
+
+    def median_dispatch(dd, name):
+        first = min(k for k, v in dd.items() if v["name"] == name)
+        es = sorted([e for e in sel(dd, name) if e is not dd[first]], key=lambda e: e["ns"])
+        e = es[len(es) // 2]
+        if "GRBM_GUI_ACTIVE" in e["c"] and e["ns"] > 100000 and e["c"]["GRBM_GUI_ACTIVE"] / N_XCD / e["ns"] >= 2.45:
+            raise SystemExit("workload %d: implausible dispatch clock in %s" % (w, name))
+        return e, [k for k, v in dd.items() if v is e][0], len(es)
+
+    ev, vid, nv = median_dispatch(valu, sweep)
+    eo, oid, _ = median_dispatch(ops, sweep)
+    tr = _trace_rows(d, "trace_w%d" % w)
+    g_sweep = grids[sweep].most_common(1)[0][0]
+    tsw = [r["ns"] for r in tr if r["name"] == sweep and r["grid"] == g_sweep]
+    cp = data["copy"]
+
+    def traffic(kernels):
+        rd = sum(statistics.mean([e["c"]["FETCH_SIZE"] for e in sel(fetch, k)]) for k in kernels)
+        wr = sum(statistics.mean([e["c"]["WRITE_SIZE"] for e in sel(write, k)]) for k in kernels)
+        return rd * 1024 * cp["fetch_scale"], wr * 1024 * cp["write_scale"]
+
+    def trace_avg(kernels):
+        tot = 0.0
+        for k in kernels:
+            g = grids[k].most_common(1)[0][0]
+            tot += statistics.mean([r["ns"] for r in tr if r["name"] == k and r["grid"] == g])
+        return tot
+
+    with open(os.path.join(d, "valu_w%d.log" % w)) as f:
+        cfg = json.loads([l for l in f if l.startswith("{")][0])["config"]
+    wl, blocks = cfg["name"], cfg["blocks"]
+    # the calls' kernels: the prologue's certificates come from the lane
+    # pre-pass above 2048 input blocks
+    pro_k = [n for n in names if n.startswith("prologue_cm_kernel")] + ["finalize_certify_kernel"]
+    if cfg["n_groups"] * cfg["c_in"] // 16 > 2048:
+        pro_k.append("sweep_certificate_lane_kernel")
+    hes_k = [n for n in names if n.startswith("hessian_cm_kernel")]
+    if "hessian_finalize_kernel" in names:
+        hes_k.append("hessian_finalize_kernel")
+    kern = data["kernels"]
+    rd, wr = traffic([sweep])
+    vc = dict(ev["c"]); vc.update(dispatch_id=vid, dispatch_ns=ev["ns"], n_dispatches=nv)
+    oc = dict(eo["c"]); oc.update(dispatch_id=oid, dispatch_ns=eo["ns"])
+    kern["sweep/%s" % wl] = {"avg_ns": statistics.mean(tsw), "bytes_per_launch": rd + wr, "kernel": sweep,
+                             "ops": oc, "read_bytes": rd, "source_hash": src_hash, "trace_dispatches": len(tsw),
+                             "valu": vc, "write_bytes": wr}
+    prd, pwr = traffic(pro_k)
+    kern["prologue/%s" % wl] = {"avg_ns": trace_avg(pro_k), "bytes_per_launch": prd + pwr, "kernels": pro_k,
+                                "read_bytes": prd, "source_hash": src_hash, "write_bytes": pwr}
+    hrd, hwr = traffic(hes_k)
+    hns = sum(statistics.mean([e["ns"] for e in sel(fetch, k)]) for k in hes_k)
+    kern["hessian/%s" % wl] = {"avg_ns_counter_run": hns, "bytes_per_launch": hrd + hwr, "kernels": hes_k,
+                               "read_bytes": hrd, "source_hash": src_hash, "write_bytes": hwr}
+
+    tr_cmd = ("python3 bench.py" if w == 5 else
+              "python3 bench.py --workload %d --steps 20 --warmup 3 --no-cpu-baseline --no-extras" % w)
+    short_cmd = "python3 bench.py --workload %d --steps 2 --warmup 1 --no-cpu-baseline --no-extras" % w
+    L = ["# Kernel profile: the benchmark step on workload %s (MI355X)\n" % wl,
+         "Commands (on the GPU box, from the repository root; each profiler run is started from `/tmp` with "
+         "`TMPDIR=/tmp`, for the profiler's files, and `-d` pointing back under `gpurun_out/prof/`):\n",
+         "```",
+         "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/trace_w%d -o trace -- %s" % (w, tr_cmd),
+         "rocprofv3 --kernel-trace --pmc %s --output-format csv -d gpurun_out/prof/valu_w%d -o pmc -- %s"
+         % (PROF_VALU, w, short_cmd),
+         "rocprofv3 --kernel-trace --pmc %s --output-format csv -d gpurun_out/prof/ops_w%d -o pmc -- %s"
+         % (PROF_OPS, w, short_cmd),
+         "rocprofv3 --kernel-trace --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof/fetch_w%d -o pmc -- %s"
+         % (w, short_cmd),
+         "rocprofv3 --kernel-trace --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof/write_w%d -o pmc -- %s"
+         % (w, short_cmd),
+         "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof/copy_fetch -o pmc -- python3 bench.py "
+         "--copy-probe",
+         "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof/copy_write -o pmc -- python3 bench.py "
+         "--copy-probe",
+         "python3 bench.py --summarize-profiles gpurun_out/prof   # this summary and profiles/counters.json",
+         "```\n",
+         "kernel source hash: `%s`\n" % src_hash,
+         "| kernel | calls | avg us | min us | max us | % time |",
+         "|---|---|---|---|---|---|"]
+    for n, c, a, mn, mx, pc in _trace_stats(d, "trace_w%d" % w):
+        L.append("| %s | %d | %.1f | %.1f | %.1f | %.1f |" % (n, c, a, mn, mx, pc))
+    L.append("")
+    L.append("Benchmarked sweep launch (`%s`): %d dispatches of this workload in the trace run "
+             "(matched by grid size), average %.1f us.\n" % (sweep, len(tsw), statistics.mean(tsw) / 1e3))
+    c = ev["c"]
+    L.append("VALU counters of one dispatch (id %d, %.1f us under the counter pass; median of %d):\n"
+             % (vid, ev["ns"] / 1e3, nv))
+    L += ["| counter | value |", "|---|---|"]
+    L += ["| %s | %d |" % (k, c[k]) for k in PROF_VALU.split()]
+    L.append("")
+    L.append("Instruction mix of one dispatch (id %d):\n" % oid)
+    L += ["| counter | value |", "|---|---|"]
+    L += ["| %s | %d |" % (k, eo["c"][k]) for k in PROF_OPS.split()[:-1]]
+    L.append("")
+    cyc = c["GRBM_GUI_ACTIVE"] / N_XCD
+    busy = c["SQ_ACTIVE_INST_VALU"] - c["SQ_ACTIVE_INST_VALU2"]
+    avg_s = statistics.mean(tsw) / 1e9
+    flop = 64.0 * (2 * eo["c"]["SQ_INSTS_VALU_FMA_F32"] + eo["c"]["SQ_INSTS_VALU_MUL_F32"]
+                   + eo["c"]["SQ_INSTS_VALU_ADD_F32"])
+    L += ["Derived (one dispatch):\n",
+          "* dispatch cycles = GRBM_GUI_ACTIVE / 8 XCDs = %d (clock %.2f GHz over the dispatch)" % (cyc, cyc / ev["ns"]),
+          "* VALU-busy SIMD quad-cycles = SQ_ACTIVE_INST_VALU - SQ_ACTIVE_INST_VALU2 = %d; **VALU busy = %.3f** of "
+          "1024 SIMDs x %d quad-cycles" % (busy, busy / (N_SIMD * cyc / 4), cyc / 4),
+          "* at the published 2.4 GHz over the trace average: %.3f of 614.4 G quad-cycles/s"
+          % (busy / avg_s / (VALU_QUAD_PEAK_G * 1e9)),
+          "* wave64 VALU instructions per busy quad-cycle = %.3f (gfx950 dual issue: %.1f%% of busy quad-cycles issue two)"
+          % (c["SQ_INSTS_VALU"] / busy, 100 * c["SQ_ACTIVE_INST_VALU2"] / busy),
+          "* lanes active per VALU instruction = %.4f" % (c["SQ_THREAD_CYCLES_VALU"] / (64.0 * c["SQ_ACTIVE_INST_VALU"])),
+          "* VALU instructions per block = %.1f (per lane-row block; 126 x 207 = 26,082 for an exhaustive evaluation)"
+          % (c["SQ_INSTS_VALU"] * 64 / blocks),
+          "* executed fp32 arithmetic = %.1f GFLOP per launch, %.1f TFLOP/s over the trace average = %.3f of the "
+          "78.6 TFLOP/s non-packed fp32 peak" % (flop / 1e9, flop / avg_s / 1e12, flop / avg_s / 1e12 / FP32_NONPACKED_TFLOPS),
+          "* dense-equivalent rate (68,544 flop per block, not executed work) = %.0f TFLOP/s\n"
+          % (SWEEP_FLOP_PER_BLOCK * blocks / avg_s / 1e12),
+          "HBM traffic (counter KiB x 1024 x the copy factor: FETCH_SIZE x %.3f, WRITE_SIZE x %.3f; %s):\n"
+          % (cp["fetch_scale"], cp["write_scale"], cp["calibration"]),
+          "| call | kernels | avg us | read MB | written MB |",
+          "|---|---|---|---|---|"]
+    e1, e2, e3 = kern["sweep/%s" % wl], kern["prologue/%s" % wl], kern["hessian/%s" % wl]
+    L.append("| lh_calibrate_sweep | %s | %.1f | %.1f | %.1f |"
+             % (sweep, e1["avg_ns"] / 1e3, e1["read_bytes"] / 1e6, e1["write_bytes"] / 1e6))
+    L.append("| lh_calibrate_prologue | %s | %.1f | %.1f | %.1f |"
+             % (" + ".join(pro_k), e2["avg_ns"] / 1e3, e2["read_bytes"] / 1e6, e2["write_bytes"] / 1e6))
+    L.append("| lh_accumulate_hessian | %s | %.1f (counter run) | %.1f | %.1f |"
+             % (" + ".join(hes_k), e3["avg_ns_counter_run"] / 1e3, e3["read_bytes"] / 1e6, e3["write_bytes"] / 1e6))
+    with open(os.path.join(PROFILES, "pipeline_%s.md" % wl), "w") as f:
+        f.write("\n".join(L) + "\n")
+
+
+def summarize_extras(d: str, src_hash: str) -> None:
+    """profiles/extras_dense-4096.md from the trace of the adjacent parts."""
+    L = ["# Kernel profile: adjacent parts on workload dense-4096 (MI355X)\n",
+         "Ragged Hessian of the MoE capture (N1), the scale rules (N2), the full Hessian,\n"
+         "output error and W/s histogram (N3), GPTQ factorisation and sweep (N4), plus\n"
+         "the hot path itself, as bench.py runs them (its extras).\n",
+         "```",
+         "# on the GPU box, from the repository root; the profiler run is started from /tmp with TMPDIR=/tmp",
+         "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/trace_extras_w2 -o trace -- python3 "
+         "bench.py --workload 2 --steps 3 --warmup 1 --no-cpu-baseline --cold \"\"",
+         "python3 bench.py --summarize-profiles gpurun_out/prof   # this summary",
+         "```\n",
+         "kernel source hash: `%s` (lh_dense.hip is not part of it)\n" % src_hash,
+         "| kernel | calls | avg us | min us | max us | % time |",
+         "|---|---|---|---|---|---|"]
+    for n, c, a, mn, mx, pc in _trace_stats(d, "trace_extras_w2"):
+        L.append("| %s | %d | %.1f | %.1f | %.1f | %.1f |" % (n, c, a, mn, mx, pc))
+    with open(os.path.join(PROFILES, "extras_dense-4096.md"), "w") as f:
+        f.write("\n".join(L) + "\n")
+
+
+def summarize_profiles(d: str, workloads: list) -> None:
+    data = {"kernels": {}}
+    if os.path.exists(COUNTERS):
+        with open(COUNTERS) as f:
+            data = json.load(f)
+    h = kernel_source_hash()
+    if os.path.isdir(os.path.join(d, "copy_fetch")):
+        data["copy"] = _copy_scales(d)
+    if "copy" not in data:
+        raise SystemExit("no copy calibration: profile bench.py --copy-probe first")
+    for w in workloads:
+        summarize_workload(d, w, data, h)
+    if os.path.isdir(os.path.join(d, "trace_extras_w2")):
+        summarize_extras(d, h)
+    data["kernels"] = dict(sorted(data["kernels"].items()))
+    with open(COUNTERS, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+
+
 def main():
     args = parse()
     if args.copy_probe:
         copy_probe()
+        return
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, [int(v) for v in args.profile_workloads.split(",") if v])
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
