@@ -50,8 +50,14 @@ __device__ __forceinline__ void load16(const T* p, float (&w)[16]) {
 }
 
 // One thread per 16-weight block.  Outputs are dense and each optional; the
-// cast and the stores are nvfp4_cast_block / nvfp4_emit_block, which the
-// fused sweep uses too.  s == 0 (amax 0) gives x = 0 for every weight.
+// cast is nvfp4_cast_block, which the fused sweep uses too.  s == 0 (amax 0)
+// gives x = 0 for every weight.  The workgroup's fp32 Q (256 blocks, 64
+// contiguous bytes each) leaves through LDS, so that every store instruction
+// writes 1 KiB of consecutive bytes: written from each thread, a wave's store
+// put 16 of every 64 bytes over 4 KiB.  The nibbles and codes are
+// consecutive per wave as they are.  In LDS the four 16-byte quarters of
+// block i sit in the order rotated by i/2, so neither the writes (64-byte
+// stride) nor the reads (16-byte stride) meet a bank twice in 8 lanes.
 template <typename T, bool kVec>
 __global__ __launch_bounds__(kThreads) void fake_quant_kernel(const T* __restrict__ wt, int64_t c_out,
                                                               int64_t ld_w, int64_t gstride_w, int64_t nb,
@@ -61,20 +67,41 @@ __global__ __launch_bounds__(kThreads) void fake_quant_kernel(const T* __restric
                                                               uint8_t* __restrict__ packed,
                                                               uint8_t* __restrict__ codes,
                                                               float* __restrict__ gscale, int64_t n_groups) {
-  const int64_t f = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  __shared__ float4 stage[kThreads * 4];
+  const int tid = threadIdx.x;
+  const int64_t f0 = (int64_t)blockIdx.x * kThreads;
+  const int64_t f = f0 + tid;
   if (gscale && f < n_groups) gscale[f] = amax[f] / kAmaxDivisor;  // S_g, written once per group
-  if (f >= total) return;
-  const int64_t b = f % nb;
-  const int64_t rg = f / nb;  // grp * c_out + row
-  const int64_t grp = rg / c_out, row = rg - grp * c_out;
-  const int k = idx[f];
-  const float Sg = amax[grp] / kAmaxDivisor;
-  const float s = e4m3_candidate(k) * Sg;
-  float w[16];
-  load16<T, kVec>(wt + grp * gstride_w + row * ld_w + 16 * b, w);
-  uint32_t pk[2];
-  nvfp4_cast_block(w, s, pk);
-  nvfp4_emit_block(pk, s, k, rg, b, nb, wq, packed, codes);
+  if (f < total) {
+    const int64_t b = f % nb;
+    const int64_t rg = f / nb;  // grp * c_out + row
+    const int64_t grp = rg / c_out, row = rg - grp * c_out;
+    const int k = idx[f];
+    const float Sg = amax[grp] / kAmaxDivisor;
+    const float s = e4m3_candidate(k) * Sg;
+    float w[16];
+    load16<T, kVec>(wt + grp * gstride_w + row * ld_w + 16 * b, w);
+    uint32_t pk[2];
+    nvfp4_cast_block(w, s, pk);
+    nvfp4_emit_at(pk, s, k, f, nullptr, packed, codes);  // block f = rg * nb + b: nibbles and code
+    if (wq) {
+      float q[16];
+      nvfp4_decode_block(pk, s, q);
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        stage[4 * tid + ((qd + (tid >> 1)) & 3)] = make_float4(q[4 * qd], q[4 * qd + 1], q[4 * qd + 2], q[4 * qd + 3]);
+    }
+  }
+  if (wq == nullptr) return;  // the same for every thread
+  __syncthreads();
+  const int64_t live = total - f0 < kThreads ? total - f0 : kThreads;  // this workgroup's blocks
+  float4* dst = reinterpret_cast<float4*>(wq + 16 * f0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = tid + kThreads * r;  // 16-byte piece i of the workgroup's Q
+    const int blk = i >> 2;
+    if (blk < live) dst[i] = stage[4 * blk + (((i & 3) + (blk >> 1)) & 3)];
+  }
 }
 
 __global__ void global_scale_kernel(const float* __restrict__ amax, float* __restrict__ out, int64_t n) {
