@@ -593,26 +593,41 @@ __global__ __launch_bounds__(kThreads) void histogram_kernel(const T* __restrict
                                                              const float* __restrict__ amax, int n_bins,
                                                              float bins_per_unit,
                                                              unsigned long long* __restrict__ counts) {
+  // A thread takes a 16-weight block at a time (one index and one scale
+  // per block, no index division per weight), and each wave
+  // counts into its own copy of the bins when four copies fit: the weights
+  // of a layer crowd into a few bins, so one shared copy serialised the LDS
+  // atomics.  Counts are integers: the result does not depend on the order.
   __shared__ unsigned int local[kMaxBins + 1];
-  for (int i = threadIdx.x; i <= n_bins; i += kThreads) local[i] = 0u;
+  const int nb1 = n_bins + 1;
+  const int copies = (4 * nb1 <= kMaxBins + 1) ? 4 : 1;
+  for (int i = threadIdx.x; i < copies * nb1; i += kThreads) local[i] = 0u;
   __syncthreads();
+  unsigned int* const mine = local + (copies == 4 ? (threadIdx.x >> 6) * nb1 : 0);
   const int64_t grp = blockIdx.y;
   const float Sg = amax[grp] / kAmaxDivisor;
   const int64_t nb = c_in / 16;
-  const int64_t total = c_out * c_in;
-  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total; e += (int64_t)gridDim.x * kThreads) {
-    const int64_t r = e / c_in, c = e - r * c_in;
-    const int k = idx[(grp * c_out + r) * nb + c / 16];
+  const int64_t nblk = c_out * nb;
+  for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < nblk; q += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = q / nb, bb = q - r * nb;
+    const int k = idx[grp * nblk + q];
     const float s = e4m3_candidate(k) * Sg;
-    const float a = fabsf(load_as_f32<T>(w, grp * gstride_w + r * ld_w + c));
-    const float x = (s == 0.0f) ? 0.0f : a / s;
-    const float y = x * bins_per_unit;
-    const int bin = (y >= (float)n_bins) ? n_bins : (int)floorf(y);
-    atomicAdd(&local[bin], 1u);
+    const int64_t base = grp * gstride_w + r * ld_w + 16 * bb;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float a = fabsf(load_as_f32<T>(w, base + i));
+      const float x = (s == 0.0f) ? 0.0f : a / s;
+      const float y = x * bins_per_unit;
+      const int bin = (y >= (float)n_bins) ? n_bins : (int)floorf(y);
+      atomicAdd(&mine[bin], 1u);
+    }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i <= n_bins; i += kThreads)
-    if (local[i]) atomicAdd(&counts[grp * (n_bins + 1) + i], (unsigned long long)local[i]);
+  for (int i = threadIdx.x; i < nb1; i += kThreads) {
+    unsigned int v = local[i];
+    for (int c = 1; c < copies; ++c) v += local[c * nb1 + i];
+    if (v) atomicAdd(&counts[grp * nb1 + i], (unsigned long long)v);
+  }
 }
 
 
