@@ -461,6 +461,16 @@ __global__ __launch_bounds__(kThreads) void hessian_ragged_finalize_kernel(
   const int nblk = (int)min((int64_t)kFinBlocks, nb - b0);
   const int64_t sstride = n_groups * nb * 256;
   const float* p = ws + (grp * nb + b0) * 256 + e;
+  float* hp = h + grp * h_gstride + b0 * 256 + e;
+  // the running mean's inputs (old count and old H) are loaded with the
+  // first slice, not after the sum
+  int64_t n_old = 0;
+  float hold[kFinBlocks];
+  if (counts != nullptr) {
+    n_old = (int64_t)(((uint64_t)snap[2 * grp + 1] << 32) | snap[2 * grp]);
+#pragma unroll
+    for (int i = 0; i < kFinBlocks; ++i) hold[i] = i < nblk ? hp[i * 256] : 0.0f;
+  }
   float v[kFinBlocks];
 #pragma unroll
   for (int i = 0; i < kFinBlocks; ++i) v[i] = i < nblk ? p[i * 256] : 0.0f;
@@ -471,13 +481,10 @@ __global__ __launch_bounds__(kThreads) void hessian_ragged_finalize_kernel(
 #pragma unroll
     for (int i = 0; i < kFinBlocks; ++i) v[i] += t[i];
   }
-  int64_t n_old = 0;
-  if (counts != nullptr) n_old = (int64_t)(((uint64_t)snap[2 * grp + 1] << 32) | snap[2 * grp]);
-  float* hp = h + grp * h_gstride + b0 * 256 + e;
 #pragma unroll
   for (int i = 0; i < kFinBlocks; ++i) {
     if (i >= nblk) break;
-    hp[i * 256] = counts != nullptr ? ((float)n_old * hp[i * 256] + v[i]) / (float)(n_old + n_g)
+    hp[i * 256] = counts != nullptr ? ((float)n_old * hold[i] + v[i]) / (float)(n_old + n_g)
                                     : v[i] / (float)n_g;
   }
   if (counts != nullptr && c == 0 && e == 0) counts[grp] = n_old + n_g;
