@@ -1749,6 +1749,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(int rule, const T* __r
   const float g = amax[grp];
   const float Sg = g / kAmaxDivisor;
   const int e_g = (Sg > 0.0f && Sg <= 0x1p127f) ? ilogbf(Sg) : 0;
+  const bool fast = (Sg >= 0x1p-117f) && (Sg <= 0x1p127f);
 
   // each row's weights are loaded while the previous row is evaluated
   // (row0 < rows_step <= c_out; past the last row the last row is loaded again)
@@ -1767,6 +1768,19 @@ __global__ __launch_bounds__(kThreads) void select_kernel(int rule, const T* __r
     uint64_t mask[2];
     rule_mask(rule, a, Sg, mask);
     Best best{INFINITY, kCandidates};
+    // In the sweep's fast range (normal candidate scales) each candidate is
+    // evaluated with the sweep's own arithmetic: weights in units of 2^e, the
+    // quotient by sigma = mu S_g of its mantissa class (reciprocal and two
+    // fma), the scaled hardware cast at 2^j; these give the definition's
+    // bits, as the sweep does (eval_direct: an IEEE division and a software
+    // rounding per weight, kept for subnormal candidate scales).
+    float ws[16];
+    const float Su = ldexpf(Sg, -e);
+    if (fast) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ws[i] = ldexpf(w[i], -e);
+    }
+    uint32_t pk[2] = {0u, 0u};
     // ascending candidate order; lanes leave the loop when their mask is empty
     while ((mask[0] | mask[1]) != 0) {
       int k;
@@ -1777,7 +1791,18 @@ __global__ __launch_bounds__(kThreads) void select_kernel(int rule, const T* __r
         k = 64 + __builtin_ctzll(mask[1]);
         mask[1] &= mask[1] - 1;
       }
-      eval_direct<kMse>(best, k, Sg, e, w, diag, sym);
+      if (fast) {
+        int m, j;
+        candidate_class(k, m, j);
+        const float sigma = (1.0f + 0.125f * (float)m) * Su;
+        const float rs = 1.0f / sigma;
+        float p[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p[i] = div_rn(ws[i], sigma, rs);
+        eval_scaled<kMse>(best, k, j, sigma, p, ws, diag, sym, pk);
+      } else {
+        eval_direct<kMse>(best, k, Sg, e, w, diag, sym);
+      }
     }
     const int k = best.k < kCandidates ? best.k : 0;  // NaN errors only
     const int64_t o = (grp * c_out + row) * nb + b;
