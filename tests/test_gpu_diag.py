@@ -171,3 +171,23 @@ def test_diagnostics_dense_4096_sampled(lh):
     print("  rows %s: full %s block-diagonal %s" % (orows[:4], e[:4], e_bd[orows][:4]), flush=True)
     counts = oracle.scaled_histogram(w_np, got["idx"][0], float(got["amax"][0]), work.c_out, c_in, 160, 20.0)
     np.testing.assert_array_equal(got["counts"][0].astype(np.uint64), counts)
+
+
+@pytest.mark.parametrize("n_bins,bins_per_unit", [(3000, 400.0), (1023, 150.0)])
+def test_histogram_many_bins(lh, n_bins, bins_per_unit):
+    """Bin counts too large for a copy of the bins per wave (one shared copy
+    per workgroup) and at the four-copy limit, against the oracle; two
+    groups, a ragged row count."""
+    work = wl.make_custom(70, 96, 8, n_groups=2, dtype="bf16", seed=17, w_dist="t3")
+    wd = work.w.to(DEV)
+    amax = lh.lh_absmax(wd)
+    h = torch.eye(16, device=DEV).expand(2, 6, 16, 16).contiguous()
+    idx, _, _ = lh.lh_scale_sweep(wd, h, amax)
+    counts = lh.lh_scaled_histogram(wd, idx, amax, n_bins=n_bins, bins_per_unit=bins_per_unit)
+    torch.cuda.synchronize()
+    w_np = wl.np_bits(work.w)
+    idx_np, amax_np, got = idx.cpu().numpy(), amax.cpu().numpy(), counts.cpu().numpy()
+    for g in range(2):
+        ref = oracle.scaled_histogram(w_np[g], idx_np[g], float(amax_np[g]), 70, 96, n_bins, bins_per_unit)
+        np.testing.assert_array_equal(got[g].astype(np.uint64), ref)
+        assert int(got[g].sum()) == 70 * 96
